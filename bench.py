@@ -1,0 +1,207 @@
+"""Benchmark: warm-map SubMConv3d on one MI355X.
+
+Workload (the pages' benchmark shape, LATO.2 MLX port page, "Fleet benchmark"): batch 1,
+128^3 grid, i.i.d. occupancy 10 %, Cin = Cout = 128, k=3, bf16 features and weights, fp32
+accumulation, neighbour map and plan built once before the timed region (warm).  A step is one
+SubMConv3d layer call as a user makes it (weights re-laid out + the conv kernel).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload iid128]
+                    [--out-dtype f32|bf16] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PAGES_MVOX_PER_S = 15.25   # M3 Ultra, 128^3, 128 ch, ~10 % occupancy, warm (context only)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix (256 CU x 2.4 GHz x 4096 FLOP/clk)
+METRIC = "SubMConv3d Mvox/s + % bf16 MFMA peak, 128^3 C=128 10% occ, warm map"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def mvox_per_s(n_sites: int, seconds: float) -> float:
+    """The pages' throughput unit: active sites per second, in millions."""
+    return n_sites / seconds / 1e6
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "submanifold_sparse_convolution_coord_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(kernel: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "conv_iid128_counters.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != digest or d.get("kernel") != kernel:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, m_nbr) -> dict:
+    """The CPU oracle as it stands (fp64 dictionary + per-voxel loop), warm: map prebuilt,
+    conv over every site of the same workload; median of three runs."""
+    import oracle
+    x = w.feats.float().numpy()
+    wt = w.layers[0].weight.float().numpy()
+    b = w.layers[0].bias.numpy()
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.conv(x, wt, b, m_nbr)
+        ts.append(time.perf_counter() - t0)
+        if sum(ts) > 30:
+            break
+    t = float(np.median(ts))
+    return {"value": round(mvox_per_s(w.n, t), 4), "unit": "Mvox/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"full workload, all {w.n} sites, warm (map prebuilt), fp64, "
+                      f"median of {len(ts)} runs of {t:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="iid128")
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path is a single-GPU "
+              "kernel and this build has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import submanifold_sparse_convolution_coord_amd as ssc
+    import workloads
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating workload {args.workload}")
+    w = workloads.make(args.workload)
+    layer = w.layers[0]
+    cin, cout = layer.cin, layer.cout
+    odt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
+    coords = torch.from_numpy(w.coords).to(dev)
+    x = w.feats.to(dev)
+    wt = layer.weight.to(dev)
+    bias = layer.bias.to(dev)
+    torch.cuda.synchronize()
+
+    # Cold path, timed on its own: neighbour map + plan (once per coordinate set).
+    cold = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        nbr = ssc.build_index(coords, w.batch, w.grid, check=False)
+        plan = ssc.build_plan(nbr)
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    pairs = int((nbr >= 0).sum().item())
+    log(f"[bench] n={w.n} valid_pairs={pairs} cold index+plan median {np.median(cold):.3f} ms")
+
+    out = torch.empty((w.n, cout), dtype=odt, device=dev)
+    for _ in range(args.warmup):
+        ssc.subm_conv3d(x, wt, bias, plan, odt, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        ssc.subm_conv3d(x, wt, bias, plan, odt, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] step {ms_step * 1e3:.1f} us (wall {t_wall / args.steps * 1e6:.1f} us)")
+
+    # Dominant kernel alone: the conv kernel with weights packed once (one launch per call),
+    # events on the stream it runs on (torch's current stream).
+    packed = ssc.pack_weights(wt)
+    for _ in range(args.warmup):
+        ssc.subm_conv3d_packed(x, packed, bias, plan, odt, out=out)
+    torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record()
+    for _ in range(args.steps):
+        ssc.subm_conv3d_packed(x, packed, bias, plan, odt, out=out)
+    k1.record()
+    torch.cuda.synchronize()
+    ms_kernel = k0.elapsed_time(k1) / args.steps
+    log(f"[bench] conv kernel {ms_kernel * 1e3:.1f} us per launch")
+
+    out_bytes = 4 if odt == torch.float32 else 2
+    bytes_alg = (w.n * cin * 2 + w.n * cout * out_bytes + 27 * cin * cout * 2 + 4 * pairs)
+    flops = 2.0 * pairs * cin * cout
+    achieved_gbs = bytes_alg / (ms_kernel * 1e-3) / 1e9
+    tflops_kernel = flops / (ms_kernel * 1e-3) / 1e12
+    tflops_step = flops / (ms_step * 1e-3) / 1e12
+    value = mvox_per_s(w.n, ms_step * 1e-3)
+    kname = f"k_conv_mfma<{cin},{cout}>"
+    digest = source_digest()
+    traffic = counted_traffic(kname, digest)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Mvox/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_MVOX_PER_S, 2) if args.workload == "iid128" else None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. occupancy, N(0,1) features, fan-in-scaled weights)",
+        "config": {"workload": f"{args.workload}: {w.description}", "n_sites": w.n,
+                   "valid_pairs": pairs, "cin": cin, "cout": cout,
+                   "out_dtype": args.out_dtype, "map": "warm (built once, outside the timing)",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": kname,
+                     "bytes_alg_per_launch": bytes_alg, "kernel_us": round(ms_kernel * 1e3, 2)},
+        "mfma": {"effective_tflops_kernel": round(tflops_kernel, 2),
+                 "effective_tflops_step": round(tflops_step, 2),
+                 "frac_bf16_peak_step": round(tflops_step / PEAK_BF16_TFLOPS, 5),
+                 "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": flops},
+        "cold_index_plan_ms": round(float(np.median(cold)), 4),
+        "source_digest": digest,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] CPU oracle baseline (map + conv on the host)")
+        m = oracle.build_map(w.coords, w.batch, w.grid)
+        res["cpu_baseline"] = cpu_baseline(w, m)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+/*
+ * ssc.h - C ABI of libssc.so: submanifold sparse 3x3x3 convolution (SubMConv3d, stride 1,
+ * output sites = input sites) over active voxel coordinates, for AMD MI355X (gfx950).
+ *
+ * The operation (as the pages define it):
+ *   - Every SparseConv3d of the TRELLIS.2-lineage sparse VAEs is built with stride 1 and no
+ *     padding and so runs as a submanifold convolution: outputs live exactly on the input
+ *     sites (LATO.2 MLX port page, "The scope, once measured").  k=3 and k=1 both occur
+ *     (same page, "Status").
+ *   - Cross-correlation: the tap at offset d reads the features of site c + d (same page,
+ *     "Correctness").
+ *   - Weights are [K^3, Cin, Cout] (Pixal3D MLX port README, "Status", the KRSC remap).
+ *   - The coordinate -> row map is built once per coordinate set and reused by every layer
+ *     on that set (LATO.2 page, "Fleet benchmark" version history: "cached device index";
+ *     trellis-mac article, gather-scatter flowchart, last step: cache the neighbour map per
+ *     tensor; Pixal3D README: the spatial cache).
+ *
+ * Conventions shared by every entry point:
+ *   - All array pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) unless
+ *     marked "host".  Arrays are contiguous and row-major.  The caller owns every buffer,
+ *     including outputs and workspaces; the library never allocates device memory and keeps
+ *     no mutable global state, so calls on different streams with different buffers are
+ *     independent.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued on it and
+ *     the call returns without waiting, except ssc_build_index with check != 0, which waits
+ *     for its own work to read two error counters back.
+ *   - Host-detectable argument errors return before anything is launched.  A failed launch
+ *     returns SSC_ERR_HIP.  On any error the contents of output buffers are unspecified.
+ *   - bf16 means IEEE-754 binary32 truncated to its upper 16 bits (bfloat16), passed as
+ *     uint16_t storage; feature, weight and output pointers must be 16-byte aligned.
+ *   - Taps are numbered t = 9*(dx+1) + 3*(dy+1) + (dz+1) for offsets dx,dy,dz in {-1,0,1};
+ *     the centre tap is t = 13.  (The pages do not fix an order; this is row-major over the
+ *     3x3x3 kernel, which is also how a [Cout,Cin,3,3,3] dense kernel flattens.)
+ */
+#ifndef SSC_H
+#define SSC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSC_OK = 0,
+  SSC_ERR_ARG = -1,          /* null pointer, negative size, bad enum, misaligned pointer    */
+  SSC_ERR_COORD_RANGE = -2,  /* a coordinate outside [0,batch) x [0,Gx) x [0,Gy) x [0,Gz)    */
+  SSC_ERR_DUPLICATE = -3,    /* two rows with the same (b, x, y, z)                            */
+  SSC_ERR_UNSUPPORTED = -4,  /* shape outside what the kernels handle (see each call)          */
+  SSC_ERR_WORKSPACE = -5,    /* workspace or plan buffer smaller than the *_bytes() figure     */
+  SSC_ERR_HIP = -6           /* a HIP runtime call failed                                      */
+} ssc_status;
+
+typedef enum { SSC_F32 = 0, SSC_BF16 = 1 } ssc_dtype;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int ssc_version(void);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* ssc_status_string(int status);
+
+/* ---------------------------------------------------------------------------------------
+ * Coordinate index (cold path, once per coordinate set)
+ * ------------------------------------------------------------------------------------- */
+
+/* Bytes of device workspace ssc_build_index needs for n sites (an open-addressing hash table
+ * of 2^ceil(log2(2n)) slots, at least 64, plus two counters). */
+size_t ssc_index_workspace_bytes(int64_t n);
+
+/* Neighbour map of n active sites (trellis-mac article, gather-scatter flowchart: "build a
+ * hash map of the active voxel coordinates", then gather per kernel offset).
+ *   coords     [n, 4] int32 rows (b, x, y, z), any order, no duplicates.
+ *   batch      number of batch entries; 1 <= batch <= 65535.
+ *   grid       host int32[3] = (Gx, Gy, Gz), each in [1, 65535].
+ *   nbr        [n, 27] int32 output: nbr[i][t] = row index (into coords) of the site at
+ *              (b, x+dx, y+dy, z+dz), or -1 when that voxel is inactive or outside the grid.
+ *              Sites in different batch entries are never neighbours.
+ *   workspace  >= ssc_index_workspace_bytes(n) bytes, 256-byte aligned, scratch only.
+ *   check      nonzero: wait for the kernels and return SSC_ERR_COORD_RANGE or
+ *              SSC_ERR_DUPLICATE if any row is out of range or repeated.  Zero: no wait; such
+ *              input then leaves nbr unspecified (never out-of-bounds memory access).
+ * n = 0 is valid and launches nothing. */
+ssc_status ssc_build_index(const int32_t* coords, int64_t n, int32_t batch, const int32_t* grid,
+                           int32_t* nbr, void* workspace, size_t workspace_bytes, int32_t check,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Warm plan (derived from the neighbour map once per coordinate set, reused by every layer)
+ * ------------------------------------------------------------------------------------- */
+
+/* Bytes of the plan buffer for n sites, and of the scratch workspace ssc_build_plan needs. */
+size_t ssc_plan_bytes(int64_t n);
+size_t ssc_plan_workspace_bytes(int64_t n);
+
+/* Reorders the sites for the convolution kernels and stores the neighbour rows in that order
+ * (the "prepared device index" the LATO.2 page caches per coordinate set).  The plan holds:
+ * the site order (rows sorted by their 26-bit mask of valid non-centre taps, so that 16-row
+ * blocks share which taps are present), each 16-row block's tap mask, and the neighbour rows
+ * tap-major in that order.  The plan depends only on nbr; it is valid for any features and
+ * weights and for every k=3 layer on the same coordinate set.
+ *   nbr   [n, 27] int32 from ssc_build_index (or any map with the same meaning).
+ *   plan  >= ssc_plan_bytes(n) bytes, 256-byte aligned; written completely.
+ *   workspace >= ssc_plan_workspace_bytes(n) bytes, 256-byte aligned, scratch only.
+ * Bit-reproducible: the same nbr always yields the same plan. */
+ssc_status ssc_build_plan(const int32_t* nbr, int64_t n, void* plan, size_t plan_bytes,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Convolution (warm path)
+ * ------------------------------------------------------------------------------------- */
+
+/* Bytes of scratch workspace ssc_subm_conv3d needs (the weights re-laid out for the matrix
+ * cores; 0 for the fp32 path). */
+size_t ssc_conv_workspace_bytes(int32_t cin, int32_t cout, int32_t in_dtype);
+
+/* SubMConv3d, k=3, stride 1, over the plan of a coordinate set:
+ *   out[i][o] = bias[o] + sum_{t : nbr[i][t] != -1} sum_c feats[nbr[i][t]][c] * weight[t][c][o]
+ * (cross-correlation; LATO.2 MLX port page, "Correctness").
+ *   feats    [n, cin], in_dtype (SSC_F32 or SSC_BF16); rows in coords order.
+ *   weight   [27, cin, cout], same dtype as feats.
+ *   bias     [cout] fp32, or NULL for none.
+ *   plan     from ssc_build_plan for the same n.
+ *   out      [n, cout], out_dtype; rows in coords order; must not alias feats.
+ *   workspace >= ssc_conv_workspace_bytes(cin, cout, in_dtype) bytes, 256-byte aligned.
+ * Accumulation is fp32 (bf16 products are exact in fp32).  With out_dtype = SSC_BF16 each
+ * output is the round-to-nearest-even bf16 of the fp32 value the SSC_F32 output holds.
+ * Results are bit-identical from run to run (no atomics in the accumulation).
+ * Shapes: 1 <= cin, cout <= 1024.  bf16 with cin % 32 == 0 and cout % 16 == 0 runs on the
+ * matrix cores; other shapes run a vector-ALU kernel with the same numerics contract. */
+ssc_status ssc_subm_conv3d(const void* feats, int32_t in_dtype, const void* weight,
+                           const float* bias, const void* plan, int64_t n, int32_t cin,
+                           int32_t cout, void* out, int32_t out_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Weights re-laid out once for the matrix cores, for callers that keep a layer's weights
+ * (the same re-layout ssc_subm_conv3d performs into its workspace on every call).
+ *   weight  [taps, cin, cout] bf16 (taps = 27 for k=3, 1 for k=1).
+ *   packed  >= ssc_packed_weight_bytes(taps, cin, cout) bytes, 256-byte aligned; receives
+ *           [taps, cout, cin] bf16.
+ * Only bf16 with cin % 32 == 0, cout % 16 == 0, cin <= 128, cout <= 128 (the shapes the
+ * matrix-core kernels are built for); otherwise SSC_ERR_UNSUPPORTED. */
+size_t ssc_packed_weight_bytes(int32_t taps, int32_t cin, int32_t cout);
+ssc_status ssc_pack_weights(const void* weight, int32_t taps, int32_t cin, int32_t cout,
+                            void* packed, size_t packed_bytes, void* stream);
+
+/* ssc_subm_conv3d with weights from ssc_pack_weights (taps = 27): one kernel launch, no
+ * workspace.  Same results, bit for bit, as ssc_subm_conv3d on the unpacked weights.
+ * bf16 inputs and the shapes ssc_pack_weights accepts only. */
+ssc_status ssc_subm_conv3d_packed(const void* feats, const void* packed_weight,
+                                  const float* bias, const void* plan, int64_t n, int32_t cin,
+                                  int32_t cout, void* out, int32_t out_dtype, void* stream);
+
+/* k=1 SubMConv3d, i.e. the per-voxel linear map out = feats @ weight + bias (LATO.2 page,
+ * "Status": SubMConv3d k=1; SparseLinear).  No map is needed.
+ *   feats [n, cin], weight [cin, cout] (the single-tap [1, cin, cout] has the same bytes),
+ *   bias [cout] fp32 or NULL, out [n, cout] out_dtype; workspace as for ssc_subm_conv3d. */
+ssc_status ssc_linear(const void* feats, int32_t in_dtype, const void* weight, const float* bias,
+                      int64_t n, int32_t cin, int32_t cout, void* out, int32_t out_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSC_H */

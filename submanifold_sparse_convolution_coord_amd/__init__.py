@@ -1,0 +1,313 @@
+"""Submanifold sparse 3x3x3 convolution (SubMConv3d) for AMD MI355X.
+
+Thin Python binding over libssc.so (include/ssc.h).  Every step of the computation runs
+in the library's HIP kernels; this module only checks and marshals arguments, allocates
+outputs and workspaces with torch, and passes torch's current HIP stream.  There is no
+fallback: if libssc.so has not been built, importing works but every call raises.
+
+    nbr  = build_index(coords, batch, grid)          # [N, 27] int32, -1 = no neighbour
+    plan = build_plan(nbr)                           # warm payload, reused by every layer
+    y    = subm_conv3d(x, w, b, plan)                # k=3, w [27, Cin, Cout]
+    y2   = linear(y.to(torch.bfloat16), w1, b1)      # k=1
+
+``SubMIndex`` bundles the map and the plan of one coordinate set, and ``cached_index``
+reuses it while the coordinate tensor is unchanged (the pages' spatial cache).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import weakref
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = ["SscError", "build_index", "build_plan", "subm_conv3d", "linear", "Plan",
+           "PackedWeight", "pack_weights", "subm_conv3d_packed",
+           "SubMIndex", "cached_index", "library_path", "load_library", "TAPS", "CENTRE_TAP"]
+
+TAPS = 27
+CENTRE_TAP = 13
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libssc.so")
+
+SSC_OK, SSC_ERR_ARG, SSC_ERR_COORD_RANGE, SSC_ERR_DUPLICATE = 0, -1, -2, -3
+SSC_ERR_UNSUPPORTED, SSC_ERR_WORKSPACE, SSC_ERR_HIP = -4, -5, -6
+SSC_F32, SSC_BF16 = 0, 1
+
+
+class SscError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({_status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libssc.so and declare its signatures; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "submanifold_sparse_convolution_coord_amd.build.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "ssc_version": ([], ctypes.c_int),
+        "ssc_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "ssc_index_workspace_bytes": ([i64], sz),
+        "ssc_build_index": ([p, i64, i32, p, p, p, sz, i32, p], ctypes.c_int),
+        "ssc_plan_bytes": ([i64], sz),
+        "ssc_plan_workspace_bytes": ([i64], sz),
+        "ssc_build_plan": ([p, i64, p, sz, p, sz, p], ctypes.c_int),
+        "ssc_conv_workspace_bytes": ([i32, i32, i32], sz),
+        "ssc_subm_conv3d": ([p, i32, p, p, p, i64, i32, i32, p, i32, p, sz, p], ctypes.c_int),
+        "ssc_linear": ([p, i32, p, p, i64, i32, i32, p, i32, p, sz, p], ctypes.c_int),
+        "ssc_packed_weight_bytes": ([i32, i32, i32], sz),
+        "ssc_pack_weights": ([p, i32, i32, i32, p, sz, p], ctypes.c_int),
+        "ssc_subm_conv3d_packed": ([p, p, p, p, i64, i32, i32, p, i32, p], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return load_library().ssc_status_string(status).decode()
+    except Exception:  # library missing while formatting an error
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != SSC_OK:
+        raise SscError(status, what)
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, dev: torch.device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
+
+
+def _dtype_code(dt: torch.dtype, name: str) -> int:
+    if dt == torch.float32:
+        return SSC_F32
+    if dt == torch.bfloat16:
+        return SSC_BF16
+    raise ValueError(f"{name}: dtype {dt} not supported (float32 or bfloat16)")
+
+
+def build_index(coords: torch.Tensor, batch: int, grid: Sequence[int],
+                check: bool = True) -> torch.Tensor:
+    """[N, 27] int32 neighbour map of the sites ``coords`` ([N, 4] int32 (b, x, y, z))."""
+    _need_cuda(coords, "coords")
+    if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 4:
+        raise ValueError("coords must be int32 [N, 4]")
+    lib = load_library()
+    dev = coords.device
+    n = coords.shape[0]
+    nbr = torch.empty((n, TAPS), dtype=torch.int32, device=dev)
+    ws = _workspace(lib.ssc_index_workspace_bytes(n), dev)
+    g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
+    with torch.cuda.device(dev):
+        st = lib.ssc_build_index(_ptr(coords), n, int(batch), g, _ptr(nbr), _ptr(ws), ws.numel(),
+                                 1 if check else 0, _stream(dev))
+    _check(st, "ssc_build_index")
+    return nbr
+
+
+class Plan:
+    """Warm plan of one coordinate set (sites sorted by tap mask, tap-major neighbour rows)."""
+
+    def __init__(self, buf: torch.Tensor, n: int):
+        self.buf = buf
+        self.n = n
+
+    @property
+    def device(self):
+        return self.buf.device
+
+
+def build_plan(nbr: torch.Tensor) -> Plan:
+    _need_cuda(nbr, "nbr")
+    if nbr.dtype != torch.int32 or nbr.dim() != 2 or nbr.shape[1] != TAPS:
+        raise ValueError("nbr must be int32 [N, 27]")
+    lib = load_library()
+    dev = nbr.device
+    n = nbr.shape[0]
+    buf = _workspace(lib.ssc_plan_bytes(n), dev)
+    ws = _workspace(lib.ssc_plan_workspace_bytes(n), dev)
+    with torch.cuda.device(dev):
+        st = lib.ssc_build_plan(_ptr(nbr), n, _ptr(buf), buf.numel(), _ptr(ws), ws.numel(),
+                                _stream(dev))
+    _check(st, "ssc_build_plan")
+    return Plan(buf, n)
+
+
+def _conv_args(x, weight, bias, taps, out_dtype):
+    _need_cuda(x, "x")
+    _need_cuda(weight, "weight")
+    if x.dim() != 2:
+        raise ValueError("x must be [N, Cin]")
+    n, cin = x.shape
+    wshape = (1, *weight.shape) if weight.dim() == 2 else tuple(weight.shape)
+    if len(wshape) != 3 or wshape[0] != taps or wshape[1] != cin:
+        raise ValueError(f"weight must be [{taps}, {cin}, Cout], got {tuple(weight.shape)}")
+    if weight.dtype != x.dtype:
+        raise ValueError("weight and x must have the same dtype")
+    cout = wshape[2]
+    if bias is not None:
+        _need_cuda(bias, "bias")
+        if bias.dtype != torch.float32 or bias.numel() != cout:
+            raise ValueError("bias must be float32 [Cout]")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    return n, cin, cout, _dtype_code(x.dtype, "x"), _dtype_code(out_dtype, "out_dtype"), out_dtype
+
+
+def subm_conv3d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor], plan: Plan,
+                out_dtype: Optional[torch.dtype] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """k=3 SubMConv3d: out[i] = bias + sum_t x[nbr[i][t]] @ weight[t] (cross-correlation).
+    ``weight`` is [27, Cin, Cout] with the dtype of ``x``; output fp32 unless ``out_dtype``."""
+    n, cin, cout, din, dout, odt = _conv_args(x, weight, bias, TAPS, out_dtype)
+    if plan.n != n:
+        raise ValueError(f"plan is for {plan.n} sites, x has {n}")
+    lib = load_library()
+    dev = x.device
+    if out is None:
+        out = torch.empty((n, cout), dtype=odt, device=dev)
+    ws = _workspace(lib.ssc_conv_workspace_bytes(cin, cout, din), dev)
+    with torch.cuda.device(dev):
+        st = lib.ssc_subm_conv3d(_ptr(x), din, _ptr(weight), _ptr(bias), _ptr(plan.buf), n, cin,
+                                 cout, _ptr(out), dout, _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "ssc_subm_conv3d")
+    return out
+
+
+def linear(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+           out_dtype: Optional[torch.dtype] = None,
+           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """k=1 SubMConv3d = per-voxel linear map x @ weight + bias (weight [Cin, Cout] or
+    [1, Cin, Cout])."""
+    n, cin, cout, din, dout, odt = _conv_args(x, weight, bias, 1, out_dtype)
+    lib = load_library()
+    dev = x.device
+    if out is None:
+        out = torch.empty((n, cout), dtype=odt, device=dev)
+    ws = _workspace(lib.ssc_conv_workspace_bytes(cin, cout, din), dev)
+    with torch.cuda.device(dev):
+        st = lib.ssc_linear(_ptr(x), din, _ptr(weight), _ptr(bias), n, cin, cout, _ptr(out), dout,
+                            _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "ssc_linear")
+    return out
+
+
+class PackedWeight:
+    """A layer's [taps, Cin, Cout] bf16 weights re-laid out once for the matrix cores."""
+
+    def __init__(self, buf: torch.Tensor, taps: int, cin: int, cout: int):
+        self.buf, self.taps, self.cin, self.cout = buf, taps, cin, cout
+
+
+def pack_weights(weight: torch.Tensor) -> PackedWeight:
+    _need_cuda(weight, "weight")
+    if weight.dtype != torch.bfloat16:
+        raise ValueError("pack_weights takes bfloat16 weights")
+    wshape = (1, *weight.shape) if weight.dim() == 2 else tuple(weight.shape)
+    taps, cin, cout = wshape
+    lib = load_library()
+    dev = weight.device
+    buf = _workspace(lib.ssc_packed_weight_bytes(taps, cin, cout), dev)
+    with torch.cuda.device(dev):
+        st = lib.ssc_pack_weights(_ptr(weight), taps, cin, cout, _ptr(buf), buf.numel(),
+                                  _stream(dev))
+    _check(st, "ssc_pack_weights")
+    return PackedWeight(buf, taps, cin, cout)
+
+
+def subm_conv3d_packed(x: torch.Tensor, packed: PackedWeight, bias: Optional[torch.Tensor],
+                       plan: Plan, out_dtype: Optional[torch.dtype] = None,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """subm_conv3d with weights from pack_weights: a single kernel launch."""
+    _need_cuda(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != packed.cin or packed.taps != TAPS:
+        raise ValueError("x must be bfloat16 [N, Cin] matching a 27-tap packed weight")
+    n = x.shape[0]
+    if plan.n != n:
+        raise ValueError(f"plan is for {plan.n} sites, x has {n}")
+    if bias is not None:
+        _need_cuda(bias, "bias")
+        if bias.dtype != torch.float32 or bias.numel() != packed.cout:
+            raise ValueError("bias must be float32 [Cout]")
+    odt = torch.float32 if out_dtype is None else out_dtype
+    dout = _dtype_code(odt, "out_dtype")
+    lib = load_library()
+    dev = x.device
+    if out is None:
+        out = torch.empty((n, packed.cout), dtype=odt, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.ssc_subm_conv3d_packed(_ptr(x), _ptr(packed.buf), _ptr(bias), _ptr(plan.buf), n,
+                                        packed.cin, packed.cout, _ptr(out), dout, _stream(dev))
+    _check(st, "ssc_subm_conv3d_packed")
+    return out
+
+
+class SubMIndex:
+    """Neighbour map + warm plan of one coordinate set, built once and shared by every
+    SubMConv3d layer on that set."""
+
+    def __init__(self, coords: torch.Tensor, batch: int, grid: Sequence[int], check: bool = True):
+        self.batch = int(batch)
+        self.grid = tuple(int(g) for g in grid)
+        self.nbr = build_index(coords, batch, grid, check=check)
+        self.plan = build_plan(self.nbr)
+        self.n = int(coords.shape[0])
+
+    def conv(self, x, weight, bias=None, out_dtype=None):
+        return subm_conv3d(x, weight, bias, self.plan, out_dtype)
+
+
+_CACHE: dict = {}
+_CACHE_MAX = 16
+
+
+def cached_index(coords: torch.Tensor, batch: int, grid: Sequence[int]) -> SubMIndex:
+    """SubMIndex of ``coords``, rebuilt only when the tensor object, its storage, shape or
+    in-place version counter changes."""
+    key = (coords.data_ptr(), tuple(coords.shape), coords.device, int(batch),
+           tuple(int(g) for g in grid))
+    hit = _CACHE.get(key)
+    if hit is not None:
+        ref, version, idx = hit
+        if ref() is coords and version == coords._version:
+            return idx
+    idx = SubMIndex(coords, batch, grid)
+    if len(_CACHE) >= _CACHE_MAX:
+        _CACHE.pop(next(iter(_CACHE)))
+    _CACHE[key] = (weakref.ref(coords), coords._version, idx)
+    return idx

@@ -1,0 +1,67 @@
+// Internal helpers shared by the libssc.so translation units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssc.h"
+
+namespace ssc {
+
+constexpr int kTaps = 27;
+constexpr int kCentreTap = 13;
+constexpr int64_t kMaxCoord = 65535;   // grid extents and batch must fit 16-bit key fields
+constexpr size_t kAlign = 256;         // every sub-buffer starts on this boundary
+
+inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline ssc_status launch_status() {
+  return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+}
+
+// Plan buffer layout (all offsets 256-byte aligned):
+//   header  int64[8]: magic, n, npad, nblocks, reserved...
+//   zero    2048 zero bytes   the source of missing neighbour rows (Cin <= 1024 bf16)
+//   perm    int32[npad]       sorted position -> original row, -1 for padding
+//   bmask   uint32[nblocks]   OR of the tap-validity masks of the 16 rows of each block
+//   gidx    int32[27][npad]   neighbour row of sorted position r for tap t, -1 if none
+constexpr int64_t kPlanMagic = 0x5353435031LL;  // "SSCP1"
+constexpr int kPlanRowAlign = 256;              // npad is a multiple of this
+constexpr int kBlockRows = 16;                  // rows per MFMA block
+
+struct PlanLayout {
+  int64_t n, npad, nblocks;
+  size_t off_zero, off_perm, off_bmask, off_gidx, total;
+};
+constexpr size_t kZeroBytes = 2048;
+
+inline PlanLayout plan_layout(int64_t n) {
+  PlanLayout L;
+  L.n = n;
+  L.npad = ((n > 0 ? n : 1) + kPlanRowAlign - 1) / kPlanRowAlign * kPlanRowAlign;
+  L.nblocks = L.npad / kBlockRows;
+  L.off_zero = kAlign;
+  L.off_perm = align_up(L.off_zero + kZeroBytes);
+  L.off_bmask = align_up(L.off_perm + sizeof(int32_t) * L.npad);
+  L.off_gidx = align_up(L.off_bmask + sizeof(uint32_t) * L.nblocks);
+  L.total = align_up(L.off_gidx + sizeof(int32_t) * kTaps * L.npad);
+  return L;
+}
+
+// Round-to-nearest-even fp32 -> bf16 (ties to even on the upper 16 bits; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+}  // namespace ssc

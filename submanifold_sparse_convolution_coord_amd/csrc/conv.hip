@@ -1,0 +1,725 @@
+// SubMConv3d (k=3) and its k=1 case on the gfx950 matrix cores.
+//
+//   out[i] = bias + sum_t sum_c feats[nbr[i][t]][c] * W[t][c][:]      (cross-correlation,
+//   LATO.2 MLX port page, "Correctness"; weights [K^3, Cin, Cout], Pixal3D README, "Status")
+//
+// The pages' own designs are a per-offset gather / matmul / scatter-add loop (trellis-mac
+// article, flowchart; LATO.2 page, "Fleet benchmark": 2*K^3 = 54 dispatches, launch bound)
+// and one fused [N, K^3*Cin] x [K^3*Cin, Cout] matmul over a cached device index (LATO.2
+// page, version history).  Here the whole layer is ONE kernel, output-stationary:
+//
+//   * a workgroup owns a tile of NB 16-row blocks of the plan's site order (sites sorted by
+//     their tap-validity mask, so a block's rows mostly share which taps exist);
+//   * for every tap present in the tile, each wave loads its slice of W[t] into registers as
+//     matrix-core B fragments, then, for each block whose mask has tap t, gathers the 16
+//     neighbour rows straight from HBM/L2 into A fragments (a missing neighbour is a zero row,
+//     never loaded) and issues bf16 16x16x32 MFMAs into fp32 accumulators held in VGPRs;
+//   * (block, tap) pairs with no neighbour at all are skipped by a wave-uniform branch;
+//   * the epilogue adds the bias and stores each row at its original index, fp32 or bf16
+//     (round-to-nearest-even of the same fp32 value).
+// Every output element is owned by exactly one lane, so there are no atomics and results
+// are bit-identical run to run, and independent of the site order.
+//
+// The matrix cores want both operands k-contiguous per lane, so W is re-laid out per call
+// as Wt[t][o][c] (k_transpose_w, 27*Cin*Cout*2 bytes, in the caller's workspace).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace ssc {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+}
+
+__device__ __forceinline__ bf16x8_t zero_bf16x8() {
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+}
+
+// Wt[t][o][c] = W[t][c][o]; 32x32 tiles through LDS.
+__global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict__ W, int cin,
+                                                     int cout, uint16_t* __restrict__ Wt) {
+  __shared__ uint16_t tile[32][33];
+  const int t = blockIdx.z, c0 = blockIdx.y * 32, o0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const uint16_t* src = W + static_cast<int64_t>(t) * cin * cout;
+  uint16_t* dst = Wt + static_cast<int64_t>(t) * cin * cout;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = c0 + ty + 8 * k, o = o0 + tx;
+    if (c < cin && o < cout) tile[ty + 8 * k][tx] = src[static_cast<int64_t>(c) * cout + o];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int o = o0 + ty + 8 * k, c = c0 + tx;
+    if (c < cin && o < cout) dst[static_cast<int64_t>(o) * cin + c] = tile[tx][ty + 8 * k];
+  }
+}
+
+// Matrix-core fragment layout of v_mfma_f32_16x16x32_bf16 (wave64), as used below:
+//   A (16 x 32): lane l holds row (l & 15), k = 8*(l >> 4) .. +7
+//   B (32 x 16): lane l holds column (l & 15), k = 8*(l >> 4) .. +7
+//   D (16 x 16): lane l holds column (l & 15), rows 4*(l >> 4) .. +3
+// Both operands use the same (lane, element) -> k assignment, so the product is the full
+// k-sum whatever order the hardware walks k in.
+//
+// DENSE = false: k=3 convolution over a plan (gather through gidx, skip by block masks).
+// DENSE = true : k=1 per-voxel linear map (row r reads feats row r, one tap, no plan).
+template <int CIN, int COUT, int WAVES, int NB, bool DENSE>
+__global__ __launch_bounds__(WAVES * 64) void k_conv_mfma(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wt,
+    const float* __restrict__ bias, const int32_t* __restrict__ perm,
+    const uint32_t* __restrict__ bmask, const int32_t* __restrict__ gidx, int64_t npad, int64_t n,
+    void* __restrict__ Y, int out_bf16) {
+  static_assert(CIN % 32 == 0 && COUT % (16 * WAVES) == 0, "tile shape");
+  constexpr int CS = COUT / WAVES;  // output columns per wave
+  constexpr int NCT = CS / 16;      // 16-column MFMA tiles per wave
+  constexpr int KS = CIN / 32;      // k-steps of 32 channels
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const int colbase = wave * CS;
+  const int64_t tile = blockIdx.x;
+  const int64_t row0 = tile * (NB * 16);
+
+  uint32_t bm[NB];
+  uint32_t taps = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (DENSE) {
+      bm[b] = (row0 + b * 16 < n) ? 1u : 0u;
+    } else {
+      bm[b] = bmask[tile * NB + b];
+    }
+    taps |= bm[b];
+  }
+
+  f32x4_t acc[NB][NCT];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[b][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  while (taps) {
+    const int t = __builtin_ctz(taps);
+    taps &= taps - 1;
+    bf16x8_t bw[NCT][KS];
+    const uint16_t* wt = Wt + (static_cast<int64_t>(t) * COUT + colbase + lr) * CIN + lk;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) bw[c][s] = load_bf16x8(wt + c * 16 * CIN + s * 32);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (!((bm[b] >> t) & 1u)) continue;
+      const int64_t r = row0 + b * 16 + lr;
+      int32_t j;
+      if (DENSE) {
+        j = r < n ? static_cast<int32_t>(r) : -1;
+      } else {
+        j = gidx[static_cast<int64_t>(t) * npad + r];
+      }
+      bf16x8_t a[KS];
+      if (j >= 0) {
+        const uint16_t* xr = X + static_cast<int64_t>(j) * CIN + lk;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a[s] = load_bf16x8(xr + s * 32);
+      } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a[s] = zero_bf16x8();
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+          acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bw[c][s], acc[b][c], 0, 0, 0);
+    }
+  }
+
+  // Epilogue: bias, then store each row at its original index.
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    const int col = colbase + c * 16 + lr;
+    const float bv = bias ? bias[col] : 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = row0 + b * 16 + (lane >> 4) * 4 + i;
+        int64_t orow;
+        if (DENSE) {
+          orow = r < n ? r : -1;
+        } else {
+          orow = perm[r];
+        }
+        if (orow < 0) continue;
+        const float v = acc[b][c][i] + bv;
+        if (out_bf16)
+          static_cast<uint16_t*>(Y)[orow * COUT + col] = f32_to_bf16_rne(v);
+        else
+          static_cast<float*>(Y)[orow * COUT + col] = v;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// k=3 convolution kernel: gathers staged in LDS, software-pipelined over the taps of a tile.
+//
+// A workgroup of 4 waves owns one tile of NB 16-row blocks of the plan's site order.  The
+// taps present in the tile (the OR of its block masks) are walked in ascending order.  For
+// each tap one stage is prepared ahead of its use:
+//   * the 16 neighbour feature rows of every block that has tap t are copied into LDS by the
+//     gfx950 direct global->LDS loads (global_load_lds_dwordx4: no VGPRs held while in
+//     flight); a missing neighbour copies a zero row;
+//   * each wave loads its column slice of W[t] (packed [Cout][Cin]) into VGPRs as matrix-core
+//     B fragments, into the register set of the stage's parity.
+// While the matrix cores consume stage q, stage q+1 is in flight.  Per tap there is one wait
+// (vmcnt 0, lgkmcnt 0: at that point only stage q is outstanding) and one bare workgroup
+// barrier, which makes the copies of all waves visible and proves that every wave finished
+// reading the buffer the next stage overwrites.
+// 16-byte chunks of each LDS row are XOR-swizzled so that the 16 rows a fragment read touches
+// fall in distinct banks.  Waves are WR x WC: column group wc owns COUT/WC output columns,
+// row group wr owns blocks wr, wr+WR, ...; fp32 accumulators stay in VGPRs.
+// ------------------------------------------------------------------------------------------
+template <int CIN, int COUT, int NB, int WR, int WC>
+struct LdsCfg {
+  static constexpr int WAVES = WR * WC;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int CPR = CIN / 8;             // 16-byte chunks per feature row
+  static constexpr int RPW = 16 / WAVES;          // rows of each block a wave copies
+  static constexpr int A_LANES = RPW * CPR;       // lanes active in a block copy
+  static constexpr int A_BLOCK = 16 * CIN;        // bf16 elements per block slot
+  static constexpr int CS = COUT / WC;            // output columns per wave
+  static constexpr int NCT = CS / 16;             // 16-column MFMA tiles per wave
+  static constexpr int KS = CIN / 32;             // k-steps
+  static constexpr int NW = NCT * KS;             // weight fragment loads per stage
+  static constexpr int BPW = NB / WR;             // blocks accumulated per wave
+  static constexpr int G_TAPS_PER_COPY = 64 / (NB * 4);  // taps of indices per 1 KB copy
+  static_assert(16 % WAVES == 0 && A_LANES <= 64 && A_LANES > 0, "block copy shape");
+  static_assert(CIN % 32 == 0 && COUT % (16 * WC) == 0 && NB % WR == 0, "tile shape");
+  static_assert(NB * 4 <= 64 && 64 % (NB * 4) == 0, "index copy shape");
+  static_assert(NB + NW < 64, "vmcnt range");
+};
+
+// LDS byte address of a __shared__ location (wave-uniform in every use below).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// One direct global->LDS copy (global_load_lds_dwordx4): every active lane fetches 16 bytes
+// from its own global address and the hardware writes them to LDS at lds_base + 16*lane.
+// Written as inline asm, not the builtin, on purpose: the compiler then does not treat the
+// copy as a pending write to every LDS location, which would otherwise make it drain all
+// copies (vmcnt 0) before each LDS read and serialize the pipeline.  The instruction has no
+// destination register (the data goes to LDS; the address VGPRs are read at issue), and
+// every wait for these copies is explicit in the kernel (wait_vm_lgkm0 before each barrier).
+// m0 (which holds the LDS base) is saved and restored inside the statement, so the compiler's
+// view of every register is unchanged by it.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+// Chunk swizzle: row r's logical 16-byte chunk c lives in slot c ^ swz(r).  For 16
+// consecutive rows and a fixed chunk the slots then differ in their bank group.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  return ((r * CPR) >> 4) & (CPR - 1);
+}
+
+// s_waitcnt vmcnt(0) lgkmcnt(0): every global load / direct copy and every LDS access issued
+// by this wave has completed.
+__device__ __forceinline__ void wait_vm_lgkm0() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
+__device__ __forceinline__ bf16x8_t lds_read16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+}
+
+// Copies of stage (union index q, tap t): NB block copies into sA, one per block.
+template <int CIN, int COUT, int NB, int WR, int WC>
+__device__ __forceinline__ void issue_gather(int q, int t, const uint32_t (&bm)[NB],
+                                             const uint16_t* __restrict__ X,
+                                             const uint16_t* __restrict__ zrow,
+                                             const int32_t* sG, uint16_t* sA, int wave,
+                                             int lane) {
+  using C = LdsCfg<CIN, COUT, NB, WR, WC>;
+  const int rr = (wave * C::RPW + lane / C::CPR) & 15;
+  const int chunk = (lane % C::CPR) ^ swz<C::CPR>(rr);
+  const int32_t* g = sG + q * (NB * 16);
+  int32_t j[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) j[b] = g[b * 16 + rr];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (!((bm[b] >> t) & 1u)) continue;
+    const uint16_t* src =
+        j[b] >= 0 ? X + static_cast<int64_t>(j[b]) * CIN + chunk * 8 : zrow + chunk * 8;
+    if (lane < C::A_LANES) dma16(src, lds_addr(sA + b * C::A_BLOCK + wave * C::RPW * CIN));
+  }
+}
+
+template <int CIN, int COUT, int NB, int WR, int WC>
+__device__ __forceinline__ void load_weights(int t, const uint16_t* __restrict__ Wt, int wc,
+                                             int lane,
+                                             bf16x8_t (&bw)[COUT / WC / 16][CIN / 32]) {
+  using C = LdsCfg<CIN, COUT, NB, WR, WC>;
+  const uint16_t* w = Wt + (static_cast<int64_t>(t) * COUT + wc * C::CS + (lane & 15)) * CIN +
+                      (lane >> 4) * 8;
+#pragma unroll
+  for (int c = 0; c < C::NCT; ++c)
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) bw[c][s] = load_bf16x8(w + c * 16 * CIN + s * 32);
+}
+
+// Byte offsets, within a block slot, of this lane's A fragments (row lane&15, logical chunk
+// (lane>>4) + 4s, swizzled).  Block b's fragments are at b * A_BLOCK * 2 bytes more, which
+// the compiler folds into the LDS instruction's immediate offset.
+template <int CIN>
+__device__ __forceinline__ void a_frag_offsets(int lane, uint32_t (&off)[CIN / 32]) {
+  constexpr int CPR = CIN / 8;
+  const int r = lane & 15;
+#pragma unroll
+  for (int s = 0; s < CIN / 32; ++s) {
+    const int chunk = (lane >> 4) + 4 * s;
+    off[s] = static_cast<uint32_t>((r * CPR + (chunk ^ swz<CPR>(r))) * 16);
+  }
+}
+
+template <int CIN, int COUT, int NB, int WR, int WC>
+__device__ __forceinline__ void compute_stage(int t, const uint32_t (&bm)[NB], const uint16_t* sA,
+                                              const bf16x8_t (&bw)[COUT / WC / 16][CIN / 32],
+                                              const uint32_t (&aoff)[CIN / 32], int wr,
+                                              f32x4_t (&acc)[NB / WR][COUT / WC / 16]) {
+  using C = LdsCfg<CIN, COUT, NB, WR, WC>;
+  const char* base = reinterpret_cast<const char*>(sA);
+#pragma unroll
+  for (int bl = 0; bl < C::BPW; ++bl) {
+    const int b = bl * WR + wr;
+    if (!((bm[b] >> t) & 1u)) continue;
+    const char* blk = base + b * (C::A_BLOCK * 2);
+    bf16x8_t a[C::KS];
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) a[s] = lds_read16(reinterpret_cast<const uint16_t*>(blk + aoff[s]));
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+#pragma unroll
+      for (int c = 0; c < C::NCT; ++c)
+        acc[bl][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bw[c][s], acc[bl][c], 0, 0, 0);
+  }
+}
+
+template <int CIN, int COUT, int NB, int WR, int WC, bool OUT_BF16>
+__global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wt,
+    const float* __restrict__ bias, const int32_t* __restrict__ perm,
+    const uint32_t* __restrict__ bmask, const int32_t* __restrict__ gidx,
+    const uint16_t* __restrict__ zrow, int64_t npad, void* __restrict__ Y) {
+  using C = LdsCfg<CIN, COUT, NB, WR, WC>;
+  __shared__ __attribute__((aligned(16))) uint16_t sA0[NB * C::A_BLOCK];
+  __shared__ __attribute__((aligned(16))) uint16_t sA1[NB * C::A_BLOCK];
+  __shared__ __attribute__((aligned(16))) int32_t sG[kTaps * NB * 16];
+  __shared__ __attribute__((aligned(16))) int32_t sP[NB * 16];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave / WC, wc = wave % WC;
+  // The plan sorts sites by tap mask, so per-tile work grows along the site order (a tile of
+  // near-empty masks has a tap or two, the last tiles a dozen or more).  Launch the heavy
+  // end first so that the workgroups dispatched last are the short ones.
+  const int64_t tile = static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x;
+  const int64_t row0 = tile * (NB * 16);
+
+  uint32_t bm[NB];
+  uint32_t U = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    bm[b] = bmask[tile * NB + b];
+    U |= bm[b];
+  }
+
+  // Neighbour rows of the tile for every tap present -> sG[q][NB*16].  One 1 KB copy holds
+  // G_TAPS_PER_COPY taps; copies are dealt to the waves round robin.
+  {
+    constexpr int TPC = C::G_TAPS_PER_COPY;
+    const int sub = lane / (NB * 4);            // which tap of the copy this lane serves
+    const int off = (lane % (NB * 4)) * 4;      // first of its 4 indices
+    uint32_t rem = U;
+    int q = 0, k = 0;
+    while (rem) {
+      int tt[TPC];
+#pragma unroll
+      for (int i = 0; i < TPC; ++i) {
+        tt[i] = rem ? __builtin_ctz(rem) : -1;
+        rem &= rem ? rem - 1 : 0u;
+      }
+      if ((k % C::WAVES) == wave) {
+        int mine = -1;
+#pragma unroll
+        for (int i = 0; i < TPC; ++i)
+          if (i == sub) mine = tt[i];
+        if (mine >= 0)
+          dma16(gidx + static_cast<int64_t>(mine) * npad + row0 + off,
+                lds_addr(sG + q * (NB * 16)));
+      }
+      q += TPC;
+      ++k;
+    }
+  }
+  // The tile's original row indices -> sP (read by the epilogue), by the last wave.
+  if (wave == C::WAVES - 1 && lane < NB * 4) dma16(perm + row0 + lane * 4, lds_addr(sP));
+  // Bias of this lane's columns, loaded now so the epilogue issues no loads among its stores
+  // (stores count in vmcnt, so a load there would make every later wait drain the stores).
+  float bv[C::NCT];
+#pragma unroll
+  for (int c = 0; c < C::NCT; ++c) bv[c] = bias ? bias[wc * C::CS + c * 16 + (lane & 15)] : 0.f;
+  wait_vm_lgkm0();
+  __builtin_amdgcn_s_barrier();
+
+  f32x4_t acc[C::BPW][C::NCT];
+#pragma unroll
+  for (int bl = 0; bl < C::BPW; ++bl)
+#pragma unroll
+    for (int c = 0; c < C::NCT; ++c) acc[bl][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (U) {
+    // Stage q lives in (sA0, bw0) for even q and (sA1, bw1) for odd q.  Per stage: wait until
+    // this wave's copies and loads of the stage have landed (nothing newer is outstanding at
+    // that point), barrier, issue the next stage, then run the matrix cores on this one.
+    bf16x8_t bw0[C::NCT][C::KS], bw1[C::NCT][C::KS];
+    uint32_t aoff[C::KS];
+    a_frag_offsets<CIN>(lane, aoff);
+    uint32_t rem = U;
+    int t_cur = __builtin_ctz(rem);
+    rem &= rem - 1;
+    int q = 0;
+    load_weights<CIN, COUT, NB, WR, WC>(t_cur, Wt, wc, lane, bw0);
+    issue_gather<CIN, COUT, NB, WR, WC>(0, t_cur, bm, X, zrow, sG, sA0, wave, lane);
+    while (true) {
+      wait_vm_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      int t_next = rem ? __builtin_ctz(rem) : -1;
+      if (t_next >= 0) {
+        load_weights<CIN, COUT, NB, WR, WC>(t_next, Wt, wc, lane, bw1);
+        issue_gather<CIN, COUT, NB, WR, WC>(q + 1, t_next, bm, X, zrow, sG, sA1, wave, lane);
+      }
+      compute_stage<CIN, COUT, NB, WR, WC>(t_cur, bm, sA0, bw0, aoff, wr, acc);
+      if (t_next < 0) break;
+      rem &= rem - 1;
+      t_cur = t_next;
+      ++q;
+      wait_vm_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      t_next = rem ? __builtin_ctz(rem) : -1;
+      if (t_next >= 0) {
+        load_weights<CIN, COUT, NB, WR, WC>(t_next, Wt, wc, lane, bw0);
+        issue_gather<CIN, COUT, NB, WR, WC>(q + 1, t_next, bm, X, zrow, sG, sA0, wave, lane);
+      }
+      compute_stage<CIN, COUT, NB, WR, WC>(t_cur, bm, sA1, bw1, aoff, wr, acc);
+      if (t_next < 0) break;
+      rem &= rem - 1;
+      t_cur = t_next;
+      ++q;
+    }
+  }
+
+  // Nothing is outstanding here; saying so lets the compiler drop its per-store waits for
+  // weight loads it cannot prove were skipped on the last tap.
+  wait_vm_lgkm0();
+
+  // Epilogue: bias, then store each row at its original index.  All row indices are read
+  // from LDS first; the stores then issue back to back.
+  int32_t orow[C::BPW][4];
+#pragma unroll
+  for (int bl = 0; bl < C::BPW; ++bl)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) orow[bl][i] = sP[(bl * WR + wr) * 16 + (lane >> 4) * 4 + i];
+#pragma unroll
+  for (int c = 0; c < C::NCT; ++c) {
+    const int col = wc * C::CS + c * 16 + (lane & 15);
+#pragma unroll
+    for (int bl = 0; bl < C::BPW; ++bl) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t o = orow[bl][i];
+        if (o < 0) continue;
+        const float v = acc[bl][c][i] + bv[c];
+        if (OUT_BF16)
+          static_cast<uint16_t*>(Y)[static_cast<int64_t>(o) * COUT + col] = f32_to_bf16_rne(v);
+        else
+          static_cast<float*>(Y)[static_cast<int64_t>(o) * COUT + col] = v;
+      }
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float load_feat(const T* p);
+template <>
+__device__ __forceinline__ float load_feat<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_feat<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// Vector-ALU path for any shape and for fp32 inputs: one thread per (sorted row, column),
+// fp32 fused multiply-add over taps in ascending order, then channels in ascending order.
+// taps = 27 with a plan; taps = 1 (DENSE) for the k=1 linear map.
+template <typename T, bool DENSE>
+__global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ X, const T* __restrict__ W,
+                                                   const float* __restrict__ bias,
+                                                   const int32_t* __restrict__ perm,
+                                                   const int32_t* __restrict__ gidx, int64_t npad,
+                                                   int64_t n, int cin, int cout,
+                                                   void* __restrict__ Y, int out_bf16) {
+  const int64_t rows = DENSE ? n : npad;
+  const int64_t total = rows * cout;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+       g += stride) {
+    const int64_t r = g / cout;
+    const int o = static_cast<int>(g - r * cout);
+    const int64_t orow = DENSE ? r : perm[r];
+    if (orow < 0) continue;
+    float acc = 0.f;
+    const int taps = DENSE ? 1 : kTaps;
+    for (int t = 0; t < taps; ++t) {
+      const int64_t j = DENSE ? r : gidx[static_cast<int64_t>(t) * npad + r];
+      if (j < 0) continue;
+      const T* xr = X + j * cin;
+      const T* wt = W + static_cast<int64_t>(t) * cin * cout + o;
+      for (int c = 0; c < cin; ++c)
+        acc = fmaf(load_feat<T>(xr + c), load_feat<T>(wt + static_cast<int64_t>(c) * cout), acc);
+    }
+    const float v = acc + (bias ? bias[o] : 0.f);
+    if (out_bf16)
+      static_cast<uint16_t*>(Y)[orow * cout + o] = f32_to_bf16_rne(v);
+    else
+      static_cast<float*>(Y)[orow * cout + o] = v;
+  }
+}
+
+constexpr int kNB = 8;  // 16-row blocks per workgroup tile of the k=1 kernel (128 rows)
+
+using MfmaFn = void (*)(const uint16_t*, const uint16_t*, const float*, const int32_t*,
+                        const uint32_t*, const int32_t*, int64_t, int64_t, void*, int);
+using LdsFn = void (*)(const uint16_t*, const uint16_t*, const float*, const int32_t*,
+                       const uint32_t*, const int32_t*, const uint16_t*, int64_t, void*);
+
+// k=1 (dense rows) kernel for the channel counts the matrix-core path is built for.
+MfmaFn pick_dense(int cin, int cout, int* waves) {
+#define SSC_CASE(CI, CO)                                          \
+  if (cin == CI && cout == CO) {                                  \
+    constexpr int W = CO >= 64 ? 4 : CO / 16;                     \
+    *waves = W;                                                   \
+    return k_conv_mfma<CI, CO, W, kNB, true>;                     \
+  }
+  SSC_CASE(32, 16) SSC_CASE(32, 32) SSC_CASE(32, 64) SSC_CASE(32, 128)
+  SSC_CASE(64, 16) SSC_CASE(64, 32) SSC_CASE(64, 64) SSC_CASE(64, 128)
+  SSC_CASE(128, 16) SSC_CASE(128, 32) SSC_CASE(128, 64) SSC_CASE(128, 128)
+#undef SSC_CASE
+  return nullptr;
+}
+
+// k=3 pipelined kernel: 4 waves as WR x WC, tile of NB blocks (NB = 8 keeps two gather
+// stages plus the indices under 80 KB of LDS, so two workgroups share a CU).
+template <int CI, int CO>
+struct LdsPick {
+  static constexpr int WC = CO >= 64 ? 4 : CO / 16;
+  static constexpr int WR = 4 / WC;
+  static constexpr int NB = CI >= 64 ? 8 : 16;
+};
+
+LdsFn pick_lds(int cin, int cout, bool out_bf16, int* threads, int* rows_per_tile) {
+#define SSC_CASE(CI, CO)                                                             \
+  if (cin == CI && cout == CO) {                                                     \
+    using P = LdsPick<CI, CO>;                                                       \
+    *threads = P::WR * P::WC * 64;                                                   \
+    *rows_per_tile = P::NB * 16;                                                     \
+    return out_bf16 ? k_subm_lds<CI, CO, P::NB, P::WR, P::WC, true>                  \
+                    : k_subm_lds<CI, CO, P::NB, P::WR, P::WC, false>;                \
+  }
+  SSC_CASE(32, 16) SSC_CASE(32, 32) SSC_CASE(32, 64) SSC_CASE(32, 128)
+  SSC_CASE(64, 16) SSC_CASE(64, 32) SSC_CASE(64, 64) SSC_CASE(64, 128)
+  SSC_CASE(128, 16) SSC_CASE(128, 32) SSC_CASE(128, 64) SSC_CASE(128, 128)
+#undef SSC_CASE
+  return nullptr;
+}
+
+bool valid_dtype(int d) { return d == SSC_F32 || d == SSC_BF16; }
+
+ssc_status launch_dense(MfmaFn fn, int waves, const void* feats, const uint16_t* wt,
+                        const float* bias, int64_t n, void* out, int ob, hipStream_t s) {
+  const int64_t tiles = (n + kNB * 16 - 1) / (kNB * 16);
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(tiles)), dim3(waves * 64), 0, s,
+                     static_cast<const uint16_t*>(feats), wt, bias, nullptr, nullptr, nullptr,
+                     int64_t(0), n, out, ob);
+  return launch_status();
+}
+
+ssc_status launch_lds(LdsFn fn, int threads, int rows_per_tile, const void* feats,
+                      const uint16_t* wt, const float* bias, const void* plan, int64_t n,
+                      void* out, hipStream_t s) {
+  const PlanLayout P = plan_layout(n);
+  const char* pb = static_cast<const char*>(plan);
+  const int64_t tiles = P.npad / rows_per_tile;
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(tiles)), dim3(threads), 0, s,
+                     static_cast<const uint16_t*>(feats), wt, bias,
+                     reinterpret_cast<const int32_t*>(pb + P.off_perm),
+                     reinterpret_cast<const uint32_t*>(pb + P.off_bmask),
+                     reinterpret_cast<const int32_t*>(pb + P.off_gidx),
+                     reinterpret_cast<const uint16_t*>(pb + P.off_zero), P.npad, out);
+  return launch_status();
+}
+
+void launch_transpose(const void* weight, int taps, int cin, int cout, uint16_t* wt,
+                      hipStream_t s) {
+  dim3 tg((cout + 31) / 32, (cin + 31) / 32, taps);
+  k_transpose_w<<<tg, 256, 0, s>>>(static_cast<const uint16_t*>(weight), cin, cout, wt);
+}
+
+ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* weight,
+                    const float* bias, const void* plan, int64_t n, int cin, int cout, void* out,
+                    int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n < 0 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSC_ERR_ARG;
+  if (cin < 1 || cout < 1 || cin > 1024 || cout > 1024) return SSC_ERR_UNSUPPORTED;
+  if (n >= (int64_t(1) << 31)) return SSC_ERR_UNSUPPORTED;
+  if (weight == nullptr || (!dense && plan == nullptr)) return SSC_ERR_ARG;
+  if (n > 0 && (feats == nullptr || out == nullptr)) return SSC_ERR_ARG;
+  if (!aligned(weight, 16) || (n > 0 && (!aligned(feats, 16) || !aligned(out, 16))))
+    return SSC_ERR_ARG;
+  if (!dense && !aligned(plan, kAlign)) return SSC_ERR_ARG;
+  if (bias && !aligned(bias, 4)) return SSC_ERR_ARG;
+  const size_t need = ssc_conv_workspace_bytes(cin, cout, in_dtype);
+  if (workspace_bytes < need || (need > 0 && (workspace == nullptr || !aligned(workspace, kAlign))))
+    return SSC_ERR_WORKSPACE;
+  if (n == 0) return SSC_OK;
+  hipStream_t s = as_stream(stream);
+  const PlanLayout P = plan_layout(n);
+  const char* pb = static_cast<const char*>(plan);
+  const int32_t* perm = dense ? nullptr : reinterpret_cast<const int32_t*>(pb + P.off_perm);
+  const uint32_t* bmask = dense ? nullptr : reinterpret_cast<const uint32_t*>(pb + P.off_bmask);
+  const int32_t* gidx = dense ? nullptr : reinterpret_cast<const int32_t*>(pb + P.off_gidx);
+  const int ob = out_dtype == SSC_BF16 ? 1 : 0;
+  const int taps = dense ? 1 : kTaps;
+
+  if (in_dtype == SSC_BF16) {
+    uint16_t* wt = static_cast<uint16_t*>(workspace);
+    if (dense) {
+      int waves = 0;
+      if (MfmaFn fn = pick_dense(cin, cout, &waves)) {
+        launch_transpose(weight, taps, cin, cout, wt, s);
+        return launch_dense(fn, waves, feats, wt, bias, n, out, ob, s);
+      }
+    } else {
+      int threads = 0, rows = 0;
+      if (LdsFn fn = pick_lds(cin, cout, ob != 0, &threads, &rows)) {
+        launch_transpose(weight, taps, cin, cout, wt, s);
+        return launch_lds(fn, threads, rows, feats, wt, bias, plan, n, out, s);
+      }
+    }
+  }
+  const int64_t rows = dense ? n : P.npad;
+  const int64_t total = rows * cout;
+  const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((total + 255) / 256, 262144));
+  if (in_dtype == SSC_BF16) {
+    auto fn = dense ? k_conv_valu<uint16_t, true> : k_conv_valu<uint16_t, false>;
+    hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, s, static_cast<const uint16_t*>(feats),
+                       static_cast<const uint16_t*>(weight), bias, perm, gidx, P.npad, n, cin,
+                       cout, out, ob);
+  } else {
+    auto fn = dense ? k_conv_valu<float, true> : k_conv_valu<float, false>;
+    hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(feats),
+                       static_cast<const float*>(weight), bias, perm, gidx, P.npad, n, cin, cout,
+                       out, ob);
+  }
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace ssc
+
+using namespace ssc;
+
+extern "C" size_t ssc_conv_workspace_bytes(int32_t cin, int32_t cout, int32_t in_dtype) {
+  if (in_dtype != SSC_BF16 || cin < 1 || cout < 1) return 0;
+  return align_up(static_cast<size_t>(kTaps) * cin * cout * sizeof(uint16_t));
+}
+
+extern "C" ssc_status ssc_subm_conv3d(const void* feats, int32_t in_dtype, const void* weight,
+                                      const float* bias, const void* plan, int64_t n, int32_t cin,
+                                      int32_t cout, void* out, int32_t out_dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return run_conv(false, feats, in_dtype, weight, bias, plan, n, cin, cout, out, out_dtype,
+                  workspace, workspace_bytes, stream);
+}
+
+extern "C" ssc_status ssc_linear(const void* feats, int32_t in_dtype, const void* weight,
+                                 const float* bias, int64_t n, int32_t cin, int32_t cout, void* out,
+                                 int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return run_conv(true, feats, in_dtype, weight, bias, nullptr, n, cin, cout, out, out_dtype,
+                  workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t ssc_packed_weight_bytes(int32_t taps, int32_t cin, int32_t cout) {
+  if (taps < 1 || cin < 1 || cout < 1) return 0;
+  return align_up(static_cast<size_t>(taps) * cin * cout * sizeof(uint16_t));
+}
+
+extern "C" ssc_status ssc_pack_weights(const void* weight, int32_t taps, int32_t cin, int32_t cout,
+                                       void* packed, size_t packed_bytes, void* stream) {
+  if (weight == nullptr || packed == nullptr || (taps != 1 && taps != kTaps)) return SSC_ERR_ARG;
+  int waves = 0;
+  if (pick_dense(cin, cout, &waves) == nullptr) return SSC_ERR_UNSUPPORTED;
+  if (!aligned(weight, 16) || !aligned(packed, kAlign)) return SSC_ERR_ARG;
+  if (packed_bytes < ssc_packed_weight_bytes(taps, cin, cout)) return SSC_ERR_WORKSPACE;
+  launch_transpose(weight, taps, cin, cout, static_cast<uint16_t*>(packed), as_stream(stream));
+  return launch_status();
+}
+
+extern "C" ssc_status ssc_subm_conv3d_packed(const void* feats, const void* packed_weight,
+                                             const float* bias, const void* plan, int64_t n,
+                                             int32_t cin, int32_t cout, void* out,
+                                             int32_t out_dtype, void* stream) {
+  if (n < 0 || !valid_dtype(out_dtype) || packed_weight == nullptr || plan == nullptr)
+    return SSC_ERR_ARG;
+  if (n >= (int64_t(1) << 31)) return SSC_ERR_UNSUPPORTED;
+  int threads = 0, rows = 0;
+  LdsFn fn = pick_lds(cin, cout, out_dtype == SSC_BF16, &threads, &rows);
+  if (fn == nullptr) return SSC_ERR_UNSUPPORTED;
+  if (n > 0 && (feats == nullptr || out == nullptr)) return SSC_ERR_ARG;
+  if (!aligned(packed_weight, 16) || !aligned(plan, kAlign) ||
+      (n > 0 && (!aligned(feats, 16) || !aligned(out, 16))) || (bias && !aligned(bias, 4)))
+    return SSC_ERR_ARG;
+  if (n == 0) return SSC_OK;
+  return launch_lds(fn, threads, rows, feats, static_cast<const uint16_t*>(packed_weight), bias,
+                    plan, n, out, as_stream(stream));
+}
+
+extern "C" int ssc_version(void) { return 100; }
+
+extern "C" const char* ssc_status_string(int status) {
+  switch (status) {
+    case SSC_OK: return "ok";
+    case SSC_ERR_ARG: return "invalid argument (null, negative size, bad dtype or misaligned)";
+    case SSC_ERR_COORD_RANGE: return "coordinate outside [0,batch) x [0,grid)";
+    case SSC_ERR_DUPLICATE: return "duplicate coordinate";
+    case SSC_ERR_UNSUPPORTED: return "unsupported shape";
+    case SSC_ERR_WORKSPACE: return "workspace or plan buffer too small";
+    case SSC_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}

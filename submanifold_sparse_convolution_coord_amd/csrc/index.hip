@@ -1,0 +1,392 @@
+// Coordinate index (neighbour map) and warm plan for submanifold 3x3x3 convolution.
+//
+// Neighbour map: the gather-scatter method starts by building a hash map of the active voxel
+// coordinates and then, per kernel offset, looks up each site's neighbour (trellis-mac
+// article, the gather-scatter flowchart).  The LATO.2 page ("Fleet benchmark", closing
+// paragraph) reports the map build as the dominant cost once the convolution is fast (232-357
+// ms of CPU numpy) and amortised only by caching per coordinate set; here it runs on the GPU:
+//
+//   k_table_init  fill the table with the empty key, clear the error counters
+//   k_insert      one thread per site: validate, pack (b,x,y,z) into a 64-bit key, insert
+//                 by linear probing with a 64-bit compare-and-swap; value = row index
+//   k_query       one thread per (site, tap): probe for (b, x+dx, y+dy, z+dz); write the
+//                 row or -1; consecutive threads write consecutive map entries
+//
+// Warm plan: the sites are reordered by their 26-bit mask of valid non-centre taps (a stable
+// LSD radix sort written here: per-tile digit histograms, one exclusive scan, then a stable
+// scatter that ranks equal digits with wave ballots), so that the 16-row blocks the matrix
+// cores consume tend to share which taps are present and empty (block, tap) pairs can be
+// skipped whole.  The neighbour rows are then stored tap-major in that order.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace ssc {
+namespace {
+
+constexpr unsigned long long kEmptyKey = ~0ull;  // no valid key: fields are < 65535
+
+__device__ __forceinline__ unsigned long long pack_key(int b, int x, int y, int z) {
+  return (static_cast<unsigned long long>(static_cast<uint32_t>(b)) << 48) |
+         (static_cast<unsigned long long>(static_cast<uint32_t>(x)) << 32) |
+         (static_cast<unsigned long long>(static_cast<uint32_t>(y)) << 16) |
+         static_cast<unsigned long long>(static_cast<uint32_t>(z));
+}
+
+// 64-bit finaliser of splitmix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014): spreads the packed coordinates over the table.
+__device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+
+struct IndexLayout {
+  uint64_t cap;
+  size_t off_keys, off_vals, total;
+};
+
+inline IndexLayout index_layout(int64_t n) {
+  IndexLayout L;
+  uint64_t want = static_cast<uint64_t>(n > 0 ? n : 1) * 2;
+  uint64_t cap = 64;
+  while (cap < want) cap <<= 1;
+  L.cap = cap;
+  L.off_keys = kAlign;  // [0, 256): two uint32 error counters
+  L.off_vals = align_up(L.off_keys + sizeof(unsigned long long) * cap);
+  L.total = align_up(L.off_vals + sizeof(int32_t) * cap);
+  return L;
+}
+
+__global__ void k_table_init(unsigned long long* __restrict__ keys, uint64_t cap,
+                             uint32_t* __restrict__ counters) {
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < cap;
+       i += stride)
+    keys[i] = kEmptyKey;
+  if (blockIdx.x == 0 && threadIdx.x < 2) counters[threadIdx.x] = 0;
+}
+
+__global__ void k_insert(const int4* __restrict__ coords, int64_t n, int batch, int gx, int gy,
+                         int gz, unsigned long long* __restrict__ keys, int32_t* __restrict__ vals,
+                         uint64_t mask, uint32_t* __restrict__ counters) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += stride) {
+    const int4 c = coords[i];  // (b, x, y, z)
+    if (c.x < 0 || c.x >= batch || c.y < 0 || c.y >= gx || c.z < 0 || c.z >= gy || c.w < 0 ||
+        c.w >= gz) {
+      atomicAdd(&counters[0], 1u);
+      continue;
+    }
+    const unsigned long long key = pack_key(c.x, c.y, c.z, c.w);
+    uint64_t h = mix64(key) & mask;
+    // The table has at least twice as many slots as sites, so an empty slot always exists
+    // and the probe ends.
+    while (true) {
+      const unsigned long long prev = atomicCAS(&keys[h], kEmptyKey, key);
+      if (prev == kEmptyKey) {
+        vals[h] = static_cast<int32_t>(i);
+        break;
+      }
+      if (prev == key) {
+        atomicAdd(&counters[1], 1u);
+        break;
+      }
+      h = (h + 1) & mask;
+    }
+  }
+}
+
+__global__ void k_query(const int4* __restrict__ coords, int64_t n, int batch, int gx, int gy,
+                        int gz, const unsigned long long* __restrict__ keys,
+                        const int32_t* __restrict__ vals, uint64_t mask,
+                        int32_t* __restrict__ nbr) {
+  const int64_t total = n * kTaps;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+       g += stride) {
+    const int64_t i = g / kTaps;
+    const int t = static_cast<int>(g - i * kTaps);
+    const int4 c = coords[i];
+    const int x = c.y + t / 9 - 1, y = c.z + (t / 3) % 3 - 1, z = c.w + t % 3 - 1;
+    int32_t r = -1;
+    if (c.x >= 0 && c.x < batch && x >= 0 && x < gx && y >= 0 && y < gy && z >= 0 && z < gz) {
+      const unsigned long long key = pack_key(c.x, x, y, z);
+      uint64_t h = mix64(key) & mask;
+      // At least half the slots are empty, so the probe ends.
+      while (true) {
+        const unsigned long long k = keys[h];
+        if (k == key) {
+          r = vals[h];
+          break;
+        }
+        if (k == kEmptyKey) break;
+        h = (h + 1) & mask;
+      }
+    }
+    nbr[g] = r;
+  }
+}
+
+__global__ void k_plan_header(int64_t* __restrict__ header, int64_t n, int64_t npad,
+                              int64_t nblocks, uint4* __restrict__ zero) {
+  if (threadIdx.x == 0) {
+    header[0] = kPlanMagic;
+    header[1] = n;
+    header[2] = npad;
+    header[3] = nblocks;
+  }
+  for (int i = threadIdx.x; i < static_cast<int>(kZeroBytes / sizeof(uint4)); i += blockDim.x)
+    zero[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// ------------------------------------------------------------------------------------------
+// Plan: stable LSD radix sort of (mask, row) pairs, then the tap-major neighbour rows.
+// ------------------------------------------------------------------------------------------
+constexpr int kSortThreads = 256;
+constexpr int kSortItems = 8;
+constexpr int kSortTile = kSortThreads * kSortItems;
+constexpr int kDigitBits = 8;
+constexpr int kDigits = 1 << kDigitBits;
+constexpr int kKeyBits = 26;
+static_assert(kSortThreads == kDigits, "one thread per digit in the histogram and scatter");
+
+struct PlanWorkLayout {
+  int64_t ntiles;
+  size_t off_keys_a, off_keys_b, off_vals_a, off_vals_b, off_hist, total;
+};
+
+inline PlanWorkLayout plan_work_layout(int64_t n) {
+  PlanWorkLayout L;
+  const int64_t m = n > 0 ? n : 1;
+  L.ntiles = (m + kSortTile - 1) / kSortTile;
+  L.off_keys_a = 0;
+  L.off_keys_b = align_up(L.off_keys_a + sizeof(uint32_t) * m);
+  L.off_vals_a = align_up(L.off_keys_b + sizeof(uint32_t) * m);
+  L.off_vals_b = align_up(L.off_vals_a + sizeof(uint32_t) * m);
+  L.off_hist = align_up(L.off_vals_b + sizeof(uint32_t) * m);
+  L.total = align_up(L.off_hist + sizeof(uint32_t) * kDigits * L.ntiles);
+  return L;
+}
+
+// Sort key of a site: bit (t < 13 ? t : t - 1) set when non-centre tap t has a neighbour.
+__global__ void k_mask_keys(const int32_t* __restrict__ nbr, int64_t n, uint32_t* __restrict__ keys,
+                            uint32_t* __restrict__ vals) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t* row = nbr + i * kTaps;
+  uint32_t m = 0;
+#pragma unroll
+  for (int t = 0; t < kTaps; ++t) {
+    if (t == kCentreTap) continue;
+    if (row[t] >= 0) m |= 1u << (t < kCentreTap ? t : t - 1);
+  }
+  keys[i] = m;
+  vals[i] = static_cast<uint32_t>(i);
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_sort_hist(const uint32_t* __restrict__ keys,
+                                                            int64_t n, int shift,
+                                                            uint32_t* __restrict__ hist,
+                                                            int64_t ntiles) {
+  __shared__ uint32_t h[kDigits];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile;
+#pragma unroll
+  for (int k = 0; k < kSortItems; ++k) {
+    const int64_t e = base + k * kSortThreads + threadIdx.x;
+    if (e < n) atomicAdd(&h[(keys[e] >> shift) & (kDigits - 1)], 1u);
+  }
+  __syncthreads();
+  hist[static_cast<int64_t>(threadIdx.x) * ntiles + blockIdx.x] = h[threadIdx.x];
+}
+
+// Exclusive prefix sum of `total` counts in place, one workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void k_sort_scan(uint32_t* __restrict__ a, int64_t total) {
+  __shared__ uint32_t part[1024];
+  const int64_t per = (total + 1023) / 1024;
+  const int64_t lo = threadIdx.x * per;
+  const int64_t hi = lo + per < total ? lo + per : total;
+  uint32_t s = 0;
+  for (int64_t e = lo; e < hi; ++e) s += a[e];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the 1024 partial sums.
+  for (int off = 1; off < 1024; off <<= 1) {
+    const uint32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0u;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  uint32_t run = threadIdx.x > 0 ? part[threadIdx.x - 1] : 0u;
+  for (int64_t e = lo; e < hi; ++e) {
+    const uint32_t v = a[e];
+    a[e] = run;
+    run += v;
+  }
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n,
+    int shift, const uint32_t* __restrict__ hist, int64_t ntiles, uint32_t* __restrict__ keys_out,
+    uint32_t* __restrict__ vals_out) {
+  constexpr int kWaves = kSortThreads / 64;
+  __shared__ uint32_t running[kDigits];
+  __shared__ uint32_t wcnt[kWaves][kDigits];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  running[tid] = hist[static_cast<int64_t>(tid) * ntiles + blockIdx.x];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile;
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  for (int k = 0; k < kSortItems; ++k) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) wcnt[w][tid] = 0;
+    __syncthreads();
+    const int64_t e = base + k * kSortThreads + tid;
+    const bool valid = e < n;
+    const uint32_t key = valid ? keys_in[e] : 0u;
+    const uint32_t d = (key >> shift) & (kDigits - 1);
+    // Lanes of this wave holding the same digit: intersect the ballots of every digit bit.
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kDigitBits; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const unsigned long long bb = __ballot(bit);
+      peers &= bit ? bb : ~bb;
+    }
+    const uint32_t rank = __popcll(peers & lt_mask);
+    if (valid && rank == 0) wcnt[wave][d] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      uint32_t pos = running[d] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][d];
+      keys_out[pos] = key;
+      vals_out[pos] = vals_in[e];
+    }
+    __syncthreads();
+    uint32_t add = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) add += wcnt[w][tid];
+    running[tid] += add;
+    __syncthreads();
+  }
+}
+
+// perm, per-block tap masks and tap-major neighbour rows in sorted order.  One thread per
+// sorted position; each 16-lane group of a wave is one block.
+__global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ nbr, int64_t n,
+                                                   const uint32_t* __restrict__ sorted_rows,
+                                                   int64_t npad, int32_t* __restrict__ perm,
+                                                   uint32_t* __restrict__ bmask,
+                                                   int32_t* __restrict__ gidx) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;  // < npad
+  const int32_t i = r < n ? static_cast<int32_t>(sorted_rows[r]) : -1;
+  perm[r] = i;
+  uint32_t m = 0;
+#pragma unroll
+  for (int t = 0; t < kTaps; ++t) {
+    const int32_t j = i >= 0 ? nbr[static_cast<int64_t>(i) * kTaps + t] : -1;
+    gidx[t * npad + r] = j;
+    if (j >= 0) m |= 1u << t;
+  }
+#pragma unroll
+  for (int off = 1; off < kBlockRows; off <<= 1) m |= __shfl_xor(m, off, 64);
+  if ((threadIdx.x & (kBlockRows - 1)) == 0) bmask[r / kBlockRows] = m;
+}
+
+}  // namespace
+}  // namespace ssc
+
+using namespace ssc;
+
+extern "C" size_t ssc_index_workspace_bytes(int64_t n) {
+  return n < 0 ? 0 : index_layout(n).total;
+}
+
+extern "C" ssc_status ssc_build_index(const int32_t* coords, int64_t n, int32_t batch,
+                                      const int32_t* grid, int32_t* nbr, void* workspace,
+                                      size_t workspace_bytes, int32_t check, void* stream) {
+  if (n < 0 || grid == nullptr) return SSC_ERR_ARG;
+  if (n > 0 && (coords == nullptr || nbr == nullptr || workspace == nullptr)) return SSC_ERR_ARG;
+  if (batch < 1 || batch > kMaxCoord) return SSC_ERR_UNSUPPORTED;
+  for (int a = 0; a < 3; ++a)
+    if (grid[a] < 1 || grid[a] > kMaxCoord) return SSC_ERR_UNSUPPORTED;
+  if (n * kTaps > (int64_t(1) << 40) || n >= (int64_t(1) << 31)) return SSC_ERR_UNSUPPORTED;
+  if (n == 0) return SSC_OK;
+  if (!aligned(coords, 16) || !aligned(workspace, kAlign) || !aligned(nbr, 4)) return SSC_ERR_ARG;
+  const IndexLayout L = index_layout(n);
+  if (workspace_bytes < L.total) return SSC_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
+  auto* keys = reinterpret_cast<unsigned long long*>(ws + L.off_keys);
+  auto* vals = reinterpret_cast<int32_t*>(ws + L.off_vals);
+  const int bs = 256;
+  const uint64_t init_blocks = std::min<uint64_t>((L.cap + bs - 1) / bs, 8192);
+  k_table_init<<<static_cast<unsigned>(init_blocks), bs, 0, s>>>(keys, L.cap, counters);
+  const unsigned ins_blocks = static_cast<unsigned>(std::min<int64_t>((n + bs - 1) / bs, 65536));
+  k_insert<<<ins_blocks, bs, 0, s>>>(
+      reinterpret_cast<const int4*>(coords), n, batch, grid[0], grid[1], grid[2], keys, vals,
+      L.cap - 1, counters);
+  const int64_t q = n * kTaps;
+  const unsigned q_blocks = static_cast<unsigned>(std::min<int64_t>((q + bs - 1) / bs, 262144));
+  k_query<<<q_blocks, bs, 0, s>>>(
+      reinterpret_cast<const int4*>(coords), n, batch, grid[0], grid[1], grid[2], keys, vals,
+      L.cap - 1, nbr);
+  if (launch_status() != SSC_OK) return SSC_ERR_HIP;
+  if (check) {
+    uint32_t host[2] = {0, 0};
+    if (hipMemcpyAsync(host, counters, sizeof(host), hipMemcpyDeviceToHost, s) != hipSuccess)
+      return SSC_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SSC_ERR_HIP;
+    if (host[0]) return SSC_ERR_COORD_RANGE;
+    if (host[1]) return SSC_ERR_DUPLICATE;
+  }
+  return SSC_OK;
+}
+
+extern "C" size_t ssc_plan_bytes(int64_t n) { return n < 0 ? 0 : plan_layout(n).total; }
+
+extern "C" size_t ssc_plan_workspace_bytes(int64_t n) {
+  return n < 0 ? 0 : plan_work_layout(n).total;
+}
+
+extern "C" ssc_status ssc_build_plan(const int32_t* nbr, int64_t n, void* plan, size_t plan_bytes,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (n < 0 || plan == nullptr || workspace == nullptr) return SSC_ERR_ARG;
+  if (n > 0 && nbr == nullptr) return SSC_ERR_ARG;
+  if (n >= (int64_t(1) << 31)) return SSC_ERR_UNSUPPORTED;
+  if (!aligned(plan, kAlign) || !aligned(workspace, kAlign)) return SSC_ERR_ARG;
+  const PlanLayout P = plan_layout(n);
+  const PlanWorkLayout W = plan_work_layout(n);
+  if (plan_bytes < P.total || workspace_bytes < W.total) return SSC_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  char* pb = static_cast<char*>(plan);
+  char* ws = static_cast<char*>(workspace);
+  k_plan_header<<<1, 64, 0, s>>>(reinterpret_cast<int64_t*>(pb), n, P.npad, P.nblocks,
+                                 reinterpret_cast<uint4*>(pb + P.off_zero));
+  uint32_t* keys[2] = {reinterpret_cast<uint32_t*>(ws + W.off_keys_a),
+                       reinterpret_cast<uint32_t*>(ws + W.off_keys_b)};
+  uint32_t* vals[2] = {reinterpret_cast<uint32_t*>(ws + W.off_vals_a),
+                       reinterpret_cast<uint32_t*>(ws + W.off_vals_b)};
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + W.off_hist);
+  int cur = 0;
+  if (n > 0) {
+    k_mask_keys<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(nbr, n, keys[0], vals[0]);
+    for (int shift = 0; shift < kKeyBits; shift += kDigitBits) {
+      k_sort_hist<<<static_cast<unsigned>(W.ntiles), kSortThreads, 0, s>>>(keys[cur], n, shift,
+                                                                           hist, W.ntiles);
+      k_sort_scan<<<1, 1024, 0, s>>>(hist, static_cast<int64_t>(kDigits) * W.ntiles);
+      k_sort_scatter<<<static_cast<unsigned>(W.ntiles), kSortThreads, 0, s>>>(
+          keys[cur], vals[cur], n, shift, hist, W.ntiles, keys[cur ^ 1], vals[cur ^ 1]);
+      cur ^= 1;
+    }
+  }
+  k_plan_fill<<<static_cast<unsigned>(P.npad / 256), 256, 0, s>>>(
+      nbr, n, vals[cur], P.npad, reinterpret_cast<int32_t*>(pb + P.off_perm),
+      reinterpret_cast<uint32_t*>(pb + P.off_bmask), reinterpret_cast<int32_t*>(pb + P.off_gidx));
+  return launch_status();
+}

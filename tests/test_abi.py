@@ -1,0 +1,130 @@
+"""libssc.so loads and exports every entry point include/ssc.h declares; host-side argument
+checks return their status before anything is launched (CPU only, no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import submanifold_sparse_convolution_coord_amd as ssc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssc.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssc_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssc.library_path()):
+        from submanifold_sparse_convolution_coord_amd import build
+        build.build()
+    return ssc.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.ssc_version() >= 100
+    for st in range(-6, 1):
+        assert lib.ssc_status_string(st)
+    assert b"unknown" in lib.ssc_status_string(42)
+
+
+def test_workspace_sizes(lib):
+    assert lib.ssc_index_workspace_bytes(0) > 0
+    a, b = lib.ssc_index_workspace_bytes(1000), lib.ssc_index_workspace_bytes(100000)
+    assert b > a and b >= 100000 * 2 * 12
+    assert lib.ssc_index_workspace_bytes(-1) == 0
+    p = lib.ssc_plan_bytes(1000)
+    assert p >= 1024 * 28 * 4 and p % 256 == 0
+    assert lib.ssc_plan_workspace_bytes(1000) >= 1000 * 16
+    assert lib.ssc_conv_workspace_bytes(128, 128, ssc.SSC_BF16) >= 27 * 128 * 128 * 2
+    assert lib.ssc_conv_workspace_bytes(16, 16, ssc.SSC_F32) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)       # aligned, never dereferenced: every call below returns
+GRID = (ctypes.c_int32 * 3)(8, 8, 8)  # before launching anything
+
+
+def test_build_index_argument_errors(lib):
+    f = lib.ssc_build_index
+    assert f(FAKE, -1, 1, GRID, FAKE, FAKE, 1 << 30, 0, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 10, 1, None, FAKE, FAKE, 1 << 30, 0, None) == ssc.SSC_ERR_ARG
+    assert f(None, 10, 1, GRID, FAKE, FAKE, 1 << 30, 0, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 10, 0, GRID, FAKE, FAKE, 1 << 30, 0, None) == ssc.SSC_ERR_UNSUPPORTED
+    assert f(FAKE, 10, 70000, GRID, FAKE, FAKE, 1 << 30, 0, None) == ssc.SSC_ERR_UNSUPPORTED
+    bad = (ctypes.c_int32 * 3)(8, 0, 8)
+    assert f(FAKE, 10, 1, bad, FAKE, FAKE, 1 << 30, 0, None) == ssc.SSC_ERR_UNSUPPORTED
+    big = (ctypes.c_int32 * 3)(8, 65536, 8)
+    assert f(FAKE, 10, 1, big, FAKE, FAKE, 1 << 30, 0, None) == ssc.SSC_ERR_UNSUPPORTED
+    assert f(FAKE, 10, 1, GRID, FAKE, FAKE, 16, 0, None) == ssc.SSC_ERR_WORKSPACE
+    assert f(ctypes.c_void_p((1 << 20) + 4), 10, 1, GRID, FAKE, FAKE, 1 << 30, 0,
+             None) == ssc.SSC_ERR_ARG
+    assert f(None, 0, 1, GRID, None, None, 0, 1, None) == ssc.SSC_OK  # empty: nothing to do
+
+
+def test_build_plan_argument_errors(lib):
+    f = lib.ssc_build_plan
+    assert f(FAKE, -1, FAKE, 1 << 30, FAKE, 1 << 30, None) == ssc.SSC_ERR_ARG
+    assert f(None, 10, FAKE, 1 << 30, FAKE, 1 << 30, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 10, None, 1 << 30, FAKE, 1 << 30, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 10, FAKE, 64, FAKE, 1 << 30, None) == ssc.SSC_ERR_WORKSPACE
+    assert f(FAKE, 10, FAKE, 1 << 30, FAKE, 8, None) == ssc.SSC_ERR_WORKSPACE
+    assert f(FAKE, 10, ctypes.c_void_p((1 << 20) + 16), 1 << 30, FAKE, 1 << 30,
+             None) == ssc.SSC_ERR_ARG
+
+
+def test_conv_argument_errors(lib):
+    f = lib.ssc_subm_conv3d
+    big = 1 << 30
+    ok = dict(x=FAKE, din=ssc.SSC_BF16, w=FAKE, b=None, plan=FAKE, n=0, cin=64, cout=64, y=FAKE,
+              dout=ssc.SSC_F32, ws=FAKE, wsb=big)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["din"], a["w"], a["b"], a["plan"], a["n"], a["cin"], a["cout"], a["y"],
+                 a["dout"], a["ws"], a["wsb"], None)
+
+    assert call() == ssc.SSC_OK                        # n = 0 launches nothing
+    assert call(din=7) == ssc.SSC_ERR_ARG
+    assert call(dout=-1) == ssc.SSC_ERR_ARG
+    assert call(n=-5) == ssc.SSC_ERR_ARG
+    assert call(cin=0) == ssc.SSC_ERR_UNSUPPORTED
+    assert call(cout=4096) == ssc.SSC_ERR_UNSUPPORTED
+    assert call(w=None) == ssc.SSC_ERR_ARG
+    assert call(plan=None) == ssc.SSC_ERR_ARG
+    assert call(n=10, x=None) == ssc.SSC_ERR_ARG
+    assert call(n=10, x=ctypes.c_void_p((1 << 20) + 2)) == ssc.SSC_ERR_ARG
+    assert call(n=10, wsb=100) == ssc.SSC_ERR_WORKSPACE
+    assert call(n=10, ws=None) == ssc.SSC_ERR_WORKSPACE
+    lf = lib.ssc_linear
+    assert lf(FAKE, ssc.SSC_BF16, FAKE, None, 0, 64, 64, FAKE, ssc.SSC_F32, FAKE, big,
+              None) == ssc.SSC_OK
+    assert lf(FAKE, 3, FAKE, None, 10, 64, 64, FAKE, ssc.SSC_F32, FAKE, big,
+              None) == ssc.SSC_ERR_ARG
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        ssc.build_index(torch.zeros((4, 4), dtype=torch.int32), 1, (4, 4, 4))
+
+
+def test_product_path_does_not_import_oracle():
+    # The package and its binding never reach the CPU oracle.
+    pkg = os.path.dirname(ssc.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in text and "liboracle" not in text, fn

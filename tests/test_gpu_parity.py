@@ -1,0 +1,259 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Bars: neighbour maps bit-exact; conv outputs max|err| <= tau * RMS(oracle) with tau = 1e-4
+for fp32 inputs and 2e-2 for bf16 inputs, taken on the fp32-stored output; the bf16-stored
+output must equal the round-to-nearest-even bf16 of the fp32-stored output bit for bit.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import submanifold_sparse_convolution_coord_amd as ssc
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TAU = {"f32": 1e-4, "bf16": 2e-2}
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(y, ref):
+    y = np.asarray(y, np.float64)
+    rms = np.sqrt((ref ** 2).mean()) if ref.size else 1.0
+    return float(np.abs(y - ref).max() / rms) if ref.size else 0.0
+
+
+def rne_bf16(t: torch.Tensor) -> torch.Tensor:
+    return t.to(torch.bfloat16)
+
+
+@functools.lru_cache(maxsize=2)
+def workload_case(name, shuffle=False):
+    w = workloads.make(name, shuffle=shuffle)
+    m = oracle.build_map(w.coords, w.batch, w.grid)
+    return w, m
+
+
+def run_gpu(coords, batch, grid):
+    c = torch.from_numpy(coords).to(DEV)
+    idx = ssc.SubMIndex(c, batch, grid)
+    return idx
+
+
+@pytest.mark.parametrize("name,shuffle", [
+    ("tiny", False), ("tiny", True), ("iid128", False), ("iid128", True), ("shell256", False),
+    ("batch4", False), ("shell512", False),
+])
+def test_workload_parity(name, shuffle):
+    say(f"[parity] workload={name} shuffle={shuffle}")
+    w, m = workload_case(name, shuffle)
+    idx = run_gpu(w.coords, w.batch, w.grid)
+    nbr = idx.nbr.cpu().numpy()
+    assert np.array_equal(nbr, m), f"{name}: neighbour map differs from the oracle"
+
+    layer = w.layers[0]
+    x = w.feats.to(DEV)
+    wt = layer.weight.to(DEV)
+    b = layer.bias.to(DEV)
+    y32 = idx.conv(x, wt, b, out_dtype=torch.float32)
+    ybf = idx.conv(x, wt, b, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.conv(w.feats.float().numpy(), layer.weight.float().numpy(),
+                      layer.bias.numpy(), m)
+    err = rel_err(y32.cpu().numpy(), ref)
+    say(f"[parity] {name} n={w.n} k3 max|err|/rms = {err:.3e}")
+    assert err <= TAU[w.dtype]
+    assert torch.equal(ybf.cpu().view(torch.int16), rne_bf16(y32.cpu()).view(torch.int16))
+
+    if len(w.layers) > 1:  # batch4: k=1 128->128 on the bf16 k=3 output
+        l2 = w.layers[1]
+        x2 = ybf
+        y2 = ssc.linear(x2, l2.weight.to(DEV), l2.bias.to(DEV))
+        torch.cuda.synchronize()
+        ref2 = oracle.linear(x2.float().cpu().numpy(), l2.weight.float().numpy(), l2.bias.numpy())
+        err2 = rel_err(y2.cpu().numpy(), ref2)
+        say(f"[parity] {name} k1 max|err|/rms = {err2:.3e}")
+        assert err2 <= TAU[w.dtype]
+        # chained: the oracle rounds its own k=3 result to bf16 and applies the k=1 layer
+        ref_chain = oracle.linear(rne_bf16(torch.from_numpy(ref).float()).float().numpy(),
+                                  l2.weight.float().numpy(), l2.bias.numpy())
+        assert rel_err(y2.cpu().numpy(), ref_chain) <= TAU[w.dtype]
+
+
+def small_case(seed, batch, grid, frac, cin, cout, dtype=torch.bfloat16, bias=True):
+    rng = np.random.default_rng(seed)
+    n = max(1, int(round(frac * grid[0] * grid[1] * grid[2])))
+    coords = workloads.random_sites(rng, batch, grid, n)
+    coords = coords[rng.permutation(len(coords))]
+    x = torch.from_numpy(rng.standard_normal((len(coords), cin), dtype=np.float32)).to(dtype)
+    w = (torch.from_numpy(rng.standard_normal((27, cin, cout), dtype=np.float32)) /
+         np.sqrt(27 * cin)).to(dtype)
+    b = torch.from_numpy(rng.standard_normal(cout, dtype=np.float32)) if bias else None
+    return coords, x, w, b
+
+
+def check_conv(coords, batch, grid, x, w, b, tau):
+    m = oracle.build_map(coords, batch, grid)
+    idx = run_gpu(coords, batch, grid)
+    assert np.array_equal(idx.nbr.cpu().numpy(), m)
+    y = idx.conv(x.to(DEV), w.to(DEV), None if b is None else b.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.conv(x.float().numpy(), w.float().numpy(), None if b is None else b.numpy(), m)
+    err = rel_err(y.cpu().numpy(), ref)
+    assert err <= tau, err
+    return idx, y
+
+
+@pytest.mark.parametrize("cin,cout", [(c, o) for c in (32, 64, 128) for o in (16, 32, 64, 128)])
+def test_mfma_shapes_ragged(cin, cout):
+    # ~1500 sites: several 128-row tiles and a ragged last tile
+    say(f"[shapes] cin={cin} cout={cout}")
+    coords, x, w, b = small_case(cin * 7 + cout, 2, (20, 20, 20), 0.09, cin, cout)
+    check_conv(coords, 2, (20, 20, 20), x, w, b, TAU["bf16"])
+
+
+@pytest.mark.parametrize("cin,cout,dtype", [
+    (16, 16, torch.float32), (5, 7, torch.float32), (16, 16, torch.bfloat16),
+    (48, 24, torch.bfloat16), (3, 130, torch.bfloat16),
+])
+def test_valu_paths(cin, cout, dtype):
+    say(f"[valu] cin={cin} cout={cout} {dtype}")
+    coords, x, w, b = small_case(cin + cout, 1, (12, 12, 12), 0.3, cin, cout, dtype)
+    check_conv(coords, 1, (12, 12, 12), x, w, b,
+               TAU["f32"] if dtype == torch.float32 else TAU["bf16"])
+
+
+@pytest.mark.parametrize("n_sites", [1, 2, 15, 16, 17, 255, 256, 257])
+def test_ragged_site_counts(n_sites):
+    say(f"[ragged] n={n_sites}")
+    rng = np.random.default_rng(n_sites)
+    grid = (8, 8, 8)
+    coords = workloads.random_sites(rng, 1, grid, n_sites)
+    x = torch.from_numpy(rng.standard_normal((n_sites, 32), dtype=np.float32)).to(torch.bfloat16)
+    w = (torch.from_numpy(rng.standard_normal((27, 32, 32), dtype=np.float32)) / 30).to(torch.bfloat16)
+    b = torch.from_numpy(rng.standard_normal(32, dtype=np.float32))
+    check_conv(coords, 1, grid, x, w, b, TAU["bf16"])
+
+
+def test_full_occupancy_and_boundaries():
+    say("[full] 10x9x8 fully occupied")
+    grid = (10, 9, 8)
+    coords = workloads.coords_from_occupancy([np.ones(grid, bool)])
+    rng = np.random.default_rng(3)
+    x = torch.from_numpy(rng.standard_normal((len(coords), 64), dtype=np.float32)).to(torch.bfloat16)
+    w = (torch.from_numpy(rng.standard_normal((27, 64, 64), dtype=np.float32)) / 40).to(torch.bfloat16)
+    idx, _ = check_conv(coords, 1, grid, x, w, None, TAU["bf16"])
+    nbr = idx.nbr.cpu().numpy()
+    assert (nbr >= 0).sum() == np.prod([3 * g - 2 for g in grid])
+
+
+def test_isolated_sites_only_centre():
+    say("[isolated]")
+    g = 16
+    pts = np.array([(x, y, z) for x in range(0, g, 2) for y in range(0, g, 2) for z in range(0, g, 2)])
+    coords = np.concatenate([np.zeros((len(pts), 1), np.int32), pts.astype(np.int32)], 1)
+    rng = np.random.default_rng(4)
+    x = torch.from_numpy(rng.standard_normal((len(coords), 64), dtype=np.float32)).to(torch.bfloat16)
+    w = (torch.from_numpy(rng.standard_normal((27, 64, 32), dtype=np.float32)) / 40).to(torch.bfloat16)
+    idx, y = check_conv(coords, 1, (g, g, g), x, w, None, TAU["bf16"])
+    assert (idx.nbr.cpu().numpy() >= 0).sum() == len(coords)
+
+
+def test_identity_centre_tap_exact():
+    say("[identity]")
+    coords, x, _, _ = small_case(5, 2, (16, 16, 16), 0.1, 64, 64)
+    w = torch.zeros((27, 64, 64))
+    w[13] = torch.eye(64)
+    idx = run_gpu(coords, 2, (16, 16, 16))
+    y = idx.conv(x.to(DEV), w.to(torch.bfloat16).to(DEV), None)
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu(), x.float())
+
+
+def test_translation_and_determinism():
+    say("[translation]")
+    coords, x, w, b = small_case(6, 1, (24, 24, 24), 0.1, 128, 128)
+    idx = run_gpu(coords, 1, (40, 40, 40))
+    idx2 = run_gpu(coords + np.array([0, 5, 9, 13], np.int32), 1, (40, 40, 40))
+    assert torch.equal(idx.nbr, idx2.nbr)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    y1 = idx.conv(xd, wd, bd)
+    y2 = idx2.conv(xd, wd, bd)
+    y3 = idx.conv(xd, wd, bd)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+
+
+def test_row_order_does_not_change_results():
+    # each output row is computed the same way whatever block it lands in
+    say("[order]")
+    coords, x, w, b = small_case(8, 1, (24, 24, 24), 0.1, 64, 128)
+    p = np.random.default_rng(8).permutation(len(coords))
+    idx = run_gpu(coords, 1, (24, 24, 24))
+    idxp = run_gpu(np.ascontiguousarray(coords[p]), 1, (24, 24, 24))
+    y = idx.conv(x.to(DEV), w.to(DEV), b.to(DEV))
+    yp = idxp.conv(x[p].contiguous().to(DEV), w.to(DEV), b.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu()[torch.from_numpy(p)], yp.cpu())
+
+
+def test_batch_isolation():
+    say("[batch]")
+    one, x, w, b = small_case(9, 1, (12, 12, 12), 0.2, 32, 32)
+    two = np.concatenate([one, one + np.array([1, 0, 0, 0], np.int32)])
+    x2 = torch.cat([x, -x])
+    idx = run_gpu(two, 2, (12, 12, 12))
+    y = idx.conv(x2.to(DEV), w.to(DEV), b.to(DEV)).cpu()
+    idx1 = run_gpu(one, 1, (12, 12, 12))
+    y1 = idx1.conv(x.to(DEV), w.to(DEV), b.to(DEV)).cpu()
+    ym = idx1.conv((-x).contiguous().to(DEV), w.to(DEV), b.to(DEV)).cpu()
+    n = len(one)
+    assert torch.equal(y[:n], y1) and torch.equal(y[n:], ym)
+
+
+@pytest.mark.parametrize("bad,status", [([0, 12, 0, 0], ssc.SSC_ERR_COORD_RANGE),
+                                        ([1, 0, 0, 0], ssc.SSC_ERR_COORD_RANGE),
+                                        ([0, 0, -1, 0], ssc.SSC_ERR_COORD_RANGE),
+                                        (None, ssc.SSC_ERR_DUPLICATE)])
+def test_bad_coordinates_are_reported(bad, status):
+    say(f"[errors] {bad}")
+    coords, _, _, _ = small_case(10, 1, (12, 12, 12), 0.1, 32, 32)
+    row = coords[3] if bad is None else np.array(bad, np.int32)
+    c = np.concatenate([coords, row[None]]).astype(np.int32)
+    with pytest.raises(ssc.SscError) as e:
+        ssc.build_index(torch.from_numpy(c).to(DEV), 1, (12, 12, 12))
+    assert e.value.status == status
+
+
+def test_empty_input():
+    say("[empty]")
+    c = torch.zeros((0, 4), dtype=torch.int32, device=DEV)
+    idx = ssc.SubMIndex(c, 1, (4, 4, 4))
+    y = idx.conv(torch.zeros((0, 32), dtype=torch.bfloat16, device=DEV),
+                 torch.zeros((27, 32, 16), dtype=torch.bfloat16, device=DEV), None)
+    assert y.shape == (0, 16)
+
+
+@pytest.mark.parametrize("n,cin,cout", [(1, 64, 64), (1000, 64, 128), (4097, 128, 128),
+                                        (300, 32, 16), (77, 16, 16)])
+def test_linear(n, cin, cout):
+    say(f"[linear] n={n} {cin}->{cout}")
+    rng = np.random.default_rng(n)
+    x = torch.from_numpy(rng.standard_normal((n, cin), dtype=np.float32)).to(torch.bfloat16)
+    w = (torch.from_numpy(rng.standard_normal((cin, cout), dtype=np.float32)) / np.sqrt(cin)).to(torch.bfloat16)
+    b = torch.from_numpy(rng.standard_normal(cout, dtype=np.float32))
+    y = ssc.linear(x.to(DEV), w.to(DEV), b.to(DEV))
+    ybf = ssc.linear(x.to(DEV), w.to(DEV), b.to(DEV), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.linear(x.float().numpy(), w.float().numpy(), b.numpy())
+    assert rel_err(y.cpu().numpy(), ref) <= TAU["bf16"]
+    assert torch.equal(ybf.cpu().view(torch.int16), rne_bf16(y.cpu()).view(torch.int16))
