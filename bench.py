@@ -60,15 +60,55 @@ def counted_traffic(kernel: str, digest: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(d: str, kernel_substr: str, counter: str):
+    """Per-dispatch values of `counter` for kernels whose name contains `kernel_substr`, read
+    from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if kernel_substr in row.get("Kernel_Name", "") and row.get("Counter_Name") == counter:
+                vals.append(float(row["Counter_Value"]))
+    return vals
+
+
+def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mb, out_path):
+    """HBM traffic of the conv kernel per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    scaled by what the same counters read for a plain device copy of cal_mb MiB."""
+    conv = "k_subm_lds"
+    copy = "copy"  # torch's elementwise copy kernel
+    f = _counter_rows(fetch_dir, conv, "FETCH_SIZE")
+    w = _counter_rows(write_dir, conv, "WRITE_SIZE")
+    cf = _counter_rows(cal_fetch_dir, copy, "FETCH_SIZE")
+    cw = _counter_rows(cal_write_dir, copy, "WRITE_SIZE")
+    if not (f and w and cf and cw):
+        raise SystemExit("missing counter rows")
+    known = cal_mb * 1024.0  # KiB read and written by the copy
+    fetch_scale = known / float(np.median(cf))
+    write_scale = known / float(np.median(cw))
+    fetch_b = float(np.mean(f)) * 1024.0 * fetch_scale
+    write_b = float(np.mean(w)) * 1024.0 * write_scale
+    d = {"kernel": "k_subm_lds<128,128>", "workload": "iid128", "source_digest": source_digest(),
+         "fetch_kib_per_dispatch": float(np.mean(f)), "write_kib_per_dispatch": float(np.mean(w)),
+         "copy_calibration_mib": cal_mb, "copy_fetch_kib": float(np.median(cf)),
+         "copy_write_kib": float(np.median(cw)), "fetch_scale": fetch_scale,
+         "write_scale": write_scale, "hbm_bytes_per_launch": fetch_b + write_b,
+         "hbm_read_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b}
+    json.dump(d, open(out_path, "w"), indent=1)
+    print(json.dumps(d))
+
+
 def cpu_baseline(w, m_nbr) -> dict:
     """The CPU oracle as it stands (fp64 dictionary + per-voxel loop), warm: map prebuilt,
-    conv over every site of the same workload; median of three runs."""
+    conv over every site of the same workload, repeated for at least a second of wall time;
+    median run."""
     import oracle
     x = w.feats.float().numpy()
     wt = w.layers[0].weight.float().numpy()
     b = w.layers[0].bias.numpy()
     ts = []
-    for _ in range(3):
+    while len(ts) < 5 or (sum(ts) < 1.0 and len(ts) < 50):
         t0 = time.perf_counter()
         oracle.conv(x, wt, b, m_nbr)
         ts.append(time.perf_counter() - t0)
@@ -78,7 +118,7 @@ def cpu_baseline(w, m_nbr) -> dict:
     return {"value": round(mvox_per_s(w.n, t), 4), "unit": "Mvox/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"full workload, all {w.n} sites, warm (map prebuilt), fp64, "
-                      f"median of {len(ts)} runs of {t:.2f} s"}
+                      f"median of {len(ts)} runs of {t:.3f} s ({sum(ts):.1f} s wall)"}
 
 
 def main():
@@ -89,7 +129,26 @@ def main():
     ap.add_argument("--workload", default="iid128")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (for counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR",
+                    "CAL_FETCH_DIR", "CAL_WRITE_DIR", "CAL_MIB"),
+                    help="write profiles/conv_iid128_counters.json from rocprofv3 --pmc output")
     args = ap.parse_args()
+    if args.summarize_counters:
+        a = args.summarize_counters
+        summarize_counters(a[0], a[1], a[2], a[3], int(a[4]),
+                           os.path.join(ROOT, "profiles", "conv_iid128_counters.json"))
+        return
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(args.copy_calibration * 262144, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration} MiB x3")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path is a single-GPU "
               "kernel and this build has no multi-GPU mode", file=sys.stderr)
@@ -161,7 +220,7 @@ def main():
     tflops_kernel = flops / (ms_kernel * 1e-3) / 1e12
     tflops_step = flops / (ms_step * 1e-3) / 1e12
     value = mvox_per_s(w.n, ms_step * 1e-3)
-    kname = f"k_conv_mfma<{cin},{cout}>"
+    kname = f"k_subm_lds<{cin},{cout}>"
     digest = source_digest()
     traffic = counted_traffic(kname, digest)
 

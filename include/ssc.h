@@ -135,11 +135,12 @@ ssc_status ssc_subm_conv3d(const void* feats, int32_t in_dtype, const void* weig
 
 /* Weights re-laid out once for the matrix cores, for callers that keep a layer's weights
  * (the same re-layout ssc_subm_conv3d performs into its workspace on every call).
- *   weight  [taps, cin, cout] bf16 (taps = 27 for k=3, 1 for k=1).
- *   packed  >= ssc_packed_weight_bytes(taps, cin, cout) bytes, 256-byte aligned; receives
- *           [taps, cout, cin] bf16.
- * Only bf16 with cin % 32 == 0, cout % 16 == 0, cin <= 128, cout <= 128 (the shapes the
- * matrix-core kernels are built for); otherwise SSC_ERR_UNSUPPORTED. */
+ *   weight  [27, cin, cout] bf16.
+ *   packed  >= ssc_packed_weight_bytes(27, cin, cout) bytes, 256-byte aligned; receives the
+ *           weights in the k=3 kernel's fragment order (an opaque layout of the same bytes
+ *           count, valid only for ssc_subm_conv3d_packed with the same cin and cout).
+ * Only taps = 27 and bf16 with cin in {32, 64, 128}, cout in {16, 32, 64, 128} (the shapes
+ * the matrix-core kernels are built for); otherwise SSC_ERR_UNSUPPORTED. */
 size_t ssc_packed_weight_bytes(int32_t taps, int32_t cin, int32_t cout);
 ssc_status ssc_pack_weights(const void* weight, int32_t taps, int32_t cin, int32_t cout,
                             void* packed, size_t packed_bytes, void* stream);

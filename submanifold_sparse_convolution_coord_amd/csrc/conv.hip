@@ -21,7 +21,8 @@
 // are bit-identical run to run, and independent of the site order.
 //
 // The matrix cores want both operands k-contiguous per lane, so W is re-laid out per call
-// as Wt[t][o][c] (k_transpose_w, 27*Cin*Cout*2 bytes, in the caller's workspace).
+// (27*Cin*Cout*2 bytes in the caller's workspace): fragment by fragment for the k=3 kernel
+// (k_pack_frag), as Wt[o][c] for the k=1 kernel (k_transpose_w).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -179,8 +180,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv_mfma(
 //   * the 16 neighbour feature rows of every block that has tap t are copied into LDS by the
 //     gfx950 direct global->LDS loads (global_load_lds_dwordx4: no VGPRs held while in
 //     flight); a missing neighbour copies a zero row;
-//   * each wave loads its column slice of W[t] (packed [Cout][Cin]) into VGPRs as matrix-core
-//     B fragments, into the register set of the stage's parity.
+//   * each wave loads its column slice of W[t] into VGPRs as matrix-core B fragments, into
+//     the register set of the stage's parity.  The packed weights are stored fragment by
+//     fragment, so each of these loads reads 1 KB of contiguous memory.
 // While the matrix cores consume stage q, stage q+1 is in flight.  Per tap there is one wait
 // (vmcnt 0, lgkmcnt 0: at that point only stage q is outstanding) and one bare workgroup
 // barrier, which makes the copies of all waves visible and proves that every wave finished
@@ -188,6 +190,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv_mfma(
 // 16-byte chunks of each LDS row are XOR-swizzled so that the 16 rows a fragment read touches
 // fall in distinct banks.  Waves are WR x WC: column group wc owns COUT/WC output columns,
 // row group wr owns blocks wr, wr+WR, ...; fp32 accumulators stay in VGPRs.
+// The epilogue adds the bias, stages the tile's output rows in LDS (over the dead gather
+// buffers) and writes every row with 16-byte stores at its original index.
 // ------------------------------------------------------------------------------------------
 template <int CIN, int COUT, int NB, int WR, int WC>
 struct LdsCfg {
@@ -200,14 +204,47 @@ struct LdsCfg {
   static constexpr int CS = COUT / WC;            // output columns per wave
   static constexpr int NCT = CS / 16;             // 16-column MFMA tiles per wave
   static constexpr int KS = CIN / 32;             // k-steps
-  static constexpr int NW = NCT * KS;             // weight fragment loads per stage
   static constexpr int BPW = NB / WR;             // blocks accumulated per wave
   static constexpr int G_TAPS_PER_COPY = 64 / (NB * 4);  // taps of indices per 1 KB copy
+  // LDS arena: [gather buffer 0][gather buffer 1][indices 27 x NB*16][row ids NB*16]
+  static constexpr int ABUF_BYTES = NB * A_BLOCK * 2;
+  static constexpr int OFF_A1 = ABUF_BYTES;
+  static constexpr int OFF_G = 2 * ABUF_BYTES;
+  static constexpr int OFF_P = OFF_G + kTaps * NB * 16 * 4;
+  static constexpr int SMEM_BYTES = OFF_P + NB * 16 * 4;
+  static constexpr int STAGE_BYTES = OFF_P;       // reusable for the output rows at the end
   static_assert(16 % WAVES == 0 && A_LANES <= 64 && A_LANES > 0, "block copy shape");
   static_assert(CIN % 32 == 0 && COUT % (16 * WC) == 0 && NB % WR == 0, "tile shape");
   static_assert(NB * 4 <= 64 && 64 % (NB * 4) == 0, "index copy shape");
-  static_assert(NB + NW < 64, "vmcnt range");
 };
+
+// Fragment-major packed weights for WC column groups: element
+//   Wp[(((t*WC + wc)*NCT + c)*KS + s)*512 + lane*8 + e] = W[t][32s + 8(lane>>4) + e][wc*CS + 16c + (lane&15)]
+// i.e. the B fragment of (tap t, wave column group wc, column tile c, k-step s) for `lane`.
+__global__ __launch_bounds__(256) void k_pack_frag(const uint16_t* __restrict__ W, int taps,
+                                                   int cin, int cout, int wc_groups,
+                                                   uint16_t* __restrict__ Wp) {
+  const int cs = cout / wc_groups, nct = cs / 16, ks = cin / 32;
+  const int64_t total = static_cast<int64_t>(taps) * wc_groups * nct * ks * 64;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
+       idx += stride) {
+    const int lane = static_cast<int>(idx % 64);
+    int64_t rest = idx / 64;
+    const int s = static_cast<int>(rest % ks);
+    rest /= ks;
+    const int c = static_cast<int>(rest % nct);
+    rest /= nct;
+    const int wc = static_cast<int>(rest % wc_groups);
+    const int64_t t = rest / wc_groups;
+    const int o = wc * cs + c * 16 + (lane & 15);
+    const int k0 = s * 32 + (lane >> 4) * 8;
+    const uint16_t* src = W + (t * cin + k0) * cout + o;
+    uint16_t* dst = Wp + idx * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = src[static_cast<int64_t>(e) * cout];
+  }
+}
 
 // LDS byte address of a __shared__ location (wave-uniform in every use below).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -247,16 +284,16 @@ __device__ __forceinline__ int swz(int r) {
 // by this wave has completed.
 __device__ __forceinline__ void wait_vm_lgkm0() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
-__device__ __forceinline__ bf16x8_t lds_read16(const uint16_t* p) {
+__device__ __forceinline__ bf16x8_t lds_read16(const void* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
 }
 
-// Copies of stage (union index q, tap t): NB block copies into sA, one per block.
+// Copies of stage (union index q, tap t): one block copy per block that has tap t.
 template <int CIN, int COUT, int NB, int WR, int WC>
 __device__ __forceinline__ void issue_gather(int q, int t, const uint32_t (&bm)[NB],
                                              const uint16_t* __restrict__ X,
                                              const uint16_t* __restrict__ zrow,
-                                             const int32_t* sG, uint16_t* sA, int wave,
+                                             const int32_t* sG, const char* sA, int wave,
                                              int lane) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
   const int rr = (wave * C::RPW + lane / C::CPR) & 15;
@@ -270,21 +307,22 @@ __device__ __forceinline__ void issue_gather(int q, int t, const uint32_t (&bm)[
     if (!((bm[b] >> t) & 1u)) continue;
     const uint16_t* src =
         j[b] >= 0 ? X + static_cast<int64_t>(j[b]) * CIN + chunk * 8 : zrow + chunk * 8;
-    if (lane < C::A_LANES) dma16(src, lds_addr(sA + b * C::A_BLOCK + wave * C::RPW * CIN));
+    if (lane < C::A_LANES)
+      dma16(src, lds_addr(sA + b * C::A_BLOCK * 2 + wave * C::RPW * CIN * 2));
   }
 }
 
 template <int CIN, int COUT, int NB, int WR, int WC>
-__device__ __forceinline__ void load_weights(int t, const uint16_t* __restrict__ Wt, int wc,
+__device__ __forceinline__ void load_weights(int t, const uint16_t* __restrict__ Wp, int wc,
                                              int lane,
                                              bf16x8_t (&bw)[COUT / WC / 16][CIN / 32]) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
-  const uint16_t* w = Wt + (static_cast<int64_t>(t) * COUT + wc * C::CS + (lane & 15)) * CIN +
-                      (lane >> 4) * 8;
+  const uint16_t* w =
+      Wp + ((static_cast<int64_t>(t) * WC + wc) * (C::NCT * C::KS)) * 512 + lane * 8;
 #pragma unroll
   for (int c = 0; c < C::NCT; ++c)
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) bw[c][s] = load_bf16x8(w + c * 16 * CIN + s * 32);
+    for (int s = 0; s < C::KS; ++s) bw[c][s] = load_bf16x8(w + (c * C::KS + s) * 512);
 }
 
 // Byte offsets, within a block slot, of this lane's A fragments (row lane&15, logical chunk
@@ -302,20 +340,19 @@ __device__ __forceinline__ void a_frag_offsets(int lane, uint32_t (&off)[CIN / 3
 }
 
 template <int CIN, int COUT, int NB, int WR, int WC>
-__device__ __forceinline__ void compute_stage(int t, const uint32_t (&bm)[NB], const uint16_t* sA,
+__device__ __forceinline__ void compute_stage(int t, const uint32_t (&bm)[NB], const char* sA,
                                               const bf16x8_t (&bw)[COUT / WC / 16][CIN / 32],
                                               const uint32_t (&aoff)[CIN / 32], int wr,
                                               f32x4_t (&acc)[NB / WR][COUT / WC / 16]) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
-  const char* base = reinterpret_cast<const char*>(sA);
 #pragma unroll
   for (int bl = 0; bl < C::BPW; ++bl) {
     const int b = bl * WR + wr;
     if (!((bm[b] >> t) & 1u)) continue;
-    const char* blk = base + b * (C::A_BLOCK * 2);
+    const char* blk = sA + b * (C::A_BLOCK * 2);
     bf16x8_t a[C::KS];
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) a[s] = lds_read16(reinterpret_cast<const uint16_t*>(blk + aoff[s]));
+    for (int s = 0; s < C::KS; ++s) a[s] = lds_read16(blk + aoff[s]);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s)
 #pragma unroll
@@ -326,15 +363,16 @@ __device__ __forceinline__ void compute_stage(int t, const uint32_t (&bm)[NB], c
 
 template <int CIN, int COUT, int NB, int WR, int WC, bool OUT_BF16>
 __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wt,
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
     const float* __restrict__ bias, const int32_t* __restrict__ perm,
     const uint32_t* __restrict__ bmask, const int32_t* __restrict__ gidx,
     const uint16_t* __restrict__ zrow, int64_t npad, void* __restrict__ Y) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
-  __shared__ __attribute__((aligned(16))) uint16_t sA0[NB * C::A_BLOCK];
-  __shared__ __attribute__((aligned(16))) uint16_t sA1[NB * C::A_BLOCK];
-  __shared__ __attribute__((aligned(16))) int32_t sG[kTaps * NB * 16];
-  __shared__ __attribute__((aligned(16))) int32_t sP[NB * 16];
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_BYTES];
+  const char* sA0 = smem;
+  const char* sA1 = smem + C::OFF_A1;
+  int32_t* sG = reinterpret_cast<int32_t*>(smem + C::OFF_G);
+  int32_t* sP = reinterpret_cast<int32_t*>(smem + C::OFF_P);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave / WC, wc = wave % WC;
@@ -382,8 +420,7 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   }
   // The tile's original row indices -> sP (read by the epilogue), by the last wave.
   if (wave == C::WAVES - 1 && lane < NB * 4) dma16(perm + row0 + lane * 4, lds_addr(sP));
-  // Bias of this lane's columns, loaded now so the epilogue issues no loads among its stores
-  // (stores count in vmcnt, so a load there would make every later wait drain the stores).
+  // Bias of this lane's columns, loaded now so the epilogue issues no global loads.
   float bv[C::NCT];
 #pragma unroll
   for (int c = 0; c < C::NCT; ++c) bv[c] = bias ? bias[wc * C::CS + c * 16 + (lane & 15)] : 0.f;
@@ -407,14 +444,14 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     int t_cur = __builtin_ctz(rem);
     rem &= rem - 1;
     int q = 0;
-    load_weights<CIN, COUT, NB, WR, WC>(t_cur, Wt, wc, lane, bw0);
+    load_weights<CIN, COUT, NB, WR, WC>(t_cur, Wp, wc, lane, bw0);
     issue_gather<CIN, COUT, NB, WR, WC>(0, t_cur, bm, X, zrow, sG, sA0, wave, lane);
     while (true) {
       wait_vm_lgkm0();
       __builtin_amdgcn_s_barrier();
       int t_next = rem ? __builtin_ctz(rem) : -1;
       if (t_next >= 0) {
-        load_weights<CIN, COUT, NB, WR, WC>(t_next, Wt, wc, lane, bw1);
+        load_weights<CIN, COUT, NB, WR, WC>(t_next, Wp, wc, lane, bw1);
         issue_gather<CIN, COUT, NB, WR, WC>(q + 1, t_next, bm, X, zrow, sG, sA1, wave, lane);
       }
       compute_stage<CIN, COUT, NB, WR, WC>(t_cur, bm, sA0, bw0, aoff, wr, acc);
@@ -426,7 +463,7 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
       __builtin_amdgcn_s_barrier();
       t_next = rem ? __builtin_ctz(rem) : -1;
       if (t_next >= 0) {
-        load_weights<CIN, COUT, NB, WR, WC>(t_next, Wt, wc, lane, bw0);
+        load_weights<CIN, COUT, NB, WR, WC>(t_next, Wp, wc, lane, bw0);
         issue_gather<CIN, COUT, NB, WR, WC>(q + 1, t_next, bm, X, zrow, sG, sA0, wave, lane);
       }
       compute_stage<CIN, COUT, NB, WR, WC>(t_cur, bm, sA1, bw1, aoff, wr, acc);
@@ -437,32 +474,62 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     }
   }
 
-  // Nothing is outstanding here; saying so lets the compiler drop its per-store waits for
-  // weight loads it cannot prove were skipped on the last tap.
+  // Epilogue.  Every wave is past its last LDS read of the gather buffers after this barrier,
+  // and nothing is outstanding (which also lets the compiler drop waits for weight loads it
+  // cannot prove were skipped on the last tap).
   wait_vm_lgkm0();
-
-  // Epilogue: bias, then store each row at its original index.  All row indices are read
-  // from LDS first; the stores then issue back to back.
-  int32_t orow[C::BPW][4];
+  __builtin_amdgcn_s_barrier();
+  // Output rows are staged in LDS over the gather buffers and indices, BPP blocks at a time,
+  // 16-byte chunks XOR-swizzled by row; then every thread writes 16-byte pieces of whole
+  // rows to their original index.
+  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  constexpr int ROWB = COUT * ESZ;
+  constexpr int CHUNKS = ROWB / 16;
+  constexpr int SWM = (CHUNKS < 16 ? CHUNKS : 16) - 1;
+  constexpr int BPP_RAW = C::STAGE_BYTES / (16 * ROWB);
+  // Blocks per pass: the largest power of two that fits (NB is a power of two, so every pass
+  // is full and covers rows [p0*16, (p0+BPP)*16) of the tile exactly).
+  constexpr int BPP = BPP_RAW >= NB ? NB : BPP_RAW >= 8 ? 8 : BPP_RAW >= 4 ? 4 : BPP_RAW >= 2 ? 2 : 1;
+  static_assert(BPP_RAW >= 1 && NB % BPP == 0, "output staging space");
+  char* sOut = smem;
 #pragma unroll
-  for (int bl = 0; bl < C::BPW; ++bl)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) orow[bl][i] = sP[(bl * WR + wr) * 16 + (lane >> 4) * 4 + i];
-#pragma unroll
-  for (int c = 0; c < C::NCT; ++c) {
-    const int col = wc * C::CS + c * 16 + (lane & 15);
+  for (int p0 = 0; p0 < NB; p0 += BPP) {
 #pragma unroll
     for (int bl = 0; bl < C::BPW; ++bl) {
+      const int b = bl * WR + wr;
+      if (b < p0 || b >= p0 + BPP) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t o = orow[bl][i];
-        if (o < 0) continue;
-        const float v = acc[bl][c][i] + bv[c];
-        if (OUT_BF16)
-          static_cast<uint16_t*>(Y)[static_cast<int64_t>(o) * COUT + col] = f32_to_bf16_rne(v);
-        else
-          static_cast<float*>(Y)[static_cast<int64_t>(o) * COUT + col] = v;
+      for (int c = 0; c < C::NCT; ++c) {
+        const int col = wc * C::CS + c * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = (b - p0) * 16 + (lane >> 4) * 4 + i;
+          const int byte = col * ESZ;
+          char* dst = sOut + row * ROWB + (((byte >> 4) ^ (row & SWM)) << 4) + (byte & 15);
+          const float v = acc[bl][c][i] + bv[c];
+          if (OUT_BF16)
+            *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_rne(v);
+          else
+            *reinterpret_cast<float*>(dst) = v;
+        }
       }
+    }
+    wait_vm_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    constexpr int PIECES = BPP * 16 * CHUNKS;
+#pragma unroll 4
+    for (int idx = threadIdx.x; idx < PIECES; idx += C::THREADS) {
+      const int row = idx / CHUNKS, ch = idx % CHUNKS;
+      const int32_t o = sP[p0 * 16 + row];
+      if (o < 0) continue;
+      const u32x4_t v =
+          *reinterpret_cast<const u32x4_t*>(sOut + row * ROWB + ((ch ^ (row & SWM)) << 4));
+      *reinterpret_cast<u32x4_t*>(static_cast<char*>(Y) + static_cast<int64_t>(o) * ROWB +
+                                  ch * 16) = v;
+    }
+    if (p0 + BPP < NB) {
+      wait_vm_lgkm0();
+      __builtin_amdgcn_s_barrier();
     }
   }
 }
@@ -539,15 +606,17 @@ template <int CI, int CO>
 struct LdsPick {
   static constexpr int WC = CO >= 64 ? 4 : CO / 16;
   static constexpr int WR = 4 / WC;
-  static constexpr int NB = CI >= 64 ? 8 : 16;
+  static constexpr int NB = (CI >= 64 || CO > 64) ? 8 : 16;
 };
 
-LdsFn pick_lds(int cin, int cout, bool out_bf16, int* threads, int* rows_per_tile) {
+LdsFn pick_lds(int cin, int cout, bool out_bf16, int* threads, int* rows_per_tile,
+               int* wc_groups) {
 #define SSC_CASE(CI, CO)                                                             \
   if (cin == CI && cout == CO) {                                                     \
     using P = LdsPick<CI, CO>;                                                       \
     *threads = P::WR * P::WC * 64;                                                   \
     *rows_per_tile = P::NB * 16;                                                     \
+    *wc_groups = P::WC;                                                              \
     return out_bf16 ? k_subm_lds<CI, CO, P::NB, P::WR, P::WC, true>                  \
                     : k_subm_lds<CI, CO, P::NB, P::WR, P::WC, false>;                \
   }
@@ -582,6 +651,14 @@ ssc_status launch_lds(LdsFn fn, int threads, int rows_per_tile, const void* feat
                      reinterpret_cast<const int32_t*>(pb + P.off_gidx),
                      reinterpret_cast<const uint16_t*>(pb + P.off_zero), P.npad, out);
   return launch_status();
+}
+
+void launch_pack_frag(const void* weight, int cin, int cout, int wc_groups, uint16_t* wp,
+                      hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(kTaps) * (cout / 16) * (cin / 32) * 64;
+  const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((total + 255) / 256, 65536));
+  k_pack_frag<<<blocks, 256, 0, s>>>(static_cast<const uint16_t*>(weight), kTaps, cin, cout,
+                                     wc_groups, wp);
 }
 
 void launch_transpose(const void* weight, int taps, int cin, int cout, uint16_t* wt,
@@ -624,9 +701,9 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
         return launch_dense(fn, waves, feats, wt, bias, n, out, ob, s);
       }
     } else {
-      int threads = 0, rows = 0;
-      if (LdsFn fn = pick_lds(cin, cout, ob != 0, &threads, &rows)) {
-        launch_transpose(weight, taps, cin, cout, wt, s);
+      int threads = 0, rows = 0, wcg = 0;
+      if (LdsFn fn = pick_lds(cin, cout, ob != 0, &threads, &rows, &wcg)) {
+        launch_pack_frag(weight, cin, cout, wcg, wt, s);
         return launch_lds(fn, threads, rows, feats, wt, bias, plan, n, out, s);
       }
     }
@@ -681,12 +758,13 @@ extern "C" size_t ssc_packed_weight_bytes(int32_t taps, int32_t cin, int32_t cou
 
 extern "C" ssc_status ssc_pack_weights(const void* weight, int32_t taps, int32_t cin, int32_t cout,
                                        void* packed, size_t packed_bytes, void* stream) {
-  if (weight == nullptr || packed == nullptr || (taps != 1 && taps != kTaps)) return SSC_ERR_ARG;
-  int waves = 0;
-  if (pick_dense(cin, cout, &waves) == nullptr) return SSC_ERR_UNSUPPORTED;
+  if (weight == nullptr || packed == nullptr) return SSC_ERR_ARG;
+  if (taps != kTaps) return SSC_ERR_UNSUPPORTED;
+  int threads = 0, rows = 0, wcg = 0;
+  if (pick_lds(cin, cout, false, &threads, &rows, &wcg) == nullptr) return SSC_ERR_UNSUPPORTED;
   if (!aligned(weight, 16) || !aligned(packed, kAlign)) return SSC_ERR_ARG;
   if (packed_bytes < ssc_packed_weight_bytes(taps, cin, cout)) return SSC_ERR_WORKSPACE;
-  launch_transpose(weight, taps, cin, cout, static_cast<uint16_t*>(packed), as_stream(stream));
+  launch_pack_frag(weight, cin, cout, wcg, static_cast<uint16_t*>(packed), as_stream(stream));
   return launch_status();
 }
 
@@ -697,8 +775,8 @@ extern "C" ssc_status ssc_subm_conv3d_packed(const void* feats, const void* pack
   if (n < 0 || !valid_dtype(out_dtype) || packed_weight == nullptr || plan == nullptr)
     return SSC_ERR_ARG;
   if (n >= (int64_t(1) << 31)) return SSC_ERR_UNSUPPORTED;
-  int threads = 0, rows = 0;
-  LdsFn fn = pick_lds(cin, cout, out_dtype == SSC_BF16, &threads, &rows);
+  int threads = 0, rows = 0, wcg = 0;
+  LdsFn fn = pick_lds(cin, cout, out_dtype == SSC_BF16, &threads, &rows, &wcg);
   if (fn == nullptr) return SSC_ERR_UNSUPPORTED;
   if (n > 0 && (feats == nullptr || out == nullptr)) return SSC_ERR_ARG;
   if (!aligned(packed_weight, 16) || !aligned(plan, kAlign) ||
