@@ -13,8 +13,9 @@
 //                 row or -1; consecutive threads write consecutive map entries
 //
 // Warm plan: the sites are reordered by their 26-bit mask of valid non-centre taps (a stable
-// LSD radix sort written here: per-tile digit histograms, one exclusive scan, then a stable
-// scatter that ranks equal digits with wave ballots), so that the 16-row blocks the matrix
+// LSD radix sort written here: per-tile digit histograms, a digit-major exclusive scan with
+// one workgroup per digit, then a stable scatter that ranks equal digits with wave ballots),
+// so that the 16-row blocks the matrix
 // cores consume tend to share which taps are present and empty (block, tap) pairs can be
 // skipped whole.  The neighbour rows are then stored tap-major in that order.
 #include <hip/hip_runtime.h>
@@ -156,7 +157,7 @@ static_assert(kSortThreads == kDigits, "one thread per digit in the histogram an
 
 struct PlanWorkLayout {
   int64_t ntiles;
-  size_t off_keys_a, off_keys_b, off_vals_a, off_vals_b, off_hist, total;
+  size_t off_keys_a, off_keys_b, off_vals_a, off_vals_b, off_hist, off_totals, total;
 };
 
 inline PlanWorkLayout plan_work_layout(int64_t n) {
@@ -168,14 +169,16 @@ inline PlanWorkLayout plan_work_layout(int64_t n) {
   L.off_vals_a = align_up(L.off_keys_b + sizeof(uint32_t) * m);
   L.off_vals_b = align_up(L.off_vals_a + sizeof(uint32_t) * m);
   L.off_hist = align_up(L.off_vals_b + sizeof(uint32_t) * m);
-  L.total = align_up(L.off_hist + sizeof(uint32_t) * kDigits * L.ntiles);
+  L.off_totals = align_up(L.off_hist + sizeof(uint32_t) * kDigits * L.ntiles);
+  L.total = align_up(L.off_totals + sizeof(uint32_t) * kDigits);
   return L;
 }
 
 // Sort key of a site: bit (t < 13 ? t : t - 1) set when non-centre tap t has a neighbour.
 __global__ void k_mask_keys(const int32_t* __restrict__ nbr, int64_t n, uint32_t* __restrict__ keys,
-                            uint32_t* __restrict__ vals) {
+                            uint32_t* __restrict__ vals, uint32_t* __restrict__ totals) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x < kDigits) totals[threadIdx.x] = 0;
   if (i >= n) return;
   const int32_t* row = nbr + i * kTaps;
   uint32_t m = 0;
@@ -188,10 +191,13 @@ __global__ void k_mask_keys(const int32_t* __restrict__ nbr, int64_t n, uint32_t
   vals[i] = static_cast<uint32_t>(i);
 }
 
+// Per-tile digit counts -> hist[digit][tile]; per-digit totals accumulate in totals[digit]
+// (zeroed by the previous scatter, or by k_mask_keys before the first pass).
 __global__ __launch_bounds__(kSortThreads) void k_sort_hist(const uint32_t* __restrict__ keys,
                                                             int64_t n, int shift,
                                                             uint32_t* __restrict__ hist,
-                                                            int64_t ntiles) {
+                                                            int64_t ntiles,
+                                                            uint32_t* __restrict__ totals) {
   __shared__ uint32_t h[kDigits];
   h[threadIdx.x] = 0;
   __syncthreads();
@@ -203,37 +209,56 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_hist(const uint32_t* __re
   }
   __syncthreads();
   hist[static_cast<int64_t>(threadIdx.x) * ntiles + blockIdx.x] = h[threadIdx.x];
+  if (h[threadIdx.x]) atomicAdd(&totals[threadIdx.x], h[threadIdx.x]);
 }
 
-// Exclusive prefix sum of `total` counts in place, one workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void k_sort_scan(uint32_t* __restrict__ a, int64_t total) {
-  __shared__ uint32_t part[1024];
-  const int64_t per = (total + 1023) / 1024;
-  const int64_t lo = threadIdx.x * per;
-  const int64_t hi = lo + per < total ? lo + per : total;
-  uint32_t s = 0;
-  for (int64_t e = lo; e < hi; ++e) s += a[e];
-  part[threadIdx.x] = s;
+// Block-wide inclusive scan of one value per thread (kSortThreads threads), Hillis-Steele.
+__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* sh) {
+  sh[threadIdx.x] = v;
   __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial sums.
-  for (int off = 1; off < 1024; off <<= 1) {
-    const uint32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0u;
+  for (int off = 1; off < kSortThreads; off <<= 1) {
+    const uint32_t add = threadIdx.x >= off ? sh[threadIdx.x - off] : 0u;
     __syncthreads();
-    part[threadIdx.x] += v;
+    sh[threadIdx.x] += add;
     __syncthreads();
   }
-  uint32_t run = threadIdx.x > 0 ? part[threadIdx.x - 1] : 0u;
-  for (int64_t e = lo; e < hi; ++e) {
-    const uint32_t v = a[e];
-    a[e] = run;
-    run += v;
+  const uint32_t r = sh[threadIdx.x];
+  __syncthreads();
+  return r;
+}
+
+// Exclusive scan of hist in digit-major order, one workgroup per digit: the digit's base is
+// the sum of the totals of all smaller digits, then its row of per-tile counts is scanned.
+__global__ __launch_bounds__(kSortThreads) void k_sort_scan_rows(uint32_t* __restrict__ hist,
+                                                                 int64_t ntiles,
+                                                                 const uint32_t* __restrict__ totals) {
+  __shared__ uint32_t sh[kSortThreads];
+  const int d = blockIdx.x;
+  const uint32_t below = block_inclusive_scan(threadIdx.x < d ? totals[threadIdx.x] : 0u, sh);
+  // The last thread's inclusive value is the sum over all smaller digits.
+  if (threadIdx.x == kSortThreads - 1) sh[0] = below;
+  __syncthreads();
+  uint32_t carry = sh[0];
+  __syncthreads();
+  uint32_t* row = hist + static_cast<int64_t>(d) * ntiles;
+  for (int64_t base = 0; base < ntiles; base += kSortThreads) {
+    const int64_t e = base + threadIdx.x;
+    const uint32_t v = e < ntiles ? row[e] : 0u;
+    const uint32_t inc = block_inclusive_scan(v, sh);
+    if (e < ntiles) row[e] = carry + inc - v;
+    if (threadIdx.x == kSortThreads - 1) sh[0] = inc;
+    __syncthreads();
+    carry += sh[0];
+    __syncthreads();
   }
 }
 
 __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n,
     int shift, const uint32_t* __restrict__ hist, int64_t ntiles, uint32_t* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out) {
+    uint32_t* __restrict__ vals_out, uint32_t* __restrict__ totals) {
+  // The totals were consumed by k_sort_scan_rows; clear them for the next pass.
+  if (blockIdx.x == 0) totals[threadIdx.x] = 0;
   constexpr int kWaves = kSortThreads / 64;
   __shared__ uint32_t running[kDigits];
   __shared__ uint32_t wcnt[kWaves][kDigits];
@@ -373,15 +398,17 @@ extern "C" ssc_status ssc_build_plan(const int32_t* nbr, int64_t n, void* plan, 
   uint32_t* vals[2] = {reinterpret_cast<uint32_t*>(ws + W.off_vals_a),
                        reinterpret_cast<uint32_t*>(ws + W.off_vals_b)};
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + W.off_hist);
+  uint32_t* totals = reinterpret_cast<uint32_t*>(ws + W.off_totals);
   int cur = 0;
   if (n > 0) {
-    k_mask_keys<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(nbr, n, keys[0], vals[0]);
+    k_mask_keys<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(nbr, n, keys[0], vals[0],
+                                                                      totals);
     for (int shift = 0; shift < kKeyBits; shift += kDigitBits) {
       k_sort_hist<<<static_cast<unsigned>(W.ntiles), kSortThreads, 0, s>>>(keys[cur], n, shift,
-                                                                           hist, W.ntiles);
-      k_sort_scan<<<1, 1024, 0, s>>>(hist, static_cast<int64_t>(kDigits) * W.ntiles);
+                                                                           hist, W.ntiles, totals);
+      k_sort_scan_rows<<<kDigits, kSortThreads, 0, s>>>(hist, W.ntiles, totals);
       k_sort_scatter<<<static_cast<unsigned>(W.ntiles), kSortThreads, 0, s>>>(
-          keys[cur], vals[cur], n, shift, hist, W.ntiles, keys[cur ^ 1], vals[cur ^ 1]);
+          keys[cur], vals[cur], n, shift, hist, W.ntiles, keys[cur ^ 1], vals[cur ^ 1], totals);
       cur ^= 1;
     }
   }
