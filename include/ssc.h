@@ -145,6 +145,14 @@ size_t ssc_packed_weight_bytes(int32_t taps, int32_t cin, int32_t cout);
 ssc_status ssc_pack_weights(const void* weight, int32_t taps, int32_t cin, int32_t cout,
                             void* packed, size_t packed_bytes, void* stream);
 
+/* ssc_pack_weights with options.  flags = 0 or SSC_PACK_FLIP:
+ *   SSC_PACK_FLIP  the other kernel orientation, which the LATO.2 page leaves open and builds
+ *                  with "--flip-kernel" ("Correctness"): the tap at offset d reads the site
+ *                  c - d, i.e. out[i] = bias + sum_t feats[nbr[i][26-t]] @ weight[t]. */
+#define SSC_PACK_FLIP 1
+ssc_status ssc_pack_weights_ex(const void* weight, int32_t taps, int32_t cin, int32_t cout,
+                               int32_t flags, void* packed, size_t packed_bytes, void* stream);
+
 /* ssc_subm_conv3d with weights from ssc_pack_weights (taps = 27): one kernel launch, no
  * workspace.  Same results, bit for bit, as ssc_subm_conv3d on the unpacked weights.
  * bf16 inputs and the shapes ssc_pack_weights accepts only. */

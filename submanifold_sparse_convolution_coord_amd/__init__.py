@@ -73,6 +73,7 @@ def load_library():
         "ssc_linear": ([p, i32, p, p, i64, i32, i32, p, i32, p, sz, p], ctypes.c_int),
         "ssc_packed_weight_bytes": ([i32, i32, i32], sz),
         "ssc_pack_weights": ([p, i32, i32, i32, p, sz, p], ctypes.c_int),
+        "ssc_pack_weights_ex": ([p, i32, i32, i32, i32, p, sz, p], ctypes.c_int),
         "ssc_subm_conv3d_packed": ([p, p, p, p, i64, i32, i32, p, i32, p], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -234,7 +235,9 @@ class PackedWeight:
         self.buf, self.taps, self.cin, self.cout = buf, taps, cin, cout
 
 
-def pack_weights(weight: torch.Tensor) -> PackedWeight:
+def pack_weights(weight: torch.Tensor, flip: bool = False) -> PackedWeight:
+    """Re-lay out [27, Cin, Cout] bf16 weights once for subm_conv3d_packed.  flip=True packs
+    the other kernel orientation (tap at offset d reads site c - d)."""
     _need_cuda(weight, "weight")
     if weight.dtype != torch.bfloat16:
         raise ValueError("pack_weights takes bfloat16 weights")
@@ -244,8 +247,8 @@ def pack_weights(weight: torch.Tensor) -> PackedWeight:
     dev = weight.device
     buf = _workspace(lib.ssc_packed_weight_bytes(taps, cin, cout), dev)
     with torch.cuda.device(dev):
-        st = lib.ssc_pack_weights(_ptr(weight), taps, cin, cout, _ptr(buf), buf.numel(),
-                                  _stream(dev))
+        st = lib.ssc_pack_weights_ex(_ptr(weight), taps, cin, cout, 1 if flip else 0, _ptr(buf),
+                                     buf.numel(), _stream(dev))
     _check(st, "ssc_pack_weights")
     return PackedWeight(buf, taps, cin, cout)
 

@@ -44,132 +44,13 @@ __device__ __forceinline__ bf16x8_t zero_bf16x8() {
   return __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
 }
 
-// Wt[t][o][c] = W[t][c][o]; 32x32 tiles through LDS.
-__global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict__ W, int cin,
-                                                     int cout, uint16_t* __restrict__ Wt) {
-  __shared__ uint16_t tile[32][33];
-  const int t = blockIdx.z, c0 = blockIdx.y * 32, o0 = blockIdx.x * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const uint16_t* src = W + static_cast<int64_t>(t) * cin * cout;
-  uint16_t* dst = Wt + static_cast<int64_t>(t) * cin * cout;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c = c0 + ty + 8 * k, o = o0 + tx;
-    if (c < cin && o < cout) tile[ty + 8 * k][tx] = src[static_cast<int64_t>(c) * cout + o];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int o = o0 + ty + 8 * k, c = c0 + tx;
-    if (c < cin && o < cout) dst[static_cast<int64_t>(o) * cin + c] = tile[tx][ty + 8 * k];
-  }
-}
-
 // Matrix-core fragment layout of v_mfma_f32_16x16x32_bf16 (wave64), as used below:
 //   A (16 x 32): lane l holds row (l & 15), k = 8*(l >> 4) .. +7
 //   B (32 x 16): lane l holds column (l & 15), k = 8*(l >> 4) .. +7
 //   D (16 x 16): lane l holds column (l & 15), rows 4*(l >> 4) .. +3
 // Both operands use the same (lane, element) -> k assignment, so the product is the full
 // k-sum whatever order the hardware walks k in.
-//
-// DENSE = false: k=3 convolution over a plan (gather through gidx, skip by block masks).
-// DENSE = true : k=1 per-voxel linear map (row r reads feats row r, one tap, no plan).
-template <int CIN, int COUT, int WAVES, int NB, bool DENSE>
-__global__ __launch_bounds__(WAVES * 64) void k_conv_mfma(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wt,
-    const float* __restrict__ bias, const int32_t* __restrict__ perm,
-    const uint32_t* __restrict__ bmask, const int32_t* __restrict__ gidx, int64_t npad, int64_t n,
-    void* __restrict__ Y, int out_bf16) {
-  static_assert(CIN % 32 == 0 && COUT % (16 * WAVES) == 0, "tile shape");
-  constexpr int CS = COUT / WAVES;  // output columns per wave
-  constexpr int NCT = CS / 16;      // 16-column MFMA tiles per wave
-  constexpr int KS = CIN / 32;      // k-steps of 32 channels
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr = lane & 15, lk = (lane >> 4) * 8;
-  const int colbase = wave * CS;
-  const int64_t tile = blockIdx.x;
-  const int64_t row0 = tile * (NB * 16);
 
-  uint32_t bm[NB];
-  uint32_t taps = 0;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    if (DENSE) {
-      bm[b] = (row0 + b * 16 < n) ? 1u : 0u;
-    } else {
-      bm[b] = bmask[tile * NB + b];
-    }
-    taps |= bm[b];
-  }
-
-  f32x4_t acc[NB][NCT];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) acc[b][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  while (taps) {
-    const int t = __builtin_ctz(taps);
-    taps &= taps - 1;
-    bf16x8_t bw[NCT][KS];
-    const uint16_t* wt = Wt + (static_cast<int64_t>(t) * COUT + colbase + lr) * CIN + lk;
-#pragma unroll
-    for (int c = 0; c < NCT; ++c)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) bw[c][s] = load_bf16x8(wt + c * 16 * CIN + s * 32);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (!((bm[b] >> t) & 1u)) continue;
-      const int64_t r = row0 + b * 16 + lr;
-      int32_t j;
-      if (DENSE) {
-        j = r < n ? static_cast<int32_t>(r) : -1;
-      } else {
-        j = gidx[static_cast<int64_t>(t) * npad + r];
-      }
-      bf16x8_t a[KS];
-      if (j >= 0) {
-        const uint16_t* xr = X + static_cast<int64_t>(j) * CIN + lk;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) a[s] = load_bf16x8(xr + s * 32);
-      } else {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) a[s] = zero_bf16x8();
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int c = 0; c < NCT; ++c)
-          acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bw[c][s], acc[b][c], 0, 0, 0);
-    }
-  }
-
-  // Epilogue: bias, then store each row at its original index.
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) {
-    const int col = colbase + c * 16 + lr;
-    const float bv = bias ? bias[col] : 0.f;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t r = row0 + b * 16 + (lane >> 4) * 4 + i;
-        int64_t orow;
-        if (DENSE) {
-          orow = r < n ? r : -1;
-        } else {
-          orow = perm[r];
-        }
-        if (orow < 0) continue;
-        const float v = acc[b][c][i] + bv;
-        if (out_bf16)
-          static_cast<uint16_t*>(Y)[orow * COUT + col] = f32_to_bf16_rne(v);
-        else
-          static_cast<float*>(Y)[orow * COUT + col] = v;
-      }
-    }
-  }
-}
 
 // ------------------------------------------------------------------------------------------
 // k=3 convolution kernel: gathers staged in LDS, software-pipelined over the taps of a tile.
@@ -221,8 +102,10 @@ struct LdsCfg {
 // Fragment-major packed weights for WC column groups: element
 //   Wp[(((t*WC + wc)*NCT + c)*KS + s)*512 + lane*8 + e] = W[t][32s + 8(lane>>4) + e][wc*CS + 16c + (lane&15)]
 // i.e. the B fragment of (tap t, wave column group wc, column tile c, k-step s) for `lane`.
+// flip = 1 packs W[taps-1-t] into tap t: the tap at offset d then reads site c - d, the other
+// orientation the LATO.2 page leaves open (its "--flip-kernel").
 __global__ __launch_bounds__(256) void k_pack_frag(const uint16_t* __restrict__ W, int taps,
-                                                   int cin, int cout, int wc_groups,
+                                                   int cin, int cout, int wc_groups, int flip,
                                                    uint16_t* __restrict__ Wp) {
   const int cs = cout / wc_groups, nct = cs / 16, ks = cin / 32;
   const int64_t total = static_cast<int64_t>(taps) * wc_groups * nct * ks * 64;
@@ -239,7 +122,8 @@ __global__ __launch_bounds__(256) void k_pack_frag(const uint16_t* __restrict__ 
     const int64_t t = rest / wc_groups;
     const int o = wc * cs + c * 16 + (lane & 15);
     const int k0 = s * 32 + (lane >> 4) * 8;
-    const uint16_t* src = W + (t * cin + k0) * cout + o;
+    const int64_t ts = flip ? taps - 1 - t : t;
+    const uint16_t* src = W + (ts * cin + k0) * cout + o;
     uint16_t* dst = Wp + idx * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dst[e] = src[static_cast<int64_t>(e) * cout];
@@ -288,7 +172,13 @@ __device__ __forceinline__ bf16x8_t lds_read16(const void* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
 }
 
-// Copies of stage (union index q, tap t): one block copy per block that has tap t.
+// Copies of stage (union index q, tap t) for every block that has tap t.  Each copy
+// instruction moves 64 lanes x 16 bytes = RPI whole rows of one block into LDS (the lane's
+// 16-byte chunk of the row goes to its swizzled slot, missing neighbours read the zero row).
+// A block is PIECES such copies; piece i of the tile (block i / PIECES, part i % PIECES) is
+// always issued by wave i % WAVES, so a wave reads all its row indices before its first copy.
+// With CIN = 128 that is one 4-row part of every block per wave; narrower rows give each
+// wave whole blocks (CIN = 32) or half blocks (CIN = 64), and no lane of a copy idles.
 template <int CIN, int COUT, int NB, int WR, int WC>
 __device__ __forceinline__ void issue_gather(int q, int t, const uint32_t (&bm)[NB],
                                              const uint16_t* __restrict__ X,
@@ -296,19 +186,50 @@ __device__ __forceinline__ void issue_gather(int q, int t, const uint32_t (&bm)[
                                              const int32_t* sG, const char* sA, int wave,
                                              int lane) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
-  const int rr = (wave * C::RPW + lane / C::CPR) & 15;
-  const int chunk = (lane % C::CPR) ^ swz<C::CPR>(rr);
-  const int32_t* g = sG + q * (NB * 16);
-  int32_t j[NB];
+  if constexpr (CIN < 128) {
+    constexpr int RPI = 64 / C::CPR;
+    constexpr int PIECES = 16 / RPI;
+    constexpr int PPW = NB * PIECES / C::WAVES;
+    static_assert(NB * PIECES % C::WAVES == 0 && (C::WAVES & (C::WAVES - 1)) == 0,
+                  "pieces per wave");
+    const int32_t* g = sG + q * (NB * 16);
+    const int rsub = lane / C::CPR;
+    uint32_t act = 0;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) j[b] = g[b * 16 + rr];
+    for (int b = 0; b < NB; ++b) act |= ((bm[b] >> t) & 1u) << b;
+    int32_t j[PPW];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    if (!((bm[b] >> t) & 1u)) continue;
-    const uint16_t* src =
-        j[b] >= 0 ? X + static_cast<int64_t>(j[b]) * CIN + chunk * 8 : zrow + chunk * 8;
-    if (lane < C::A_LANES)
-      dma16(src, lds_addr(sA + b * C::A_BLOCK * 2 + wave * C::RPW * CIN * 2));
+    for (int i = 0; i < PPW; ++i) {
+      const int piece = i * C::WAVES + wave;
+      j[i] = g[(piece / PIECES) * 16 + (piece % PIECES) * RPI + rsub];
+    }
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int piece = i * C::WAVES + wave;
+      const int b = piece / PIECES, part = piece % PIECES;
+      if (!((act >> b) & 1u)) continue;
+      const int chunk = (lane % C::CPR) ^ swz<C::CPR>(part * RPI + rsub);
+      const uint16_t* src =
+          j[i] >= 0 ? X + static_cast<int64_t>(j[i]) * CIN + chunk * 8 : zrow + chunk * 8;
+      dma16(src, lds_addr(sA + b * C::A_BLOCK * 2 + part * 1024));
+    }
+  } else {
+    // CIN = 128: wave w copies rows 4w..4w+3 of every block (the same pieces as above, with
+    // the block's test hoisted out of the index arithmetic).
+    const int rr = (wave * C::RPW + lane / C::CPR) & 15;
+    const int chunk = (lane % C::CPR) ^ swz<C::CPR>(rr);
+    const int32_t* g = sG + q * (NB * 16);
+    int32_t j[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) j[b] = g[b * 16 + rr];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (!((bm[b] >> t) & 1u)) continue;
+      const uint16_t* src =
+          j[b] >= 0 ? X + static_cast<int64_t>(j[b]) * CIN + chunk * 8 : zrow + chunk * 8;
+      if (lane < C::A_LANES)
+        dma16(src, lds_addr(sA + b * C::A_BLOCK * 2 + wave * C::RPW * CIN * 2));
+    }
   }
 }
 
@@ -578,20 +499,168 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ X, cons
   }
 }
 
-constexpr int kNB = 8;  // 16-row blocks per workgroup tile of the k=1 kernel (128 rows)
+// ------------------------------------------------------------------------------------------
+// k=1 layer (per-site linear map) on bf16 features: a persistent streaming kernel.
+//
+// The map reads each feature row once and writes each output row once, so it is bound by
+// HBM, not by the matrix cores.  Each workgroup keeps its column slice of W as B fragments in
+// VGPRs for its whole life and walks tiles of TR contiguous rows (tile, tile + gridDim.x, ...).
+// Per tile: the next tile's rows are copied into the other LDS buffer (direct global->LDS
+// loads, whole 1 KB copies) while the matrix cores work on this one; the outputs plus bias
+// are staged in LDS and leave as contiguous 16-byte stores of whole rows.
+// The only vector-memory operations in the loop are those copies and the output stores, and
+// both retire in issue order, so "this tile's copies have landed" is "at most STORES (the
+// previous tile's stores, issued after them) are outstanding": the loop waits for exactly
+// that, not for the stores.  Only the last tile of the layer can be partial, and it is the
+// last tile its workgroup handles; rows past n are copied from row n-1 and never stored.
+// ------------------------------------------------------------------------------------------
+template <int CIN, int COUT, bool OUT_BF16>
+struct LinCfg {
+  static constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  static constexpr int ROWB = COUT * ESZ;                  // output bytes per row
+  static constexpr int TR = ROWB >= 64 ? 64 : 128;         // rows per tile
+  static constexpr int NB = TR / 16;
+  static constexpr int WC = COUT >= 64 ? 4 : COUT / 16;
+  static constexpr int WR = 4 / WC;
+  using C = LdsCfg<CIN, COUT, NB, WR, WC>;
+  static constexpr int XBUF = TR * CIN * 2;                // one tile of bf16 rows
+  static constexpr int OBUF = TR * ROWB;                   // one tile of output rows
+  static constexpr int SMEM = 2 * XBUF + OBUF;
+  static constexpr int COPIES = XBUF / 1024;               // 1 KB copies per tile
+  static constexpr int CPW = COPIES / C::WAVES;
+  static constexpr int RPI = 512 / CIN;                    // rows per copy
+  static constexpr int CHUNKS = ROWB / 16;
+  static constexpr int SWM = (CHUNKS < 16 ? CHUNKS : 16) - 1;
+  static constexpr int STORES = OBUF / 16 / C::THREADS;    // 16-byte stores per thread
+  static_assert(COPIES % C::WAVES == 0 && OBUF % (16 * C::THREADS) == 0, "tile shape");
+  static_assert(STORES >= 1 && STORES <= 63, "vmcnt range");
+};
 
-using MfmaFn = void (*)(const uint16_t*, const uint16_t*, const float*, const int32_t*,
-                        const uint32_t*, const int32_t*, int64_t, int64_t, void*, int);
+// s_waitcnt vmcnt(N) lgkmcnt(0), N < 64 (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4] << 14).
+template <int N>
+__device__ __forceinline__ void wait_vm_n_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+
+template <int CIN, int COUT, bool OUT_BF16>
+__device__ __forceinline__ void linear_copies(int64_t tile, int64_t n,
+                                              const uint16_t* __restrict__ X, char* buf,
+                                              int wave, int lane) {
+  using L = LinCfg<CIN, COUT, OUT_BF16>;
+  constexpr int CPR = CIN / 8;
+  const int rsub = lane / CPR, phys = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < L::CPW; ++i) {
+    const int k = i * L::C::WAVES + wave;
+    const int r = k * L::RPI + rsub;                       // row of the tile
+    int64_t g = tile * L::TR + r;
+    g = g < n ? g : n - 1;
+    const int chunk = phys ^ swz<CPR>(r & 15);
+    dma16(X + g * CIN + chunk * 8, lds_addr(buf + k * 1024));
+  }
+}
+
+template <int CIN, int COUT, bool OUT_BF16>
+__global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __restrict__ X,
+                                                          const uint16_t* __restrict__ Wp,
+                                                          const float* __restrict__ bias,
+                                                          int64_t n, void* __restrict__ Y) {
+  using L = LinCfg<CIN, COUT, OUT_BF16>;
+  using C = typename L::C;
+  __shared__ __attribute__((aligned(1024))) char smem[L::SMEM];
+  char* sX0 = smem;
+  char* sX1 = smem + L::XBUF;
+  char* sOut = smem + 2 * L::XBUF;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave / L::WC, wc = wave % L::WC;
+  const int64_t tiles = (n + L::TR - 1) / L::TR;
+  int64_t tile = blockIdx.x;
+  if (tile >= tiles) return;
+
+  bf16x8_t bw[C::NCT][C::KS];
+  load_weights<CIN, COUT, L::NB, L::WR, L::WC>(0, Wp, wc, lane, bw);
+  float bv[C::NCT];
+#pragma unroll
+  for (int c = 0; c < C::NCT; ++c) bv[c] = bias ? bias[wc * C::CS + c * 16 + (lane & 15)] : 0.f;
+  uint32_t aoff[C::KS];
+  a_frag_offsets<CIN>(lane, aoff);
+  // Weights and bias are in registers before the loop: inside it nothing waits for them, so
+  // the compiler has no reason to drain the copies in flight.
+  wait_vm_lgkm0();
+
+  linear_copies<CIN, COUT, OUT_BF16>(tile, n, X, sX0, wave, lane);
+  for (int k = 0; tile < tiles; tile += gridDim.x, ++k) {
+    if (k == 0)
+      wait_vm_lgkm0();
+    else
+      wait_vm_n_lgkm0<L::STORES>();
+    __builtin_amdgcn_s_barrier();
+    char* cur = (k & 1) ? sX1 : sX0;
+    const int64_t next = tile + gridDim.x;
+    if (next < tiles) linear_copies<CIN, COUT, OUT_BF16>(next, n, X, (k & 1) ? sX0 : sX1, wave, lane);
+
+    f32x4_t acc[C::BPW][C::NCT];
+#pragma unroll
+    for (int bl = 0; bl < C::BPW; ++bl) {
+      const char* blk = cur + (bl * L::WR + wr) * (C::A_BLOCK * 2);
+      bf16x8_t a[C::KS];
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) a[s] = lds_read16(blk + aoff[s]);
+#pragma unroll
+      for (int c = 0; c < C::NCT; ++c) {
+        acc[bl][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s)
+          acc[bl][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bw[c][s], acc[bl][c], 0, 0, 0);
+      }
+    }
+    // Stage bias-added outputs (16-byte chunks XOR-swizzled by row).
+#pragma unroll
+    for (int bl = 0; bl < C::BPW; ++bl) {
+      const int b = bl * L::WR + wr;
+#pragma unroll
+      for (int c = 0; c < C::NCT; ++c) {
+        const int col = wc * C::CS + c * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = b * 16 + (lane >> 4) * 4 + i;
+          const int byte = col * L::ESZ;
+          char* dst = sOut + row * L::ROWB + (((byte >> 4) ^ (row & L::SWM)) << 4) + (byte & 15);
+          const float v = acc[bl][c][i] + bv[c];
+          if (OUT_BF16)
+            *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_rne(v);
+          else
+            *reinterpret_cast<float*>(dst) = v;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_s_barrier();
+    const int64_t row0 = tile * L::TR;
+#pragma unroll
+    for (int it = 0; it < L::STORES; ++it) {
+      const int idx = threadIdx.x + it * C::THREADS;
+      const int row = idx / L::CHUNKS, ch = idx % L::CHUNKS;
+      const u32x4_t v =
+          *reinterpret_cast<const u32x4_t*>(sOut + row * L::ROWB + ((ch ^ (row & L::SWM)) << 4));
+      if (row0 + row < n)
+        *reinterpret_cast<u32x4_t*>(static_cast<char*>(Y) + (row0 + row) * L::ROWB + ch * 16) = v;
+    }
+  }
+}
+
+using LinFn = void (*)(const uint16_t*, const uint16_t*, const float*, int64_t, void*);
 using LdsFn = void (*)(const uint16_t*, const uint16_t*, const float*, const int32_t*,
                        const uint32_t*, const int32_t*, const uint16_t*, int64_t, void*);
 
-// k=1 (dense rows) kernel for the channel counts the matrix-core path is built for.
-MfmaFn pick_dense(int cin, int cout, int* waves) {
-#define SSC_CASE(CI, CO)                                          \
-  if (cin == CI && cout == CO) {                                  \
-    constexpr int W = CO >= 64 ? 4 : CO / 16;                     \
-    *waves = W;                                                   \
-    return k_conv_mfma<CI, CO, W, kNB, true>;                     \
+// k=1 streaming kernel for the channel counts the matrix-core path is built for.
+LinFn pick_linear(int cin, int cout, bool out_bf16, int* wc_groups, int* rows_per_tile) {
+#define SSC_CASE(CI, CO)                                                                      \
+  if (cin == CI && cout == CO) {                                                              \
+    *wc_groups = LinCfg<CI, CO, false>::WC;                                                   \
+    *rows_per_tile = out_bf16 ? LinCfg<CI, CO, true>::TR : LinCfg<CI, CO, false>::TR;         \
+    return out_bf16 ? k_linear_stream<CI, CO, true> : k_linear_stream<CI, CO, false>;         \
   }
   SSC_CASE(32, 16) SSC_CASE(32, 32) SSC_CASE(32, 64) SSC_CASE(32, 128)
   SSC_CASE(64, 16) SSC_CASE(64, 32) SSC_CASE(64, 64) SSC_CASE(64, 128)
@@ -629,12 +698,28 @@ LdsFn pick_lds(int cin, int cout, bool out_bf16, int* threads, int* rows_per_til
 
 bool valid_dtype(int d) { return d == SSC_F32 || d == SSC_BF16; }
 
-ssc_status launch_dense(MfmaFn fn, int waves, const void* feats, const uint16_t* wt,
-                        const float* bias, int64_t n, void* out, int ob, hipStream_t s) {
-  const int64_t tiles = (n + kNB * 16 - 1) / (kNB * 16);
-  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(tiles)), dim3(waves * 64), 0, s,
-                     static_cast<const uint16_t*>(feats), wt, bias, nullptr, nullptr, nullptr,
-                     int64_t(0), n, out, ob);
+// Compute units of the current device (cached per device id).
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+ssc_status launch_linear(LinFn fn, int rows_per_tile, const void* feats, const uint16_t* wp,
+                         const float* bias, int64_t n, void* out, hipStream_t s) {
+  // Persistent: two resident workgroups per compute unit, each walking tiles with a stride.
+  const int64_t tiles = (n + rows_per_tile - 1) / rows_per_tile;
+  const int64_t grid = std::min<int64_t>(tiles, 2 * static_cast<int64_t>(device_cu_count()));
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(feats), wp, bias, n, out);
   return launch_status();
 }
 
@@ -653,19 +738,14 @@ ssc_status launch_lds(LdsFn fn, int threads, int rows_per_tile, const void* feat
   return launch_status();
 }
 
-void launch_pack_frag(const void* weight, int cin, int cout, int wc_groups, uint16_t* wp,
-                      hipStream_t s) {
-  const int64_t total = static_cast<int64_t>(kTaps) * (cout / 16) * (cin / 32) * 64;
+void launch_pack_frag(const void* weight, int taps, int cin, int cout, int wc_groups, int flip,
+                      uint16_t* wp, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(taps) * (cout / 16) * (cin / 32) * 64;
   const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((total + 255) / 256, 65536));
-  k_pack_frag<<<blocks, 256, 0, s>>>(static_cast<const uint16_t*>(weight), kTaps, cin, cout,
-                                     wc_groups, wp);
+  k_pack_frag<<<blocks, 256, 0, s>>>(static_cast<const uint16_t*>(weight), taps, cin, cout,
+                                     wc_groups, flip, wp);
 }
 
-void launch_transpose(const void* weight, int taps, int cin, int cout, uint16_t* wt,
-                      hipStream_t s) {
-  dim3 tg((cout + 31) / 32, (cin + 31) / 32, taps);
-  k_transpose_w<<<tg, 256, 0, s>>>(static_cast<const uint16_t*>(weight), cin, cout, wt);
-}
 
 ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* weight,
                     const float* bias, const void* plan, int64_t n, int cin, int cout, void* out,
@@ -690,20 +770,19 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
   const uint32_t* bmask = dense ? nullptr : reinterpret_cast<const uint32_t*>(pb + P.off_bmask);
   const int32_t* gidx = dense ? nullptr : reinterpret_cast<const int32_t*>(pb + P.off_gidx);
   const int ob = out_dtype == SSC_BF16 ? 1 : 0;
-  const int taps = dense ? 1 : kTaps;
 
   if (in_dtype == SSC_BF16) {
     uint16_t* wt = static_cast<uint16_t*>(workspace);
     if (dense) {
-      int waves = 0;
-      if (MfmaFn fn = pick_dense(cin, cout, &waves)) {
-        launch_transpose(weight, taps, cin, cout, wt, s);
-        return launch_dense(fn, waves, feats, wt, bias, n, out, ob, s);
+      int wcg = 0, rows = 0;
+      if (LinFn fn = pick_linear(cin, cout, ob != 0, &wcg, &rows)) {
+        launch_pack_frag(weight, 1, cin, cout, wcg, 0, wt, s);
+        return launch_linear(fn, rows, feats, wt, bias, n, out, s);
       }
     } else {
       int threads = 0, rows = 0, wcg = 0;
       if (LdsFn fn = pick_lds(cin, cout, ob != 0, &threads, &rows, &wcg)) {
-        launch_pack_frag(weight, cin, cout, wcg, wt, s);
+        launch_pack_frag(weight, kTaps, cin, cout, wcg, 0, wt, s);
         return launch_lds(fn, threads, rows, feats, wt, bias, plan, n, out, s);
       }
     }
@@ -758,13 +837,21 @@ extern "C" size_t ssc_packed_weight_bytes(int32_t taps, int32_t cin, int32_t cou
 
 extern "C" ssc_status ssc_pack_weights(const void* weight, int32_t taps, int32_t cin, int32_t cout,
                                        void* packed, size_t packed_bytes, void* stream) {
+  return ssc_pack_weights_ex(weight, taps, cin, cout, 0, packed, packed_bytes, stream);
+}
+
+extern "C" ssc_status ssc_pack_weights_ex(const void* weight, int32_t taps, int32_t cin,
+                                          int32_t cout, int32_t flags, void* packed,
+                                          size_t packed_bytes, void* stream) {
   if (weight == nullptr || packed == nullptr) return SSC_ERR_ARG;
+  if (flags & ~SSC_PACK_FLIP) return SSC_ERR_ARG;
   if (taps != kTaps) return SSC_ERR_UNSUPPORTED;
   int threads = 0, rows = 0, wcg = 0;
   if (pick_lds(cin, cout, false, &threads, &rows, &wcg) == nullptr) return SSC_ERR_UNSUPPORTED;
   if (!aligned(weight, 16) || !aligned(packed, kAlign)) return SSC_ERR_ARG;
   if (packed_bytes < ssc_packed_weight_bytes(taps, cin, cout)) return SSC_ERR_WORKSPACE;
-  launch_pack_frag(weight, cin, cout, wcg, static_cast<uint16_t*>(packed), as_stream(stream));
+  launch_pack_frag(weight, kTaps, cin, cout, wcg, (flags & SSC_PACK_FLIP) ? 1 : 0,
+                   static_cast<uint16_t*>(packed), as_stream(stream));
   return launch_status();
 }
 

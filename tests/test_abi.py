@@ -114,6 +114,22 @@ def test_conv_argument_errors(lib):
               None) == ssc.SSC_ERR_ARG
 
 
+def test_pack_weights_argument_errors(lib):
+    f = lib.ssc_pack_weights_ex
+    big = 1 << 30
+    assert f(FAKE, 27, 128, 128, 0, None, big, None) == ssc.SSC_ERR_ARG
+    assert f(None, 27, 128, 128, 0, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 27, 128, 128, 4, FAKE, big, None) == ssc.SSC_ERR_ARG        # unknown flag
+    assert f(FAKE, 1, 128, 128, 0, FAKE, big, None) == ssc.SSC_ERR_UNSUPPORTED  # k=3 only
+    assert f(FAKE, 27, 48, 128, 0, FAKE, big, None) == ssc.SSC_ERR_UNSUPPORTED  # no MFMA shape
+    assert f(FAKE, 27, 128, 128, 1, FAKE, 100, None) == ssc.SSC_ERR_WORKSPACE
+    assert lib.ssc_packed_weight_bytes(27, 128, 128) >= 27 * 128 * 128 * 2
+    g = lib.ssc_subm_conv3d_packed
+    assert g(FAKE, FAKE, None, FAKE, 0, 128, 128, FAKE, ssc.SSC_F32, None) == ssc.SSC_OK
+    assert g(FAKE, FAKE, None, FAKE, 10, 48, 128, FAKE, ssc.SSC_F32, None) == ssc.SSC_ERR_UNSUPPORTED
+    assert g(FAKE, None, None, FAKE, 10, 128, 128, FAKE, ssc.SSC_F32, None) == ssc.SSC_ERR_ARG
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):

@@ -257,3 +257,32 @@ def test_linear(n, cin, cout):
     ref = oracle.linear(x.float().numpy(), w.float().numpy(), b.numpy())
     assert rel_err(y.cpu().numpy(), ref) <= TAU["bf16"]
     assert torch.equal(ybf.cpu().view(torch.int16), rne_bf16(y.cpu()).view(torch.int16))
+
+
+@pytest.mark.parametrize("cin,cout", [(128, 128), (64, 32), (32, 64)])
+def test_packed_matches_per_call_packing(cin, cout):
+    say(f"[packed] cin={cin} cout={cout}")
+    coords, x, w, b = small_case(cin + 3 * cout, 1, (20, 20, 20), 0.1, cin, cout)
+    idx = run_gpu(coords, 1, (20, 20, 20))
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    y = idx.conv(xd, wd, bd)
+    pw = ssc.pack_weights(wd)
+    yp = ssc.subm_conv3d_packed(xd, pw, bd, idx.plan)
+    ypb = ssc.subm_conv3d_packed(xd, pw, bd, idx.plan, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yp)
+    assert torch.equal(ypb.cpu().view(torch.int16), rne_bf16(y.cpu()).view(torch.int16))
+
+
+def test_flip_orientation_matches_oracle():
+    say("[flip]")
+    coords, x, w, b = small_case(31, 2, (14, 14, 14), 0.2, 64, 64)
+    m = oracle.build_map(coords, 2, (14, 14, 14))
+    idx = run_gpu(coords, 2, (14, 14, 14))
+    pw = ssc.pack_weights(w.to(DEV), flip=True)
+    y = ssc.subm_conv3d_packed(x.to(DEV), pw, b.to(DEV), idx.plan)
+    torch.cuda.synchronize()
+    ref = oracle.conv(x.float().numpy(), w.float().numpy(), b.numpy(), m, flip=True)
+    assert rel_err(y.cpu().numpy(), ref) <= TAU["bf16"]
+    ref_cc = oracle.conv(x.float().numpy(), w.float().numpy(), b.numpy(), m)
+    assert rel_err(y.cpu().numpy(), ref_cc) > 0.1  # really the other orientation
