@@ -95,9 +95,9 @@ size_t ssc_plan_workspace_bytes(int64_t n);
 
 /* Reorders the sites for the convolution kernels and stores the neighbour rows in that order
  * (the "prepared device index" the LATO.2 page caches per coordinate set).  The plan holds:
- * the site order (rows sorted by their 26-bit mask of valid non-centre taps, so that 16-row
- * blocks share which taps are present), each 16-row block's tap mask, and the neighbour rows
- * tap-major in that order.  The plan depends only on nbr; it is valid for any features and
+ * the site order (rows stably sorted by the rank of their 26-bit mask of valid non-centre
+ * taps read as a reflected Gray code, so that 16-row blocks share which taps are present),
+ * each 16-row block's tap mask, and the neighbour rows tap-major in that order.  The plan depends only on nbr; it is valid for any features and
  * weights and for every k=3 layer on the same coordinate set.
  *   nbr   [n, 27] int32 from ssc_build_index (or any map with the same meaning).
  *   plan  >= ssc_plan_bytes(n) bytes, 256-byte aligned; written completely.
@@ -105,6 +105,15 @@ size_t ssc_plan_workspace_bytes(int64_t n);
  * Bit-reproducible: the same nbr always yields the same plan. */
 ssc_status ssc_build_plan(const int32_t* nbr, int64_t n, void* plan, size_t plan_bytes,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Where the parts of a plan for n sites live (for inspection and tests; host only, no GPU).
+ * Writes layout[0] = npad (rows, n rounded up to a multiple of 256, at least 256), then byte
+ * offsets within the plan buffer: layout[1] perm (int32 [npad]: original site of each sorted
+ * row, -1 on padding rows), layout[2] block masks (uint32 [npad / 16]: OR over the block's
+ * rows of (1 << t) for every tap t with a neighbour), layout[3] neighbour rows (int32
+ * [27][npad]: row r of tap t holds nbr[perm[r]][t], -1 on padding), layout[4] the zero row
+ * (2048 bytes of zeros).  Returns SSC_ERR_ARG for n < 0 or a null layout. */
+ssc_status ssc_plan_layout(int64_t n, int64_t* layout);
 
 /* ---------------------------------------------------------------------------------------
  * Convolution (warm path)

@@ -68,6 +68,7 @@ def load_library():
         "ssc_plan_bytes": ([i64], sz),
         "ssc_plan_workspace_bytes": ([i64], sz),
         "ssc_build_plan": ([p, i64, p, sz, p, sz, p], ctypes.c_int),
+        "ssc_plan_layout": ([i64, p], ctypes.c_int),
         "ssc_conv_workspace_bytes": ([i32, i32, i32], sz),
         "ssc_subm_conv3d": ([p, i32, p, p, p, i64, i32, i32, p, i32, p, sz, p], ctypes.c_int),
         "ssc_linear": ([p, i32, p, p, i64, i32, i32, p, i32, p, sz, p], ctypes.c_int),
@@ -152,6 +153,19 @@ class Plan:
     @property
     def device(self):
         return self.buf.device
+
+    def parts(self):
+        """Device views of the plan: (perm int32 [npad], block masks int32 [npad/16],
+        neighbour rows int32 [27, npad]) as laid out by ssc_plan_layout."""
+        lay = (ctypes.c_int64 * 5)()
+        _check(load_library().ssc_plan_layout(self.n, lay), "ssc_plan_layout")
+        npad, o_perm, o_bm, o_g = lay[0], lay[1], lay[2], lay[3]
+
+        def view(off, count):
+            return self.buf[off:off + 4 * count].view(torch.int32)
+
+        return (view(o_perm, npad), view(o_bm, npad // 16),
+                view(o_g, TAPS * npad).view(TAPS, npad))
 
 
 def build_plan(nbr: torch.Tensor) -> Plan:

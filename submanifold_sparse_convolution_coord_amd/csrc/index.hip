@@ -187,6 +187,15 @@ __global__ void k_mask_keys(const int32_t* __restrict__ nbr, int64_t n, uint32_t
     if (t == kCentreTap) continue;
     if (row[t] >= 0) m |= 1u << (t < kCentreTap ? t : t - 1);
   }
+  // Sort key: the rank of m read as a reflected Gray code (bit i of the key is the XOR of
+  // bits i..25 of m).  Neighbouring ranks differ in one tap, so sites next to each other in
+  // key order share more taps than in plain numeric order (fewer taps per tile, fewer
+  // partly-empty 16-row blocks).
+  m ^= m >> 1;
+  m ^= m >> 2;
+  m ^= m >> 4;
+  m ^= m >> 8;
+  m ^= m >> 16;
   keys[i] = m;
   vals[i] = static_cast<uint32_t>(i);
 }
@@ -377,6 +386,17 @@ extern "C" size_t ssc_plan_bytes(int64_t n) { return n < 0 ? 0 : plan_layout(n).
 
 extern "C" size_t ssc_plan_workspace_bytes(int64_t n) {
   return n < 0 ? 0 : plan_work_layout(n).total;
+}
+
+extern "C" ssc_status ssc_plan_layout(int64_t n, int64_t* layout) {
+  if (n < 0 || layout == nullptr) return SSC_ERR_ARG;
+  const PlanLayout L = plan_layout(n);
+  layout[0] = L.npad;
+  layout[1] = static_cast<int64_t>(L.off_perm);
+  layout[2] = static_cast<int64_t>(L.off_bmask);
+  layout[3] = static_cast<int64_t>(L.off_gidx);
+  layout[4] = static_cast<int64_t>(L.off_zero);
+  return SSC_OK;
 }
 
 extern "C" ssc_status ssc_build_plan(const int32_t* nbr, int64_t n, void* plan, size_t plan_bytes,

@@ -144,3 +144,17 @@ def test_product_path_does_not_import_oracle():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "liboracle" not in text, fn
+
+
+def test_plan_layout(lib):
+    lay = (ctypes.c_int64 * 5)()
+    assert lib.ssc_plan_layout(-1, lay) == ssc.SSC_ERR_ARG
+    assert lib.ssc_plan_layout(10, None) == ssc.SSC_ERR_ARG
+    for n in (0, 1, 255, 256, 257, 100000):
+        assert lib.ssc_plan_layout(n, lay) == ssc.SSC_OK
+        npad, o_perm, o_bm, o_g, o_zero = lay
+        assert npad % 256 == 0 and npad >= max(n, 1) and npad - max(n, 1) < 256
+        assert o_zero + 2048 <= o_perm and o_perm + 4 * npad <= o_bm
+        assert o_bm + 4 * (npad // 16) <= o_g
+        assert o_g + 4 * 27 * npad <= lib.ssc_plan_bytes(n)
+        assert all(o % 256 == 0 for o in (o_perm, o_bm, o_g, o_zero))

@@ -286,3 +286,37 @@ def test_flip_orientation_matches_oracle():
     assert rel_err(y.cpu().numpy(), ref) <= TAU["bf16"]
     ref_cc = oracle.conv(x.float().numpy(), w.float().numpy(), b.numpy(), m)
     assert rel_err(y.cpu().numpy(), ref_cc) > 0.1  # really the other orientation
+
+
+def gray_rank_keys(nbr: np.ndarray) -> np.ndarray:
+    """Sort key of the plan, computed here from its definition: the 26-bit mask of valid
+    non-centre taps (tap t < 13 at bit t, t > 13 at bit t - 1), read as a reflected Gray code
+    and converted to its rank (bit i = XOR of mask bits i..25)."""
+    valid = np.delete(nbr >= 0, 13, axis=1).astype(np.int64)
+    rank = np.zeros(len(valid), np.int64)
+    for i in range(26):
+        rank |= np.bitwise_xor.reduce(valid[:, i:], axis=1) << i
+    return rank
+
+
+@pytest.mark.parametrize("name", ["tiny", "batch4", "iid128"])
+def test_plan_structure(name):
+    """The plan is a stable sort of the sites by Gray rank of their tap mask, with every
+    part (row ids, block masks, tap-major neighbour rows) consistent with the map."""
+    say(f"[plan] {name}")
+    w, m = workload_case(name)
+    idx = run_gpu(w.coords, w.batch, w.grid)
+    nbr = idx.nbr.cpu().numpy()
+    np.testing.assert_array_equal(nbr, m)
+    perm, bmask, gidx = (t.cpu().numpy() for t in idx.plan.parts())
+    n, npad = len(m), perm.shape[0]
+    assert npad % 256 == 0 and npad >= n
+    assert np.array_equal(np.sort(perm[:n]), np.arange(n)) and (perm[n:] == -1).all()
+    assert np.array_equal(gidx[:, :n], m[perm[:n]].T) and (gidx[:, n:] == -1).all()
+    bits = ((gidx >= 0).astype(np.int64) << np.arange(27)[:, None]).reshape(27, -1, 16)
+    want = np.bitwise_or.reduce(np.bitwise_or.reduce(bits, axis=2), axis=0)
+    assert np.array_equal(bmask.astype(np.uint32).astype(np.int64), want)
+    keys = gray_rank_keys(m)[perm[:n]]
+    assert (np.diff(keys) >= 0).all()
+    same = np.diff(keys) == 0
+    assert (np.diff(perm[:n])[same] > 0).all()          # stable among equal keys
