@@ -179,24 +179,25 @@ __device__ __forceinline__ bf16x8_t lds_read16(const void* p) {
 // always issued by wave i % WAVES, so a wave reads all its row indices before its first copy.
 // With CIN = 128 that is one 4-row part of every block per wave; narrower rows give each
 // wave whole blocks (CIN = 32) or half blocks (CIN = 64), and no lane of a copy idles.
+// Blocks of the tile that have tap t, as a bit set (lane b of bmv holds block b's tap mask,
+// lanes past the tile hold 0).
+__device__ __forceinline__ uint32_t block_taps(uint32_t bmv, int t) {
+  return static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(((bmv >> t) & 1u) != 0u));
+}
+
 template <int CIN, int COUT, int NB, int WR, int WC>
-__device__ __forceinline__ void issue_gather(int q, int t, const uint32_t (&bm)[NB],
-                                             const uint16_t* __restrict__ X,
+__device__ __forceinline__ void issue_gather(int q, uint32_t act, const uint16_t* __restrict__ X,
                                              const uint16_t* __restrict__ zrow,
-                                             const int32_t* sG, const char* sA, int wave,
-                                             int lane) {
+                                             const int32_t* sG, uint32_t sA, int wave, int lane) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
+  const int32_t* g = sG + q * (NB * 16);
   if constexpr (CIN < 128) {
     constexpr int RPI = 64 / C::CPR;
     constexpr int PIECES = 16 / RPI;
     constexpr int PPW = NB * PIECES / C::WAVES;
     static_assert(NB * PIECES % C::WAVES == 0 && (C::WAVES & (C::WAVES - 1)) == 0,
                   "pieces per wave");
-    const int32_t* g = sG + q * (NB * 16);
     const int rsub = lane / C::CPR;
-    uint32_t act = 0;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) act |= ((bm[b] >> t) & 1u) << b;
     int32_t j[PPW];
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
@@ -211,24 +212,22 @@ __device__ __forceinline__ void issue_gather(int q, int t, const uint32_t (&bm)[
       const int chunk = (lane % C::CPR) ^ swz<C::CPR>(part * RPI + rsub);
       const uint16_t* src =
           j[i] >= 0 ? X + static_cast<int64_t>(j[i]) * CIN + chunk * 8 : zrow + chunk * 8;
-      dma16(src, lds_addr(sA + b * C::A_BLOCK * 2 + part * 1024));
+      dma16(src, sA + b * C::A_BLOCK * 2 + part * 1024);
     }
   } else {
     // CIN = 128: wave w copies rows 4w..4w+3 of every block (the same pieces as above, with
     // the block's test hoisted out of the index arithmetic).
     const int rr = (wave * C::RPW + lane / C::CPR) & 15;
     const int chunk = (lane % C::CPR) ^ swz<C::CPR>(rr);
-    const int32_t* g = sG + q * (NB * 16);
     int32_t j[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) j[b] = g[b * 16 + rr];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      if (!((bm[b] >> t) & 1u)) continue;
+      if (!((act >> b) & 1u)) continue;
       const uint16_t* src =
           j[b] >= 0 ? X + static_cast<int64_t>(j[b]) * CIN + chunk * 8 : zrow + chunk * 8;
-      if (lane < C::A_LANES)
-        dma16(src, lds_addr(sA + b * C::A_BLOCK * 2 + wave * C::RPW * CIN * 2));
+      dma16(src, sA + b * C::A_BLOCK * 2 + wave * C::RPW * CIN * 2);
     }
   }
 }
@@ -261,7 +260,7 @@ __device__ __forceinline__ void a_frag_offsets(int lane, uint32_t (&off)[CIN / 3
 }
 
 template <int CIN, int COUT, int NB, int WR, int WC>
-__device__ __forceinline__ void compute_stage(int t, const uint32_t (&bm)[NB], const char* sA,
+__device__ __forceinline__ void compute_stage(uint32_t act, const char* sA,
                                               const bf16x8_t (&bw)[COUT / WC / 16][CIN / 32],
                                               const uint32_t (&aoff)[CIN / 32], int wr,
                                               f32x4_t (&acc)[NB / WR][COUT / WC / 16]) {
@@ -269,7 +268,7 @@ __device__ __forceinline__ void compute_stage(int t, const uint32_t (&bm)[NB], c
 #pragma unroll
   for (int bl = 0; bl < C::BPW; ++bl) {
     const int b = bl * WR + wr;
-    if (!((bm[b] >> t) & 1u)) continue;
+    if (!((act >> b) & 1u)) continue;
     const char* blk = sA + b * (C::A_BLOCK * 2);
     bf16x8_t a[C::KS];
 #pragma unroll
@@ -295,21 +294,25 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   int32_t* sG = reinterpret_cast<int32_t*>(smem + C::OFF_G);
   int32_t* sP = reinterpret_cast<int32_t*>(smem + C::OFF_P);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Wave index as a scalar: every per-block decision below is uniform across the wave and
+  // compiles to scalar branches, and LDS destinations are scalar byte addresses.
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int wr = wave / WC, wc = wave % WC;
+  const uint32_t lds0 = lds_addr(smem);
   // The plan sorts sites by tap mask, so per-tile work grows along the site order (a tile of
   // near-empty masks has a tap or two, the last tiles a dozen or more).  Launch the heavy
   // end first so that the workgroups dispatched last are the short ones.
   const int64_t tile = static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x;
   const int64_t row0 = tile * (NB * 16);
 
-  uint32_t bm[NB];
-  uint32_t U = 0;
+  // Block tap masks: lane b holds block b's (for the per-tap block sets, one ballot each), and
+  // their union U is the set of taps the tile walks.
+  const uint32_t bmv = lane < NB ? bmask[tile * NB + lane] : 0u;
+  uint32_t U = bmv;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    bm[b] = bmask[tile * NB + b];
-    U |= bm[b];
-  }
+  for (int off = 1; off < NB; off <<= 1) U |= __shfl_xor(U, off, 64);
+  U = __builtin_amdgcn_readfirstlane(U);
 
   // Neighbour rows of the tile for every tap present -> sG[q][NB*16].  One 1 KB copy holds
   // G_TAPS_PER_COPY taps; copies are dealt to the waves round robin.
@@ -333,14 +336,14 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
           if (i == sub) mine = tt[i];
         if (mine >= 0)
           dma16(gidx + static_cast<int64_t>(mine) * npad + row0 + off,
-                lds_addr(sG + q * (NB * 16)));
+                lds0 + C::OFF_G + q * (NB * 16 * 4));
       }
       q += TPC;
       ++k;
     }
   }
   // The tile's original row indices -> sP (read by the epilogue), by the last wave.
-  if (wave == C::WAVES - 1 && lane < NB * 4) dma16(perm + row0 + lane * 4, lds_addr(sP));
+  if (wave == C::WAVES - 1 && lane < NB * 4) dma16(perm + row0 + lane * 4, lds0 + C::OFF_P);
   // Bias of this lane's columns, loaded now so the epilogue issues no global loads.
   float bv[C::NCT];
 #pragma unroll
@@ -365,32 +368,38 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     int t_cur = __builtin_ctz(rem);
     rem &= rem - 1;
     int q = 0;
+    uint32_t act = block_taps(bmv, t_cur);
     load_weights<CIN, COUT, NB, WR, WC>(t_cur, Wp, wc, lane, bw0);
-    issue_gather<CIN, COUT, NB, WR, WC>(0, t_cur, bm, X, zrow, sG, sA0, wave, lane);
+    issue_gather<CIN, COUT, NB, WR, WC>(0, act, X, zrow, sG, lds0, wave, lane);
     while (true) {
       wait_vm_lgkm0();
       __builtin_amdgcn_s_barrier();
       int t_next = rem ? __builtin_ctz(rem) : -1;
+      uint32_t act_next = 0;
       if (t_next >= 0) {
+        act_next = block_taps(bmv, t_next);
         load_weights<CIN, COUT, NB, WR, WC>(t_next, Wp, wc, lane, bw1);
-        issue_gather<CIN, COUT, NB, WR, WC>(q + 1, t_next, bm, X, zrow, sG, sA1, wave, lane);
+        issue_gather<CIN, COUT, NB, WR, WC>(q + 1, act_next, X, zrow, sG, lds0 + C::OFF_A1, wave,
+                                            lane);
       }
-      compute_stage<CIN, COUT, NB, WR, WC>(t_cur, bm, sA0, bw0, aoff, wr, acc);
+      compute_stage<CIN, COUT, NB, WR, WC>(act, sA0, bw0, aoff, wr, acc);
       if (t_next < 0) break;
       rem &= rem - 1;
-      t_cur = t_next;
+      act = act_next;
       ++q;
       wait_vm_lgkm0();
       __builtin_amdgcn_s_barrier();
       t_next = rem ? __builtin_ctz(rem) : -1;
+      act_next = 0;
       if (t_next >= 0) {
+        act_next = block_taps(bmv, t_next);
         load_weights<CIN, COUT, NB, WR, WC>(t_next, Wp, wc, lane, bw0);
-        issue_gather<CIN, COUT, NB, WR, WC>(q + 1, t_next, bm, X, zrow, sG, sA0, wave, lane);
+        issue_gather<CIN, COUT, NB, WR, WC>(q + 1, act_next, X, zrow, sG, lds0, wave, lane);
       }
-      compute_stage<CIN, COUT, NB, WR, WC>(t_cur, bm, sA1, bw1, aoff, wr, acc);
+      compute_stage<CIN, COUT, NB, WR, WC>(act, sA1, bw1, aoff, wr, acc);
       if (t_next < 0) break;
       rem &= rem - 1;
-      t_cur = t_next;
+      act = act_next;
       ++q;
     }
   }
