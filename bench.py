@@ -49,15 +49,16 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def counted_traffic(kernel: str, digest: str):
+def counted_traffic(kernel: str, digest: str, workload: str, out_dtype: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel sources; else None."""
+    the current kernel sources for this kernel, workload and output type; else None."""
     path = os.path.join(ROOT, "profiles", "conv_iid128_counters.json")
     try:
         d = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if d.get("source_digest") != digest or d.get("kernel") != kernel:
+    if (d.get("source_digest") != digest or d.get("kernel") != kernel
+            or d.get("workload") != workload or d.get("out_dtype", "f32") != out_dtype):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -75,13 +76,14 @@ def _counter_rows(d: str, kernel_substr: str, counter: str):
     return vals
 
 
-def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mb, out_path):
-    """HBM traffic of the conv kernel per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mb, out_path,
+                       kernel="k_subm_lds<128, 128", label="k_subm_lds<128,128>",
+                       workload="iid128"):
+    """HBM traffic of one kernel per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
     scaled by what the same counters read for a plain device copy of cal_mb MiB."""
-    conv = "k_subm_lds"
     copy = "copy"  # torch's elementwise copy kernel
-    f = _counter_rows(fetch_dir, conv, "FETCH_SIZE")
-    w = _counter_rows(write_dir, conv, "WRITE_SIZE")
+    f = _counter_rows(fetch_dir, kernel, "FETCH_SIZE")
+    w = _counter_rows(write_dir, kernel, "WRITE_SIZE")
     cf = _counter_rows(cal_fetch_dir, copy, "FETCH_SIZE")
     cw = _counter_rows(cal_write_dir, copy, "WRITE_SIZE")
     if not (f and w and cf and cw):
@@ -91,7 +93,7 @@ def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_m
     write_scale = known / float(np.median(cw))
     fetch_b = float(np.mean(f)) * 1024.0 * fetch_scale
     write_b = float(np.mean(w)) * 1024.0 * write_scale
-    d = {"kernel": "k_subm_lds<128,128>", "workload": "iid128", "source_digest": source_digest(),
+    d = {"kernel": label, "workload": workload, "out_dtype": "f32", "source_digest": source_digest(),
          "fetch_kib_per_dispatch": float(np.mean(f)), "write_kib_per_dispatch": float(np.mean(w)),
          "copy_calibration_mib": cal_mb, "copy_fetch_kib": float(np.median(cf)),
          "copy_write_kib": float(np.median(cw)), "fetch_scale": fetch_scale,
@@ -110,7 +112,8 @@ def cpu_baseline(w, m_nbr) -> dict:
     wt = w.layers[0].weight.float().numpy()
     b = w.layers[0].bias.numpy()
     ts = []
-    while len(ts) < 5 or (sum(ts) < 1.0 and len(ts) < 50):
+    # About 10 s of oracle work (at least 3 runs, at most 30 s).
+    while len(ts) < 3 or sum(ts) < 10.0:
         t0 = time.perf_counter()
         oracle.conv(x, wt, b, m_nbr)
         ts.append(time.perf_counter() - t0)
@@ -261,7 +264,7 @@ def main():
     value = mvox_per_s(w.n, ms_step * 1e-3)
     kname = f"k_subm_lds<{cin},{cout}>" if use_packed else "k_conv_valu"
     digest = source_digest()
-    traffic = counted_traffic(kname, digest)
+    traffic = counted_traffic(kname, digest, args.workload, args.out_dtype)
 
     res = {
         "metric": METRIC,
