@@ -176,17 +176,21 @@ def main():
     torch.cuda.synchronize()
 
     # Cold path, timed on its own: neighbour map + plan (once per coordinate set).
-    cold = []
+    cold, cold_index, cold_plan = [], [], []
     for _ in range(5):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         e0.record()
         nbr = ssc.build_index(coords, w.batch, w.grid, check=False)
-        plan = ssc.build_plan(nbr)
         e1.record()
+        plan = ssc.build_plan(nbr)
+        e2.record()
         torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
+        cold.append(e0.elapsed_time(e2))
+        cold_index.append(e0.elapsed_time(e1))
+        cold_plan.append(e1.elapsed_time(e2))
     pairs = int((nbr >= 0).sum().item())
-    log(f"[bench] n={w.n} valid_pairs={pairs} cold index+plan median {np.median(cold):.3f} ms")
+    log(f"[bench] n={w.n} valid_pairs={pairs} cold index+plan median {np.median(cold):.3f} ms "
+        f"(index {np.median(cold_index):.3f}, plan {np.median(cold_plan):.3f})")
 
     # Layer weights are re-laid out once, at load time, as the pages' ports convert their
     # checkpoints once (Pixal3D README / LATO.2 page, weight converters); a step is then the
@@ -294,6 +298,15 @@ def main():
                  "frac_bf16_peak_step": round(tflops_step / PEAK_BF16_TFLOPS, 5),
                  "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": flops},
         "cold_index_plan_ms": round(float(np.median(cold)), 4),
+        # Algorithmic bytes of the cold path: the index reads the coordinates (16 B per site)
+        # and writes the map (27 x 4 B); the plan reads the map and writes the row ids, block
+        # masks and tap-major rows (4 + 27 x 4 + 0.25 B).
+        "cold_index": {
+            "index_ms": round(float(np.median(cold_index)), 4),
+            "index_gbs": round(w.n * (16 + 108) / (float(np.median(cold_index)) * 1e-3) / 1e9, 1),
+            "plan_ms": round(float(np.median(cold_plan)), 4),
+            "plan_gbs": round(w.n * (108 + 4 + 108 + 0.25) / (float(np.median(cold_plan)) * 1e-3)
+                              / 1e9, 1)},
         "layer_us_per_call_weight_relayout": round(ms_percall * 1e3, 2),
         "k1_layer_us": None if k1_us is None else round(k1_us, 2),
         "host_enqueue_us_per_step": round(t_host * 1e6, 2),

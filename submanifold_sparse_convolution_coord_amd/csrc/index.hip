@@ -44,9 +44,17 @@ __device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
   return z ^ (z >> 31);
 }
 
+// One 16-byte slot holds a key and its row, so a probe that finds its key reads one cache
+// line, not two.
+struct alignas(16) Slot {
+  unsigned long long key;
+  int32_t val;
+  int32_t pad;
+};
+
 struct IndexLayout {
   uint64_t cap;
-  size_t off_keys, off_vals, total;
+  size_t off_slots, total;
 };
 
 inline IndexLayout index_layout(int64_t n) {
@@ -55,24 +63,23 @@ inline IndexLayout index_layout(int64_t n) {
   uint64_t cap = 64;
   while (cap < want) cap <<= 1;
   L.cap = cap;
-  L.off_keys = kAlign;  // [0, 256): two uint32 error counters
-  L.off_vals = align_up(L.off_keys + sizeof(unsigned long long) * cap);
-  L.total = align_up(L.off_vals + sizeof(int32_t) * cap);
+  L.off_slots = kAlign;  // [0, 256): two uint32 error counters
+  L.total = align_up(L.off_slots + sizeof(Slot) * cap);
   return L;
 }
 
-__global__ void k_table_init(unsigned long long* __restrict__ keys, uint64_t cap,
+__global__ void k_table_init(Slot* __restrict__ slots, uint64_t cap,
                              uint32_t* __restrict__ counters) {
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
   for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < cap;
        i += stride)
-    keys[i] = kEmptyKey;
+    slots[i].key = kEmptyKey;
   if (blockIdx.x == 0 && threadIdx.x < 2) counters[threadIdx.x] = 0;
 }
 
 __global__ void k_insert(const int4* __restrict__ coords, int64_t n, int batch, int gx, int gy,
-                         int gz, unsigned long long* __restrict__ keys, int32_t* __restrict__ vals,
-                         uint64_t mask, uint32_t* __restrict__ counters) {
+                         int gz, Slot* __restrict__ slots, uint64_t mask,
+                         uint32_t* __restrict__ counters) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += stride) {
@@ -87,9 +94,9 @@ __global__ void k_insert(const int4* __restrict__ coords, int64_t n, int batch, 
     // The table has at least twice as many slots as sites, so an empty slot always exists
     // and the probe ends.
     while (true) {
-      const unsigned long long prev = atomicCAS(&keys[h], kEmptyKey, key);
+      const unsigned long long prev = atomicCAS(&slots[h].key, kEmptyKey, key);
       if (prev == kEmptyKey) {
-        vals[h] = static_cast<int32_t>(i);
+        slots[h].val = static_cast<int32_t>(i);
         break;
       }
       if (prev == key) {
@@ -102,8 +109,7 @@ __global__ void k_insert(const int4* __restrict__ coords, int64_t n, int batch, 
 }
 
 __global__ void k_query(const int4* __restrict__ coords, int64_t n, int batch, int gx, int gy,
-                        int gz, const unsigned long long* __restrict__ keys,
-                        const int32_t* __restrict__ vals, uint64_t mask,
+                        int gz, const Slot* __restrict__ slots, uint64_t mask,
                         int32_t* __restrict__ nbr) {
   const int64_t total = n * kTaps;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -119,9 +125,10 @@ __global__ void k_query(const int4* __restrict__ coords, int64_t n, int batch, i
       uint64_t h = mix64(key) & mask;
       // At least half the slots are empty, so the probe ends.
       while (true) {
-        const unsigned long long k = keys[h];
+        const uint4 v = *reinterpret_cast<const uint4*>(&slots[h]);  // key and row, one load
+        const unsigned long long k = (static_cast<unsigned long long>(v.y) << 32) | v.x;
         if (k == key) {
-          r = vals[h];
+          r = static_cast<int32_t>(v.z);
           break;
         }
         if (k == kEmptyKey) break;
@@ -309,26 +316,42 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
   }
 }
 
-// perm, per-block tap masks and tap-major neighbour rows in sorted order.  One thread per
-// sorted position; each 16-lane group of a wave is one block.
+// perm, per-block tap masks and tap-major neighbour rows in sorted order.  A workgroup owns
+// 256 sorted positions: it reads their 256 map rows cooperatively (consecutive lanes read
+// consecutive entries of a row, so a wave touches a few 108-byte rows instead of 64 scattered
+// words), stages them in LDS, then writes each tap's 256 entries as one coalesced run.  Each
+// 16-lane group of a wave is one block for the tap masks.
 __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ nbr, int64_t n,
                                                    const uint32_t* __restrict__ sorted_rows,
                                                    int64_t npad, int32_t* __restrict__ perm,
                                                    uint32_t* __restrict__ bmask,
                                                    int32_t* __restrict__ gidx) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;  // < npad
+  __shared__ int32_t rows[256 * kTaps];  // row-major [position][tap]; stride 27 is odd, so a
+                                         // wave's column reads hit distinct banks
+  __shared__ int32_t src[256];
+  const int tid = threadIdx.x;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 256;
+  const int64_t r = r0 + tid;  // < npad
   const int32_t i = r < n ? static_cast<int32_t>(sorted_rows[r]) : -1;
   perm[r] = i;
+  src[tid] = i;
+  __syncthreads();
+  for (int e = tid; e < 256 * kTaps; e += 256) {
+    const int p = e / kTaps, t = e - p * kTaps;
+    const int32_t ii = src[p];
+    rows[e] = ii >= 0 ? nbr[static_cast<int64_t>(ii) * kTaps + t] : -1;
+  }
+  __syncthreads();
   uint32_t m = 0;
 #pragma unroll
   for (int t = 0; t < kTaps; ++t) {
-    const int32_t j = i >= 0 ? nbr[static_cast<int64_t>(i) * kTaps + t] : -1;
+    const int32_t j = rows[tid * kTaps + t];
     gidx[t * npad + r] = j;
     if (j >= 0) m |= 1u << t;
   }
 #pragma unroll
   for (int off = 1; off < kBlockRows; off <<= 1) m |= __shfl_xor(m, off, 64);
-  if ((threadIdx.x & (kBlockRows - 1)) == 0) bmask[r / kBlockRows] = m;
+  if ((tid & (kBlockRows - 1)) == 0) bmask[r / kBlockRows] = m;
 }
 
 }  // namespace
@@ -356,19 +379,18 @@ extern "C" ssc_status ssc_build_index(const int32_t* coords, int64_t n, int32_t 
   hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
-  auto* keys = reinterpret_cast<unsigned long long*>(ws + L.off_keys);
-  auto* vals = reinterpret_cast<int32_t*>(ws + L.off_vals);
+  auto* slots = reinterpret_cast<Slot*>(ws + L.off_slots);
   const int bs = 256;
   const uint64_t init_blocks = std::min<uint64_t>((L.cap + bs - 1) / bs, 8192);
-  k_table_init<<<static_cast<unsigned>(init_blocks), bs, 0, s>>>(keys, L.cap, counters);
+  k_table_init<<<static_cast<unsigned>(init_blocks), bs, 0, s>>>(slots, L.cap, counters);
   const unsigned ins_blocks = static_cast<unsigned>(std::min<int64_t>((n + bs - 1) / bs, 65536));
   k_insert<<<ins_blocks, bs, 0, s>>>(
-      reinterpret_cast<const int4*>(coords), n, batch, grid[0], grid[1], grid[2], keys, vals,
+      reinterpret_cast<const int4*>(coords), n, batch, grid[0], grid[1], grid[2], slots,
       L.cap - 1, counters);
   const int64_t q = n * kTaps;
   const unsigned q_blocks = static_cast<unsigned>(std::min<int64_t>((q + bs - 1) / bs, 262144));
   k_query<<<q_blocks, bs, 0, s>>>(
-      reinterpret_cast<const int4*>(coords), n, batch, grid[0], grid[1], grid[2], keys, vals,
+      reinterpret_cast<const int4*>(coords), n, batch, grid[0], grid[1], grid[2], slots,
       L.cap - 1, nbr);
   if (launch_status() != SSC_OK) return SSC_ERR_HIP;
   if (check) {
