@@ -103,6 +103,63 @@ def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_m
     print(json.dumps(d))
 
 
+def time_resample(ssc, torch, coords, x, w, dev, reps: int = 20) -> dict:
+    """Device time of the downsample (max), its upsample and the subdivide on the workload's
+    sites and features, called through the C ABI on preallocated buffers (the binding's
+    downsample reads the parent count back, which would put a host round trip in the
+    timing).  GB/s from the algorithmic bytes of each op."""
+    import ctypes
+    lib = ssc.load_library()
+    n, ch = x.shape
+    esz = x.element_size()
+    dt = ssc.SSC_BF16 if x.dtype == torch.bfloat16 else ssc.SSC_F32
+    g = (ctypes.c_int32 * 3)(*w.grid)
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    oc = torch.empty((n, 4), dtype=torch.int32, device=dev)
+    of = torch.empty((n, ch), dtype=x.dtype, device=dev)
+    par = torch.empty(n, dtype=torch.int32, device=dev)
+    res = torch.zeros(2, dtype=torch.int64, device=dev)
+    ws = torch.empty(lib.ssc_downsample_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    sc = torch.empty((8 * n, 4), dtype=torch.int32, device=dev)
+    sf = torch.empty((8 * n, ch), dtype=x.dtype, device=dev)
+    up = torch.empty((n, ch), dtype=x.dtype, device=dev)
+
+    def down():
+        return lib.ssc_downsample2(p(coords), n, w.batch, g, p(x), dt, ch, p(oc), p(of), p(par),
+                                   p(res), p(ws), ws.numel(), st)
+
+    assert down() == 0
+    torch.cuda.synchronize()
+    m = int(res[0].item())
+
+    def ups():
+        return lib.ssc_upsample2(p(of), dt, ch, p(par), n, m, p(up), st)
+
+    def sub():
+        return lib.ssc_subdivide2(p(coords), n, g, p(x), dt, ch, p(sc), p(sf), st)
+
+    def t(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    row = ch * esz
+    d_us, u_us, s_us = t(down), t(ups), t(sub)
+    d_bytes = n * (16 + row + 4) + m * (16 + row)
+    u_bytes = n * (4 + row) + m * row
+    s_bytes = n * (16 + row) + 8 * n * (16 + row)
+    return {"n": n, "parents": m, "channels": ch,
+            "downsample_us": round(d_us, 2), "downsample_gbs": round(d_bytes / d_us / 1e3, 1),
+            "upsample_us": round(u_us, 2), "upsample_gbs": round(u_bytes / u_us / 1e3, 1),
+            "subdivide_us": round(s_us, 2), "subdivide_gbs": round(s_bytes / s_us / 1e3, 1)}
+
+
 def cpu_baseline(w, m_nbr) -> dict:
     """The CPU oracle as it stands (fp64 dictionary + per-voxel loop), warm: map prebuilt,
     conv over every site of the same workload, repeated for at least a second of wall time;
@@ -255,6 +312,25 @@ def main():
     if two:
         k1_us = timed(lambda: ssc.linear(y1, w2, b2, odt, out=y2), args.steps) * 1e3
         log(f"[bench] k=1 layer {k1_us:.1f} us")
+    # Single launches with the caches flushed: a 512 MiB fill runs between calls (outside the
+    # events), so the conv's inputs come from HBM, not from the 256 MB MALL.
+    flush = torch.empty(512 * 262144, dtype=torch.float32, device=dev)
+    single = []
+    for _ in range(min(args.steps, 100)):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        conv()
+        e1.record()
+        torch.cuda.synchronize()
+        single.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    flushed = {"median_us": round(float(np.median(single)), 2),
+               "p10_us": round(float(np.percentile(single, 10)), 2),
+               "p90_us": round(float(np.percentile(single, 90)), 2), "calls": len(single)}
+    log(f"[bench] conv kernel, caches flushed: median {flushed['median_us']} us")
+
+    resample = time_resample(ssc, torch, coords, x, w, dev)
 
     out_bytes = 4 if mid_dt == torch.float32 else 2
     in_bytes = x.element_size()
@@ -297,6 +373,8 @@ def main():
                  "effective_tflops_step": round(tflops_step, 2),
                  "frac_bf16_peak_step": round(tflops_step / PEAK_BF16_TFLOPS, 5),
                  "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": flops},
+        "conv_flushed": flushed,
+        "resample": resample,
         "cold_index_plan_ms": round(float(np.median(cold)), 4),
         # Algorithmic bytes of the cold path: the index reads the coordinates (16 B per site)
         # and writes the map (27 x 4 B); the plan reads the map and writes the row ids, block

@@ -177,6 +177,55 @@ ssc_status ssc_linear(const void* feats, int32_t in_dtype, const void* weight, c
                       int64_t n, int32_t cin, int32_t cout, void* out, int32_t out_dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Coordinate-changing neighbours: factor-2 downsample (max pool), its paired upsample, and
+ * the x8 subdivide.  Each yields a new coordinate set, indexed cold by ssc_build_index.
+ * ------------------------------------------------------------------------------------- */
+
+/* Bytes of scratch workspace ssc_downsample2 needs for n sites. */
+size_t ssc_downsample_workspace_bytes(int64_t n);
+
+/* SparseDownsample(2) with the max reduction (LATO.2 page, "Status": a max pool, not an
+ * average, as upstream passes reduce="amax").  The parent of site (b,x,y,z) is
+ * (b, x>>1, y>>1, z>>1) in the grid (ceil(gx/2), ceil(gy/2), ceil(gz/2)); every distinct
+ * parent is one output site, in ascending (b,x,y,z) order; its feature is the channel-wise
+ * maximum over its sites (only the sites present; the value returned is one of theirs,
+ * bit for bit).
+ *   coords     [n, 4] int32 (b,x,y,z), 16-byte aligned, inside batch / grid (as for
+ *              ssc_build_index; rows outside are counted in result[1], outputs then undefined).
+ *   feats      [n, channels] dtype (SSC_F32 or SSC_BF16); may be NULL when channels = 0.
+ *   out_coords [n, 4] int32 capacity, 16-byte aligned: rows [0, m) receive the parents.
+ *   out_feats  [n, channels] capacity: rows [0, m) receive the maxima.
+ *   parent     [n] int32: parent[i] = output row of site i's parent (the cache that
+ *              ssc_upsample2 consumes).
+ *   result     device int64[2], 8-byte aligned: result[0] = m, result[1] = rows outside the
+ *              grid.  Written on the stream (read it after synchronising).
+ *   workspace  >= ssc_downsample_workspace_bytes(n) bytes, 256-byte aligned, scratch only.
+ * Deterministic: a stable sort by parent. */
+ssc_status ssc_downsample2(const int32_t* coords, int64_t n, int32_t batch, const int32_t* grid,
+                           const void* feats, int32_t dtype, int32_t channels,
+                           int32_t* out_coords, void* out_feats, int32_t* parent, int64_t* result,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* SparseUpsample(2), the cache-paired inverse of a downsample (Pixal3D README, module table):
+ * out[i] = parent_feats[parent[i]] for the n sites of the finer set.
+ *   parent_feats [m, channels] dtype; parent [n] int32 from ssc_downsample2 (entries outside
+ *   [0, m) produce zero rows); out [n, channels] dtype.  Rows must be a multiple of 4 bytes. */
+ssc_status ssc_upsample2(const void* parent_feats, int32_t dtype, int32_t channels,
+                         const int32_t* parent, int64_t n, int64_t m, void* out, void* stream);
+
+/* SparseSubdivide: the x8 coordinate expansion the LATO.2 page uses for upsampling (module
+ * table: "upsampling is SparseSubdivide").  Site i becomes the 8 sites 8i + 4dx + 2dy + dz,
+ * dx,dy,dz in {0,1}, at (b, 2x+dx, 2y+dy, 2z+dz) in the grid (2gx, 2gy, 2gz), each carrying
+ * site i's features.
+ *   coords [n, 4] int32 inside the grid (not checked); grid extents <= 32767 (so the
+ *   subdivided grid fits the 16-bit key fields), else SSC_ERR_UNSUPPORTED.
+ *   feats [n, channels] dtype or NULL with channels = 0; out_coords [8n, 4];
+ *   out_feats [8n, channels].  Rows must be a multiple of 4 bytes. */
+ssc_status ssc_subdivide2(const int32_t* coords, int64_t n, const int32_t* grid,
+                          const void* feats, int32_t dtype, int32_t channels,
+                          int32_t* out_coords, void* out_feats, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,6 +76,10 @@ def load_library():
         "ssc_pack_weights": ([p, i32, i32, i32, p, sz, p], ctypes.c_int),
         "ssc_pack_weights_ex": ([p, i32, i32, i32, i32, p, sz, p], ctypes.c_int),
         "ssc_subm_conv3d_packed": ([p, p, p, p, i64, i32, i32, p, i32, p], ctypes.c_int),
+        "ssc_downsample_workspace_bytes": ([i64], sz),
+        "ssc_downsample2": ([p, i64, i32, p, p, i32, i32, p, p, p, p, p, sz, p], ctypes.c_int),
+        "ssc_upsample2": ([p, i32, i32, p, i64, i64, p, p], ctypes.c_int),
+        "ssc_subdivide2": ([p, i64, p, p, i32, i32, p, p, p], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -240,6 +244,83 @@ def linear(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
                             _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "ssc_linear")
     return out
+
+
+def _feat_args(feats: Optional[torch.Tensor], n: int):
+    if feats is None:
+        return None, SSC_F32, 0
+    _need_cuda(feats, "feats")
+    if feats.dim() != 2 or feats.shape[0] != n:
+        raise ValueError(f"feats must be [{n}, C]")
+    return feats, _dtype_code(feats.dtype, "feats"), feats.shape[1]
+
+
+def downsample2(coords: torch.Tensor, batch: int, grid: Sequence[int],
+                feats: Optional[torch.Tensor] = None):
+    """SparseDownsample(2), max reduction.  Returns (parent coords [m, 4] int32 in ascending
+    (b, x, y, z) order, parent features [m, C] (None without feats), parent [n] int32 = the
+    output row of each input site's parent, the parent grid)."""
+    _need_cuda(coords, "coords")
+    if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 4:
+        raise ValueError("coords must be int32 [N, 4]")
+    n = coords.shape[0]
+    feats, dt, ch = _feat_args(feats, n)
+    lib = load_library()
+    dev = coords.device
+    g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
+    out_c = torch.empty((max(n, 1), 4), dtype=torch.int32, device=dev)
+    out_f = torch.empty((max(n, 1), ch), dtype=feats.dtype, device=dev) if ch else None
+    parent = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    result = torch.zeros(2, dtype=torch.int64, device=dev)
+    ws = _workspace(lib.ssc_downsample_workspace_bytes(n), dev)
+    with torch.cuda.device(dev):
+        st = lib.ssc_downsample2(_ptr(coords), n, int(batch), g, _ptr(feats), dt, ch, _ptr(out_c),
+                                 _ptr(out_f), _ptr(parent), _ptr(result), _ptr(ws), ws.numel(),
+                                 _stream(dev))
+    _check(st, "ssc_downsample2")
+    m, bad = (int(v) for v in result.cpu())
+    if bad:
+        raise SscError(SSC_ERR_COORD_RANGE, "ssc_downsample2")
+    hgrid = tuple((int(v) + 1) // 2 for v in grid)
+    return out_c[:m], (out_f[:m] if ch else None), parent[:n], hgrid
+
+
+def upsample2(parent_feats: torch.Tensor, parent: torch.Tensor) -> torch.Tensor:
+    """SparseUpsample(2) through a downsample's parent map: out[i] = parent_feats[parent[i]]."""
+    _need_cuda(parent_feats, "parent_feats")
+    _need_cuda(parent, "parent")
+    if parent.dtype != torch.int32 or parent.dim() != 1 or parent_feats.dim() != 2:
+        raise ValueError("parent must be int32 [N], parent_feats [M, C]")
+    m, ch = parent_feats.shape
+    n = parent.shape[0]
+    dt = _dtype_code(parent_feats.dtype, "parent_feats")
+    out = torch.empty((n, ch), dtype=parent_feats.dtype, device=parent.device)
+    lib = load_library()
+    with torch.cuda.device(parent.device):
+        st = lib.ssc_upsample2(_ptr(parent_feats), dt, ch, _ptr(parent), n, m, _ptr(out),
+                               _stream(parent.device))
+    _check(st, "ssc_upsample2")
+    return out
+
+
+def subdivide2(coords: torch.Tensor, grid: Sequence[int], feats: Optional[torch.Tensor] = None):
+    """SparseSubdivide: each site -> 8 children 8i + 4dx + 2dy + dz at (b, 2x+dx, 2y+dy, 2z+dz)
+    carrying its features.  Returns (coords [8N, 4], feats [8N, C] or None, the doubled grid)."""
+    _need_cuda(coords, "coords")
+    if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 4:
+        raise ValueError("coords must be int32 [N, 4]")
+    n = coords.shape[0]
+    feats, dt, ch = _feat_args(feats, n)
+    dev = coords.device
+    g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
+    out_c = torch.empty((8 * n, 4), dtype=torch.int32, device=dev)
+    out_f = torch.empty((8 * n, ch), dtype=feats.dtype, device=dev) if ch else None
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.ssc_subdivide2(_ptr(coords), n, g, _ptr(feats), dt, ch, _ptr(out_c), _ptr(out_f),
+                                _stream(dev))
+    _check(st, "ssc_subdivide2")
+    return out_c, out_f, tuple(2 * int(v) for v in grid)
 
 
 class PackedWeight:

@@ -23,6 +23,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "sort.h"
 
 namespace ssc {
 namespace {
@@ -154,32 +155,9 @@ __global__ void k_plan_header(int64_t* __restrict__ header, int64_t n, int64_t n
 // ------------------------------------------------------------------------------------------
 // Plan: stable LSD radix sort of (mask, row) pairs, then the tap-major neighbour rows.
 // ------------------------------------------------------------------------------------------
-constexpr int kSortThreads = 256;
-constexpr int kSortItems = 8;
-constexpr int kSortTile = kSortThreads * kSortItems;
-constexpr int kDigitBits = 8;
-constexpr int kDigits = 1 << kDigitBits;
-constexpr int kKeyBits = 26;
-static_assert(kSortThreads == kDigits, "one thread per digit in the histogram and scatter");
-
-struct PlanWorkLayout {
-  int64_t ntiles;
-  size_t off_keys_a, off_keys_b, off_vals_a, off_vals_b, off_hist, off_totals, total;
-};
-
-inline PlanWorkLayout plan_work_layout(int64_t n) {
-  PlanWorkLayout L;
-  const int64_t m = n > 0 ? n : 1;
-  L.ntiles = (m + kSortTile - 1) / kSortTile;
-  L.off_keys_a = 0;
-  L.off_keys_b = align_up(L.off_keys_a + sizeof(uint32_t) * m);
-  L.off_vals_a = align_up(L.off_keys_b + sizeof(uint32_t) * m);
-  L.off_vals_b = align_up(L.off_vals_a + sizeof(uint32_t) * m);
-  L.off_hist = align_up(L.off_vals_b + sizeof(uint32_t) * m);
-  L.off_totals = align_up(L.off_hist + sizeof(uint32_t) * kDigits * L.ntiles);
-  L.total = align_up(L.off_totals + sizeof(uint32_t) * kDigits);
-  return L;
-}
+constexpr int kKeyBits = 26;                     // the plan's sort key (Gray rank of the mask)
+// The plan's sort scratch is one 32-bit-key sort of n pairs.
+inline SortLayout<uint32_t> plan_work_layout(int64_t n) { return sort_layout<uint32_t>(n, 0); }
 
 // Sort key of a site: bit (t < 13 ? t : t - 1) set when non-centre tap t has a neighbour.
 __global__ void k_mask_keys(const int32_t* __restrict__ nbr, int64_t n, uint32_t* __restrict__ keys,
@@ -205,115 +183,6 @@ __global__ void k_mask_keys(const int32_t* __restrict__ nbr, int64_t n, uint32_t
   m ^= m >> 16;
   keys[i] = m;
   vals[i] = static_cast<uint32_t>(i);
-}
-
-// Per-tile digit counts -> hist[digit][tile]; per-digit totals accumulate in totals[digit]
-// (zeroed by the previous scatter, or by k_mask_keys before the first pass).
-__global__ __launch_bounds__(kSortThreads) void k_sort_hist(const uint32_t* __restrict__ keys,
-                                                            int64_t n, int shift,
-                                                            uint32_t* __restrict__ hist,
-                                                            int64_t ntiles,
-                                                            uint32_t* __restrict__ totals) {
-  __shared__ uint32_t h[kDigits];
-  h[threadIdx.x] = 0;
-  __syncthreads();
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile;
-#pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
-    const int64_t e = base + k * kSortThreads + threadIdx.x;
-    if (e < n) atomicAdd(&h[(keys[e] >> shift) & (kDigits - 1)], 1u);
-  }
-  __syncthreads();
-  hist[static_cast<int64_t>(threadIdx.x) * ntiles + blockIdx.x] = h[threadIdx.x];
-  if (h[threadIdx.x]) atomicAdd(&totals[threadIdx.x], h[threadIdx.x]);
-}
-
-// Block-wide inclusive scan of one value per thread (kSortThreads threads), Hillis-Steele.
-__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* sh) {
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  for (int off = 1; off < kSortThreads; off <<= 1) {
-    const uint32_t add = threadIdx.x >= off ? sh[threadIdx.x - off] : 0u;
-    __syncthreads();
-    sh[threadIdx.x] += add;
-    __syncthreads();
-  }
-  const uint32_t r = sh[threadIdx.x];
-  __syncthreads();
-  return r;
-}
-
-// Exclusive scan of hist in digit-major order, one workgroup per digit: the digit's base is
-// the sum of the totals of all smaller digits, then its row of per-tile counts is scanned.
-__global__ __launch_bounds__(kSortThreads) void k_sort_scan_rows(uint32_t* __restrict__ hist,
-                                                                 int64_t ntiles,
-                                                                 const uint32_t* __restrict__ totals) {
-  __shared__ uint32_t sh[kSortThreads];
-  const int d = blockIdx.x;
-  const uint32_t below = block_inclusive_scan(threadIdx.x < d ? totals[threadIdx.x] : 0u, sh);
-  // The last thread's inclusive value is the sum over all smaller digits.
-  if (threadIdx.x == kSortThreads - 1) sh[0] = below;
-  __syncthreads();
-  uint32_t carry = sh[0];
-  __syncthreads();
-  uint32_t* row = hist + static_cast<int64_t>(d) * ntiles;
-  for (int64_t base = 0; base < ntiles; base += kSortThreads) {
-    const int64_t e = base + threadIdx.x;
-    const uint32_t v = e < ntiles ? row[e] : 0u;
-    const uint32_t inc = block_inclusive_scan(v, sh);
-    if (e < ntiles) row[e] = carry + inc - v;
-    if (threadIdx.x == kSortThreads - 1) sh[0] = inc;
-    __syncthreads();
-    carry += sh[0];
-    __syncthreads();
-  }
-}
-
-__global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
-    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n,
-    int shift, const uint32_t* __restrict__ hist, int64_t ntiles, uint32_t* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out, uint32_t* __restrict__ totals) {
-  // The totals were consumed by k_sort_scan_rows; clear them for the next pass.
-  if (blockIdx.x == 0) totals[threadIdx.x] = 0;
-  constexpr int kWaves = kSortThreads / 64;
-  __shared__ uint32_t running[kDigits];
-  __shared__ uint32_t wcnt[kWaves][kDigits];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  running[tid] = hist[static_cast<int64_t>(tid) * ntiles + blockIdx.x];
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile;
-  const unsigned long long lt_mask = (1ull << lane) - 1ull;
-  for (int k = 0; k < kSortItems; ++k) {
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) wcnt[w][tid] = 0;
-    __syncthreads();
-    const int64_t e = base + k * kSortThreads + tid;
-    const bool valid = e < n;
-    const uint32_t key = valid ? keys_in[e] : 0u;
-    const uint32_t d = (key >> shift) & (kDigits - 1);
-    // Lanes of this wave holding the same digit: intersect the ballots of every digit bit.
-    unsigned long long peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < kDigitBits; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const unsigned long long bb = __ballot(bit);
-      peers &= bit ? bb : ~bb;
-    }
-    const uint32_t rank = __popcll(peers & lt_mask);
-    if (valid && rank == 0) wcnt[wave][d] = __popcll(peers);
-    __syncthreads();
-    if (valid) {
-      uint32_t pos = running[d] + rank;
-      for (int w = 0; w < wave; ++w) pos += wcnt[w][d];
-      keys_out[pos] = key;
-      vals_out[pos] = vals_in[e];
-    }
-    __syncthreads();
-    uint32_t add = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) add += wcnt[w][tid];
-    running[tid] += add;
-    __syncthreads();
-  }
 }
 
 // perm, per-block tap masks and tap-major neighbour rows in sorted order.  A workgroup owns
@@ -428,34 +297,23 @@ extern "C" ssc_status ssc_build_plan(const int32_t* nbr, int64_t n, void* plan, 
   if (n >= (int64_t(1) << 31)) return SSC_ERR_UNSUPPORTED;
   if (!aligned(plan, kAlign) || !aligned(workspace, kAlign)) return SSC_ERR_ARG;
   const PlanLayout P = plan_layout(n);
-  const PlanWorkLayout W = plan_work_layout(n);
+  const SortLayout<uint32_t> W = plan_work_layout(n);
   if (plan_bytes < P.total || workspace_bytes < W.total) return SSC_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   char* pb = static_cast<char*>(plan);
   char* ws = static_cast<char*>(workspace);
   k_plan_header<<<1, 64, 0, s>>>(reinterpret_cast<int64_t*>(pb), n, P.npad, P.nblocks,
                                  reinterpret_cast<uint4*>(pb + P.off_zero));
-  uint32_t* keys[2] = {reinterpret_cast<uint32_t*>(ws + W.off_keys_a),
-                       reinterpret_cast<uint32_t*>(ws + W.off_keys_b)};
-  uint32_t* vals[2] = {reinterpret_cast<uint32_t*>(ws + W.off_vals_a),
-                       reinterpret_cast<uint32_t*>(ws + W.off_vals_b)};
-  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + W.off_hist);
-  uint32_t* totals = reinterpret_cast<uint32_t*>(ws + W.off_totals);
-  int cur = 0;
+  uint32_t* sorted_rows = reinterpret_cast<uint32_t*>(ws + W.off_vals_a);
   if (n > 0) {
-    k_mask_keys<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(nbr, n, keys[0], vals[0],
-                                                                      totals);
-    for (int shift = 0; shift < kKeyBits; shift += kDigitBits) {
-      k_sort_hist<<<static_cast<unsigned>(W.ntiles), kSortThreads, 0, s>>>(keys[cur], n, shift,
-                                                                           hist, W.ntiles, totals);
-      k_sort_scan_rows<<<kDigits, kSortThreads, 0, s>>>(hist, W.ntiles, totals);
-      k_sort_scatter<<<static_cast<unsigned>(W.ntiles), kSortThreads, 0, s>>>(
-          keys[cur], vals[cur], n, shift, hist, W.ntiles, keys[cur ^ 1], vals[cur ^ 1], totals);
-      cur ^= 1;
-    }
+    k_mask_keys<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+        nbr, n, reinterpret_cast<uint32_t*>(ws + W.off_keys_a), sorted_rows,
+        reinterpret_cast<uint32_t*>(ws + W.off_totals));
+    if (radix_sort_pairs<uint32_t>(ws, W, n, kKeyBits, s) == 1)
+      sorted_rows = reinterpret_cast<uint32_t*>(ws + W.off_vals_b);
   }
   k_plan_fill<<<static_cast<unsigned>(P.npad / 256), 256, 0, s>>>(
-      nbr, n, vals[cur], P.npad, reinterpret_cast<int32_t*>(pb + P.off_perm),
+      nbr, n, sorted_rows, P.npad, reinterpret_cast<int32_t*>(pb + P.off_perm),
       reinterpret_cast<uint32_t*>(pb + P.off_bmask), reinterpret_cast<int32_t*>(pb + P.off_gidx));
   return launch_status();
 }

@@ -1,0 +1,339 @@
+// Coordinate-changing neighbours of the convolution: the factor-2 sparse downsample (max
+// pool), its cache-paired upsample, and the x8 subdivide.
+//
+// The LATO.2 page ("Status") lists SparseDownsample as a max pool (upstream passes
+// reduce="amax") and, in its module table, replaces strided sparse convolution by
+// SparseSubdivide (a coordinate expansion by 8); the Pixal3D README's module table pairs
+// SparseUpsample(2) with a downsample through the cached mapping.  Each produces a new
+// coordinate set, which the convolution then indexes cold.
+//
+//   downsample: parent(b,x,y,z) = (b, x>>1, y>>1, z>>1).  Parent keys are the dense row-major
+//               index of the parent in [batch, ceil(gx/2), ceil(gy/2), ceil(gz/2)]; a stable
+//               LSD radix sort of (key, site) orders the sites by parent, the first site of
+//               each run starts a parent (an exclusive scan numbers them), and each parent's
+//               feature is the channel-wise maximum over its run.  Output parents are in
+//               ascending (b, x, y, z) order; `parent[i]` maps every input site to its parent.
+//   upsample:   out[i] = parent_feats[parent[i]] for the parent map of a downsample.
+//   subdivide:  site i becomes 8 sites 8i + 4dx + 2dy + dz at (b, 2x+dx, 2y+dy, 2z+dz), each
+//               with site i's features.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "sort.h"
+
+namespace ssc {
+namespace {
+
+constexpr int kScanTile = 2048;  // items per workgroup in the parent numbering scan
+
+struct DownLayout {
+  SortLayout<uint64_t> sort;
+  int64_t scan_tiles;
+  size_t off_tile_sums, off_heads, off_counter, total;
+};
+
+// Small device-side initialisations (no memset nodes in a stream a caller may capture).
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int count, uint32_t v) {
+  if (static_cast<int>(threadIdx.x) < count) p[threadIdx.x] = v;
+}
+__global__ void k_zero_result(int64_t* __restrict__ result) {
+  if (threadIdx.x < 2) result[threadIdx.x] = 0;
+}
+
+inline DownLayout down_layout(int64_t n) {
+  DownLayout L;
+  const int64_t m = n > 0 ? n : 1;
+  L.sort = sort_layout<uint64_t>(m, 0);
+  L.scan_tiles = (m + kScanTile - 1) / kScanTile;
+  L.off_tile_sums = align_up(L.sort.total);
+  L.off_heads = align_up(L.off_tile_sums + sizeof(uint32_t) * L.scan_tiles);
+  L.off_counter = align_up(L.off_heads + sizeof(int32_t) * m);
+  L.total = align_up(L.off_counter + sizeof(uint32_t) * 4);
+  return L;
+}
+
+// Parent key of every site (invalid rows are counted and keyed 0); clears the sort totals and
+// the invalid-row counter's neighbours.
+__global__ void k_parent_keys(const int4* __restrict__ coords, int64_t n, int batch, int gx, int gy,
+                              int gz, uint64_t hx, uint64_t hy, uint64_t hz,
+                              uint64_t* __restrict__ keys, uint32_t* __restrict__ vals,
+                              uint32_t* __restrict__ totals, uint32_t* __restrict__ bad) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x < kDigits) totals[threadIdx.x] = 0;
+  if (i >= n) return;
+  const int4 c = coords[i];
+  uint64_t key = 0;
+  if (c.x < 0 || c.x >= batch || c.y < 0 || c.y >= gx || c.z < 0 || c.z >= gy || c.w < 0 ||
+      c.w >= gz) {
+    atomicAdd(bad, 1u);
+  } else {
+    key = ((static_cast<uint64_t>(c.x) * hx + static_cast<uint64_t>(c.y >> 1)) * hy +
+           static_cast<uint64_t>(c.z >> 1)) * hz + static_cast<uint64_t>(c.w >> 1);
+  }
+  keys[i] = key;
+  vals[i] = static_cast<uint32_t>(i);
+}
+
+__device__ __forceinline__ uint32_t is_head(const uint64_t* __restrict__ keys, int64_t r, int64_t n) {
+  return (r < n && (r == 0 || keys[r] != keys[r - 1])) ? 1u : 0u;
+}
+
+// Parents starting in each scan tile.
+__global__ __launch_bounds__(256) void k_head_counts(const uint64_t* __restrict__ keys, int64_t n,
+                                                     uint32_t* __restrict__ tile_sums) {
+  __shared__ uint32_t sh[256];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanTile;
+  uint32_t c = 0;
+  for (int k = 0; k < kScanTile / 256; ++k) c += is_head(keys, base + k * 256 + threadIdx.x, n);
+  const uint32_t tot = block_inclusive_scan(c, sh);
+  if (threadIdx.x == 255) tile_sums[blockIdx.x] = tot;
+}
+
+// Exclusive scan of the tile counts in place (one workgroup); the parent count goes to
+// result[0].
+__global__ __launch_bounds__(256) void k_scan_tile_sums(uint32_t* __restrict__ tile_sums,
+                                                        int64_t tiles, int64_t* __restrict__ result,
+                                                        const uint32_t* __restrict__ bad) {
+  __shared__ uint32_t sh[256];
+  uint32_t carry = 0;
+  for (int64_t base = 0; base < tiles; base += 256) {
+    const int64_t e = base + threadIdx.x;
+    const uint32_t v = e < tiles ? tile_sums[e] : 0u;
+    const uint32_t inc = block_inclusive_scan(v, sh);
+    if (e < tiles) tile_sums[e] = carry + inc - v;
+    if (threadIdx.x == 255) sh[0] = inc;
+    __syncthreads();
+    carry += sh[0];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    result[0] = carry;
+    result[1] = *bad;
+  }
+}
+
+// Numbers the parents in sorted order: parent id of sorted position r = (heads in [0, r]) - 1.
+// Writes each site's parent, each parent's coordinates and the position its run starts at.
+__global__ __launch_bounds__(256) void k_assign_parents(
+    const uint64_t* __restrict__ keys, const uint32_t* __restrict__ vals, int64_t n,
+    const uint32_t* __restrict__ tile_offsets, uint64_t hx, uint64_t hy, uint64_t hz,
+    int32_t* __restrict__ parent, int4* __restrict__ out_coords, int32_t* __restrict__ heads) {
+  __shared__ uint32_t sh[256];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanTile;
+  constexpr int kPer = kScanTile / 256;
+  // Thread t owns the kPer consecutive positions base + t*kPer .. +kPer-1.
+  uint32_t h[kPer];
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    h[k] = is_head(keys, base + threadIdx.x * kPer + k, n);
+    c += h[k];
+  }
+  const uint32_t inc = block_inclusive_scan(c, sh);
+  uint32_t run = tile_offsets[blockIdx.x] + inc - c;  // heads before this thread's first item
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int64_t r = base + threadIdx.x * kPer + k;
+    if (r >= n) break;
+    run += h[k];
+    const int32_t p = static_cast<int32_t>(run) - 1;
+    parent[vals[r]] = p;
+    if (h[k]) {
+      const uint64_t key = keys[r];
+      const uint64_t z = key % hz, rest = key / hz;
+      const uint64_t y = rest % hy, rest2 = rest / hy;
+      const uint64_t x = rest2 % hx, b = rest2 / hx;
+      out_coords[p] = make_int4(static_cast<int>(b), static_cast<int>(x), static_cast<int>(y),
+                                static_cast<int>(z));
+      heads[p] = static_cast<int32_t>(r);
+    }
+  }
+}
+
+__device__ __forceinline__ float ld_f(const float* p) { return *p; }
+__device__ __forceinline__ float ld_f(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// Channel-wise maximum over each parent's run of sites.  Thread per (parent, channel);
+// parents past the count (read on the device) do nothing.
+template <typename T>
+__global__ void k_maxpool(const T* __restrict__ feats, int32_t channels,
+                          const uint32_t* __restrict__ sorted_sites,
+                          const int32_t* __restrict__ heads, const int64_t* __restrict__ result,
+                          int64_t n, T* __restrict__ out) {
+  const int64_t m = result[0];
+  const int64_t total = m * channels;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+       g += stride) {
+    const int64_t p = g / channels;
+    const int c = static_cast<int>(g - p * channels);
+    const int64_t r0 = heads[p];
+    const int64_t r1 = p + 1 < m ? heads[p + 1] : n;
+    int64_t best_row = sorted_sites[r0];
+    float best = ld_f(feats + best_row * channels + c);
+    for (int64_t r = r0 + 1; r < r1; ++r) {
+      const int64_t row = sorted_sites[r];
+      const float v = ld_f(feats + row * channels + c);
+      if (v > best) {
+        best = v;
+        best_row = row;
+      }
+    }
+    out[g] = feats[best_row * channels + c];  // the maximum's own bits
+  }
+}
+
+// out[i] = src[parent[i]] row by row (rows of `row_bytes`, a multiple of 4); rows whose parent
+// is outside [0, m) are written as zeros.
+__global__ void k_gather_rows(const uint32_t* __restrict__ src, const int32_t* __restrict__ parent,
+                              int64_t n, int64_t m, int64_t row_words,
+                              uint32_t* __restrict__ out) {
+  const int64_t total = n * row_words;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+       g += stride) {
+    const int64_t i = g / row_words;
+    const int64_t w = g - i * row_words;
+    const int32_t p = parent[i];
+    out[g] = (p >= 0 && p < m) ? src[static_cast<int64_t>(p) * row_words + w] : 0u;
+  }
+}
+
+__global__ void k_subdivide(const int4* __restrict__ coords, int64_t n,
+                            const uint32_t* __restrict__ feats, int64_t row_words,
+                            int4* __restrict__ out_coords, uint32_t* __restrict__ out_feats) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < 8 * n;
+       c += stride) {
+    const int64_t i = c >> 3;
+    const int k = static_cast<int>(c & 7);
+    const int4 v = coords[i];
+    out_coords[c] = make_int4(v.x, 2 * v.y + (k >> 2), 2 * v.z + ((k >> 1) & 1), 2 * v.w + (k & 1));
+  }
+  if (feats == nullptr) return;
+  const int64_t total = 8 * n * row_words;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+       g += stride) {
+    const int64_t child = g / row_words;
+    const int64_t w = g - child * row_words;
+    out_feats[g] = feats[(child >> 3) * row_words + w];
+  }
+}
+
+unsigned grid_for(int64_t items, int64_t cap = 262144) {
+  return static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>((items + 255) / 256, cap)));
+}
+
+int bits_for(uint64_t count) {  // bits needed for keys in [0, count)
+  int b = 0;
+  while (b < 64 && (count - 1) >> b) ++b;
+  return b;
+}
+
+}  // namespace
+}  // namespace ssc
+
+using namespace ssc;
+
+extern "C" size_t ssc_downsample_workspace_bytes(int64_t n) {
+  return n < 0 ? 0 : down_layout(n).total;
+}
+
+extern "C" ssc_status ssc_downsample2(const int32_t* coords, int64_t n, int32_t batch,
+                                      const int32_t* grid, const void* feats, int32_t dtype,
+                                      int32_t channels, int32_t* out_coords, void* out_feats,
+                                      int32_t* parent, int64_t* result, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (n < 0 || grid == nullptr || result == nullptr || channels < 0) return SSC_ERR_ARG;
+  if (dtype != SSC_F32 && dtype != SSC_BF16) return SSC_ERR_ARG;
+  if (batch < 1 || batch > kMaxCoord) return SSC_ERR_UNSUPPORTED;
+  for (int a = 0; a < 3; ++a)
+    if (grid[a] < 1 || grid[a] > kMaxCoord) return SSC_ERR_UNSUPPORTED;
+  if (n >= (int64_t(1) << 31)) return SSC_ERR_UNSUPPORTED;
+  if (n > 0 && (coords == nullptr || out_coords == nullptr || parent == nullptr ||
+                workspace == nullptr))
+    return SSC_ERR_ARG;
+  if (n > 0 && channels > 0 && (feats == nullptr || out_feats == nullptr)) return SSC_ERR_ARG;
+  if (!aligned(coords, 16) || !aligned(out_coords, 16) || !aligned(workspace, kAlign) ||
+      !aligned(result, 8))
+    return SSC_ERR_ARG;
+  const DownLayout L = down_layout(n);
+  if (n > 0 && workspace_bytes < L.total) return SSC_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  if (n == 0) {
+    k_zero_result<<<1, 64, 0, s>>>(result);
+    return launch_status();
+  }
+  const uint64_t hx = (grid[0] + 1) / 2, hy = (grid[1] + 1) / 2, hz = (grid[2] + 1) / 2;
+  char* ws = static_cast<char*>(workspace);
+  auto* keys = reinterpret_cast<uint64_t*>(ws + L.sort.off_keys_a);
+  auto* vals = reinterpret_cast<uint32_t*>(ws + L.sort.off_vals_a);
+  auto* totals = reinterpret_cast<uint32_t*>(ws + L.sort.off_totals);
+  auto* tile_sums = reinterpret_cast<uint32_t*>(ws + L.off_tile_sums);
+  auto* heads = reinterpret_cast<int32_t*>(ws + L.off_heads);
+  auto* bad = reinterpret_cast<uint32_t*>(ws + L.off_counter);
+  k_fill_u32<<<1, 64, 0, s>>>(bad, 1, 0u);
+  k_parent_keys<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+      reinterpret_cast<const int4*>(coords), n, batch, grid[0], grid[1], grid[2], hx, hy, hz,
+      keys, vals, totals, bad);
+  const int bits = bits_for(static_cast<uint64_t>(batch) * hx * hy * hz);
+  if (radix_sort_pairs<uint64_t>(ws, L.sort, n, bits, s) == 1) {
+    keys = reinterpret_cast<uint64_t*>(ws + L.sort.off_keys_b);
+    vals = reinterpret_cast<uint32_t*>(ws + L.sort.off_vals_b);
+  }
+  k_head_counts<<<static_cast<unsigned>(L.scan_tiles), 256, 0, s>>>(keys, n, tile_sums);
+  k_scan_tile_sums<<<1, 256, 0, s>>>(tile_sums, L.scan_tiles, result, bad);
+  k_assign_parents<<<static_cast<unsigned>(L.scan_tiles), 256, 0, s>>>(
+      keys, vals, n, tile_sums, hx, hy, hz, parent, reinterpret_cast<int4*>(out_coords), heads);
+  if (channels > 0) {
+    const unsigned g = grid_for(n * channels);
+    if (dtype == SSC_BF16)
+      k_maxpool<uint16_t><<<g, 256, 0, s>>>(static_cast<const uint16_t*>(feats), channels, vals,
+                                            heads, result, n, static_cast<uint16_t*>(out_feats));
+    else
+      k_maxpool<float><<<g, 256, 0, s>>>(static_cast<const float*>(feats), channels, vals, heads,
+                                         result, n, static_cast<float*>(out_feats));
+  }
+  return launch_status();
+}
+
+extern "C" ssc_status ssc_upsample2(const void* parent_feats, int32_t dtype, int32_t channels,
+                                    const int32_t* parent, int64_t n, int64_t m, void* out,
+                                    void* stream) {
+  if (n < 0 || m < 0 || channels < 1) return SSC_ERR_ARG;
+  if (dtype != SSC_F32 && dtype != SSC_BF16) return SSC_ERR_ARG;
+  if (n == 0) return SSC_OK;
+  if (parent_feats == nullptr || parent == nullptr || out == nullptr) return SSC_ERR_ARG;
+  const int64_t row_bytes = static_cast<int64_t>(channels) * (dtype == SSC_BF16 ? 2 : 4);
+  if (row_bytes % 4 != 0 || !aligned(parent_feats, 4) || !aligned(out, 4)) return SSC_ERR_ARG;
+  hipStream_t s = as_stream(stream);
+  k_gather_rows<<<grid_for(n * (row_bytes / 4)), 256, 0, s>>>(
+      static_cast<const uint32_t*>(parent_feats), parent, n, m, row_bytes / 4,
+      static_cast<uint32_t*>(out));
+  return launch_status();
+}
+
+extern "C" ssc_status ssc_subdivide2(const int32_t* coords, int64_t n, const int32_t* grid,
+                                     const void* feats, int32_t dtype, int32_t channels,
+                                     int32_t* out_coords, void* out_feats, void* stream) {
+  if (n < 0 || grid == nullptr || channels < 0) return SSC_ERR_ARG;
+  if (dtype != SSC_F32 && dtype != SSC_BF16) return SSC_ERR_ARG;
+  for (int a = 0; a < 3; ++a)
+    if (grid[a] < 1 || 2 * static_cast<int64_t>(grid[a]) > kMaxCoord) return SSC_ERR_UNSUPPORTED;
+  if (n >= (int64_t(1) << 28)) return SSC_ERR_UNSUPPORTED;
+  if (n == 0) return SSC_OK;
+  if (coords == nullptr || out_coords == nullptr) return SSC_ERR_ARG;
+  if (channels > 0 && (feats == nullptr || out_feats == nullptr)) return SSC_ERR_ARG;
+  const int64_t row_bytes = static_cast<int64_t>(channels) * (dtype == SSC_BF16 ? 2 : 4);
+  if (row_bytes % 4 != 0 || !aligned(coords, 16) || !aligned(out_coords, 16) ||
+      (channels > 0 && (!aligned(feats, 4) || !aligned(out_feats, 4))))
+    return SSC_ERR_ARG;
+  hipStream_t s = as_stream(stream);
+  k_subdivide<<<grid_for(8 * n * std::max<int64_t>(1, row_bytes / 4)), 256, 0, s>>>(
+      reinterpret_cast<const int4*>(coords), n,
+      channels > 0 ? static_cast<const uint32_t*>(feats) : nullptr, row_bytes / 4,
+      reinterpret_cast<int4*>(out_coords), channels > 0 ? static_cast<uint32_t*>(out_feats) : nullptr);
+  return launch_status();
+}

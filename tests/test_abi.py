@@ -158,3 +158,30 @@ def test_plan_layout(lib):
         assert o_bm + 4 * (npad // 16) <= o_g
         assert o_g + 4 * 27 * npad <= lib.ssc_plan_bytes(n)
         assert all(o % 256 == 0 for o in (o_perm, o_bm, o_g, o_zero))
+
+
+def test_resample_argument_errors(lib):
+    big = 1 << 30
+    f = lib.ssc_downsample2
+    # coords, n, batch, grid, feats, dtype, channels, out_coords, out_feats, parent, result, ws, wsb, stream
+    assert f(FAKE, -1, 1, GRID, None, 0, 0, FAKE, None, FAKE, FAKE, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 10, 1, None, None, 0, 0, FAKE, None, FAKE, FAKE, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 10, 1, GRID, None, 0, 0, FAKE, None, FAKE, None, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 10, 1, GRID, None, 5, 0, FAKE, None, FAKE, FAKE, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 10, 0, GRID, None, 0, 0, FAKE, None, FAKE, FAKE, FAKE, big, None) == ssc.SSC_ERR_UNSUPPORTED
+    assert f(FAKE, 10, 1, GRID, None, 0, 4, FAKE, None, FAKE, FAKE, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 10, 1, GRID, None, 0, 0, None, None, FAKE, FAKE, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 10, 1, GRID, None, 0, 0, FAKE, None, FAKE, FAKE, FAKE, 64, None) == ssc.SSC_ERR_WORKSPACE
+    assert lib.ssc_downsample_workspace_bytes(1000) > 1000 * 16
+    assert lib.ssc_downsample_workspace_bytes(-1) == 0
+    u = lib.ssc_upsample2
+    assert u(FAKE, 0, 0, FAKE, 10, 5, FAKE, None) == ssc.SSC_ERR_ARG          # channels 0
+    assert u(FAKE, 3, 4, FAKE, 10, 5, FAKE, None) == ssc.SSC_ERR_ARG          # dtype
+    assert u(FAKE, ssc.SSC_BF16, 3, FAKE, 10, 5, FAKE, None) == ssc.SSC_ERR_ARG  # 6-byte rows
+    assert u(FAKE, 0, 4, FAKE, 0, 5, FAKE, None) == ssc.SSC_OK                # nothing to do
+    s = lib.ssc_subdivide2
+    big_grid = (ctypes.c_int32 * 3)(8, 40000, 8)
+    assert s(FAKE, 10, big_grid, None, 0, 0, FAKE, None, None) == ssc.SSC_ERR_UNSUPPORTED
+    assert s(FAKE, 10, None, None, 0, 0, FAKE, None, None) == ssc.SSC_ERR_ARG
+    assert s(FAKE, 10, GRID, None, 0, 4, FAKE, None, None) == ssc.SSC_ERR_ARG
+    assert s(FAKE, 0, GRID, None, 0, 0, FAKE, None, None) == ssc.SSC_OK

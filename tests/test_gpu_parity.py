@@ -156,6 +156,27 @@ def test_full_occupancy_and_boundaries():
     assert (nbr >= 0).sum() == np.prod([3 * g - 2 for g in grid])
 
 
+def test_extreme_coordinates():
+    """Largest supported grid and batch: clusters at both ends of every axis, in the first and
+    last batch entries (keys use all 16 bits of every field)."""
+    say("[extreme] grid 65535^3, batch 65535")
+    G, B = 65535, 65535
+    blk = np.array([(x, y, z) for x in range(4) for y in range(4) for z in range(3)], np.int32)
+    parts = []
+    for b, off in ((0, (0, 0, 0)), (0, (G - 4, G - 4, G - 3)), (B - 1, (0, G - 4, 0)),
+                   (B - 1, (G - 4, 0, G - 3)), (B - 1, (0, 0, 0))):
+        parts.append(np.concatenate([np.full((len(blk), 1), b, np.int32), blk + np.array(off)], 1))
+    coords = np.concatenate(parts).astype(np.int32)
+    rng = np.random.default_rng(12)
+    x = torch.from_numpy(rng.standard_normal((len(coords), 32), dtype=np.float32)).to(torch.bfloat16)
+    w = (torch.from_numpy(rng.standard_normal((27, 32, 32), dtype=np.float32)) / 30).to(torch.bfloat16)
+    idx, _ = check_conv(coords, B, (G, G, G), x, w, None, TAU["bf16"])
+    # clusters never see each other: every cluster is the same 4x4x3 block
+    nbr = idx.nbr.cpu().numpy()
+    per = (nbr >= 0).sum(1).reshape(len(parts), -1)
+    assert (per == per[0]).all()
+
+
 def test_isolated_sites_only_centre():
     say("[isolated]")
     g = 16

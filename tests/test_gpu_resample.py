@@ -1,0 +1,113 @@
+"""Downsample (max) / upsample / subdivide: HIP path vs the CPU oracle, through the C ABI
+(needs an MI355X).  All three are exact (a maximum returns one of its inputs, the rest are
+copies and integer arithmetic), so every comparison is bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import resample as rs
+import submanifold_sparse_convolution_coord_amd as ssc
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def as_np(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def check_down(coords, batch, grid, x):
+    gc, gf, gp, ggrid = ssc.downsample2(torch.from_numpy(coords).to(DEV), batch, grid,
+                                        None if x is None else x.to(DEV))
+    oc, of, op, ogrid = rs.downsample2(coords, batch, grid, None if x is None else as_np(x))
+    assert ggrid == ogrid
+    np.testing.assert_array_equal(gc.cpu().numpy(), oc)
+    np.testing.assert_array_equal(gp.cpu().numpy(), op)
+    if x is not None:
+        np.testing.assert_array_equal(as_np(gf), of)
+    return gc, gf, gp
+
+
+@pytest.mark.parametrize("name", ["tiny", "iid128", "batch4", "shell512"])
+def test_downsample_workloads(name):
+    say(f"[down] {name}")
+    w = workloads.make(name)
+    gc, gf, gp = check_down(w.coords, w.batch, w.grid, w.feats)
+    # the new coordinate set indexes cold like any other
+    hgrid = tuple((g + 1) // 2 for g in w.grid)
+    nbr = ssc.build_index(gc.contiguous(), w.batch, hgrid)
+    np.testing.assert_array_equal(nbr.cpu().numpy(),
+                                  oracle.build_map(gc.cpu().numpy(), w.batch, hgrid))
+
+
+@pytest.mark.parametrize("name", ["tiny", "batch4"])
+def test_subdivide_and_upsample_workloads(name):
+    say(f"[subdivide/upsample] {name}")
+    w = workloads.make(name)
+    c = torch.from_numpy(w.coords).to(DEV)
+    sc, sf, sgrid = ssc.subdivide2(c, w.grid, w.feats.to(DEV))
+    oc, of, ogrid = rs.subdivide2(w.coords, w.grid, as_np(w.feats))
+    assert sgrid == ogrid
+    np.testing.assert_array_equal(sc.cpu().numpy(), oc)
+    np.testing.assert_array_equal(as_np(sf), of)
+    # upsample through the downsample of the subdivided set: every child gets back its site
+    dc, df, dp, _ = ssc.downsample2(sc, w.batch, sgrid, sf)
+    up = ssc.upsample2(df, dp)
+    np.testing.assert_array_equal(as_np(up), of)
+    # and the upsample itself matches the oracle on a pooled set
+    gc, gf, gp = check_down(w.coords, w.batch, w.grid, w.feats)
+    np.testing.assert_array_equal(as_np(ssc.upsample2(gf, gp)),
+                                  rs.upsample2(as_np(gf), gp.cpu().numpy()))
+
+
+@pytest.mark.parametrize("dtype,c", [(torch.float32, 4), (torch.bfloat16, 8), (torch.float32, 3),
+                                     (torch.bfloat16, 2)])
+def test_channels_and_dtypes(dtype, c):
+    say(f"[down] channels {c} {dtype}")
+    rng = np.random.default_rng(c)
+    coords = workloads.random_sites(rng, 2, (9, 7, 5), 120)
+    x = torch.from_numpy(rng.standard_normal((len(coords), c), dtype=np.float32)).to(dtype)
+    check_down(coords, 2, (9, 7, 5), x)
+
+
+def test_coordinates_only_and_single_site():
+    say("[down] coords only, single site")
+    check_down(np.array([[0, 5, 6, 7]], np.int32), 1, (8, 8, 8), None)
+    rng = np.random.default_rng(3)
+    check_down(workloads.random_sites(rng, 3, (11, 3, 6), 60), 3, (11, 3, 6), None)
+
+
+def test_extreme_coordinates():
+    say("[down] 65535^3 grid, last batch entry")
+    G, B = 65535, 65535
+    coords = np.array([[B - 1, G - 1, G - 1, G - 1], [B - 1, G - 2, G - 1, G - 2], [0, 0, 0, 0],
+                       [B - 1, 0, G - 1, 1], [0, 1, 1, 1]], np.int32)
+    x = torch.from_numpy(np.arange(10, dtype=np.float32).reshape(5, 2))
+    check_down(coords, B, (G, G, G), x)
+
+
+def test_empty():
+    say("[down] empty")
+    c = torch.zeros((0, 4), dtype=torch.int32, device=DEV)
+    gc, gf, gp, _ = ssc.downsample2(c, 1, (4, 4, 4), torch.zeros((0, 8), device=DEV))
+    assert gc.shape == (0, 4) and gf.shape == (0, 8) and gp.shape == (0,)
+    sc, sf, _ = ssc.subdivide2(c, (4, 4, 4), torch.zeros((0, 8), device=DEV))
+    assert sc.shape == (0, 4) and sf.shape == (0, 8)
+
+
+def test_downsample_reports_outside_sites():
+    say("[down] bad coordinate")
+    c = torch.tensor([[0, 1, 1, 1], [0, 8, 0, 0]], dtype=torch.int32, device=DEV)
+    with pytest.raises(ssc.SscError) as e:
+        ssc.downsample2(c, 1, (8, 8, 8))
+    assert e.value.status == ssc.SSC_ERR_COORD_RANGE
