@@ -152,6 +152,40 @@ __global__ __launch_bounds__(256) void k_assign_parents(
   }
 }
 
+// Channel-wise maximum, 8 bf16 channels (one 16-byte word) per thread; channels % 8 == 0.
+__global__ void k_maxpool_bf16x8(const uint4* __restrict__ feats, int32_t words,
+                                 const uint32_t* __restrict__ sorted_sites,
+                                 const int32_t* __restrict__ heads,
+                                 const int64_t* __restrict__ result, int64_t n,
+                                 uint4* __restrict__ out) {
+  const int64_t m = result[0];
+  const int64_t total = m * words;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+       g += stride) {
+    const int64_t p = g / words;
+    const int w = static_cast<int>(g - p * words);
+    const int64_t r0 = heads[p];
+    const int64_t r1 = p + 1 < m ? heads[p + 1] : n;
+    uint4 best = feats[static_cast<int64_t>(sorted_sites[r0]) * words + w];
+    for (int64_t r = r0 + 1; r < r1; ++r) {
+      const uint4 v = feats[static_cast<int64_t>(sorted_sites[r]) * words + w];
+      uint32_t* bb = reinterpret_cast<uint32_t*>(&best);
+      const uint32_t* vv = reinterpret_cast<const uint32_t*>(&v);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // two bf16 per word: keep the larger of each half, bits and all
+        const uint32_t lo_b = bb[k] & 0xffffu, hi_b = bb[k] >> 16;
+        const uint32_t lo_v = vv[k] & 0xffffu, hi_v = vv[k] >> 16;
+        const uint32_t lo = bf16_to_f32(static_cast<uint16_t>(lo_v)) > bf16_to_f32(static_cast<uint16_t>(lo_b)) ? lo_v : lo_b;
+        const uint32_t hi = bf16_to_f32(static_cast<uint16_t>(hi_v)) > bf16_to_f32(static_cast<uint16_t>(hi_b)) ? hi_v : hi_b;
+        bb[k] = lo | (hi << 16);
+      }
+    }
+    out[g] = best;
+  }
+}
+
 __device__ __forceinline__ float ld_f(const float* p) { return *p; }
 __device__ __forceinline__ float ld_f(const uint16_t* p) { return bf16_to_f32(*p); }
 
@@ -185,11 +219,11 @@ __global__ void k_maxpool(const T* __restrict__ feats, int32_t channels,
   }
 }
 
-// out[i] = src[parent[i]] row by row (rows of `row_bytes`, a multiple of 4); rows whose parent
-// is outside [0, m) are written as zeros.
-__global__ void k_gather_rows(const uint32_t* __restrict__ src, const int32_t* __restrict__ parent,
-                              int64_t n, int64_t m, int64_t row_words,
-                              uint32_t* __restrict__ out) {
+// out[i] = src[parent[i]] row by row, in words of 16 bytes (rows a multiple of 16 bytes) or 4
+// bytes; rows whose parent is outside [0, m) are written as zeros.
+template <typename Word>
+__global__ void k_gather_rows(const Word* __restrict__ src, const int32_t* __restrict__ parent,
+                              int64_t n, int64_t m, int64_t row_words, Word* __restrict__ out) {
   const int64_t total = n * row_words;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
@@ -197,13 +231,14 @@ __global__ void k_gather_rows(const uint32_t* __restrict__ src, const int32_t* _
     const int64_t i = g / row_words;
     const int64_t w = g - i * row_words;
     const int32_t p = parent[i];
-    out[g] = (p >= 0 && p < m) ? src[static_cast<int64_t>(p) * row_words + w] : 0u;
+    out[g] = (p >= 0 && p < m) ? src[static_cast<int64_t>(p) * row_words + w] : Word{};
   }
 }
 
+template <typename Word>
 __global__ void k_subdivide(const int4* __restrict__ coords, int64_t n,
-                            const uint32_t* __restrict__ feats, int64_t row_words,
-                            int4* __restrict__ out_coords, uint32_t* __restrict__ out_feats) {
+                            const Word* __restrict__ feats, int64_t row_words,
+                            int4* __restrict__ out_coords, Word* __restrict__ out_feats) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < 8 * n;
        c += stride) {
@@ -289,7 +324,11 @@ extern "C" ssc_status ssc_downsample2(const int32_t* coords, int64_t n, int32_t 
       keys, vals, n, tile_sums, hx, hy, hz, parent, reinterpret_cast<int4*>(out_coords), heads);
   if (channels > 0) {
     const unsigned g = grid_for(n * channels);
-    if (dtype == SSC_BF16)
+    if (dtype == SSC_BF16 && channels % 8 == 0 && aligned(feats, 16) && aligned(out_feats, 16))
+      k_maxpool_bf16x8<<<grid_for(n * (channels / 8)), 256, 0, s>>>(
+          static_cast<const uint4*>(feats), channels / 8, vals, heads, result, n,
+          static_cast<uint4*>(out_feats));
+    else if (dtype == SSC_BF16)
       k_maxpool<uint16_t><<<g, 256, 0, s>>>(static_cast<const uint16_t*>(feats), channels, vals,
                                             heads, result, n, static_cast<uint16_t*>(out_feats));
     else
@@ -309,9 +348,14 @@ extern "C" ssc_status ssc_upsample2(const void* parent_feats, int32_t dtype, int
   const int64_t row_bytes = static_cast<int64_t>(channels) * (dtype == SSC_BF16 ? 2 : 4);
   if (row_bytes % 4 != 0 || !aligned(parent_feats, 4) || !aligned(out, 4)) return SSC_ERR_ARG;
   hipStream_t s = as_stream(stream);
-  k_gather_rows<<<grid_for(n * (row_bytes / 4)), 256, 0, s>>>(
-      static_cast<const uint32_t*>(parent_feats), parent, n, m, row_bytes / 4,
-      static_cast<uint32_t*>(out));
+  if (row_bytes % 16 == 0 && aligned(parent_feats, 16) && aligned(out, 16))
+    k_gather_rows<uint4><<<grid_for(n * (row_bytes / 16)), 256, 0, s>>>(
+        static_cast<const uint4*>(parent_feats), parent, n, m, row_bytes / 16,
+        static_cast<uint4*>(out));
+  else
+    k_gather_rows<uint32_t><<<grid_for(n * (row_bytes / 4)), 256, 0, s>>>(
+        static_cast<const uint32_t*>(parent_feats), parent, n, m, row_bytes / 4,
+        static_cast<uint32_t*>(out));
   return launch_status();
 }
 
@@ -331,9 +375,15 @@ extern "C" ssc_status ssc_subdivide2(const int32_t* coords, int64_t n, const int
       (channels > 0 && (!aligned(feats, 4) || !aligned(out_feats, 4))))
     return SSC_ERR_ARG;
   hipStream_t s = as_stream(stream);
-  k_subdivide<<<grid_for(8 * n * std::max<int64_t>(1, row_bytes / 4)), 256, 0, s>>>(
-      reinterpret_cast<const int4*>(coords), n,
-      channels > 0 ? static_cast<const uint32_t*>(feats) : nullptr, row_bytes / 4,
-      reinterpret_cast<int4*>(out_coords), channels > 0 ? static_cast<uint32_t*>(out_feats) : nullptr);
+  const int4* c4 = reinterpret_cast<const int4*>(coords);
+  int4* o4 = reinterpret_cast<int4*>(out_coords);
+  if (channels > 0 && row_bytes % 16 == 0 && aligned(feats, 16) && aligned(out_feats, 16))
+    k_subdivide<uint4><<<grid_for(8 * n * (row_bytes / 16)), 256, 0, s>>>(
+        c4, n, static_cast<const uint4*>(feats), row_bytes / 16, o4,
+        static_cast<uint4*>(out_feats));
+  else
+    k_subdivide<uint32_t><<<grid_for(8 * n * std::max<int64_t>(1, row_bytes / 4)), 256, 0, s>>>(
+        c4, n, channels > 0 ? static_cast<const uint32_t*>(feats) : nullptr, row_bytes / 4, o4,
+        channels > 0 ? static_cast<uint32_t*>(out_feats) : nullptr);
   return launch_status();
 }

@@ -77,7 +77,13 @@ def test_channels_and_dtypes(dtype, c):
     rng = np.random.default_rng(c)
     coords = workloads.random_sites(rng, 2, (9, 7, 5), 120)
     x = torch.from_numpy(rng.standard_normal((len(coords), c), dtype=np.float32)).to(dtype)
-    check_down(coords, 2, (9, 7, 5), x)
+    gc, gf, gp = check_down(coords, 2, (9, 7, 5), x)
+    np.testing.assert_array_equal(as_np(ssc.upsample2(gf, gp)),
+                                  rs.upsample2(as_np(gf), gp.cpu().numpy()))
+    sc, sf, _ = ssc.subdivide2(torch.from_numpy(coords).to(DEV), (9, 7, 5), x.to(DEV))
+    oc, of, _ = rs.subdivide2(coords, (9, 7, 5), as_np(x))
+    np.testing.assert_array_equal(sc.cpu().numpy(), oc)
+    np.testing.assert_array_equal(as_np(sf), of)
 
 
 def test_coordinates_only_and_single_site():
