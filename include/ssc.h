@@ -52,7 +52,7 @@ typedef enum {
   SSC_ERR_HIP = -6           /* a HIP runtime call failed                                      */
 } ssc_status;
 
-typedef enum { SSC_F32 = 0, SSC_BF16 = 1 } ssc_dtype;
+typedef enum { SSC_F32 = 0, SSC_BF16 = 1, SSC_F16 = 2 } ssc_dtype;
 
 /* Library version (major*10000 + minor*100 + patch). */
 int ssc_version(void);
@@ -126,17 +126,20 @@ size_t ssc_conv_workspace_bytes(int32_t cin, int32_t cout, int32_t in_dtype);
 /* SubMConv3d, k=3, stride 1, over the plan of a coordinate set:
  *   out[i][o] = bias[o] + sum_{t : nbr[i][t] != -1} sum_c feats[nbr[i][t]][c] * weight[t][c][o]
  * (cross-correlation; LATO.2 MLX port page, "Correctness").
- *   feats    [n, cin], in_dtype (SSC_F32 or SSC_BF16); rows in coords order.
+ *   feats    [n, cin], in_dtype (SSC_F32, SSC_BF16 or SSC_F16); rows in coords order.
  *   weight   [27, cin, cout], same dtype as feats.
  *   bias     [cout] fp32, or NULL for none.
  *   plan     from ssc_build_plan for the same n.
  *   out      [n, cout], out_dtype; rows in coords order; must not alias feats.
  *   workspace >= ssc_conv_workspace_bytes(cin, cout, in_dtype) bytes, 256-byte aligned.
- * Accumulation is fp32 (bf16 products are exact in fp32).  With out_dtype = SSC_BF16 each
- * output is the round-to-nearest-even bf16 of the fp32 value the SSC_F32 output holds.
+ * Accumulation is fp32 (bf16 and fp16 products are exact in fp32).  out_dtype is SSC_F32 or
+ * a 16-bit type: each 16-bit output is the round-to-nearest-even value of the fp32 result
+ * the SSC_F32 output holds.  fp16 is the checkpoints' source precision (trellis2-mlx-8bit
+ * page); the matrix-core kernels store fp32 or the input's own 16-bit type.
  * Results are bit-identical from run to run (no atomics in the accumulation).
- * Shapes: 1 <= cin, cout <= 1024.  bf16 with cin % 32 == 0 and cout % 16 == 0 runs on the
- * matrix cores; other shapes run a vector-ALU kernel with the same numerics contract. */
+ * Shapes: 1 <= cin, cout <= 1024.  bf16 or fp16 with cin in {32, 64, 128} and cout in
+ * {16, 32, 64, 128} (and out_dtype fp32 or the input's type) runs on the matrix cores; the
+ * rest runs a vector-ALU kernel with the same numerics contract. */
 ssc_status ssc_subm_conv3d(const void* feats, int32_t in_dtype, const void* weight,
                            const float* bias, const void* plan, int64_t n, int32_t cin,
                            int32_t cout, void* out, int32_t out_dtype, void* workspace,

@@ -34,7 +34,7 @@ _LIB_PATH = os.path.join(_PKG, "libssc.so")
 
 SSC_OK, SSC_ERR_ARG, SSC_ERR_COORD_RANGE, SSC_ERR_DUPLICATE = 0, -1, -2, -3
 SSC_ERR_UNSUPPORTED, SSC_ERR_WORKSPACE, SSC_ERR_HIP = -4, -5, -6
-SSC_F32, SSC_BF16 = 0, 1
+SSC_F32, SSC_BF16, SSC_F16 = 0, 1, 2
 
 
 class SscError(RuntimeError):
@@ -125,7 +125,9 @@ def _dtype_code(dt: torch.dtype, name: str) -> int:
         return SSC_F32
     if dt == torch.bfloat16:
         return SSC_BF16
-    raise ValueError(f"{name}: dtype {dt} not supported (float32 or bfloat16)")
+    if dt == torch.float16:
+        return SSC_F16
+    raise ValueError(f"{name}: dtype {dt} not supported (float32, bfloat16 or float16)")
 
 
 def build_index(coords: torch.Tensor, batch: int, grid: Sequence[int],

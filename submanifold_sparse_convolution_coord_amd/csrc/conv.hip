@@ -172,6 +172,26 @@ __device__ __forceinline__ bf16x8_t lds_read16(const void* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
 }
 
+// 16-bit element kinds of the matrix-core paths: EK = 0 bf16, EK = 1 fp16.  Fragments are
+// carried as 16-byte words; the kind only picks the instruction and the output rounding.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+template <int EK>
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  if constexpr (EK == 0)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+// fp32 -> 16-bit output of kind EK, round to nearest even.
+template <int EK>
+__device__ __forceinline__ uint16_t to16(float v) {
+  if constexpr (EK == 0)
+    return f32_to_bf16_rne(v);
+  else
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+
 // Copies of stage (union index q, tap t) for every block that has tap t.  Each copy
 // instruction moves 64 lanes x 16 bytes = RPI whole rows of one block into LDS (the lane's
 // 16-byte chunk of the row goes to its swizzled slot, missing neighbours read the zero row).
@@ -259,7 +279,7 @@ __device__ __forceinline__ void a_frag_offsets(int lane, uint32_t (&off)[CIN / 3
   }
 }
 
-template <int CIN, int COUT, int NB, int WR, int WC>
+template <int CIN, int COUT, int NB, int WR, int WC, int EK>
 __device__ __forceinline__ void compute_stage(uint32_t act, const char* sA,
                                               const bf16x8_t (&bw)[COUT / WC / 16][CIN / 32],
                                               const uint32_t (&aoff)[CIN / 32], int wr,
@@ -277,11 +297,11 @@ __device__ __forceinline__ void compute_stage(uint32_t act, const char* sA,
     for (int s = 0; s < C::KS; ++s)
 #pragma unroll
       for (int c = 0; c < C::NCT; ++c)
-        acc[bl][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bw[c][s], acc[bl][c], 0, 0, 0);
+        acc[bl][c] = mfma16x16x32<EK>(a[s], bw[c][s], acc[bl][c]);
   }
 }
 
-template <int CIN, int COUT, int NB, int WR, int WC, bool OUT_BF16>
+template <int CIN, int COUT, int NB, int WR, int WC, bool OUT16, int EK>
 __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
     const float* __restrict__ bias, const int32_t* __restrict__ perm,
@@ -382,7 +402,7 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
         issue_gather<CIN, COUT, NB, WR, WC>(q + 1, act_next, X, zrow, sG, lds0 + C::OFF_A1, wave,
                                             lane);
       }
-      compute_stage<CIN, COUT, NB, WR, WC>(act, sA0, bw0, aoff, wr, acc);
+      compute_stage<CIN, COUT, NB, WR, WC, EK>(act, sA0, bw0, aoff, wr, acc);
       if (t_next < 0) break;
       rem &= rem - 1;
       act = act_next;
@@ -396,7 +416,7 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
         load_weights<CIN, COUT, NB, WR, WC>(t_next, Wp, wc, lane, bw0);
         issue_gather<CIN, COUT, NB, WR, WC>(q + 1, act_next, X, zrow, sG, lds0, wave, lane);
       }
-      compute_stage<CIN, COUT, NB, WR, WC>(act, sA1, bw1, aoff, wr, acc);
+      compute_stage<CIN, COUT, NB, WR, WC, EK>(act, sA1, bw1, aoff, wr, acc);
       if (t_next < 0) break;
       rem &= rem - 1;
       act = act_next;
@@ -412,7 +432,7 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   // Output rows are staged in LDS over the gather buffers and indices, BPP blocks at a time,
   // 16-byte chunks XOR-swizzled by row; then every thread writes 16-byte pieces of whole
   // rows to their original index.
-  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  constexpr int ESZ = OUT16 ? 2 : 4;
   constexpr int ROWB = COUT * ESZ;
   constexpr int CHUNKS = ROWB / 16;
   constexpr int SWM = (CHUNKS < 16 ? CHUNKS : 16) - 1;
@@ -437,8 +457,8 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
           const int byte = col * ESZ;
           char* dst = sOut + row * ROWB + (((byte >> 4) ^ (row & SWM)) << 4) + (byte & 15);
           const float v = acc[bl][c][i] + bv[c];
-          if (OUT_BF16)
-            *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_rne(v);
+          if (OUT16)
+            *reinterpret_cast<uint16_t*>(dst) = to16<EK>(v);
           else
             *reinterpret_cast<float*>(dst) = v;
         }
@@ -470,6 +490,10 @@ template <>
 __device__ __forceinline__ float load_feat<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float load_feat<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+template <>
+__device__ __forceinline__ float load_feat<_Float16>(const _Float16* p) {
+  return static_cast<float>(*p);
+}
 
 // Vector-ALU path for any shape and for fp32 inputs: one thread per (sorted row, column),
 // fp32 fused multiply-add over taps in ascending order, then channels in ascending order.
@@ -480,7 +504,7 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ X, cons
                                                    const int32_t* __restrict__ perm,
                                                    const int32_t* __restrict__ gidx, int64_t npad,
                                                    int64_t n, int cin, int cout,
-                                                   void* __restrict__ Y, int out_bf16) {
+                                                   void* __restrict__ Y, int out_kind) {
   const int64_t rows = DENSE ? n : npad;
   const int64_t total = rows * cout;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -501,8 +525,10 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ X, cons
         acc = fmaf(load_feat<T>(xr + c), load_feat<T>(wt + static_cast<int64_t>(c) * cout), acc);
     }
     const float v = acc + (bias ? bias[o] : 0.f);
-    if (out_bf16)
+    if (out_kind == SSC_BF16)
       static_cast<uint16_t*>(Y)[orow * cout + o] = f32_to_bf16_rne(v);
+    else if (out_kind == SSC_F16)
+      static_cast<uint16_t*>(Y)[orow * cout + o] = to16<1>(v);
     else
       static_cast<float*>(Y)[orow * cout + o] = v;
   }
@@ -523,9 +549,9 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ X, cons
 // that, not for the stores.  Only the last tile of the layer can be partial, and it is the
 // last tile its workgroup handles; rows past n are copied from row n-1 and never stored.
 // ------------------------------------------------------------------------------------------
-template <int CIN, int COUT, bool OUT_BF16>
+template <int CIN, int COUT, bool OUT16>
 struct LinCfg {
-  static constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  static constexpr int ESZ = OUT16 ? 2 : 4;
   static constexpr int ROWB = COUT * ESZ;                  // output bytes per row
   static constexpr int TR = ROWB >= 64 ? 64 : 128;         // rows per tile
   static constexpr int NB = TR / 16;
@@ -552,11 +578,11 @@ __device__ __forceinline__ void wait_vm_n_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
 }
 
-template <int CIN, int COUT, bool OUT_BF16>
+template <int CIN, int COUT, bool OUT16>
 __device__ __forceinline__ void linear_copies(int64_t tile, int64_t n,
                                               const uint16_t* __restrict__ X, char* buf,
                                               int wave, int lane) {
-  using L = LinCfg<CIN, COUT, OUT_BF16>;
+  using L = LinCfg<CIN, COUT, OUT16>;
   constexpr int CPR = CIN / 8;
   const int rsub = lane / CPR, phys = lane % CPR;
 #pragma unroll
@@ -570,12 +596,12 @@ __device__ __forceinline__ void linear_copies(int64_t tile, int64_t n,
   }
 }
 
-template <int CIN, int COUT, bool OUT_BF16>
+template <int CIN, int COUT, bool OUT16, int EK>
 __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __restrict__ X,
                                                           const uint16_t* __restrict__ Wp,
                                                           const float* __restrict__ bias,
                                                           int64_t n, void* __restrict__ Y) {
-  using L = LinCfg<CIN, COUT, OUT_BF16>;
+  using L = LinCfg<CIN, COUT, OUT16>;
   using C = typename L::C;
   __shared__ __attribute__((aligned(1024))) char smem[L::SMEM];
   char* sX0 = smem;
@@ -598,7 +624,7 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
   // the compiler has no reason to drain the copies in flight.
   wait_vm_lgkm0();
 
-  linear_copies<CIN, COUT, OUT_BF16>(tile, n, X, sX0, wave, lane);
+  linear_copies<CIN, COUT, OUT16>(tile, n, X, sX0, wave, lane);
   for (int k = 0; tile < tiles; tile += gridDim.x, ++k) {
     if (k == 0)
       wait_vm_lgkm0();
@@ -607,7 +633,7 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
     __builtin_amdgcn_s_barrier();
     char* cur = (k & 1) ? sX1 : sX0;
     const int64_t next = tile + gridDim.x;
-    if (next < tiles) linear_copies<CIN, COUT, OUT_BF16>(next, n, X, (k & 1) ? sX0 : sX1, wave, lane);
+    if (next < tiles) linear_copies<CIN, COUT, OUT16>(next, n, X, (k & 1) ? sX0 : sX1, wave, lane);
 
     f32x4_t acc[C::BPW][C::NCT];
 #pragma unroll
@@ -621,7 +647,7 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
         acc[bl][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < C::KS; ++s)
-          acc[bl][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bw[c][s], acc[bl][c], 0, 0, 0);
+          acc[bl][c] = mfma16x16x32<EK>(a[s], bw[c][s], acc[bl][c]);
       }
     }
     // Stage bias-added outputs (16-byte chunks XOR-swizzled by row).
@@ -637,8 +663,8 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
           const int byte = col * L::ESZ;
           char* dst = sOut + row * L::ROWB + (((byte >> 4) ^ (row & L::SWM)) << 4) + (byte & 15);
           const float v = acc[bl][c][i] + bv[c];
-          if (OUT_BF16)
-            *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_rne(v);
+          if (OUT16)
+            *reinterpret_cast<uint16_t*>(dst) = to16<EK>(v);
           else
             *reinterpret_cast<float*>(dst) = v;
         }
@@ -664,12 +690,13 @@ using LdsFn = void (*)(const uint16_t*, const uint16_t*, const float*, const int
                        const uint32_t*, const int32_t*, const uint16_t*, int64_t, void*);
 
 // k=1 streaming kernel for the channel counts the matrix-core path is built for.
-LinFn pick_linear(int cin, int cout, bool out_bf16, int* wc_groups, int* rows_per_tile) {
+LinFn pick_linear(int cin, int cout, bool out16, int ek, int* wc_groups, int* rows_per_tile) {
 #define SSC_CASE(CI, CO)                                                                      \
   if (cin == CI && cout == CO) {                                                              \
     *wc_groups = LinCfg<CI, CO, false>::WC;                                                   \
-    *rows_per_tile = out_bf16 ? LinCfg<CI, CO, true>::TR : LinCfg<CI, CO, false>::TR;         \
-    return out_bf16 ? k_linear_stream<CI, CO, true> : k_linear_stream<CI, CO, false>;         \
+    *rows_per_tile = out16 ? LinCfg<CI, CO, true>::TR : LinCfg<CI, CO, false>::TR;            \
+    if (ek == 1) return out16 ? k_linear_stream<CI, CO, true, 1> : k_linear_stream<CI, CO, false, 1>; \
+    return out16 ? k_linear_stream<CI, CO, true, 0> : k_linear_stream<CI, CO, false, 0>;      \
   }
   SSC_CASE(32, 16) SSC_CASE(32, 32) SSC_CASE(32, 64) SSC_CASE(32, 128)
   SSC_CASE(64, 16) SSC_CASE(64, 32) SSC_CASE(64, 64) SSC_CASE(64, 128)
@@ -687,7 +714,7 @@ struct LdsPick {
   static constexpr int NB = (CI >= 64 || CO > 64) ? 8 : 16;
 };
 
-LdsFn pick_lds(int cin, int cout, bool out_bf16, int* threads, int* rows_per_tile,
+LdsFn pick_lds(int cin, int cout, bool out16, int ek, int* threads, int* rows_per_tile,
                int* wc_groups) {
 #define SSC_CASE(CI, CO)                                                             \
   if (cin == CI && cout == CO) {                                                     \
@@ -695,8 +722,11 @@ LdsFn pick_lds(int cin, int cout, bool out_bf16, int* threads, int* rows_per_til
     *threads = P::WR * P::WC * 64;                                                   \
     *rows_per_tile = P::NB * 16;                                                     \
     *wc_groups = P::WC;                                                              \
-    return out_bf16 ? k_subm_lds<CI, CO, P::NB, P::WR, P::WC, true>                  \
-                    : k_subm_lds<CI, CO, P::NB, P::WR, P::WC, false>;                \
+    if (ek == 1)                                                                     \
+      return out16 ? k_subm_lds<CI, CO, P::NB, P::WR, P::WC, true, 1>                \
+                   : k_subm_lds<CI, CO, P::NB, P::WR, P::WC, false, 1>;              \
+    return out16 ? k_subm_lds<CI, CO, P::NB, P::WR, P::WC, true, 0>                  \
+                 : k_subm_lds<CI, CO, P::NB, P::WR, P::WC, false, 0>;                \
   }
   SSC_CASE(32, 16) SSC_CASE(32, 32) SSC_CASE(32, 64) SSC_CASE(32, 128)
   SSC_CASE(64, 16) SSC_CASE(64, 32) SSC_CASE(64, 64) SSC_CASE(64, 128)
@@ -705,7 +735,10 @@ LdsFn pick_lds(int cin, int cout, bool out_bf16, int* threads, int* rows_per_til
   return nullptr;
 }
 
-bool valid_dtype(int d) { return d == SSC_F32 || d == SSC_BF16; }
+bool valid_dtype(int d) { return d == SSC_F32 || d == SSC_BF16 || d == SSC_F16; }
+
+// Element kind of a 16-bit feature type for the matrix-core kernels (-1: none).
+int elem_kind(int d) { return d == SSC_BF16 ? 0 : d == SSC_F16 ? 1 : -1; }
 
 // Compute units of the current device (cached per device id).
 int device_cu_count() {
@@ -778,19 +811,20 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
   const int32_t* perm = dense ? nullptr : reinterpret_cast<const int32_t*>(pb + P.off_perm);
   const uint32_t* bmask = dense ? nullptr : reinterpret_cast<const uint32_t*>(pb + P.off_bmask);
   const int32_t* gidx = dense ? nullptr : reinterpret_cast<const int32_t*>(pb + P.off_gidx);
-  const int ob = out_dtype == SSC_BF16 ? 1 : 0;
-
-  if (in_dtype == SSC_BF16) {
+  const int ek = elem_kind(in_dtype);
+  // Matrix-core kernels store fp32 or the input's own 16-bit type.
+  if (ek >= 0 && (out_dtype == SSC_F32 || out_dtype == in_dtype)) {
+    const bool out16 = out_dtype != SSC_F32;
     uint16_t* wt = static_cast<uint16_t*>(workspace);
     if (dense) {
       int wcg = 0, rows = 0;
-      if (LinFn fn = pick_linear(cin, cout, ob != 0, &wcg, &rows)) {
+      if (LinFn fn = pick_linear(cin, cout, out16, ek, &wcg, &rows)) {
         launch_pack_frag(weight, 1, cin, cout, wcg, 0, wt, s);
         return launch_linear(fn, rows, feats, wt, bias, n, out, s);
       }
     } else {
       int threads = 0, rows = 0, wcg = 0;
-      if (LdsFn fn = pick_lds(cin, cout, ob != 0, &threads, &rows, &wcg)) {
+      if (LdsFn fn = pick_lds(cin, cout, out16, ek, &threads, &rows, &wcg)) {
         launch_pack_frag(weight, kTaps, cin, cout, wcg, 0, wt, s);
         return launch_lds(fn, threads, rows, feats, wt, bias, plan, n, out, s);
       }
@@ -803,12 +837,17 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
     auto fn = dense ? k_conv_valu<uint16_t, true> : k_conv_valu<uint16_t, false>;
     hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, s, static_cast<const uint16_t*>(feats),
                        static_cast<const uint16_t*>(weight), bias, perm, gidx, P.npad, n, cin,
-                       cout, out, ob);
+                       cout, out, out_dtype);
+  } else if (in_dtype == SSC_F16) {
+    auto fn = dense ? k_conv_valu<_Float16, true> : k_conv_valu<_Float16, false>;
+    hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, s, static_cast<const _Float16*>(feats),
+                       static_cast<const _Float16*>(weight), bias, perm, gidx, P.npad, n, cin,
+                       cout, out, out_dtype);
   } else {
     auto fn = dense ? k_conv_valu<float, true> : k_conv_valu<float, false>;
     hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(feats),
                        static_cast<const float*>(weight), bias, perm, gidx, P.npad, n, cin, cout,
-                       out, ob);
+                       out, out_dtype);
   }
   return launch_status();
 }
@@ -819,7 +858,7 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
 using namespace ssc;
 
 extern "C" size_t ssc_conv_workspace_bytes(int32_t cin, int32_t cout, int32_t in_dtype) {
-  if (in_dtype != SSC_BF16 || cin < 1 || cout < 1) return 0;
+  if ((in_dtype != SSC_BF16 && in_dtype != SSC_F16) || cin < 1 || cout < 1) return 0;
   return align_up(static_cast<size_t>(kTaps) * cin * cout * sizeof(uint16_t));
 }
 
@@ -856,7 +895,7 @@ extern "C" ssc_status ssc_pack_weights_ex(const void* weight, int32_t taps, int3
   if (flags & ~SSC_PACK_FLIP) return SSC_ERR_ARG;
   if (taps != kTaps) return SSC_ERR_UNSUPPORTED;
   int threads = 0, rows = 0, wcg = 0;
-  if (pick_lds(cin, cout, false, &threads, &rows, &wcg) == nullptr) return SSC_ERR_UNSUPPORTED;
+  if (pick_lds(cin, cout, false, 0, &threads, &rows, &wcg) == nullptr) return SSC_ERR_UNSUPPORTED;
   if (!aligned(weight, 16) || !aligned(packed, kAlign)) return SSC_ERR_ARG;
   if (packed_bytes < ssc_packed_weight_bytes(taps, cin, cout)) return SSC_ERR_WORKSPACE;
   launch_pack_frag(weight, kTaps, cin, cout, wcg, (flags & SSC_PACK_FLIP) ? 1 : 0,
@@ -870,9 +909,9 @@ extern "C" ssc_status ssc_subm_conv3d_packed(const void* feats, const void* pack
                                              int32_t out_dtype, void* stream) {
   if (n < 0 || !valid_dtype(out_dtype) || packed_weight == nullptr || plan == nullptr)
     return SSC_ERR_ARG;
-  if (n >= (int64_t(1) << 31)) return SSC_ERR_UNSUPPORTED;
+  if (n >= (int64_t(1) << 31) || out_dtype == SSC_F16) return SSC_ERR_UNSUPPORTED;
   int threads = 0, rows = 0, wcg = 0;
-  LdsFn fn = pick_lds(cin, cout, out_dtype == SSC_BF16, &threads, &rows, &wcg);
+  LdsFn fn = pick_lds(cin, cout, out_dtype == SSC_BF16, 0, &threads, &rows, &wcg);
   if (fn == nullptr) return SSC_ERR_UNSUPPORTED;
   if (n > 0 && (feats == nullptr || out == nullptr)) return SSC_ERR_ARG;
   if (!aligned(packed_weight, 16) || !aligned(plan, kAlign) ||

@@ -17,7 +17,9 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-TAU = {"f32": 1e-4, "bf16": 2e-2}
+# fp16 inputs: products of two fp16 values are exact in fp32 and accumulation is fp32, as for
+# fp32 inputs, so the fp32-input bound applies (the 2e-2 bf16 bound is for bf16 inputs).
+TAU = {"f32": 1e-4, "bf16": 2e-2, "f16": 1e-4}
 DEV = torch.device("cuda:0")
 
 
@@ -341,3 +343,48 @@ def test_plan_structure(name):
     assert (np.diff(keys) >= 0).all()
     same = np.diff(keys) == 0
     assert (np.diff(perm[:n])[same] > 0).all()          # stable among equal keys
+
+
+@pytest.mark.parametrize("cin,cout", [(32, 16), (64, 64), (128, 128), (64, 128), (128, 32)])
+def test_fp16_inputs_matrix_cores(cin, cout):
+    """fp16 features and weights (the checkpoints' source precision): fp32 store within the
+    fp32-input bound; the fp16 store is the round-to-nearest-even fp16 of the fp32 store."""
+    say(f"[fp16] k3 cin={cin} cout={cout}")
+    coords, x, w, b = small_case(cin * 3 + cout, 2, (20, 20, 20), 0.09, cin, cout, torch.float16)
+    idx, y32 = check_conv(coords, 2, (20, 20, 20), x, w, b, TAU["f16"])
+    y16 = idx.conv(x.to(DEV), w.to(DEV), b.to(DEV), torch.float16)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.float16
+    assert torch.equal(y16.cpu(), y32.cpu().to(torch.float16))
+
+
+@pytest.mark.parametrize("cin,cout,odt", [(16, 16, torch.float32), (48, 24, torch.float16),
+                                          (3, 130, torch.float32)])
+def test_fp16_inputs_valu(cin, cout, odt):
+    say(f"[fp16] valu cin={cin} cout={cout} {odt}")
+    coords, x, w, b = small_case(cin + cout + 1, 1, (12, 12, 12), 0.3, cin, cout, torch.float16)
+    m = oracle.build_map(coords, 1, (12, 12, 12))
+    idx = run_gpu(coords, 1, (12, 12, 12))
+    y = idx.conv(x.to(DEV), w.to(DEV), b.to(DEV), odt)
+    torch.cuda.synchronize()
+    ref = oracle.conv(x.float().numpy(), w.float().numpy(), b.numpy(), m)
+    if odt == torch.float32:
+        assert rel_err(y.cpu().numpy(), ref) <= TAU["f16"]
+    else:
+        y32 = idx.conv(x.to(DEV), w.to(DEV), b.to(DEV), torch.float32)
+        assert torch.equal(y.cpu(), y32.cpu().to(torch.float16))
+
+
+@pytest.mark.parametrize("n,cin,cout", [(1000, 64, 128), (4097, 128, 128), (77, 16, 16)])
+def test_fp16_linear(n, cin, cout):
+    say(f"[fp16] linear n={n} {cin}->{cout}")
+    rng = np.random.default_rng(n + 7)
+    x = torch.from_numpy(rng.standard_normal((n, cin), dtype=np.float32)).to(torch.float16)
+    w = (torch.from_numpy(rng.standard_normal((cin, cout), dtype=np.float32)) / np.sqrt(cin)).to(torch.float16)
+    b = torch.from_numpy(rng.standard_normal(cout, dtype=np.float32))
+    y = ssc.linear(x.to(DEV), w.to(DEV), b.to(DEV))
+    y16 = ssc.linear(x.to(DEV), w.to(DEV), b.to(DEV), torch.float16)
+    torch.cuda.synchronize()
+    ref = oracle.linear(x.float().numpy(), w.float().numpy(), b.numpy())
+    assert rel_err(y.cpu().numpy(), ref) <= TAU["f16"]
+    assert torch.equal(y16.cpu(), y.cpu().to(torch.float16))
