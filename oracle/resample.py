@@ -13,6 +13,8 @@ module table):
               maximum over the sites that belong to it ("max pool, not average").
   upsample    a site of the finer set takes the feature of its parent (the downsample's
               cached mapping, run backwards).
+  spatial2channel  the downsample's parents, each holding its 8 children's features side by
+              side (a sparse pixel unshuffle); absent children contribute zeros.
   subdivide   a site becomes its 8 children (b, 2x+dx, 2y+dy, 2z+dz), dx, dy, dz in {0, 1},
               listed as child 4dx + 2dy + dz of the site, each with the site's feature.
 """
@@ -45,6 +47,23 @@ def downsample2(coords, batch: int, grid, feats=None):
         if out_f is not None:
             out_f[p] = f[rows].max(axis=0)
     hgrid = tuple((int(g) + 1) // 2 for g in grid)
+    return out_c, out_f, parent, hgrid
+
+
+def spatial2channel2(coords, batch: int, grid, feats):
+    """Parents as in downsample2; parent p's row has, for channel c of its child k (child
+    (b, x, y, z) is k = 4(x%2) + 2(y%2) + z%2), the value at column c*8 + k, and zeros where
+    a child is absent (the channel-major order torch's pixel_unshuffle uses; the pages fix
+    no order)."""
+    c = np.asarray(coords, dtype=np.int64).reshape(-1, 4)
+    f = np.asarray(feats)
+    out_c, _, parent, hgrid = downsample2(c, batch, grid)
+    ch = f.shape[1]
+    out_f = np.zeros((len(out_c), ch * 8), dtype=f.dtype)
+    for i in range(len(c)):
+        _, x, y, z = (int(v) for v in c[i])
+        k = 4 * (x % 2) + 2 * (y % 2) + z % 2
+        out_f[parent[i], k::8] = f[i]
     return out_c, out_f, parent, hgrid
 
 

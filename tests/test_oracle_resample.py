@@ -1,6 +1,7 @@
-"""Pins of the resample oracle (downsample / upsample / subdivide) against things other than
-itself (CPU only): a dense max pool from torch (the library routine for the textbook
-operation), brute force over coordinates, and exact identities between the three ops.
+"""Pins of the resample oracle (downsample / upsample / spatial2channel / subdivide) against
+things other than itself (CPU only): a dense max pool from torch (the library routine for the
+textbook operation), a dense space-to-depth reshape, brute force over coordinates, and exact
+identities between the ops.
 """
 import numpy as np
 import pytest
@@ -106,6 +107,44 @@ def test_batches_never_mix():
     np.testing.assert_array_equal(oc2[m:], oc1 + np.array([1, 0, 0, 0]))
     np.testing.assert_array_equal(of2[:m], of1)
     np.testing.assert_array_equal(p2[len(one):], p1 + m)
+
+
+@pytest.mark.parametrize("seed,batch,grid,frac", [
+    (10, 1, (6, 6, 6), 0.3), (11, 2, (5, 7, 3), 0.6), (12, 1, (4, 4, 4), 1.0),
+])
+def test_spatial2channel_matches_dense_space_to_depth(seed, batch, grid, frac):
+    """A dense grid (zeros off the sites, padded to even sides) reshaped to
+    [B, C, X/2, 2, Y/2, 2, Z/2, 2] and permuted to [B, X/2, Y/2, Z/2, C, 2, 2, 2]: its rows at
+    the parents are the oracle's rows (channel-major: column c*8 + 4dx + 2dy + dz)."""
+    coords = sites(seed, batch, grid, frac)
+    x = feats_for(seed, len(coords), 3) + 10.0          # no zero among the site values
+    oc, of, parent, hgrid = rs.spatial2channel2(coords, batch, grid, x)
+    dc, _, dp, _ = rs.downsample2(coords, batch, grid)
+    np.testing.assert_array_equal(oc, dc)
+    np.testing.assert_array_equal(parent, dp)
+    ex = tuple(2 * h for h in hgrid)
+    dense = torch.zeros((batch, 3) + ex, dtype=torch.float64)
+    c = torch.from_numpy(coords.astype(np.int64))
+    dense[c[:, 0], :, c[:, 1], c[:, 2], c[:, 3]] = torch.from_numpy(x.astype(np.float64))
+    d = dense.reshape(batch, 3, hgrid[0], 2, hgrid[1], 2, hgrid[2], 2)
+    d = d.permute(0, 2, 4, 6, 1, 3, 5, 7).reshape(batch, *hgrid, 24)
+    o = torch.from_numpy(oc.astype(np.int64))
+    np.testing.assert_array_equal(of.astype(np.float64), d[o[:, 0], o[:, 1], o[:, 2], o[:, 3]].numpy())
+    # the parents are exactly the cells with a nonzero value
+    want = torch.nonzero((d != 0).any(-1)).numpy()
+    np.testing.assert_array_equal(oc, want)
+
+
+def test_spatial2channel_max_over_children_is_downsample():
+    """Max over the 8 child slots of each channel, with absent slots as -inf, is the max pool."""
+    coords = sites(13, 2, (7, 5, 6), 0.4)
+    x = feats_for(13, len(coords), 4)
+    oc, of, parent, _ = rs.spatial2channel2(coords, 2, (7, 5, 6), x)
+    present = np.zeros((len(oc), 8), bool)
+    k = 4 * (coords[:, 1] % 2) + 2 * (coords[:, 2] % 2) + coords[:, 3] % 2
+    present[parent, k] = True
+    v = np.where(present[:, None, :], of.reshape(len(oc), 4, 8), -np.inf).max(-1)
+    np.testing.assert_array_equal(v, rs.downsample2(coords, 2, (7, 5, 6), x)[1])
 
 
 def test_downsample_rejects_outside_sites():
