@@ -104,10 +104,10 @@ def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_m
 
 
 def time_resample(ssc, torch, coords, x, w, dev, reps: int = 20) -> dict:
-    """Device time of the downsample (max), its upsample and the subdivide on the workload's
-    sites and features, called through the C ABI on preallocated buffers (the binding's
-    downsample reads the parent count back, which would put a host round trip in the
-    timing).  GB/s from the algorithmic bytes of each op."""
+    """Device time of the downsample (max), its upsample, the spatial-to-channel shuffle and the
+    subdivide on the workload's sites and features, called through the C ABI on preallocated
+    buffers (the binding's downsample reads the parent count back, which would put a host
+    round trip in the timing).  GB/s from the algorithmic bytes of each op."""
     import ctypes
     lib = ssc.load_library()
     n, ch = x.shape
@@ -124,6 +124,7 @@ def time_resample(ssc, torch, coords, x, w, dev, reps: int = 20) -> dict:
     sc = torch.empty((8 * n, 4), dtype=torch.int32, device=dev)
     sf = torch.empty((8 * n, ch), dtype=x.dtype, device=dev)
     up = torch.empty((n, ch), dtype=x.dtype, device=dev)
+    s2c = torch.empty((n, 8 * ch), dtype=x.dtype, device=dev)
 
     def down():
         return lib.ssc_downsample2(p(coords), n, w.batch, g, p(x), dt, ch, p(oc), p(of), p(par),
@@ -139,6 +140,14 @@ def time_resample(ssc, torch, coords, x, w, dev, reps: int = 20) -> dict:
     def sub():
         return lib.ssc_subdivide2(p(coords), n, g, p(x), dt, ch, p(sc), p(sf), st)
 
+    def front():  # the parent numbering alone (sort, scan, parent map, parent coordinates)
+        return lib.ssc_downsample2(p(coords), n, w.batch, g, None, dt, 0, p(oc), None, p(par),
+                                   p(res), p(ws), ws.numel(), st)
+
+    def s2ch():
+        return lib.ssc_spatial2channel2(p(coords), n, w.batch, g, p(x), dt, ch, p(oc), p(s2c),
+                                        p(par), p(res), p(ws), ws.numel(), st)
+
     def t(fn):
         fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -150,14 +159,17 @@ def time_resample(ssc, torch, coords, x, w, dev, reps: int = 20) -> dict:
         return e0.elapsed_time(e1) / reps * 1e3
 
     row = ch * esz
-    d_us, u_us, s_us = t(down), t(ups), t(sub)
+    d_us, u_us, s_us, c_us, f_us = t(down), t(ups), t(sub), t(s2ch), t(front)
     d_bytes = n * (16 + row + 4) + m * (16 + row)
+    c_bytes = n * (16 + row + 4) + m * (16 + 8 * row)
     u_bytes = n * (4 + row) + m * row
     s_bytes = n * (16 + row) + 8 * n * (16 + row)
-    return {"n": n, "parents": m, "channels": ch,
+    return {"n": n, "parents": m, "channels": ch, "parent_numbering_us": round(f_us, 2),
             "downsample_us": round(d_us, 2), "downsample_gbs": round(d_bytes / d_us / 1e3, 1),
             "upsample_us": round(u_us, 2), "upsample_gbs": round(u_bytes / u_us / 1e3, 1),
-            "subdivide_us": round(s_us, 2), "subdivide_gbs": round(s_bytes / s_us / 1e3, 1)}
+            "subdivide_us": round(s_us, 2), "subdivide_gbs": round(s_bytes / s_us / 1e3, 1),
+            "spatial2channel_us": round(c_us, 2),
+            "spatial2channel_gbs": round(c_bytes / c_us / 1e3, 1)}
 
 
 def cpu_baseline(w, m_nbr) -> dict:

@@ -196,7 +196,8 @@ size_t ssc_downsample_workspace_bytes(int64_t n);
  * bit for bit).
  *   coords     [n, 4] int32 (b,x,y,z), 16-byte aligned, inside batch / grid (as for
  *              ssc_build_index; rows outside are counted in result[1], outputs then undefined).
- *   feats      [n, channels] dtype (SSC_F32 or SSC_BF16); may be NULL when channels = 0.
+ *   feats      [n, channels] dtype (SSC_F32, SSC_BF16 or SSC_F16); may be NULL when
+ *              channels = 0.
  *   out_coords [n, 4] int32 capacity, 16-byte aligned: rows [0, m) receive the parents.
  *   out_feats  [n, channels] capacity: rows [0, m) receive the maxima.
  *   parent     [n] int32: parent[i] = output row of site i's parent (the cache that
@@ -209,6 +210,17 @@ ssc_status ssc_downsample2(const int32_t* coords, int64_t n, int32_t batch, cons
                            const void* feats, int32_t dtype, int32_t channels,
                            int32_t* out_coords, void* out_feats, int32_t* parent, int64_t* result,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* SparseSpatial2Channel(2), the sparse pixel unshuffle (Pixal3D README, module table): the
+ * parents and parent map of ssc_downsample2, and each parent's row of 8 * channels values
+ * holds channel c of its child k = 4(x&1) + 2(y&1) + (z&1) at column c * 8 + k (zero where the
+ * child is absent).  Arguments as for ssc_downsample2, with out_feats [n, 8 * channels] of
+ * capacity and channels >= 1; the values are moved, never converted. */
+ssc_status ssc_spatial2channel2(const int32_t* coords, int64_t n, int32_t batch,
+                                const int32_t* grid, const void* feats, int32_t dtype,
+                                int32_t channels, int32_t* out_coords, void* out_feats,
+                                int32_t* parent, int64_t* result, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* SparseUpsample(2), the cache-paired inverse of a downsample (Pixal3D README, module table):
  * out[i] = parent_feats[parent[i]] for the n sites of the finer set.

@@ -79,6 +79,8 @@ def load_library():
         "ssc_downsample_workspace_bytes": ([i64], sz),
         "ssc_downsample2": ([p, i64, i32, p, p, i32, i32, p, p, p, p, p, sz, p], ctypes.c_int),
         "ssc_upsample2": ([p, i32, i32, p, i64, i64, p, p], ctypes.c_int),
+        "ssc_spatial2channel2": ([p, i64, i32, p, p, i32, i32, p, p, p, p, p, sz, p],
+                                 ctypes.c_int),
         "ssc_subdivide2": ([p, i64, p, p, i32, i32, p, p, p], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -285,6 +287,37 @@ def downsample2(coords: torch.Tensor, batch: int, grid: Sequence[int],
         raise SscError(SSC_ERR_COORD_RANGE, "ssc_downsample2")
     hgrid = tuple((int(v) + 1) // 2 for v in grid)
     return out_c[:m], (out_f[:m] if ch else None), parent[:n], hgrid
+
+
+def spatial2channel2(coords: torch.Tensor, batch: int, grid: Sequence[int],
+                     feats: torch.Tensor):
+    """SparseSpatial2Channel(2): returns (parent coords [m, 4], features [m, 8C] with channel c
+    of child k = 4(x&1) + 2(y&1) + (z&1) at column c*8 + k (zeros for absent children),
+    parent [n], the parent grid)."""
+    _need_cuda(coords, "coords")
+    if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 4:
+        raise ValueError("coords must be int32 [N, 4]")
+    n = coords.shape[0]
+    feats, dt, ch = _feat_args(feats, n)
+    if ch < 1:
+        raise ValueError("spatial2channel2 needs features")
+    lib = load_library()
+    dev = coords.device
+    g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
+    out_c = torch.empty((max(n, 1), 4), dtype=torch.int32, device=dev)
+    out_f = torch.empty((max(n, 1), 8 * ch), dtype=feats.dtype, device=dev)
+    parent = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    result = torch.zeros(2, dtype=torch.int64, device=dev)
+    ws = _workspace(lib.ssc_downsample_workspace_bytes(n), dev)
+    with torch.cuda.device(dev):
+        st = lib.ssc_spatial2channel2(_ptr(coords), n, int(batch), g, _ptr(feats), dt, ch,
+                                      _ptr(out_c), _ptr(out_f), _ptr(parent), _ptr(result),
+                                      _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "ssc_spatial2channel2")
+    m, bad = (int(v) for v in result.cpu())
+    if bad:
+        raise SscError(SSC_ERR_COORD_RANGE, "ssc_spatial2channel2")
+    return out_c[:m], out_f[:m], parent[:n], tuple((int(v) + 1) // 2 for v in grid)
 
 
 def upsample2(parent_feats: torch.Tensor, parent: torch.Tensor) -> torch.Tensor:

@@ -1,5 +1,5 @@
 // Coordinate-changing neighbours of the convolution: the factor-2 sparse downsample (max
-// pool), its cache-paired upsample, and the x8 subdivide.
+// pool), its cache-paired upsample, the spatial-to-channel shuffle, and the x8 subdivide.
 //
 // The LATO.2 page ("Status") lists SparseDownsample as a max pool (upstream passes
 // reduce="amax") and, in its module table, replaces strided sparse convolution by
@@ -14,6 +14,9 @@
 //               feature is the channel-wise maximum over its run.  Output parents are in
 //               ascending (b, x, y, z) order; `parent[i]` maps every input site to its parent.
 //   upsample:   out[i] = parent_feats[parent[i]] for the parent map of a downsample.
+//   spatial2channel: the same parents; parent p's features are its 8 children's, channel c of
+//               child k = 4(x&1) + 2(y&1) + (z&1) at column c*8 + k, zeros for absent
+//               children (Pixal3D README, module table: SparseSpatial2Channel(2)).
 //   subdivide:  site i becomes 8 sites 8i + 4dx + 2dy + dz at (b, 2x+dx, 2y+dy, 2z+dz), each
 //               with site i's features.
 #include <hip/hip_runtime.h>
@@ -188,6 +191,7 @@ __global__ void k_maxpool_bf16x8(const uint4* __restrict__ feats, int32_t words,
 
 __device__ __forceinline__ float ld_f(const float* p) { return *p; }
 __device__ __forceinline__ float ld_f(const uint16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float ld_f(const _Float16* p) { return static_cast<float>(*p); }
 
 // Channel-wise maximum over each parent's run of sites.  Thread per (parent, channel);
 // parents past the count (read on the device) do nothing.
@@ -216,6 +220,102 @@ __global__ void k_maxpool(const T* __restrict__ feats, int32_t channels,
       }
     }
     out[g] = feats[best_row * channels + c];  // the maximum's own bits
+  }
+}
+
+// Spatial-to-channel (a sparse 3D pixel unshuffle): parent p's row holds, for every channel c,
+// its 8 children's values at c*8 + k, k = 4(x&1) + 2(y&1) + (z&1); absent children give 0.
+// Thread per (parent, channel); the element type only moves bits.
+template <typename T>
+__global__ void k_space2channel(const T* __restrict__ feats, int32_t channels,
+                                const int4* __restrict__ coords,
+                                const uint32_t* __restrict__ sorted_sites,
+                                const int32_t* __restrict__ heads,
+                                const int64_t* __restrict__ result, int64_t n,
+                                T* __restrict__ out) {
+  const int64_t m = result[0];
+  const int64_t total = m * channels;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+       g += stride) {
+    const int64_t p = g / channels;
+    const int c = static_cast<int>(g - p * channels);
+    const int64_t r0 = heads[p];
+    const int64_t r1 = p + 1 < m ? heads[p + 1] : n;
+    T v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = T{};
+    for (int64_t r = r0; r < r1; ++r) {
+      const int64_t i = sorted_sites[r];
+      const int4 q = coords[i];
+      const int k = ((q.y & 1) << 2) | ((q.z & 1) << 1) | (q.w & 1);
+      const T x = feats[i * channels + c];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)  // a select per slot keeps v in registers
+        if (j == k) v[j] = x;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[g * 8 + k] = v[k];
+  }
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Spatial-to-channel in words of 16 bytes (rows a multiple of 16 bytes): thread per (parent,
+// word of E = 16 / ESZ channels).  The children's words land in 8 slot registers (zero for an
+// absent child) and are transposed in registers, so the thread writes the 8 * E values of its
+// channels, 128 contiguous bytes at columns c0*8 .. (c0+E)*8 - 1, as 8 words.
+template <int ESZ>
+__global__ void k_space2channel_w(const uint4* __restrict__ feats, int32_t words,
+                                  const int4* __restrict__ coords,
+                                  const uint32_t* __restrict__ sorted_sites,
+                                  const int32_t* __restrict__ heads,
+                                  const int64_t* __restrict__ result, int64_t n,
+                                  uint4* __restrict__ out) {
+  const int64_t m = result[0];
+  const int64_t total = m * words;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+       g += stride) {
+    const int64_t p = g / words;
+    const int w = static_cast<int>(g - p * words);
+    const int64_t r0 = heads[p];
+    const int64_t r1 = p + 1 < m ? heads[p + 1] : n;
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t r = r0; r < r1; ++r) {
+      const int64_t i = sorted_sites[r];
+      const int4 q = coords[i];
+      const int k = ((q.y & 1) << 2) | ((q.z & 1) << 1) | (q.w & 1);
+      const uint4 x = feats[i * words + w];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j == k) v[j] = x;
+    }
+    uint4* o = out + g * 8;
+    if constexpr (ESZ == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // channel c0 + e: its 8 slots make one word
+        const int sh = (e & 1) * 16;
+        uint32_t d[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          d[h] = ((dword_of(v[2 * h], e >> 1) >> sh) & 0xffffu) |
+                 (((dword_of(v[2 * h + 1], e >> 1) >> sh) & 0xffffu) << 16);
+        o[e] = make_uint4(d[0], d[1], d[2], d[3]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // channel c0 + e: slots 0-3, then 4-7
+        o[2 * e] = make_uint4(dword_of(v[0], e), dword_of(v[1], e), dword_of(v[2], e),
+                              dword_of(v[3], e));
+        o[2 * e + 1] = make_uint4(dword_of(v[4], e), dword_of(v[5], e), dword_of(v[6], e),
+                                  dword_of(v[7], e));
+      }
+    }
   }
 }
 
@@ -276,13 +376,20 @@ extern "C" size_t ssc_downsample_workspace_bytes(int64_t n) {
   return n < 0 ? 0 : down_layout(n).total;
 }
 
-extern "C" ssc_status ssc_downsample2(const int32_t* coords, int64_t n, int32_t batch,
-                                      const int32_t* grid, const void* feats, int32_t dtype,
-                                      int32_t channels, int32_t* out_coords, void* out_feats,
-                                      int32_t* parent, int64_t* result, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+namespace ssc {
+namespace {
+
+// Shared front of the downsample and the spatial-to-channel: checks, then numbers the
+// parents.  On success *vals / *heads point at the sorted sites and at each parent's first
+// sorted position.  Returns SSC_OK with *done = true when there is nothing left to launch.
+ssc_status number_parents(const int32_t* coords, int64_t n, int32_t batch, const int32_t* grid,
+                          const void* feats, int32_t dtype, int32_t channels, int32_t* out_coords,
+                          void* out_feats, int32_t* parent, int64_t* result, void* workspace,
+                          size_t workspace_bytes, hipStream_t s, const uint32_t** vals_out,
+                          const int32_t** heads_out, bool* done) {
+  *done = true;
   if (n < 0 || grid == nullptr || result == nullptr || channels < 0) return SSC_ERR_ARG;
-  if (dtype != SSC_F32 && dtype != SSC_BF16) return SSC_ERR_ARG;
+  if (dtype != SSC_F32 && dtype != SSC_BF16 && dtype != SSC_F16) return SSC_ERR_ARG;
   if (batch < 1 || batch > kMaxCoord) return SSC_ERR_UNSUPPORTED;
   for (int a = 0; a < 3; ++a)
     if (grid[a] < 1 || grid[a] > kMaxCoord) return SSC_ERR_UNSUPPORTED;
@@ -296,7 +403,6 @@ extern "C" ssc_status ssc_downsample2(const int32_t* coords, int64_t n, int32_t 
     return SSC_ERR_ARG;
   const DownLayout L = down_layout(n);
   if (n > 0 && workspace_bytes < L.total) return SSC_ERR_WORKSPACE;
-  hipStream_t s = as_stream(stream);
   if (n == 0) {
     k_zero_result<<<1, 64, 0, s>>>(result);
     return launch_status();
@@ -322,19 +428,81 @@ extern "C" ssc_status ssc_downsample2(const int32_t* coords, int64_t n, int32_t 
   k_scan_tile_sums<<<1, 256, 0, s>>>(tile_sums, L.scan_tiles, result, bad);
   k_assign_parents<<<static_cast<unsigned>(L.scan_tiles), 256, 0, s>>>(
       keys, vals, n, tile_sums, hx, hy, hz, parent, reinterpret_cast<int4*>(out_coords), heads);
-  if (channels > 0) {
-    const unsigned g = grid_for(n * channels);
-    if (dtype == SSC_BF16 && channels % 8 == 0 && aligned(feats, 16) && aligned(out_feats, 16))
-      k_maxpool_bf16x8<<<grid_for(n * (channels / 8)), 256, 0, s>>>(
-          static_cast<const uint4*>(feats), channels / 8, vals, heads, result, n,
-          static_cast<uint4*>(out_feats));
-    else if (dtype == SSC_BF16)
-      k_maxpool<uint16_t><<<g, 256, 0, s>>>(static_cast<const uint16_t*>(feats), channels, vals,
-                                            heads, result, n, static_cast<uint16_t*>(out_feats));
+  *vals_out = vals;
+  *heads_out = heads;
+  *done = channels == 0;
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace ssc
+
+extern "C" ssc_status ssc_downsample2(const int32_t* coords, int64_t n, int32_t batch,
+                                      const int32_t* grid, const void* feats, int32_t dtype,
+                                      int32_t channels, int32_t* out_coords, void* out_feats,
+                                      int32_t* parent, int64_t* result, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  hipStream_t s = as_stream(stream);
+  const uint32_t* vals = nullptr;
+  const int32_t* heads = nullptr;
+  bool done = true;
+  const ssc_status st = number_parents(coords, n, batch, grid, feats, dtype, channels, out_coords,
+                                       out_feats, parent, result, workspace, workspace_bytes, s,
+                                       &vals, &heads, &done);
+  if (st != SSC_OK || done) return st;
+  const unsigned g = grid_for(n * channels);
+  if (dtype == SSC_BF16 && channels % 8 == 0 && aligned(feats, 16) && aligned(out_feats, 16))
+    k_maxpool_bf16x8<<<grid_for(n * (channels / 8)), 256, 0, s>>>(
+        static_cast<const uint4*>(feats), channels / 8, vals, heads, result, n,
+        static_cast<uint4*>(out_feats));
+  else if (dtype == SSC_BF16)
+    k_maxpool<uint16_t><<<g, 256, 0, s>>>(static_cast<const uint16_t*>(feats), channels, vals,
+                                          heads, result, n, static_cast<uint16_t*>(out_feats));
+  else if (dtype == SSC_F16)
+    k_maxpool<_Float16><<<g, 256, 0, s>>>(static_cast<const _Float16*>(feats), channels, vals,
+                                          heads, result, n, static_cast<_Float16*>(out_feats));
+  else
+    k_maxpool<float><<<g, 256, 0, s>>>(static_cast<const float*>(feats), channels, vals, heads,
+                                       result, n, static_cast<float*>(out_feats));
+  return launch_status();
+}
+
+extern "C" ssc_status ssc_spatial2channel2(const int32_t* coords, int64_t n, int32_t batch,
+                                           const int32_t* grid, const void* feats, int32_t dtype,
+                                           int32_t channels, int32_t* out_coords,
+                                           void* out_feats, int32_t* parent, int64_t* result,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (channels < 1) return SSC_ERR_ARG;
+  hipStream_t s = as_stream(stream);
+  const uint32_t* vals = nullptr;
+  const int32_t* heads = nullptr;
+  bool done = true;
+  const ssc_status st = number_parents(coords, n, batch, grid, feats, dtype, channels, out_coords,
+                                       out_feats, parent, result, workspace, workspace_bytes, s,
+                                       &vals, &heads, &done);
+  if (st != SSC_OK || done) return st;
+  const int4* c4 = reinterpret_cast<const int4*>(coords);
+  const int64_t row_bytes = static_cast<int64_t>(channels) * (dtype == SSC_F32 ? 4 : 2);
+  if (row_bytes % 16 == 0 && aligned(feats, 16) && aligned(out_feats, 16)) {
+    const int32_t words = static_cast<int32_t>(row_bytes / 16);
+    const unsigned gw = grid_for(n * words);
+    const auto* f4 = static_cast<const uint4*>(feats);
+    auto* o4 = static_cast<uint4*>(out_feats);
+    if (dtype == SSC_F32)
+      k_space2channel_w<4><<<gw, 256, 0, s>>>(f4, words, c4, vals, heads, result, n, o4);
     else
-      k_maxpool<float><<<g, 256, 0, s>>>(static_cast<const float*>(feats), channels, vals, heads,
-                                         result, n, static_cast<float*>(out_feats));
+      k_space2channel_w<2><<<gw, 256, 0, s>>>(f4, words, c4, vals, heads, result, n, o4);
+    return launch_status();
   }
+  const unsigned g = grid_for(n * channels);
+  if (dtype == SSC_F32)
+    k_space2channel<float><<<g, 256, 0, s>>>(static_cast<const float*>(feats), channels, c4, vals,
+                                             heads, result, n, static_cast<float*>(out_feats));
+  else
+    k_space2channel<uint16_t><<<g, 256, 0, s>>>(static_cast<const uint16_t*>(feats), channels,
+                                                c4, vals, heads, result, n,
+                                                static_cast<uint16_t*>(out_feats));
   return launch_status();
 }
 
@@ -342,10 +510,10 @@ extern "C" ssc_status ssc_upsample2(const void* parent_feats, int32_t dtype, int
                                     const int32_t* parent, int64_t n, int64_t m, void* out,
                                     void* stream) {
   if (n < 0 || m < 0 || channels < 1) return SSC_ERR_ARG;
-  if (dtype != SSC_F32 && dtype != SSC_BF16) return SSC_ERR_ARG;
+  if (dtype != SSC_F32 && dtype != SSC_BF16 && dtype != SSC_F16) return SSC_ERR_ARG;
   if (n == 0) return SSC_OK;
   if (parent_feats == nullptr || parent == nullptr || out == nullptr) return SSC_ERR_ARG;
-  const int64_t row_bytes = static_cast<int64_t>(channels) * (dtype == SSC_BF16 ? 2 : 4);
+  const int64_t row_bytes = static_cast<int64_t>(channels) * (dtype == SSC_F32 ? 4 : 2);
   if (row_bytes % 4 != 0 || !aligned(parent_feats, 4) || !aligned(out, 4)) return SSC_ERR_ARG;
   hipStream_t s = as_stream(stream);
   if (row_bytes % 16 == 0 && aligned(parent_feats, 16) && aligned(out, 16))
@@ -363,14 +531,14 @@ extern "C" ssc_status ssc_subdivide2(const int32_t* coords, int64_t n, const int
                                      const void* feats, int32_t dtype, int32_t channels,
                                      int32_t* out_coords, void* out_feats, void* stream) {
   if (n < 0 || grid == nullptr || channels < 0) return SSC_ERR_ARG;
-  if (dtype != SSC_F32 && dtype != SSC_BF16) return SSC_ERR_ARG;
+  if (dtype != SSC_F32 && dtype != SSC_BF16 && dtype != SSC_F16) return SSC_ERR_ARG;
   for (int a = 0; a < 3; ++a)
     if (grid[a] < 1 || 2 * static_cast<int64_t>(grid[a]) > kMaxCoord) return SSC_ERR_UNSUPPORTED;
   if (n >= (int64_t(1) << 28)) return SSC_ERR_UNSUPPORTED;
   if (n == 0) return SSC_OK;
   if (coords == nullptr || out_coords == nullptr) return SSC_ERR_ARG;
   if (channels > 0 && (feats == nullptr || out_feats == nullptr)) return SSC_ERR_ARG;
-  const int64_t row_bytes = static_cast<int64_t>(channels) * (dtype == SSC_BF16 ? 2 : 4);
+  const int64_t row_bytes = static_cast<int64_t>(channels) * (dtype == SSC_F32 ? 4 : 2);
   if (row_bytes % 4 != 0 || !aligned(coords, 16) || !aligned(out_coords, 16) ||
       (channels > 0 && (!aligned(feats, 4) || !aligned(out_feats, 4))))
     return SSC_ERR_ARG;

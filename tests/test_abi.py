@@ -174,6 +174,12 @@ def test_resample_argument_errors(lib):
     assert f(FAKE, 10, 1, GRID, None, 0, 0, FAKE, None, FAKE, FAKE, FAKE, 64, None) == ssc.SSC_ERR_WORKSPACE
     assert lib.ssc_downsample_workspace_bytes(1000) > 1000 * 16
     assert lib.ssc_downsample_workspace_bytes(-1) == 0
+    s2c = lib.ssc_spatial2channel2                                   # same arguments
+    assert s2c(FAKE, 10, 1, GRID, FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert s2c(FAKE, 10, 1, GRID, FAKE, 5, 4, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert s2c(FAKE, 10, 1, None, FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert s2c(FAKE, 10, 1, GRID, None, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert s2c(FAKE, 10, 1, GRID, FAKE, 2, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 64, None) == ssc.SSC_ERR_WORKSPACE
     u = lib.ssc_upsample2
     assert u(FAKE, 0, 0, FAKE, 10, 5, FAKE, None) == ssc.SSC_ERR_ARG          # channels 0
     assert u(FAKE, 3, 4, FAKE, 10, 5, FAKE, None) == ssc.SSC_ERR_ARG          # dtype
