@@ -181,6 +181,98 @@ ssc_status ssc_linear(const void* feats, int32_t in_dtype, const void* weight, c
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Epilogues and the sparse group norm of the blocks around the convolution.
+ *
+ * The LATO.2 MLX port page ("Status") lists what surrounds SubMConv3d in the sparse blocks:
+ * SparseLinear, LayerNorm32, SparseGroupNorm32, activations, SparseResBlock; its repository
+ * layout says the "32" norms accumulate in fp32.  The pages give no formulas; the readings
+ * here are the textbook ones:
+ *   activation   relu(v) = max(v, 0); silu(v) = v * sigmoid(v).
+ *   group norm   per batch entry b and group g of C / groups consecutive channels: mean and
+ *                population variance over the ACTIVE sites of b (inactive voxels are not
+ *                zeros) and the channels of g; y = act((x - mean) / sqrt(var + eps) * gamma
+ *                + beta).  Statistics in fp32 per slot, fp64 across slots.
+ * ------------------------------------------------------------------------------------- */
+
+#define SSC_ACT_NONE 0
+#define SSC_ACT_RELU 1
+#define SSC_ACT_SILU 2
+#define SSC_GN_MAX_BATCH 64
+
+/* What the _ex convolution entry points do after the sum, in this order:
+ *   v = act(conv + bias);  v += residual (if any);  store v in out_dtype;
+ *   and, if gn_partials != NULL, the group-norm partial sums of the STORED values (as
+ *   ssc_gn_partials computes them from out) into gn_partials, ready for ssc_gn_finalize.
+ * A zeroed struct (or a NULL pointer) is the plain convolution.
+ *   act        SSC_ACT_NONE, SSC_ACT_RELU or SSC_ACT_SILU.
+ *   gn_groups  groups of the statistics (1..256, dividing cout); read with gn_partials.
+ *   batch      batch entries of the sites (1..SSC_GN_MAX_BATCH); read with gn_partials.
+ *   reserved   0.
+ *   residual   [n, cout] in out_dtype, 16-byte aligned, rows in coords order, or NULL; may
+ *              be the same buffer as out (each row is read before it is written).
+ *   coords     [n, 4] int32 sites (their batch ids), 16-byte aligned; needed with
+ *              gn_partials when batch > 1.
+ *   gn_partials, gn_partials_bytes  >= ssc_gn_partials_bytes(n, batch, gn_groups) bytes,
+ *              16-byte aligned; written completely.
+ * The k=3 matrix-core kernels sum the statistics in their own epilogue when batch = 1;
+ * otherwise one extra pass over out runs after the convolution, on the same stream. */
+typedef struct ssc_epilogue {
+  int32_t act;
+  int32_t gn_groups;
+  int32_t batch;
+  int32_t reserved;
+  const void* residual;
+  const int32_t* coords;
+  float* gn_partials;
+  size_t gn_partials_bytes;
+} ssc_epilogue;
+
+/* ssc_subm_conv3d, ssc_subm_conv3d_packed and ssc_linear with an epilogue (NULL = none);
+ * other arguments, shapes and errors as there.  Bad epilogue fields return SSC_ERR_ARG, a
+ * short gn_partials buffer SSC_ERR_WORKSPACE. */
+ssc_status ssc_subm_conv3d_ex(const void* feats, int32_t in_dtype, const void* weight,
+                              const float* bias, const void* plan, int64_t n, int32_t cin,
+                              int32_t cout, void* out, int32_t out_dtype,
+                              const ssc_epilogue* epilogue, void* workspace,
+                              size_t workspace_bytes, void* stream);
+ssc_status ssc_subm_conv3d_packed_ex(const void* feats, const void* packed_weight,
+                                     const float* bias, const void* plan, int64_t n,
+                                     int32_t cin, int32_t cout, void* out, int32_t out_dtype,
+                                     const ssc_epilogue* epilogue, void* stream);
+ssc_status ssc_linear_ex(const void* feats, int32_t in_dtype, const void* weight,
+                         const float* bias, int64_t n, int32_t cin, int32_t cout, void* out,
+                         int32_t out_dtype, const ssc_epilogue* epilogue, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Bytes of the group-norm partial sums for n sites: one slot per 128 rows of n rounded up
+ * to a multiple of 256, each slot holding float4 (count, sum, sum of squares, 0) per
+ * (batch entry, group).  0 for bad arguments. */
+size_t ssc_gn_partials_bytes(int64_t n, int32_t batch, int32_t groups);
+
+/* Partial sums of x [n, channels] (dtype SSC_F32, SSC_BF16 or SSC_F16) per slot of 128
+ * rows, batch entry and group.  coords [n, 4] int32 (batch ids) is needed when batch > 1;
+ * sites whose batch id is outside [0, batch) are left out.  The work grows with
+ * ceil(batch / 4) passes over x.  partials as for ssc_gn_partials_bytes; written completely. */
+ssc_status ssc_gn_partials(const void* x, int32_t dtype, int64_t n, int32_t channels,
+                           const int32_t* coords, int32_t batch, int32_t groups,
+                           float* partials, size_t partials_bytes, void* stream);
+
+/* stats [batch][groups] float2 = (mean, 1 / sqrt(var + eps)) from partials written for the
+ * same n, batch and groups (by ssc_gn_partials or a convolution epilogue); slots are added
+ * in fp64 in slot order, the variance is the population variance; an entry without sites
+ * gets mean 0 and 1 / sqrt(eps).  Bit-reproducible. */
+ssc_status ssc_gn_finalize(const float* partials, int64_t n, int32_t batch, int32_t groups,
+                           float eps, float* stats, void* stream);
+
+/* out[i][c] = act((x[i][c] - mean) * rstd * gamma[c] + beta[c]) with (mean, rstd) =
+ * stats[b][c / (channels / groups)] for the batch id b of site i (0 when batch = 1, else from
+ * coords).  gamma / beta fp32 [channels] or NULL (1 / 0); out in x's dtype, may be x. */
+ssc_status ssc_gn_apply(const void* x, int32_t dtype, int64_t n, int32_t channels,
+                        const int32_t* coords, int32_t batch, int32_t groups,
+                        const float* stats, const float* gamma, const float* beta, int32_t act,
+                        void* out, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Coordinate-changing neighbours: factor-2 downsample (max pool), its paired upsample, and
  * the x8 subdivide.  Each yields a new coordinate set, indexed cold by ssc_build_index.
  * ------------------------------------------------------------------------------------- */

@@ -24,6 +24,8 @@ import torch
 
 __all__ = ["SscError", "build_index", "build_plan", "subm_conv3d", "linear", "Plan",
            "PackedWeight", "pack_weights", "subm_conv3d_packed",
+           "GroupNormPartials", "gn_partials", "gn_finalize", "gn_apply", "group_norm",
+           "downsample2", "upsample2", "spatial2channel2", "subdivide2",
            "SubMIndex", "cached_index", "library_path", "load_library", "TAPS", "CENTRE_TAP"]
 
 TAPS = 27
@@ -35,6 +37,16 @@ _LIB_PATH = os.path.join(_PKG, "libssc.so")
 SSC_OK, SSC_ERR_ARG, SSC_ERR_COORD_RANGE, SSC_ERR_DUPLICATE = 0, -1, -2, -3
 SSC_ERR_UNSUPPORTED, SSC_ERR_WORKSPACE, SSC_ERR_HIP = -4, -5, -6
 SSC_F32, SSC_BF16, SSC_F16 = 0, 1, 2
+ACTS = {"none": 0, "relu": 1, "silu": 2}
+GN_MAX_BATCH = 64
+
+
+class _Epilogue(ctypes.Structure):
+    """ssc_epilogue (include/ssc.h)."""
+    _fields_ = [("act", ctypes.c_int32), ("gn_groups", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("residual", ctypes.c_void_p), ("coords", ctypes.c_void_p),
+                ("gn_partials", ctypes.c_void_p), ("gn_partials_bytes", ctypes.c_size_t)]
 
 
 class SscError(RuntimeError):
@@ -82,6 +94,14 @@ def load_library():
         "ssc_spatial2channel2": ([p, i64, i32, p, p, i32, i32, p, p, p, p, p, sz, p],
                                  ctypes.c_int),
         "ssc_subdivide2": ([p, i64, p, p, i32, i32, p, p, p], ctypes.c_int),
+        "ssc_subm_conv3d_ex": ([p, i32, p, p, p, i64, i32, i32, p, i32, p, p, sz, p],
+                               ctypes.c_int),
+        "ssc_subm_conv3d_packed_ex": ([p, p, p, p, i64, i32, i32, p, i32, p, p], ctypes.c_int),
+        "ssc_linear_ex": ([p, i32, p, p, i64, i32, i32, p, i32, p, p, sz, p], ctypes.c_int),
+        "ssc_gn_partials_bytes": ([i64, i32, i32], sz),
+        "ssc_gn_partials": ([p, i32, i64, i32, p, i32, i32, p, sz, p], ctypes.c_int),
+        "ssc_gn_finalize": ([p, i64, i32, i32, ctypes.c_float, p, p], ctypes.c_int),
+        "ssc_gn_apply": ([p, i32, i64, i32, p, i32, i32, p, p, p, i32, p, p], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -212,11 +232,54 @@ def _conv_args(x, weight, bias, taps, out_dtype):
     return n, cin, cout, _dtype_code(x.dtype, "x"), _dtype_code(out_dtype, "out_dtype"), out_dtype
 
 
+class GroupNormPartials:
+    """Group-norm partial sums of n sites (ssc_gn_partials_bytes): filled by gn_partials or
+    by a convolution's epilogue, read by gn_finalize."""
+
+    def __init__(self, n: int, batch: int, groups: int, device, coords=None):
+        if not 1 <= batch <= GN_MAX_BATCH:
+            raise ValueError(f"batch must be in [1, {GN_MAX_BATCH}]")
+        if batch > 1 and coords is None:
+            raise ValueError("coords (batch ids) are needed when batch > 1")
+        nbytes = load_library().ssc_gn_partials_bytes(n, batch, groups)
+        if nbytes == 0:
+            raise ValueError("bad group-norm shape")
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.n, self.batch, self.groups, self.coords = int(n), int(batch), int(groups), coords
+
+
+def _epilogue(n, cout, out_dtype, act, residual, gn):
+    """The ssc_epilogue struct for the _ex entry points (None when it would be the plain
+    convolution)."""
+    if act == "none" and residual is None and gn is None:
+        return None
+    if act not in ACTS:
+        raise ValueError(f"act must be one of {sorted(ACTS)}")
+    e = _Epilogue()
+    e.act = ACTS[act]
+    if residual is not None:
+        _need_cuda(residual, "residual")
+        if residual.shape != (n, cout) or residual.dtype != out_dtype:
+            raise ValueError(f"residual must be [{n}, {cout}] {out_dtype}")
+        e.residual = residual.data_ptr()
+    if gn is not None:
+        if not isinstance(gn, GroupNormPartials) or gn.n != n:
+            raise ValueError(f"gn must be GroupNormPartials for {n} sites")
+        e.gn_groups, e.batch = gn.groups, gn.batch
+        e.coords = None if gn.coords is None else gn.coords.data_ptr()
+        e.gn_partials, e.gn_partials_bytes = gn.buf.data_ptr(), gn.buf.numel()
+    return e
+
+
 def subm_conv3d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor], plan: Plan,
                 out_dtype: Optional[torch.dtype] = None,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, act: str = "none",
+                residual: Optional[torch.Tensor] = None,
+                gn: Optional[GroupNormPartials] = None) -> torch.Tensor:
     """k=3 SubMConv3d: out[i] = bias + sum_t x[nbr[i][t]] @ weight[t] (cross-correlation).
-    ``weight`` is [27, Cin, Cout] with the dtype of ``x``; output fp32 unless ``out_dtype``."""
+    ``weight`` is [27, Cin, Cout] with the dtype of ``x``; output fp32 unless ``out_dtype``.
+    Epilogue: out = act(conv + bias) + residual, and with ``gn`` the group-norm partial sums
+    of the stored output."""
     n, cin, cout, din, dout, odt = _conv_args(x, weight, bias, TAPS, out_dtype)
     if plan.n != n:
         raise ValueError(f"plan is for {plan.n} sites, x has {n}")
@@ -224,30 +287,118 @@ def subm_conv3d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tens
     dev = x.device
     if out is None:
         out = torch.empty((n, cout), dtype=odt, device=dev)
+    epi = _epilogue(n, cout, odt, act, residual, gn)
     ws = _workspace(lib.ssc_conv_workspace_bytes(cin, cout, din), dev)
     with torch.cuda.device(dev):
-        st = lib.ssc_subm_conv3d(_ptr(x), din, _ptr(weight), _ptr(bias), _ptr(plan.buf), n, cin,
-                                 cout, _ptr(out), dout, _ptr(ws), ws.numel(), _stream(dev))
+        if epi is None:
+            st = lib.ssc_subm_conv3d(_ptr(x), din, _ptr(weight), _ptr(bias), _ptr(plan.buf), n,
+                                     cin, cout, _ptr(out), dout, _ptr(ws), ws.numel(),
+                                     _stream(dev))
+        else:
+            st = lib.ssc_subm_conv3d_ex(_ptr(x), din, _ptr(weight), _ptr(bias), _ptr(plan.buf),
+                                        n, cin, cout, _ptr(out), dout, ctypes.byref(epi),
+                                        _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "ssc_subm_conv3d")
     return out
 
 
 def linear(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
            out_dtype: Optional[torch.dtype] = None,
-           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+           out: Optional[torch.Tensor] = None, act: str = "none",
+           residual: Optional[torch.Tensor] = None,
+           gn: Optional[GroupNormPartials] = None) -> torch.Tensor:
     """k=1 SubMConv3d = per-voxel linear map x @ weight + bias (weight [Cin, Cout] or
-    [1, Cin, Cout])."""
+    [1, Cin, Cout]); the same epilogue as subm_conv3d."""
     n, cin, cout, din, dout, odt = _conv_args(x, weight, bias, 1, out_dtype)
     lib = load_library()
     dev = x.device
     if out is None:
         out = torch.empty((n, cout), dtype=odt, device=dev)
+    epi = _epilogue(n, cout, odt, act, residual, gn)
     ws = _workspace(lib.ssc_conv_workspace_bytes(cin, cout, din), dev)
     with torch.cuda.device(dev):
-        st = lib.ssc_linear(_ptr(x), din, _ptr(weight), _ptr(bias), n, cin, cout, _ptr(out), dout,
-                            _ptr(ws), ws.numel(), _stream(dev))
+        if epi is None:
+            st = lib.ssc_linear(_ptr(x), din, _ptr(weight), _ptr(bias), n, cin, cout, _ptr(out),
+                                dout, _ptr(ws), ws.numel(), _stream(dev))
+        else:
+            st = lib.ssc_linear_ex(_ptr(x), din, _ptr(weight), _ptr(bias), n, cin, cout,
+                                   _ptr(out), dout, ctypes.byref(epi), _ptr(ws), ws.numel(),
+                                   _stream(dev))
     _check(st, "ssc_linear")
     return out
+
+
+def _gn_coords(coords, batch, n):
+    if batch == 1:
+        return None
+    _need_cuda(coords, "coords")
+    if coords.dtype != torch.int32 or coords.shape != (n, 4):
+        raise ValueError(f"coords must be int32 [{n}, 4]")
+    return coords
+
+
+def gn_partials(x: torch.Tensor, batch: int = 1, groups: int = 32,
+                coords: Optional[torch.Tensor] = None) -> GroupNormPartials:
+    """Group-norm partial sums of x [N, C] (the statistics pass of SparseGroupNorm32)."""
+    _need_cuda(x, "x")
+    n, c = x.shape
+    coords = _gn_coords(coords, batch, n)
+    parts = GroupNormPartials(n, batch, groups, x.device, coords)
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        st = lib.ssc_gn_partials(_ptr(x), _dtype_code(x.dtype, "x"), n, c, _ptr(coords), batch,
+                                 groups, _ptr(parts.buf), parts.buf.numel(), _stream(x.device))
+    _check(st, "ssc_gn_partials")
+    return parts
+
+
+def gn_finalize(parts: GroupNormPartials, eps: float = 1e-5) -> torch.Tensor:
+    """[batch, groups, 2] float32 (mean, 1 / sqrt(var + eps)) from the partial sums."""
+    dev = parts.buf.device
+    stats = torch.empty((parts.batch, parts.groups, 2), dtype=torch.float32, device=dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.ssc_gn_finalize(_ptr(parts.buf), parts.n, parts.batch, parts.groups,
+                                 float(eps), _ptr(stats), _stream(dev))
+    _check(st, "ssc_gn_finalize")
+    return stats
+
+
+def gn_apply(x: torch.Tensor, stats: torch.Tensor, gamma: Optional[torch.Tensor] = None,
+             beta: Optional[torch.Tensor] = None, act: str = "none",
+             coords: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """act((x - mean) * rstd * gamma + beta) with stats from gn_finalize; ``out`` may be x."""
+    _need_cuda(x, "x")
+    _need_cuda(stats, "stats")
+    n, c = x.shape
+    batch, groups = stats.shape[0], stats.shape[1]
+    coords = _gn_coords(coords, batch, n)
+    for t, name in ((gamma, "gamma"), (beta, "beta")):
+        if t is not None:
+            _need_cuda(t, name)
+            if t.dtype != torch.float32 or t.numel() != c:
+                raise ValueError(f"{name} must be float32 [{c}]")
+    if act not in ACTS:
+        raise ValueError(f"act must be one of {sorted(ACTS)}")
+    if out is None:
+        out = torch.empty_like(x)
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        st = lib.ssc_gn_apply(_ptr(x), _dtype_code(x.dtype, "x"), n, c, _ptr(coords), batch,
+                              groups, _ptr(stats), _ptr(gamma), _ptr(beta), ACTS[act], _ptr(out),
+                              _stream(x.device))
+    _check(st, "ssc_gn_apply")
+    return out
+
+
+def group_norm(x: torch.Tensor, batch: int = 1, groups: int = 32,
+               gamma: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
+               eps: float = 1e-5, act: str = "none", coords: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """SparseGroupNorm32 (+ activation): statistics, finalize and apply, three launches."""
+    stats = gn_finalize(gn_partials(x, batch, groups, coords), eps)
+    return gn_apply(x, stats, gamma, beta, act, coords, out)
 
 
 def _feat_args(feats: Optional[torch.Tensor], n: int):
@@ -385,8 +536,11 @@ def pack_weights(weight: torch.Tensor, flip: bool = False) -> PackedWeight:
 
 def subm_conv3d_packed(x: torch.Tensor, packed: PackedWeight, bias: Optional[torch.Tensor],
                        plan: Plan, out_dtype: Optional[torch.dtype] = None,
-                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """subm_conv3d with weights from pack_weights: a single kernel launch."""
+                       out: Optional[torch.Tensor] = None, act: str = "none",
+                       residual: Optional[torch.Tensor] = None,
+                       gn: Optional[GroupNormPartials] = None) -> torch.Tensor:
+    """subm_conv3d with weights from pack_weights: a single kernel launch (plus one
+    statistics pass when ``gn`` has batch > 1)."""
     _need_cuda(x, "x")
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != packed.cin or packed.taps != TAPS:
         raise ValueError("x must be bfloat16 [N, Cin] matching a 27-tap packed weight")
@@ -403,9 +557,16 @@ def subm_conv3d_packed(x: torch.Tensor, packed: PackedWeight, bias: Optional[tor
     dev = x.device
     if out is None:
         out = torch.empty((n, packed.cout), dtype=odt, device=dev)
+    epi = _epilogue(n, packed.cout, odt, act, residual, gn)
     with torch.cuda.device(dev):
-        st = lib.ssc_subm_conv3d_packed(_ptr(x), _ptr(packed.buf), _ptr(bias), _ptr(plan.buf), n,
-                                        packed.cin, packed.cout, _ptr(out), dout, _stream(dev))
+        if epi is None:
+            st = lib.ssc_subm_conv3d_packed(_ptr(x), _ptr(packed.buf), _ptr(bias), _ptr(plan.buf),
+                                            n, packed.cin, packed.cout, _ptr(out), dout,
+                                            _stream(dev))
+        else:
+            st = lib.ssc_subm_conv3d_packed_ex(_ptr(x), _ptr(packed.buf), _ptr(bias),
+                                               _ptr(plan.buf), n, packed.cin, packed.cout,
+                                               _ptr(out), dout, ctypes.byref(epi), _stream(dev))
     _check(st, "ssc_subm_conv3d_packed")
     return out
 

@@ -30,6 +30,10 @@
 #include "common.h"
 
 namespace ssc {
+// Standalone group-norm partial sums (norm.hip), for epilogues whose kernel cannot sum them.
+ssc_status gn_partials_launch(const void* x, int32_t dtype, int64_t n, int32_t channels,
+                              const int32_t* coords, int32_t batch, int32_t groups,
+                              float* partials, hipStream_t s);
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -301,12 +305,53 @@ __device__ __forceinline__ void compute_stage(uint32_t act, const char* sA,
   }
 }
 
+// Epilogue arguments of the kernels: a residual added after the activation, and (k=3
+// matrix-core kernel, batch 1) the group-norm partial slots it sums from its own stores.
+struct Epi {
+  const void* res;   // [n, cout] in the output type, rows in coords order, or null
+  float* gn;         // float4 slots [npad / 128][groups] (count, sum, sum of squares, 0)
+  int act;           // SSC_ACT_*
+  int gn_groups;
+};
+
+// One output value of a residual row (the output's own type).
+template <bool OUT16, int EK>
+__device__ __forceinline__ float load_out(const void* p, int64_t i) {
+  if constexpr (!OUT16) return static_cast<const float*>(p)[i];
+  const uint16_t h = static_cast<const uint16_t*>(p)[i];
+  if constexpr (EK == 0) return bf16_to_f32(h);
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Adds the values of one 16-byte piece of a stored row (8 16-bit or 4 fp32 values) to
+// per-channel sums and sums of squares.
+template <bool OUT16, int EK>
+__device__ __forceinline__ void piece_sums(const u32x4_t& v, float* s, float* q) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if constexpr (OUT16) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint16_t bits = static_cast<uint16_t>(v[d] >> (16 * h));
+        const float f = EK == 0 ? bf16_to_f32(bits)
+                                : static_cast<float>(__builtin_bit_cast(_Float16, bits));
+        s[2 * d + h] += f;
+        q[2 * d + h] = fmaf(f, f, q[2 * d + h]);
+      }
+    } else {
+      const float f = __uint_as_float(v[d]);
+      s[d] += f;
+      q[d] = fmaf(f, f, q[d]);
+    }
+  }
+}
+
 template <int CIN, int COUT, int NB, int WR, int WC, bool OUT16, int EK>
 __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
     const float* __restrict__ bias, const int32_t* __restrict__ perm,
     const uint32_t* __restrict__ bmask, const int32_t* __restrict__ gidx,
-    const uint16_t* __restrict__ zrow, int64_t npad, void* __restrict__ Y) {
+    const uint16_t* __restrict__ zrow, int64_t npad, void* __restrict__ Y, Epi ep) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_BYTES];
   const char* sA0 = smem;
@@ -442,6 +487,13 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   constexpr int BPP = BPP_RAW >= NB ? NB : BPP_RAW >= 8 ? 8 : BPP_RAW >= 4 ? 4 : BPP_RAW >= 2 ? 2 : 1;
   static_assert(BPP_RAW >= 1 && NB % BPP == 0, "output staging space");
   char* sOut = smem;
+  // Group-norm partials: every thread always stores the same 16-byte piece of a row (THREADS
+  // is a multiple of CHUNKS), so it keeps per-channel sums of its E channels.
+  constexpr int E = 16 / ESZ;
+  static_assert(C::THREADS % CHUNKS == 0 && 64 % CHUNKS == 0, "piece ownership");
+  float gsum[E], gsq[E], gcnt = 0.f;
+#pragma unroll
+  for (int j = 0; j < E; ++j) gsum[j] = gsq[j] = 0.f;
 #pragma unroll
   for (int p0 = 0; p0 < NB; p0 += BPP) {
 #pragma unroll
@@ -456,7 +508,11 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
           const int row = (b - p0) * 16 + (lane >> 4) * 4 + i;
           const int byte = col * ESZ;
           char* dst = sOut + row * ROWB + (((byte >> 4) ^ (row & SWM)) << 4) + (byte & 15);
-          const float v = acc[bl][c][i] + bv[c];
+          float v = apply_act(acc[bl][c][i] + bv[c], ep.act);
+          if (ep.res) {
+            const int32_t o = sP[b * 16 + (lane >> 4) * 4 + i];
+            if (o >= 0) v += load_out<OUT16, EK>(ep.res, static_cast<int64_t>(o) * COUT + col);
+          }
           if (OUT16)
             *reinterpret_cast<uint16_t*>(dst) = to16<EK>(v);
           else
@@ -476,10 +532,75 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
           *reinterpret_cast<const u32x4_t*>(sOut + row * ROWB + ((ch ^ (row & SWM)) << 4));
       *reinterpret_cast<u32x4_t*>(static_cast<char*>(Y) + static_cast<int64_t>(o) * ROWB +
                                   ch * 16) = v;
+      if (ep.gn) {
+        piece_sums<OUT16, EK>(v, gsum, gsq);
+        gcnt += 1.f;
+      }
     }
     if (p0 + BPP < NB) {
       wait_vm_lgkm0();
       __builtin_amdgcn_s_barrier();
+    }
+  }
+  if (ep.gn) {
+    // Fixed-order reduction: lanes that own the same piece (lane bits above CHUNKS) by a
+    // butterfly (every lane ends with the same sums), then the waves in order, then the
+    // channels of each group in order.  One or two 128-row slots per tile.
+#pragma unroll
+    for (int m = CHUNKS; m < 64; m <<= 1) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        gsum[j] += __shfl_xor(gsum[j], m, 64);
+        gsq[j] += __shfl_xor(gsq[j], m, 64);
+      }
+      gcnt += __shfl_xor(gcnt, m, 64);
+    }
+    constexpr int REC = 2 * E + 1;
+    constexpr int GN_OFF = BPP * 16 * ROWB;
+    constexpr int GN_BYTES = (C::WAVES * CHUNKS * REC + 2 * COUT + 1) * 4;
+    static_assert(GN_OFF + GN_BYTES <= C::OFF_P, "group-norm reduction space");
+    float* red = reinterpret_cast<float*>(smem + GN_OFF);
+    float* tot = red + C::WAVES * CHUNKS * REC;
+    if (lane < CHUNKS) {
+      float* r = red + (wave * CHUNKS + lane) * REC;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        r[j] = gsum[j];
+        r[E + j] = gsq[j];
+      }
+      r[2 * E] = gcnt;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); the row stores may still be in flight
+    __builtin_amdgcn_s_barrier();
+    if (threadIdx.x < COUT) {
+      const int c = threadIdx.x, ch = c / E, j = c % E;
+      float S = 0.f, Q = 0.f;
+      for (int w = 0; w < C::WAVES; ++w) {
+        S += red[(w * CHUNKS + ch) * REC + j];
+        Q += red[(w * CHUNKS + ch) * REC + E + j];
+      }
+      tot[2 * c] = S;
+      tot[2 * c + 1] = Q;
+    }
+    if (threadIdx.x == 0) {
+      float cnt = 0.f;
+      for (int w = 0; w < C::WAVES; ++w) cnt += red[(w * CHUNKS) * REC + 2 * E];
+      tot[2 * COUT] = cnt;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    constexpr int SLOTS = NB * 16 / 128;
+    const int groups = ep.gn_groups, gsz = COUT / groups;
+    float4* part = reinterpret_cast<float4*>(ep.gn) + tile * SLOTS * groups;
+    for (int g = threadIdx.x; g < groups; g += C::THREADS) {
+      float S = 0.f, Q = 0.f;
+      for (int k = 0; k < gsz; ++k) {
+        S += tot[2 * (g * gsz + k)];
+        Q += tot[2 * (g * gsz + k) + 1];
+      }
+      part[g] = make_float4(tot[2 * COUT] * gsz, S, Q, 0.f);
+#pragma unroll
+      for (int sl = 1; sl < SLOTS; ++sl) part[sl * groups + g] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
 }
@@ -504,7 +625,8 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ X, cons
                                                    const int32_t* __restrict__ perm,
                                                    const int32_t* __restrict__ gidx, int64_t npad,
                                                    int64_t n, int cin, int cout,
-                                                   void* __restrict__ Y, int out_kind) {
+                                                   void* __restrict__ Y, int out_kind, int act,
+                                                   const void* __restrict__ res) {
   const int64_t rows = DENSE ? n : npad;
   const int64_t total = rows * cout;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -524,7 +646,13 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ X, cons
       for (int c = 0; c < cin; ++c)
         acc = fmaf(load_feat<T>(xr + c), load_feat<T>(wt + static_cast<int64_t>(c) * cout), acc);
     }
-    const float v = acc + (bias ? bias[o] : 0.f);
+    float v = apply_act(acc + (bias ? bias[o] : 0.f), act);
+    if (res) {
+      const int64_t k = orow * cout + o;
+      v += out_kind == SSC_BF16  ? bf16_to_f32(static_cast<const uint16_t*>(res)[k])
+           : out_kind == SSC_F16 ? static_cast<float>(static_cast<const _Float16*>(res)[k])
+                                 : static_cast<const float*>(res)[k];
+    }
     if (out_kind == SSC_BF16)
       static_cast<uint16_t*>(Y)[orow * cout + o] = f32_to_bf16_rne(v);
     else if (out_kind == SSC_F16)
@@ -600,7 +728,8 @@ template <int CIN, int COUT, bool OUT16, int EK>
 __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __restrict__ X,
                                                           const uint16_t* __restrict__ Wp,
                                                           const float* __restrict__ bias,
-                                                          int64_t n, void* __restrict__ Y) {
+                                                          int64_t n, void* __restrict__ Y,
+                                                          int act, const void* __restrict__ res) {
   using L = LinCfg<CIN, COUT, OUT16>;
   using C = typename L::C;
   __shared__ __attribute__((aligned(1024))) char smem[L::SMEM];
@@ -650,7 +779,8 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
           acc[bl][c] = mfma16x16x32<EK>(a[s], bw[c][s], acc[bl][c]);
       }
     }
-    // Stage bias-added outputs (16-byte chunks XOR-swizzled by row).
+    // Stage the outputs: act(acc + bias) + residual (16-byte chunks XOR-swizzled by row).
+    const int64_t row0 = tile * L::TR;
 #pragma unroll
     for (int bl = 0; bl < C::BPW; ++bl) {
       const int b = bl * L::WR + wr;
@@ -662,7 +792,9 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
           const int row = b * 16 + (lane >> 4) * 4 + i;
           const int byte = col * L::ESZ;
           char* dst = sOut + row * L::ROWB + (((byte >> 4) ^ (row & L::SWM)) << 4) + (byte & 15);
-          const float v = acc[bl][c][i] + bv[c];
+          float v = apply_act(acc[bl][c][i] + bv[c], act);
+          if (res && row0 + row < n)
+            v += load_out<OUT16, EK>(res, (row0 + row) * COUT + col);
           if (OUT16)
             *reinterpret_cast<uint16_t*>(dst) = to16<EK>(v);
           else
@@ -672,7 +804,6 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
     __builtin_amdgcn_s_barrier();
-    const int64_t row0 = tile * L::TR;
 #pragma unroll
     for (int it = 0; it < L::STORES; ++it) {
       const int idx = threadIdx.x + it * C::THREADS;
@@ -685,9 +816,10 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
   }
 }
 
-using LinFn = void (*)(const uint16_t*, const uint16_t*, const float*, int64_t, void*);
+using LinFn = void (*)(const uint16_t*, const uint16_t*, const float*, int64_t, void*, int,
+                      const void*);
 using LdsFn = void (*)(const uint16_t*, const uint16_t*, const float*, const int32_t*,
-                       const uint32_t*, const int32_t*, const uint16_t*, int64_t, void*);
+                       const uint32_t*, const int32_t*, const uint16_t*, int64_t, void*, Epi);
 
 // k=1 streaming kernel for the channel counts the matrix-core path is built for.
 LinFn pick_linear(int cin, int cout, bool out16, int ek, int* wc_groups, int* rows_per_tile) {
@@ -756,18 +888,18 @@ int device_cu_count() {
 }
 
 ssc_status launch_linear(LinFn fn, int rows_per_tile, const void* feats, const uint16_t* wp,
-                         const float* bias, int64_t n, void* out, hipStream_t s) {
+                         const float* bias, int64_t n, void* out, const Epi& ep, hipStream_t s) {
   // Persistent: two resident workgroups per compute unit, each walking tiles with a stride.
   const int64_t tiles = (n + rows_per_tile - 1) / rows_per_tile;
   const int64_t grid = std::min<int64_t>(tiles, 2 * static_cast<int64_t>(device_cu_count()));
   hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(feats), wp, bias, n, out);
+                     static_cast<const uint16_t*>(feats), wp, bias, n, out, ep.act, ep.res);
   return launch_status();
 }
 
 ssc_status launch_lds(LdsFn fn, int threads, int rows_per_tile, const void* feats,
                       const uint16_t* wt, const float* bias, const void* plan, int64_t n,
-                      void* out, hipStream_t s) {
+                      void* out, const Epi& ep, hipStream_t s) {
   const PlanLayout P = plan_layout(n);
   const char* pb = static_cast<const char*>(plan);
   const int64_t tiles = P.npad / rows_per_tile;
@@ -776,8 +908,38 @@ ssc_status launch_lds(LdsFn fn, int threads, int rows_per_tile, const void* feat
                      reinterpret_cast<const int32_t*>(pb + P.off_perm),
                      reinterpret_cast<const uint32_t*>(pb + P.off_bmask),
                      reinterpret_cast<const int32_t*>(pb + P.off_gidx),
-                     reinterpret_cast<const uint16_t*>(pb + P.off_zero), P.npad, out);
+                     reinterpret_cast<const uint16_t*>(pb + P.off_zero), P.npad, out, ep);
   return launch_status();
+}
+
+// Host checks of an epilogue; fills the kernel-side arguments (gn left null: the caller
+// decides whether the kernel sums the statistics itself).
+ssc_status check_epilogue(const ssc_epilogue* e, int64_t n, int cout, Epi* ep) {
+  *ep = Epi{nullptr, nullptr, SSC_ACT_NONE, 0};
+  if (e == nullptr) return SSC_OK;
+  if (e->act < SSC_ACT_NONE || e->act > SSC_ACT_SILU || e->reserved != 0) return SSC_ERR_ARG;
+  if (e->residual && !aligned(e->residual, 16)) return SSC_ERR_ARG;
+  if (e->gn_partials) {
+    if (e->gn_groups < 1 || e->gn_groups > 256 || cout % e->gn_groups != 0) return SSC_ERR_ARG;
+    if (e->batch < 1 || e->batch > SSC_GN_MAX_BATCH) return SSC_ERR_ARG;
+    if (e->batch > 1 && n > 0 && e->coords == nullptr) return SSC_ERR_ARG;
+    if (!aligned(e->gn_partials, 16) || (e->coords && !aligned(e->coords, 16)))
+      return SSC_ERR_ARG;
+    if (e->gn_partials_bytes < ssc_gn_partials_bytes(n, e->batch, e->gn_groups))
+      return SSC_ERR_WORKSPACE;
+  }
+  ep->act = e->act;
+  ep->res = e->residual;
+  ep->gn_groups = e->gn_groups;
+  return SSC_OK;
+}
+
+// The group-norm partial sums of out, when the kernel did not sum them in its epilogue.
+ssc_status gn_after(const ssc_epilogue* e, bool fused, const void* out, int out_dtype, int64_t n,
+                    int cout, hipStream_t s) {
+  if (e == nullptr || e->gn_partials == nullptr || fused) return SSC_OK;
+  return gn_partials_launch(out, out_dtype, n, cout, e->coords, e->batch, e->gn_groups,
+                            e->gn_partials, s);
 }
 
 void launch_pack_frag(const void* weight, int taps, int cin, int cout, int wc_groups, int flip,
@@ -791,7 +953,8 @@ void launch_pack_frag(const void* weight, int taps, int cin, int cout, int wc_gr
 
 ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* weight,
                     const float* bias, const void* plan, int64_t n, int cin, int cout, void* out,
-                    int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                    int out_dtype, const ssc_epilogue* epi, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   if (n < 0 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSC_ERR_ARG;
   if (cin < 1 || cout < 1 || cin > 1024 || cout > 1024) return SSC_ERR_UNSUPPORTED;
   if (n >= (int64_t(1) << 31)) return SSC_ERR_UNSUPPORTED;
@@ -804,8 +967,10 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
   const size_t need = ssc_conv_workspace_bytes(cin, cout, in_dtype);
   if (workspace_bytes < need || (need > 0 && (workspace == nullptr || !aligned(workspace, kAlign))))
     return SSC_ERR_WORKSPACE;
-  if (n == 0) return SSC_OK;
+  Epi ep;
+  if (const ssc_status st = check_epilogue(epi, n, cout, &ep); st != SSC_OK) return st;
   hipStream_t s = as_stream(stream);
+  if (n == 0) return gn_after(epi, false, out, out_dtype, n, cout, s);
   const PlanLayout P = plan_layout(n);
   const char* pb = static_cast<const char*>(plan);
   const int32_t* perm = dense ? nullptr : reinterpret_cast<const int32_t*>(pb + P.off_perm);
@@ -820,13 +985,21 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
       int wcg = 0, rows = 0;
       if (LinFn fn = pick_linear(cin, cout, out16, ek, &wcg, &rows)) {
         launch_pack_frag(weight, 1, cin, cout, wcg, 0, wt, s);
-        return launch_linear(fn, rows, feats, wt, bias, n, out, s);
+        if (const ssc_status st = launch_linear(fn, rows, feats, wt, bias, n, out, ep, s);
+            st != SSC_OK)
+          return st;
+        return gn_after(epi, false, out, out_dtype, n, cout, s);
       }
     } else {
       int threads = 0, rows = 0, wcg = 0;
       if (LdsFn fn = pick_lds(cin, cout, out16, ek, &threads, &rows, &wcg)) {
         launch_pack_frag(weight, kTaps, cin, cout, wcg, 0, wt, s);
-        return launch_lds(fn, threads, rows, feats, wt, bias, plan, n, out, s);
+        const bool fused = epi && epi->gn_partials && epi->batch == 1;
+        if (fused) ep.gn = epi->gn_partials;
+        if (const ssc_status st = launch_lds(fn, threads, rows, feats, wt, bias, plan, n, out, ep, s);
+            st != SSC_OK)
+          return st;
+        return gn_after(epi, fused, out, out_dtype, n, cout, s);
       }
     }
   }
@@ -837,19 +1010,20 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
     auto fn = dense ? k_conv_valu<uint16_t, true> : k_conv_valu<uint16_t, false>;
     hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, s, static_cast<const uint16_t*>(feats),
                        static_cast<const uint16_t*>(weight), bias, perm, gidx, P.npad, n, cin,
-                       cout, out, out_dtype);
+                       cout, out, out_dtype, ep.act, ep.res);
   } else if (in_dtype == SSC_F16) {
     auto fn = dense ? k_conv_valu<_Float16, true> : k_conv_valu<_Float16, false>;
     hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, s, static_cast<const _Float16*>(feats),
                        static_cast<const _Float16*>(weight), bias, perm, gidx, P.npad, n, cin,
-                       cout, out, out_dtype);
+                       cout, out, out_dtype, ep.act, ep.res);
   } else {
     auto fn = dense ? k_conv_valu<float, true> : k_conv_valu<float, false>;
     hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(feats),
                        static_cast<const float*>(weight), bias, perm, gidx, P.npad, n, cin, cout,
-                       out, out_dtype);
+                       out, out_dtype, ep.act, ep.res);
   }
-  return launch_status();
+  if (const ssc_status st = launch_status(); st != SSC_OK) return st;
+  return gn_after(epi, false, out, out_dtype, n, cout, s);
 }
 
 }  // namespace
@@ -867,7 +1041,16 @@ extern "C" ssc_status ssc_subm_conv3d(const void* feats, int32_t in_dtype, const
                                       int32_t cout, void* out, int32_t out_dtype, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   return run_conv(false, feats, in_dtype, weight, bias, plan, n, cin, cout, out, out_dtype,
-                  workspace, workspace_bytes, stream);
+                  nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" ssc_status ssc_subm_conv3d_ex(const void* feats, int32_t in_dtype, const void* weight,
+                                         const float* bias, const void* plan, int64_t n,
+                                         int32_t cin, int32_t cout, void* out, int32_t out_dtype,
+                                         const ssc_epilogue* epilogue, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  return run_conv(false, feats, in_dtype, weight, bias, plan, n, cin, cout, out, out_dtype,
+                  epilogue, workspace, workspace_bytes, stream);
 }
 
 extern "C" ssc_status ssc_linear(const void* feats, int32_t in_dtype, const void* weight,
@@ -875,7 +1058,15 @@ extern "C" ssc_status ssc_linear(const void* feats, int32_t in_dtype, const void
                                  int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                  void* stream) {
   return run_conv(true, feats, in_dtype, weight, bias, nullptr, n, cin, cout, out, out_dtype,
-                  workspace, workspace_bytes, stream);
+                  nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" ssc_status ssc_linear_ex(const void* feats, int32_t in_dtype, const void* weight,
+                                    const float* bias, int64_t n, int32_t cin, int32_t cout,
+                                    void* out, int32_t out_dtype, const ssc_epilogue* epilogue,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return run_conv(true, feats, in_dtype, weight, bias, nullptr, n, cin, cout, out, out_dtype,
+                  epilogue, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t ssc_packed_weight_bytes(int32_t taps, int32_t cin, int32_t cout) {
@@ -907,6 +1098,15 @@ extern "C" ssc_status ssc_subm_conv3d_packed(const void* feats, const void* pack
                                              const float* bias, const void* plan, int64_t n,
                                              int32_t cin, int32_t cout, void* out,
                                              int32_t out_dtype, void* stream) {
+  return ssc_subm_conv3d_packed_ex(feats, packed_weight, bias, plan, n, cin, cout, out,
+                                   out_dtype, nullptr, stream);
+}
+
+extern "C" ssc_status ssc_subm_conv3d_packed_ex(const void* feats, const void* packed_weight,
+                                                const float* bias, const void* plan, int64_t n,
+                                                int32_t cin, int32_t cout, void* out,
+                                                int32_t out_dtype, const ssc_epilogue* epilogue,
+                                                void* stream) {
   if (n < 0 || !valid_dtype(out_dtype) || packed_weight == nullptr || plan == nullptr)
     return SSC_ERR_ARG;
   if (n >= (int64_t(1) << 31) || out_dtype == SSC_F16) return SSC_ERR_UNSUPPORTED;
@@ -917,9 +1117,18 @@ extern "C" ssc_status ssc_subm_conv3d_packed(const void* feats, const void* pack
   if (!aligned(packed_weight, 16) || !aligned(plan, kAlign) ||
       (n > 0 && (!aligned(feats, 16) || !aligned(out, 16))) || (bias && !aligned(bias, 4)))
     return SSC_ERR_ARG;
-  if (n == 0) return SSC_OK;
-  return launch_lds(fn, threads, rows, feats, static_cast<const uint16_t*>(packed_weight), bias,
-                    plan, n, out, as_stream(stream));
+  Epi ep;
+  if (const ssc_status st = check_epilogue(epilogue, n, cout, &ep); st != SSC_OK) return st;
+  hipStream_t s = as_stream(stream);
+  if (n == 0) return gn_after(epilogue, false, out, out_dtype, n, cout, s);
+  const bool fused = epilogue && epilogue->gn_partials && epilogue->batch == 1;
+  if (fused) ep.gn = epilogue->gn_partials;
+  if (const ssc_status st = launch_lds(fn, threads, rows, feats,
+                                       static_cast<const uint16_t*>(packed_weight), bias, plan, n,
+                                       out, ep, s);
+      st != SSC_OK)
+    return st;
+  return gn_after(epilogue, fused, out, out_dtype, n, cout, s);
 }
 
 extern "C" int ssc_version(void) { return 100; }

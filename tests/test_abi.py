@@ -191,3 +191,49 @@ def test_resample_argument_errors(lib):
     assert s(FAKE, 10, None, None, 0, 0, FAKE, None, None) == ssc.SSC_ERR_ARG
     assert s(FAKE, 10, GRID, None, 0, 4, FAKE, None, None) == ssc.SSC_ERR_ARG
     assert s(FAKE, 0, GRID, None, 0, 0, FAKE, None, None) == ssc.SSC_OK
+
+
+def test_epilogue_and_group_norm_argument_errors(lib):
+    big = 1 << 30
+    E = ssc._Epilogue
+
+    def conv(epi, n=10, cout=64):
+        return lib.ssc_subm_conv3d_ex(FAKE, ssc.SSC_BF16, FAKE, None, FAKE, n, 64, cout, FAKE,
+                                      ssc.SSC_F32, ctypes.byref(epi), FAKE, big, None)
+
+    assert conv(E(act=3)) == ssc.SSC_ERR_ARG                               # unknown activation
+    assert conv(E(act=-1)) == ssc.SSC_ERR_ARG
+    assert conv(E(reserved=1)) == ssc.SSC_ERR_ARG
+    assert conv(E(residual=(1 << 20) + 8)) == ssc.SSC_ERR_ARG             # misaligned residual
+    gn = dict(gn_partials=1 << 20, gn_partials_bytes=big, batch=1)
+    assert conv(E(gn_groups=0, **gn)) == ssc.SSC_ERR_ARG
+    assert conv(E(gn_groups=24, **gn)) == ssc.SSC_ERR_ARG                 # 64 % 24 != 0
+    assert conv(E(gn_groups=512, **gn)) == ssc.SSC_ERR_ARG
+    assert conv(E(gn_groups=32, gn_partials=1 << 20, gn_partials_bytes=big, batch=0)) == ssc.SSC_ERR_ARG
+    assert conv(E(gn_groups=32, gn_partials=1 << 20, gn_partials_bytes=big, batch=65)) == ssc.SSC_ERR_ARG
+    assert conv(E(gn_groups=32, gn_partials=1 << 20, gn_partials_bytes=big, batch=2)) == ssc.SSC_ERR_ARG  # no coords
+    assert conv(E(gn_groups=32, gn_partials=1 << 20, gn_partials_bytes=64, batch=1)) == ssc.SSC_ERR_WORKSPACE
+    lin = lib.ssc_linear_ex(FAKE, ssc.SSC_BF16, FAKE, None, 10, 64, 64, FAKE, ssc.SSC_F32,
+                            ctypes.byref(E(act=9)), FAKE, big, None)
+    assert lin == ssc.SSC_ERR_ARG
+    pk = lib.ssc_subm_conv3d_packed_ex(FAKE, FAKE, None, FAKE, 10, 128, 128, FAKE, ssc.SSC_F32,
+                                       ctypes.byref(E(act=9)), None)
+    assert pk == ssc.SSC_ERR_ARG
+    # partial-sum buffer sizes: one float4 per (128-row slot, batch entry, group)
+    assert lib.ssc_gn_partials_bytes(1000, 1, 32) == 8 * 32 * 16
+    assert lib.ssc_gn_partials_bytes(0, 2, 4) >= 2 * 2 * 4 * 16
+    assert lib.ssc_gn_partials_bytes(10, 65, 32) == 0 and lib.ssc_gn_partials_bytes(-1, 1, 1) == 0
+    p = lib.ssc_gn_partials
+    assert p(FAKE, 0, 10, 64, None, 1, 0, FAKE, big, None) == ssc.SSC_ERR_ARG       # groups 0
+    assert p(FAKE, 0, 10, 64, None, 1, 24, FAKE, big, None) == ssc.SSC_ERR_ARG      # 64 % 24
+    assert p(FAKE, 7, 10, 64, None, 1, 32, FAKE, big, None) == ssc.SSC_ERR_ARG      # dtype
+    assert p(FAKE, 0, 10, 64, None, 2, 32, FAKE, big, None) == ssc.SSC_ERR_ARG      # coords
+    assert p(FAKE, 0, 10, 64, None, 1, 32, FAKE, 16, None) == ssc.SSC_ERR_WORKSPACE
+    f = lib.ssc_gn_finalize
+    assert f(FAKE, 10, 0, 32, 1e-5, FAKE, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 10, 1, 32, float("nan"), FAKE, None) == ssc.SSC_ERR_ARG
+    assert f(None, 10, 1, 32, 1e-5, FAKE, None) == ssc.SSC_ERR_ARG
+    a = lib.ssc_gn_apply
+    assert a(FAKE, 0, 10, 64, None, 1, 32, FAKE, None, None, 7, FAKE, None) == ssc.SSC_ERR_ARG
+    assert a(FAKE, 0, 10, 64, None, 1, 32, None, None, None, 0, FAKE, None) == ssc.SSC_ERR_ARG
+    assert a(FAKE, 0, 0, 64, None, 1, 32, FAKE, None, None, 0, None, None) == ssc.SSC_OK
