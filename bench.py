@@ -175,6 +175,97 @@ def time_resample(ssc, torch, coords, x, w, dev, reps: int = 20) -> dict:
             "spatial2channel_gbs": round(c_bytes / c_us / 1e3, 1)}
 
 
+def time_block(ssc, torch, coords, x, plan, batch, dev, reps: int = 50) -> dict:
+    """A pre-norm residual block on the workload's sites, C = the input channels (bf16, C in
+    {32, 64, 128}): h = conv1(silu(gn1(x))); y = conv2(silu(gn2(h))) + x with 32-group norms.
+    Launches (C ABI, preallocated buffers): gn1 statistics + finalize + apply; conv1 summing
+    gn2's statistics in its epilogue (batch 1; else a pass after it); gn2 finalize + apply in
+    place; conv2 adding x in its epilogue.  Random weights (seeded), device time per stage."""
+    import ctypes
+    import math
+    lib = ssc.load_library()
+    n, c = x.shape
+    groups, eps = 32, 1e-5
+    gen = torch.Generator().manual_seed(1234)
+
+    def rnd(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=gen) * scale)
+
+    w1 = rnd(27, c, c, scale=1 / math.sqrt(27 * c)).to(torch.bfloat16).to(dev)
+    w2 = rnd(27, c, c, scale=1 / math.sqrt(27 * c)).to(torch.bfloat16).to(dev)
+    pw1, pw2 = ssc.pack_weights(w1), ssc.pack_weights(w2)
+    b1, b2 = rnd(c, scale=0.1).to(dev), rnd(c, scale=0.1).to(dev)
+    g1, g2 = (1 + rnd(c, scale=0.1)).to(dev), (1 + rnd(c, scale=0.1)).to(dev)
+    be1, be2 = rnd(c, scale=0.1).to(dev), rnd(c, scale=0.1).to(dev)
+    cd = coords if batch > 1 else None
+    parts0 = ssc.GroupNormPartials(n, batch, groups, dev, cd)
+    parts1 = ssc.GroupNormPartials(n, batch, groups, dev, cd)
+    stats0 = torch.empty((batch, groups, 2), dtype=torch.float32, device=dev)
+    stats1 = torch.empty_like(stats0)
+    h, h1, y = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    BF, SILU = ssc.SSC_BF16, ssc.ACTS["silu"]
+    nb = parts0.buf.numel()
+    epi1 = ssc._Epilogue(gn_groups=groups, batch=batch, coords=None if cd is None else cd.data_ptr(),
+                         gn_partials=parts1.buf.data_ptr(), gn_partials_bytes=nb)
+    epi2 = ssc._Epilogue(residual=x.data_ptr())
+
+    def norm1():
+        lib.ssc_gn_partials(p(x), BF, n, c, p(cd), batch, groups, p(parts0.buf), nb, st)
+        lib.ssc_gn_finalize(p(parts0.buf), n, batch, groups, eps, p(stats0), st)
+        lib.ssc_gn_apply(p(x), BF, n, c, p(cd), batch, groups, p(stats0), p(g1), p(be1), SILU,
+                         p(h), st)
+
+    def conv1():
+        lib.ssc_subm_conv3d_packed_ex(p(h), p(pw1.buf), p(b1), p(plan.buf), n, c, c, p(h1), BF,
+                                      ctypes.byref(epi1), st)
+
+    def norm2():
+        lib.ssc_gn_finalize(p(parts1.buf), n, batch, groups, eps, p(stats1), st)
+        lib.ssc_gn_apply(p(h1), BF, n, c, p(cd), batch, groups, p(stats1), p(g2), p(be2), SILU,
+                         p(h1), st)
+
+    def conv2():
+        lib.ssc_subm_conv3d_packed_ex(p(h1), p(pw2.buf), p(b2), p(plan.buf), n, c, c, p(y), BF,
+                                      ctypes.byref(epi2), st)
+
+    def plain_conv():
+        lib.ssc_subm_conv3d_packed(p(h), p(pw1.buf), p(b1), p(plan.buf), n, c, c, p(h1), BF, st)
+
+    def block():
+        norm1()
+        conv1()
+        norm2()
+        conv2()
+
+    def t(fn):
+        for _ in range(5):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    us = {k: t(f) for k, f in (("block", block), ("norm1", norm1), ("conv1_gn_stats", conv1),
+                               ("norm2", norm2), ("conv2_residual", conv2),
+                               ("conv_plain", plain_conv))}
+    row = c * 2
+    # algorithmic bytes of the two norms: read x twice (statistics, apply) and write h; read
+    # and write h1 (its statistics come from conv1's epilogue)
+    norm_bytes = n * row * 3 + n * row * 2
+    return {"channels": c, "groups": groups, "batch": batch,
+            "block_us": round(us["block"], 2), "block_mvox_s": round(n / us["block"], 1),
+            "stages_us": {k: round(v, 2) for k, v in us.items() if k != "block"},
+            "norm_gbs": round(norm_bytes / (us["norm1"] + us["norm2"]) / 1e3, 1),
+            "epilogue_overhead_us": {
+                "gn_stats": round(us["conv1_gn_stats"] - us["conv_plain"], 2),
+                "residual": round(us["conv2_residual"] - us["conv_plain"], 2)}}
+
+
 def cpu_baseline(w, m_nbr) -> dict:
     """The CPU oracle as it stands (fp64 dictionary + per-voxel loop), warm: map prebuilt,
     conv over every site of the same workload, repeated for at least a second of wall time;
@@ -346,6 +437,10 @@ def main():
     log(f"[bench] conv kernel, caches flushed: median {flushed['median_us']} us")
 
     resample = time_resample(ssc, torch, coords, x, w, dev)
+    block = None
+    if x.dtype == torch.bfloat16 and cin in (32, 64, 128):
+        block = time_block(ssc, torch, coords, x, plan, w.batch, dev)
+        log(f"[bench] residual block {block['block_us']} us {block['stages_us']}")
 
     out_bytes = 4 if mid_dt == torch.float32 else 2
     in_bytes = x.element_size()
@@ -390,6 +485,7 @@ def main():
                  "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": flops},
         "conv_flushed": flushed,
         "resample": resample,
+        "res_block": block,
         "cold_index_plan_ms": round(float(np.median(cold)), 4),
         # Algorithmic bytes of the cold path: the index reads the coordinates (16 B per site)
         # and writes the map (27 x 4 B); the plan reads the map and writes the row ids, block

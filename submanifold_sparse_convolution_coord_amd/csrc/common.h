@@ -64,11 +64,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Epilogue activations: relu = max(v, 0), silu = v * sigmoid(v) = v / (1 + e^-v) (e^-v from
-// the hardware exp; at very negative v it overflows to inf and the quotient is -0).
+// Epilogue activations: relu = max(v, 0), silu = v * sigmoid(v) = v * 1 / (1 + e^-v) (e^-v
+// and the reciprocal from the hardware's approximate exp and rcp, each within about an ulp;
+// at very negative v, e^-v overflows to inf and the product is -0).
 __device__ __forceinline__ float apply_act(float v, int act) {
   if (act == SSC_ACT_RELU) return v > 0.f ? v : 0.f;
-  if (act == SSC_ACT_SILU) return v / (1.f + __expf(-v));
+  if (act == SSC_ACT_SILU) return v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
   return v;
 }
 

@@ -346,7 +346,9 @@ __device__ __forceinline__ void piece_sums(const u32x4_t& v, float* s, float* q)
   }
 }
 
-template <int CIN, int COUT, int NB, int WR, int WC, bool OUT16, int EK>
+// EPI = false is the plain convolution (bias only); EPI = true adds the activation, the
+// residual and the group-norm statistics as the Epi arguments ask.
+template <int CIN, int COUT, int NB, int WR, int WC, bool OUT16, int EK, bool EPI>
 __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
     const float* __restrict__ bias, const int32_t* __restrict__ perm,
@@ -496,6 +498,25 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   for (int j = 0; j < E; ++j) gsum[j] = gsq[j] = 0.f;
 #pragma unroll
   for (int p0 = 0; p0 < NB; p0 += BPP) {
+    if constexpr (EPI) {
+      // Residual rows of this pass, fetched as whole 16-byte pieces into the staging tile
+      // (the layout the output takes there); each value is then added by the lane that
+      // stages the output value at the same place.
+      if (ep.res) {
+        constexpr int RPIECES = BPP * 16 * CHUNKS;
+#pragma unroll 4
+        for (int idx = threadIdx.x; idx < RPIECES; idx += C::THREADS) {
+          const int row = idx / CHUNKS, ch = idx % CHUNKS;
+          const int32_t o = sP[p0 * 16 + row];
+          if (o < 0) continue;
+          *reinterpret_cast<u32x4_t*>(sOut + row * ROWB + ((ch ^ (row & SWM)) << 4)) =
+              *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(ep.res) +
+                                                static_cast<int64_t>(o) * ROWB + ch * 16);
+        }
+        wait_vm_lgkm0();
+        __builtin_amdgcn_s_barrier();
+      }
+    }
 #pragma unroll
     for (int bl = 0; bl < C::BPW; ++bl) {
       const int b = bl * WR + wr;
@@ -508,10 +529,17 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
           const int row = (b - p0) * 16 + (lane >> 4) * 4 + i;
           const int byte = col * ESZ;
           char* dst = sOut + row * ROWB + (((byte >> 4) ^ (row & SWM)) << 4) + (byte & 15);
-          float v = apply_act(acc[bl][c][i] + bv[c], ep.act);
-          if (ep.res) {
-            const int32_t o = sP[b * 16 + (lane >> 4) * 4 + i];
-            if (o >= 0) v += load_out<OUT16, EK>(ep.res, static_cast<int64_t>(o) * COUT + col);
+          float v = acc[bl][c][i] + bv[c];
+          if constexpr (EPI) {
+            v = apply_act(v, ep.act);
+            if (ep.res) {
+              if constexpr (!OUT16)
+                v += *reinterpret_cast<const float*>(dst);
+              else if constexpr (EK == 0)
+                v += bf16_to_f32(*reinterpret_cast<const uint16_t*>(dst));
+              else
+                v += static_cast<float>(*reinterpret_cast<const _Float16*>(dst));
+            }
           }
           if (OUT16)
             *reinterpret_cast<uint16_t*>(dst) = to16<EK>(v);
@@ -532,9 +560,11 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
           *reinterpret_cast<const u32x4_t*>(sOut + row * ROWB + ((ch ^ (row & SWM)) << 4));
       *reinterpret_cast<u32x4_t*>(static_cast<char*>(Y) + static_cast<int64_t>(o) * ROWB +
                                   ch * 16) = v;
-      if (ep.gn) {
-        piece_sums<OUT16, EK>(v, gsum, gsq);
-        gcnt += 1.f;
+      if constexpr (EPI) {
+        if (ep.gn) {
+          piece_sums<OUT16, EK>(v, gsum, gsq);
+          gcnt += 1.f;
+        }
       }
     }
     if (p0 + BPP < NB) {
@@ -542,7 +572,7 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
       __builtin_amdgcn_s_barrier();
     }
   }
-  if (ep.gn) {
+  if (EPI && ep.gn) {
     // Fixed-order reduction: lanes that own the same piece (lane bits above CHUNKS) by a
     // butterfly (every lane ends with the same sums), then the waves in order, then the
     // channels of each group in order.  One or two 128-row slots per tile.
@@ -626,7 +656,7 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ X, cons
                                                    const int32_t* __restrict__ gidx, int64_t npad,
                                                    int64_t n, int cin, int cout,
                                                    void* __restrict__ Y, int out_kind, int act,
-                                                   const void* __restrict__ res) {
+                                                   const void* res) {
   const int64_t rows = DENSE ? n : npad;
   const int64_t total = rows * cout;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -724,12 +754,12 @@ __device__ __forceinline__ void linear_copies(int64_t tile, int64_t n,
   }
 }
 
-template <int CIN, int COUT, bool OUT16, int EK>
+template <int CIN, int COUT, bool OUT16, int EK, bool EPI>
 __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __restrict__ X,
                                                           const uint16_t* __restrict__ Wp,
                                                           const float* __restrict__ bias,
                                                           int64_t n, void* __restrict__ Y,
-                                                          int act, const void* __restrict__ res) {
+                                                          int act, const void* res) {
   using L = LinCfg<CIN, COUT, OUT16>;
   using C = typename L::C;
   __shared__ __attribute__((aligned(1024))) char smem[L::SMEM];
@@ -792,9 +822,11 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
           const int row = b * 16 + (lane >> 4) * 4 + i;
           const int byte = col * L::ESZ;
           char* dst = sOut + row * L::ROWB + (((byte >> 4) ^ (row & L::SWM)) << 4) + (byte & 15);
-          float v = apply_act(acc[bl][c][i] + bv[c], act);
-          if (res && row0 + row < n)
-            v += load_out<OUT16, EK>(res, (row0 + row) * COUT + col);
+          float v = acc[bl][c][i] + bv[c];
+          if constexpr (EPI) {
+            v = apply_act(v, act);
+            if (res && row0 + row < n) v += load_out<OUT16, EK>(res, (row0 + row) * COUT + col);
+          }
           if (OUT16)
             *reinterpret_cast<uint16_t*>(dst) = to16<EK>(v);
           else
@@ -822,13 +854,19 @@ using LdsFn = void (*)(const uint16_t*, const uint16_t*, const float*, const int
                        const uint32_t*, const int32_t*, const uint16_t*, int64_t, void*, Epi);
 
 // k=1 streaming kernel for the channel counts the matrix-core path is built for.
-LinFn pick_linear(int cin, int cout, bool out16, int ek, int* wc_groups, int* rows_per_tile) {
+template <int CI, int CO, bool O16, int EK>
+LinFn linear_fn(bool epi) {
+  return epi ? k_linear_stream<CI, CO, O16, EK, true> : k_linear_stream<CI, CO, O16, EK, false>;
+}
+
+LinFn pick_linear(int cin, int cout, bool out16, int ek, int* wc_groups, int* rows_per_tile,
+                  bool epi) {
 #define SSC_CASE(CI, CO)                                                                      \
   if (cin == CI && cout == CO) {                                                              \
     *wc_groups = LinCfg<CI, CO, false>::WC;                                                   \
     *rows_per_tile = out16 ? LinCfg<CI, CO, true>::TR : LinCfg<CI, CO, false>::TR;            \
-    if (ek == 1) return out16 ? k_linear_stream<CI, CO, true, 1> : k_linear_stream<CI, CO, false, 1>; \
-    return out16 ? k_linear_stream<CI, CO, true, 0> : k_linear_stream<CI, CO, false, 0>;      \
+    if (ek == 1) return out16 ? linear_fn<CI, CO, true, 1>(epi) : linear_fn<CI, CO, false, 1>(epi); \
+    return out16 ? linear_fn<CI, CO, true, 0>(epi) : linear_fn<CI, CO, false, 0>(epi);        \
   }
   SSC_CASE(32, 16) SSC_CASE(32, 32) SSC_CASE(32, 64) SSC_CASE(32, 128)
   SSC_CASE(64, 16) SSC_CASE(64, 32) SSC_CASE(64, 64) SSC_CASE(64, 128)
@@ -846,19 +884,23 @@ struct LdsPick {
   static constexpr int NB = (CI >= 64 || CO > 64) ? 8 : 16;
 };
 
+template <int CI, int CO, bool O16, int EK>
+LdsFn lds_fn(bool epi) {
+  using P = LdsPick<CI, CO>;
+  return epi ? k_subm_lds<CI, CO, P::NB, P::WR, P::WC, O16, EK, true>
+             : k_subm_lds<CI, CO, P::NB, P::WR, P::WC, O16, EK, false>;
+}
+
 LdsFn pick_lds(int cin, int cout, bool out16, int ek, int* threads, int* rows_per_tile,
-               int* wc_groups) {
+               int* wc_groups, bool epi) {
 #define SSC_CASE(CI, CO)                                                             \
   if (cin == CI && cout == CO) {                                                     \
     using P = LdsPick<CI, CO>;                                                       \
     *threads = P::WR * P::WC * 64;                                                   \
     *rows_per_tile = P::NB * 16;                                                     \
     *wc_groups = P::WC;                                                              \
-    if (ek == 1)                                                                     \
-      return out16 ? k_subm_lds<CI, CO, P::NB, P::WR, P::WC, true, 1>                \
-                   : k_subm_lds<CI, CO, P::NB, P::WR, P::WC, false, 1>;              \
-    return out16 ? k_subm_lds<CI, CO, P::NB, P::WR, P::WC, true, 0>                  \
-                 : k_subm_lds<CI, CO, P::NB, P::WR, P::WC, false, 0>;                \
+    if (ek == 1) return out16 ? lds_fn<CI, CO, true, 1>(epi) : lds_fn<CI, CO, false, 1>(epi); \
+    return out16 ? lds_fn<CI, CO, true, 0>(epi) : lds_fn<CI, CO, false, 0>(epi);     \
   }
   SSC_CASE(32, 16) SSC_CASE(32, 32) SSC_CASE(32, 64) SSC_CASE(32, 128)
   SSC_CASE(64, 16) SSC_CASE(64, 32) SSC_CASE(64, 64) SSC_CASE(64, 128)
@@ -983,7 +1025,8 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
     uint16_t* wt = static_cast<uint16_t*>(workspace);
     if (dense) {
       int wcg = 0, rows = 0;
-      if (LinFn fn = pick_linear(cin, cout, out16, ek, &wcg, &rows)) {
+      const bool use_epi = ep.act != SSC_ACT_NONE || ep.res != nullptr;
+      if (LinFn fn = pick_linear(cin, cout, out16, ek, &wcg, &rows, use_epi)) {
         launch_pack_frag(weight, 1, cin, cout, wcg, 0, wt, s);
         if (const ssc_status st = launch_linear(fn, rows, feats, wt, bias, n, out, ep, s);
             st != SSC_OK)
@@ -992,10 +1035,11 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
       }
     } else {
       int threads = 0, rows = 0, wcg = 0;
-      if (LdsFn fn = pick_lds(cin, cout, out16, ek, &threads, &rows, &wcg)) {
+      const bool fused = epi && epi->gn_partials && epi->batch == 1;
+      if (fused) ep.gn = epi->gn_partials;
+      const bool use_epi = fused || ep.act != SSC_ACT_NONE || ep.res != nullptr;
+      if (LdsFn fn = pick_lds(cin, cout, out16, ek, &threads, &rows, &wcg, use_epi)) {
         launch_pack_frag(weight, kTaps, cin, cout, wcg, 0, wt, s);
-        const bool fused = epi && epi->gn_partials && epi->batch == 1;
-        if (fused) ep.gn = epi->gn_partials;
         if (const ssc_status st = launch_lds(fn, threads, rows, feats, wt, bias, plan, n, out, ep, s);
             st != SSC_OK)
           return st;
@@ -1086,7 +1130,8 @@ extern "C" ssc_status ssc_pack_weights_ex(const void* weight, int32_t taps, int3
   if (flags & ~SSC_PACK_FLIP) return SSC_ERR_ARG;
   if (taps != kTaps) return SSC_ERR_UNSUPPORTED;
   int threads = 0, rows = 0, wcg = 0;
-  if (pick_lds(cin, cout, false, 0, &threads, &rows, &wcg) == nullptr) return SSC_ERR_UNSUPPORTED;
+  if (pick_lds(cin, cout, false, 0, &threads, &rows, &wcg, false) == nullptr)
+    return SSC_ERR_UNSUPPORTED;
   if (!aligned(weight, 16) || !aligned(packed, kAlign)) return SSC_ERR_ARG;
   if (packed_bytes < ssc_packed_weight_bytes(taps, cin, cout)) return SSC_ERR_WORKSPACE;
   launch_pack_frag(weight, kTaps, cin, cout, wcg, (flags & SSC_PACK_FLIP) ? 1 : 0,
@@ -1111,8 +1156,8 @@ extern "C" ssc_status ssc_subm_conv3d_packed_ex(const void* feats, const void* p
     return SSC_ERR_ARG;
   if (n >= (int64_t(1) << 31) || out_dtype == SSC_F16) return SSC_ERR_UNSUPPORTED;
   int threads = 0, rows = 0, wcg = 0;
-  LdsFn fn = pick_lds(cin, cout, out_dtype == SSC_BF16, 0, &threads, &rows, &wcg);
-  if (fn == nullptr) return SSC_ERR_UNSUPPORTED;
+  if (pick_lds(cin, cout, out_dtype == SSC_BF16, 0, &threads, &rows, &wcg, false) == nullptr)
+    return SSC_ERR_UNSUPPORTED;
   if (n > 0 && (feats == nullptr || out == nullptr)) return SSC_ERR_ARG;
   if (!aligned(packed_weight, 16) || !aligned(plan, kAlign) ||
       (n > 0 && (!aligned(feats, 16) || !aligned(out, 16))) || (bias && !aligned(bias, 4)))
@@ -1123,6 +1168,8 @@ extern "C" ssc_status ssc_subm_conv3d_packed_ex(const void* feats, const void* p
   if (n == 0) return gn_after(epilogue, false, out, out_dtype, n, cout, s);
   const bool fused = epilogue && epilogue->gn_partials && epilogue->batch == 1;
   if (fused) ep.gn = epilogue->gn_partials;
+  const bool use_epi = fused || ep.act != SSC_ACT_NONE || ep.res != nullptr;
+  LdsFn fn = pick_lds(cin, cout, out_dtype == SSC_BF16, 0, &threads, &rows, &wcg, use_epi);
   if (const ssc_status st = launch_lds(fn, threads, rows, feats,
                                        static_cast<const uint16_t*>(packed_weight), bias, plan, n,
                                        out, ep, s);

@@ -95,6 +95,118 @@ __global__ __launch_bounds__(256) void k_gn_partials(const T* __restrict__ x, in
   }
 }
 
+// Values of one 16-byte word as floats.
+template <typename T>
+__device__ __forceinline__ void word_to_f32(const uint4& w, float* f) {
+  if constexpr (sizeof(T) == 4) {
+    f[0] = __uint_as_float(w.x);
+    f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z);
+    f[3] = __uint_as_float(w.w);
+  } else {
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t h = static_cast<uint16_t>(d[i >> 1] >> (16 * (i & 1)));
+      f[i] = ld_val(reinterpret_cast<const T*>(&h));
+    }
+  }
+}
+
+// Partial sums with rows of whole 16-byte words (E values each).  Thread (w, rl) = (t %
+// words, t / words) owns word w (channels E*w ...) and rows rl, rl + lanes, ... of the slot,
+// all loaded before any is summed; per-channel sums for 4 batch entries per pass, then, one
+// entry at a time, a fixed-order sum over the row lanes and over each group's channels.
+template <typename T>
+__global__ __launch_bounds__(256) void k_gn_partials_w(const uint4* __restrict__ x, int64_t n,
+                                                       int channels, int groups,
+                                                       const int4* __restrict__ coords,
+                                                       int batch, float4* __restrict__ partials) {
+  constexpr int E = 16 / sizeof(T);
+  constexpr int MAXR = kSlotRows;              // rows per thread at most (words = 1... 256)
+  __shared__ float red[256 * (2 * E + 1)];
+  __shared__ float tot[2 * 1024 + 1];
+  const int t = threadIdx.x;
+  const int64_t slot = blockIdx.x;
+  const int base = blockIdx.y * kPassBatch;
+  const int words = channels / E;
+  const int lanes = 256 / words;
+  const int w = t % words, rl = t / words;
+  const bool active = rl < lanes;
+  float s[kPassBatch][E], q[kPassBatch][E], cnt[kPassBatch];
+#pragma unroll
+  for (int k = 0; k < kPassBatch; ++k) {
+    cnt[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[k][e] = q[k][e] = 0.f;
+  }
+  if (active) {
+    for (int r0 = rl; r0 < MAXR; r0 += 4 * lanes) {
+      uint4 v[4];
+      int kk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // issue up to 4 rows' loads, then sum them
+        const int r = r0 + u * lanes;
+        const int64_t row = slot * kSlotRows + r;
+        const bool ok = r < MAXR && row < n;
+        kk[u] = ok ? (coords ? coords[row].x : 0) - base : -1;
+        v[u] = ok ? x[row * words + w] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float f[E];
+        word_to_f32<T>(v[u], f);
+#pragma unroll
+        for (int k = 0; k < kPassBatch; ++k)
+          if (kk[u] == k) {
+            cnt[k] += 1.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              s[k][e] += f[e];
+              q[k][e] = fmaf(f[e], f[e], q[k][e]);
+            }
+          }
+      }
+    }
+  }
+  const int gs = channels / groups;
+  for (int k = 0; k < kPassBatch && base + k < batch; ++k) {
+    __syncthreads();  // red / tot of the previous entry are consumed
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      red[(2 * e) * 256 + t] = s[k][e];
+      red[(2 * e + 1) * 256 + t] = q[k][e];
+    }
+    red[(2 * E) * 256 + t] = cnt[k];
+    __syncthreads();
+    for (int c = t; c < channels; c += 256) {  // channel c = word c / E, element c % E
+      const int ww = c / E, e = c % E;
+      float S = 0.f, Q = 0.f;
+      for (int l = 0; l < lanes; ++l) {
+        S += red[(2 * e) * 256 + l * words + ww];
+        Q += red[(2 * e + 1) * 256 + l * words + ww];
+      }
+      tot[2 * c] = S;
+      tot[2 * c + 1] = Q;
+    }
+    if (t == 0) {
+      float C = 0.f;
+      for (int l = 0; l < lanes; ++l) C += red[(2 * E) * 256 + l * words];
+      tot[2 * channels] = C;
+    }
+    __syncthreads();
+    for (int g = t; g < groups; g += 256) {
+      float S = 0.f, Q = 0.f;
+      for (int j = 0; j < gs; ++j) {
+        S += tot[2 * (g * gs + j)];
+        Q += tot[2 * (g * gs + j) + 1];
+      }
+      partials[(slot * batch + base + k) * groups + g] =
+          make_float4(tot[2 * channels] * gs, S, Q, 0.f);
+    }
+  }
+}
+
 // Block per (entry, group): thread t adds slots t, t + 256, ... in fp64, then a fixed tree.
 __global__ __launch_bounds__(256) void k_gn_finalize(const float4* __restrict__ partials,
                                                      int64_t slots, int batch_groups, float eps,
@@ -132,13 +244,13 @@ __global__ __launch_bounds__(256) void k_gn_finalize(const float4* __restrict__ 
 
 // Thread per (row, E consecutive channels); E = 16 bytes of elements when rows allow, else 1.
 template <typename T, int E>
-__global__ __launch_bounds__(256) void k_gn_apply(const T* __restrict__ x, int64_t n,
+__global__ __launch_bounds__(256) void k_gn_apply(const T* x, int64_t n,
                                                   int channels, int groups,
                                                   const int4* __restrict__ coords, int batch,
                                                   const float2* __restrict__ stats,
                                                   const float* __restrict__ gamma,
                                                   const float* __restrict__ beta, int act,
-                                                  T* __restrict__ out) {
+                                                  T* out) {
   const int words = channels / E;
   const int gs = channels / groups;
   const int64_t total = n * words;
@@ -173,6 +285,66 @@ __global__ __launch_bounds__(256) void k_gn_apply(const T* __restrict__ x, int64
   }
 }
 
+// Apply with rows of whole 16-byte words: thread (w, rl) owns word w and 4 rows (rl + u *
+// lanes of its block's 4 * lanes); per channel y = x * a + sh with a = rstd * gamma and
+// sh = beta - mean * a, computed once per thread for batch 1 and per row otherwise.
+template <typename T>
+// x and out may be the same buffer (no __restrict__ on either).
+__global__ __launch_bounds__(256) void k_gn_apply_w(const uint4* x, int64_t n,
+                                                    int channels, int groups,
+                                                    const int4* __restrict__ coords, int batch,
+                                                    const float2* __restrict__ stats,
+                                                    const float* __restrict__ gamma,
+                                                    const float* __restrict__ beta, int act,
+                                                    uint4* out) {
+  constexpr int E = 16 / sizeof(T);
+  const int words = channels / E;
+  const int lanes = 256 / words;
+  const int w = threadIdx.x % words, rl = threadIdx.x / words;
+  if (rl >= lanes) return;
+  const int gs = channels / groups;
+  float gm[E], bt[E], a[E], sh[E];
+  int grp[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = w * E + e;
+    gm[e] = gamma ? gamma[c] : 1.f;
+    bt[e] = beta ? beta[c] : 0.f;
+    grp[e] = c / gs;
+  }
+  auto coeffs = [&](int b) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float2 m = stats[static_cast<int64_t>(b) * groups + grp[e]];
+      a[e] = m.y * gm[e];
+      sh[e] = fmaf(-m.x, a[e], bt[e]);
+    }
+  };
+  if (!coords) coeffs(0);
+  const int64_t step = static_cast<int64_t>(gridDim.x) * 4 * lanes;
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * 4 * lanes + rl; r0 < n; r0 += step) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t row = r0 + u * lanes;
+      if (row < n) v[u] = x[row * words + w];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t row = r0 + u * lanes;
+      if (row >= n) break;
+      // batch ids outside [0, batch) are invalid input; clamped so the read stays in bounds
+      if (coords) coeffs(min(max(coords[row].x, 0), batch - 1));
+      float f[E];
+      word_to_f32<T>(v[u], f);
+      alignas(16) T o[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) st_val(&o[e], apply_act(fmaf(f[e], a[e], sh[e]), act));
+      out[row * words + w] = *reinterpret_cast<const uint4*>(o);
+    }
+  }
+}
+
 int64_t gn_slots(int64_t n) {
   const int64_t rows = std::max<int64_t>(n, 1);
   return (rows + kPlanRowAlign - 1) / kPlanRowAlign * (kPlanRowAlign / kSlotRows);
@@ -196,6 +368,18 @@ ssc_status gn_partials_launch(const void* x, int32_t dtype, int64_t n, int32_t c
                   static_cast<unsigned>((batch + kPassBatch - 1) / kPassBatch));
   const int4* c4 = batch > 1 ? reinterpret_cast<const int4*>(coords) : nullptr;
   auto* p4 = reinterpret_cast<float4*>(partials);
+  const int esz = dtype == SSC_F32 ? 4 : 2;
+  const int64_t row_bytes = static_cast<int64_t>(channels) * esz;
+  if (row_bytes % 16 == 0 && row_bytes / 16 <= 256 && channels <= 1024 && aligned(x, 16)) {
+    const auto* x4 = static_cast<const uint4*>(x);
+    if (dtype == SSC_F32)
+      k_gn_partials_w<float><<<grid, 256, 0, s>>>(x4, n, channels, groups, c4, batch, p4);
+    else if (dtype == SSC_BF16)
+      k_gn_partials_w<uint16_t><<<grid, 256, 0, s>>>(x4, n, channels, groups, c4, batch, p4);
+    else
+      k_gn_partials_w<_Float16><<<grid, 256, 0, s>>>(x4, n, channels, groups, c4, batch, p4);
+    return launch_status();
+  }
   if (dtype == SSC_F32)
     k_gn_partials<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), n, channels, groups,
                                               c4, batch, p4);
@@ -254,13 +438,27 @@ extern "C" ssc_status ssc_gn_apply(const void* x, int32_t dtype, int64_t n, int3
   const int esz = dtype == SSC_F32 ? 4 : 2;
   const bool vec = (static_cast<int64_t>(channels) * esz) % 16 == 0 && aligned(x, 16) &&
                    aligned(out, 16);
+  hipStream_t s = as_stream(stream);
+  const int4* c4 = batch > 1 ? reinterpret_cast<const int4*>(coords) : nullptr;
+  const auto* st = reinterpret_cast<const float2*>(stats);
+  if (vec && channels * esz / 16 <= 256) {
+    const int lanes = 256 / (channels * esz / 16);
+    const int64_t blocks = (n + 4 * lanes - 1) / (4 * lanes);
+    const unsigned g = static_cast<unsigned>(std::min<int64_t>(blocks, 65536));
+    const auto* x4 = static_cast<const uint4*>(x);
+    auto* o4 = static_cast<uint4*>(out);
+    if (dtype == SSC_F32)
+      k_gn_apply_w<float><<<g, 256, 0, s>>>(x4, n, channels, groups, c4, batch, st, gamma, beta, act, o4);
+    else if (dtype == SSC_BF16)
+      k_gn_apply_w<uint16_t><<<g, 256, 0, s>>>(x4, n, channels, groups, c4, batch, st, gamma, beta, act, o4);
+    else
+      k_gn_apply_w<_Float16><<<g, 256, 0, s>>>(x4, n, channels, groups, c4, batch, st, gamma, beta, act, o4);
+    return launch_status();
+  }
   const int E = vec ? 16 / esz : 1;
   const int64_t items = n * (channels / E);
   const unsigned grid =
       static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>((items + 255) / 256, 262144)));
-  hipStream_t s = as_stream(stream);
-  const int4* c4 = batch > 1 ? reinterpret_cast<const int4*>(coords) : nullptr;
-  const auto* st = reinterpret_cast<const float2*>(stats);
   if (dtype == SSC_F32) {
     auto* xi = static_cast<const float*>(x);
     auto* xo = static_cast<float*>(out);
