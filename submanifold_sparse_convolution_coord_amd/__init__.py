@@ -246,6 +246,14 @@ class GroupNormPartials:
             raise ValueError("bad group-norm shape")
         self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.n, self.batch, self.groups, self.coords = int(n), int(batch), int(groups), coords
+        # one slot per 128 rows of n rounded up to a multiple of 256 (the header's layout)
+        self.slots = (max(self.n, 1) + 255) // 256 * 2
+
+    def sums(self) -> torch.Tensor:
+        """The partial sums as float32 [slots, batch, groups, 4] = (count, sum, sum of
+        squares, 0); the buffer's tail past them is alignment padding."""
+        used = self.slots * self.batch * self.groups * 16
+        return self.buf[:used].view(torch.float32).view(self.slots, self.batch, self.groups, 4)
 
 
 def _epilogue(n, cout, out_dtype, act, residual, gn):

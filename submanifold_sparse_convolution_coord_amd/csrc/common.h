@@ -67,7 +67,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 // Epilogue activations: relu = max(v, 0), silu = v * sigmoid(v) = v * 1 / (1 + e^-v) (e^-v
 // and the reciprocal from the hardware's approximate exp and rcp, each within about an ulp;
 // at very negative v, e^-v overflows to inf and the product is -0).
+// Contraction is off here: the silu product must round on its own, so that a caller adding to
+// it (a residual) gets the same fp32 value in every kernel variant, whatever it then stores.
 __device__ __forceinline__ float apply_act(float v, int act) {
+#pragma clang fp contract(off)
   if (act == SSC_ACT_RELU) return v > 0.f ? v : 0.f;
   if (act == SSC_ACT_SILU) return v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
   return v;

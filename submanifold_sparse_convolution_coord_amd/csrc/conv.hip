@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -310,8 +311,9 @@ __device__ __forceinline__ void compute_stage(uint32_t act, const char* sA,
 struct Epi {
   const void* res;   // [n, cout] in the output type, rows in coords order, or null
   float* gn;         // float4 slots [npad / 128][groups] (count, sum, sum of squares, 0)
+  int64_t rows;      // n: plan rows at or past it are padding (they sort last)
   int act;           // SSC_ACT_*
-  int gn_groups;
+  int gn_groups;     // with gn: groups of cout / gn_groups channels, a power of two <= 16
 };
 
 // One output value of a residual row (the output's own type).
@@ -321,29 +323,6 @@ __device__ __forceinline__ float load_out(const void* p, int64_t i) {
   const uint16_t h = static_cast<const uint16_t*>(p)[i];
   if constexpr (EK == 0) return bf16_to_f32(h);
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
-}
-
-// Adds the values of one 16-byte piece of a stored row (8 16-bit or 4 fp32 values) to
-// per-channel sums and sums of squares.
-template <bool OUT16, int EK>
-__device__ __forceinline__ void piece_sums(const u32x4_t& v, float* s, float* q) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    if constexpr (OUT16) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint16_t bits = static_cast<uint16_t>(v[d] >> (16 * h));
-        const float f = EK == 0 ? bf16_to_f32(bits)
-                                : static_cast<float>(__builtin_bit_cast(_Float16, bits));
-        s[2 * d + h] += f;
-        q[2 * d + h] = fmaf(f, f, q[2 * d + h]);
-      }
-    } else {
-      const float f = __uint_as_float(v[d]);
-      s[d] += f;
-      q[d] = fmaf(f, f, q[d]);
-    }
-  }
 }
 
 // EPI = false is the plain convolution (bias only); EPI = true adds the activation, the
@@ -418,6 +397,37 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   wait_vm_lgkm0();
   __builtin_amdgcn_s_barrier();
 
+  // Output staging geometry (used by the epilogue below).
+  constexpr int ESZ = OUT16 ? 2 : 4;
+  constexpr int ROWB = COUT * ESZ;
+  constexpr int CHUNKS = ROWB / 16;
+  constexpr int SWM = (CHUNKS < 16 ? CHUNKS : 16) - 1;
+  constexpr int BPP_RAW = C::STAGE_BYTES / (16 * ROWB);
+  // Blocks per pass: the largest power of two that fits (NB is a power of two, so every pass
+  // is full and covers rows [p0*16, (p0+BPP)*16) of the tile exactly).
+  constexpr int BPP = BPP_RAW >= NB ? NB : BPP_RAW >= 8 ? 8 : BPP_RAW >= 4 ? 4 : BPP_RAW >= 2 ? 2 : 1;
+  static_assert(BPP_RAW >= 1 && NB % BPP == 0, "output staging space");
+  // Residual rows: when the tile leaves in one pass and each thread's share is at most 8
+  // pieces, they are loaded now, in flight with the first gather, and held in registers.
+  constexpr int RPT = BPP * 16 * CHUNKS / C::THREADS;
+  constexpr bool RPRE = EPI && BPP == NB && RPT >= 1 && RPT <= 8 &&
+                        BPP * 16 * CHUNKS % C::THREADS == 0;
+  u32x4_t rpre[RPRE ? RPT : 1];
+  if constexpr (RPRE) {
+    if (ep.res) {
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const int idx = threadIdx.x + k * C::THREADS;
+        const int row = idx / CHUNKS, ch = idx % CHUNKS;
+        const int32_t o = sP[row];
+        rpre[k] = o >= 0 ? *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(ep.res) +
+                                                              static_cast<int64_t>(o) * ROWB +
+                                                              ch * 16)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
   f32x4_t acc[C::BPW][C::NCT];
 #pragma unroll
   for (int bl = 0; bl < C::BPW; ++bl)
@@ -479,60 +489,62 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   // Output rows are staged in LDS over the gather buffers and indices, BPP blocks at a time,
   // 16-byte chunks XOR-swizzled by row; then every thread writes 16-byte pieces of whole
   // rows to their original index.
-  constexpr int ESZ = OUT16 ? 2 : 4;
-  constexpr int ROWB = COUT * ESZ;
-  constexpr int CHUNKS = ROWB / 16;
-  constexpr int SWM = (CHUNKS < 16 ? CHUNKS : 16) - 1;
-  constexpr int BPP_RAW = C::STAGE_BYTES / (16 * ROWB);
-  // Blocks per pass: the largest power of two that fits (NB is a power of two, so every pass
-  // is full and covers rows [p0*16, (p0+BPP)*16) of the tile exactly).
-  constexpr int BPP = BPP_RAW >= NB ? NB : BPP_RAW >= 8 ? 8 : BPP_RAW >= 4 ? 4 : BPP_RAW >= 2 ? 2 : 1;
-  static_assert(BPP_RAW >= 1 && NB % BPP == 0, "output staging space");
   char* sOut = smem;
-  // Group-norm partials: every thread always stores the same 16-byte piece of a row (THREADS
-  // is a multiple of CHUNKS), so it keeps per-channel sums of its E channels.
-  constexpr int E = 16 / ESZ;
-  static_assert(C::THREADS % CHUNKS == 0 && 64 % CHUNKS == 0, "piece ownership");
-  float gsum[E], gsq[E], gcnt = 0.f;
+  // Group-norm statistics of the stored values: each lane sums its own columns (NCT of
+  // them) over the rows it stages that hold a site.
+  float csum[C::NCT], csq[C::NCT];
 #pragma unroll
-  for (int j = 0; j < E; ++j) gsum[j] = gsq[j] = 0.f;
+  for (int c = 0; c < C::NCT; ++c) csum[c] = csq[c] = 0.f;
+  const int64_t site_rows = EPI ? ep.rows - row0 : 0;  // rows of this tile holding a site
+  // The epilogue, one copy per combination of its options (activation, residual, group-norm
+  // statistics), chosen once per tile, so that no element pays a branch for them.
+  auto epilogue = [&](auto act_c, auto res_c, auto gn_c) __attribute__((always_inline)) {
+    constexpr int ACT = decltype(act_c)::value;
+    constexpr bool RES = decltype(res_c)::value;
+    constexpr bool GN = decltype(gn_c)::value;
 #pragma unroll
-  for (int p0 = 0; p0 < NB; p0 += BPP) {
-    if constexpr (EPI) {
-      // Residual rows of this pass, fetched as whole 16-byte pieces into the staging tile
-      // (the layout the output takes there); each value is then added by the lane that
-      // stages the output value at the same place.
-      if (ep.res) {
-        constexpr int RPIECES = BPP * 16 * CHUNKS;
+    for (int p0 = 0; p0 < NB; p0 += BPP) {
+      if constexpr (RES) {
+        // Residual rows of this pass as whole 16-byte pieces in the staging tile (the layout
+        // the output takes there); each value is then added by the lane that stages the output
+        // value at the same place.
+        if constexpr (RPRE) {
+#pragma unroll
+          for (int k = 0; k < RPT; ++k) {
+            const int idx = threadIdx.x + k * C::THREADS;
+            const int row = idx / CHUNKS, ch = idx % CHUNKS;
+            *reinterpret_cast<u32x4_t*>(sOut + row * ROWB + ((ch ^ (row & SWM)) << 4)) = rpre[k];
+          }
+        } else {
+          constexpr int RPIECES = BPP * 16 * CHUNKS;
 #pragma unroll 4
-        for (int idx = threadIdx.x; idx < RPIECES; idx += C::THREADS) {
-          const int row = idx / CHUNKS, ch = idx % CHUNKS;
-          const int32_t o = sP[p0 * 16 + row];
-          if (o < 0) continue;
-          *reinterpret_cast<u32x4_t*>(sOut + row * ROWB + ((ch ^ (row & SWM)) << 4)) =
-              *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(ep.res) +
-                                                static_cast<int64_t>(o) * ROWB + ch * 16);
+          for (int idx = threadIdx.x; idx < RPIECES; idx += C::THREADS) {
+            const int row = idx / CHUNKS, ch = idx % CHUNKS;
+            const int32_t o = sP[p0 * 16 + row];
+            if (o < 0) continue;
+            *reinterpret_cast<u32x4_t*>(sOut + row * ROWB + ((ch ^ (row & SWM)) << 4)) =
+                *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(ep.res) +
+                                                  static_cast<int64_t>(o) * ROWB + ch * 16);
+          }
         }
         wait_vm_lgkm0();
         __builtin_amdgcn_s_barrier();
       }
-    }
+      // Stage this pass's outputs (the epilogue's options are compile-time here).
 #pragma unroll
-    for (int bl = 0; bl < C::BPW; ++bl) {
-      const int b = bl * WR + wr;
-      if (b < p0 || b >= p0 + BPP) continue;
+      for (int bl = 0; bl < C::BPW; ++bl) {
+        const int b = bl * WR + wr;
+        if (b < p0 || b >= p0 + BPP) continue;
 #pragma unroll
-      for (int c = 0; c < C::NCT; ++c) {
-        const int col = wc * C::CS + c * 16 + (lane & 15);
+        for (int c = 0; c < C::NCT; ++c) {
+          const int col = wc * C::CS + c * 16 + (lane & 15);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = (b - p0) * 16 + (lane >> 4) * 4 + i;
-          const int byte = col * ESZ;
-          char* dst = sOut + row * ROWB + (((byte >> 4) ^ (row & SWM)) << 4) + (byte & 15);
-          float v = acc[bl][c][i] + bv[c];
-          if constexpr (EPI) {
-            v = apply_act(v, ep.act);
-            if (ep.res) {
+          for (int i = 0; i < 4; ++i) {
+            const int row = (b - p0) * 16 + (lane >> 4) * 4 + i;
+            const int byte = col * ESZ;
+            char* dst = sOut + row * ROWB + (((byte >> 4) ^ (row & SWM)) << 4) + (byte & 15);
+            float v = apply_act(acc[bl][c][i] + bv[c], ACT);
+            if constexpr (RES) {
               if constexpr (!OUT16)
                 v += *reinterpret_cast<const float*>(dst);
               else if constexpr (EK == 0)
@@ -540,97 +552,125 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
               else
                 v += static_cast<float>(*reinterpret_cast<const _Float16*>(dst));
             }
+            float stored = v;
+            if constexpr (OUT16) {
+              const uint16_t h = to16<EK>(v);
+              *reinterpret_cast<uint16_t*>(dst) = h;
+              if constexpr (GN)
+                stored = EK == 0 ? bf16_to_f32(h)
+                                 : static_cast<float>(__builtin_bit_cast(_Float16, h));
+            } else {
+              *reinterpret_cast<float*>(dst) = v;
+            }
+            if constexpr (GN) {
+              if (b * 16 + (lane >> 4) * 4 + i < site_rows) {
+                csum[c] += stored;
+                csq[c] = fmaf(stored, stored, csq[c]);
+              }
+            }
           }
-          if (OUT16)
-            *reinterpret_cast<uint16_t*>(dst) = to16<EK>(v);
-          else
-            *reinterpret_cast<float*>(dst) = v;
         }
       }
-    }
-    wait_vm_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    constexpr int PIECES = BPP * 16 * CHUNKS;
-#pragma unroll 4
-    for (int idx = threadIdx.x; idx < PIECES; idx += C::THREADS) {
-      const int row = idx / CHUNKS, ch = idx % CHUNKS;
-      const int32_t o = sP[p0 * 16 + row];
-      if (o < 0) continue;
-      const u32x4_t v =
-          *reinterpret_cast<const u32x4_t*>(sOut + row * ROWB + ((ch ^ (row & SWM)) << 4));
-      *reinterpret_cast<u32x4_t*>(static_cast<char*>(Y) + static_cast<int64_t>(o) * ROWB +
-                                  ch * 16) = v;
-      if constexpr (EPI) {
-        if (ep.gn) {
-          piece_sums<OUT16, EK>(v, gsum, gsq);
-          gcnt += 1.f;
-        }
-      }
-    }
-    if (p0 + BPP < NB) {
       wait_vm_lgkm0();
       __builtin_amdgcn_s_barrier();
+      constexpr int PIECES = BPP * 16 * CHUNKS;
+#pragma unroll 4
+      for (int idx = threadIdx.x; idx < PIECES; idx += C::THREADS) {
+        const int row = idx / CHUNKS, ch = idx % CHUNKS;
+        const int32_t o = sP[p0 * 16 + row];
+        if (o < 0) continue;
+        const u32x4_t v =
+            *reinterpret_cast<const u32x4_t*>(sOut + row * ROWB + ((ch ^ (row & SWM)) << 4));
+        *reinterpret_cast<u32x4_t*>(static_cast<char*>(Y) + static_cast<int64_t>(o) * ROWB +
+                                    ch * 16) = v;
+      }
+      if (p0 + BPP < NB) {
+        wait_vm_lgkm0();
+        __builtin_amdgcn_s_barrier();
+      }
+    }
+  };
+  using A0 = std::integral_constant<int, SSC_ACT_NONE>;
+  using A1 = std::integral_constant<int, SSC_ACT_RELU>;
+  using A2 = std::integral_constant<int, SSC_ACT_SILU>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if constexpr (!EPI) {
+    epilogue(A0{}, F_{}, F_{});
+  } else {
+    switch (ep.act * 4 + (ep.res ? 2 : 0) + (ep.gn ? 1 : 0)) {
+      case 0: epilogue(A0{}, F_{}, F_{}); break;
+      case 1: epilogue(A0{}, F_{}, T_{}); break;
+      case 2: epilogue(A0{}, T_{}, F_{}); break;
+      case 3: epilogue(A0{}, T_{}, T_{}); break;
+      case 4: epilogue(A1{}, F_{}, F_{}); break;
+      case 5: epilogue(A1{}, F_{}, T_{}); break;
+      case 6: epilogue(A1{}, T_{}, F_{}); break;
+      case 7: epilogue(A1{}, T_{}, T_{}); break;
+      case 8: epilogue(A2{}, F_{}, F_{}); break;
+      case 9: epilogue(A2{}, F_{}, T_{}); break;
+      case 10: epilogue(A2{}, T_{}, F_{}); break;
+      default: epilogue(A2{}, T_{}, T_{}); break;
     }
   }
   if (EPI && ep.gn) {
-    // Fixed-order reduction: lanes that own the same piece (lane bits above CHUNKS) by a
-    // butterfly (every lane ends with the same sums), then the waves in order, then the
-    // channels of each group in order.  One or two 128-row slots per tile.
+    // Fixed-order reduction, every step a butterfly (all lanes end with the same sums): over
+    // the four row quads of a column (lane bits 4, 5), then over the gs columns of a group
+    // (lane bits below log2 gs; a group never leaves a 16-column tile).  The tile's count is
+    // its rows that hold a site.  One or two 128-row slots per tile.
+    const int groups = ep.gn_groups, gs = COUT / groups;
 #pragma unroll
-    for (int m = CHUNKS; m < 64; m <<= 1) {
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        gsum[j] += __shfl_xor(gsum[j], m, 64);
-        gsq[j] += __shfl_xor(gsq[j], m, 64);
+    for (int c = 0; c < C::NCT; ++c) {
+      csum[c] += __shfl_xor(csum[c], 16, 64);
+      csq[c] += __shfl_xor(csq[c], 16, 64);
+      csum[c] += __shfl_xor(csum[c], 32, 64);
+      csq[c] += __shfl_xor(csq[c], 32, 64);
+      for (int m = 1; m < gs; m <<= 1) {
+        csum[c] += __shfl_xor(csum[c], m, 64);
+        csq[c] += __shfl_xor(csq[c], m, 64);
       }
-      gcnt += __shfl_xor(gcnt, m, 64);
     }
-    constexpr int REC = 2 * E + 1;
-    constexpr int GN_OFF = BPP * 16 * ROWB;
-    constexpr int GN_BYTES = (C::WAVES * CHUNKS * REC + 2 * COUT + 1) * 4;
-    static_assert(GN_OFF + GN_BYTES <= C::OFF_P, "group-norm reduction space");
-    float* red = reinterpret_cast<float*>(smem + GN_OFF);
-    float* tot = red + C::WAVES * CHUNKS * REC;
-    if (lane < CHUNKS) {
-      float* r = red + (wave * CHUNKS + lane) * REC;
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        r[j] = gsum[j];
-        r[E + j] = gsq[j];
-      }
-      r[2 * E] = gcnt;
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); the row stores may still be in flight
-    __builtin_amdgcn_s_barrier();
-    if (threadIdx.x < COUT) {
-      const int c = threadIdx.x, ch = c / E, j = c % E;
-      float S = 0.f, Q = 0.f;
-      for (int w = 0; w < C::WAVES; ++w) {
-        S += red[(w * CHUNKS + ch) * REC + j];
-        Q += red[(w * CHUNKS + ch) * REC + E + j];
-      }
-      tot[2 * c] = S;
-      tot[2 * c + 1] = Q;
-    }
-    if (threadIdx.x == 0) {
-      float cnt = 0.f;
-      for (int w = 0; w < C::WAVES; ++w) cnt += red[(w * CHUNKS) * REC + 2 * E];
-      tot[2 * COUT] = cnt;
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
+    const float cnt = static_cast<float>(
+        site_rows < 0 ? 0 : site_rows > NB * 16 ? NB * 16 : site_rows) * static_cast<float>(gs);
     constexpr int SLOTS = NB * 16 / 128;
-    const int groups = ep.gn_groups, gsz = COUT / groups;
     float4* part = reinterpret_cast<float4*>(ep.gn) + tile * SLOTS * groups;
-    for (int g = threadIdx.x; g < groups; g += C::THREADS) {
-      float S = 0.f, Q = 0.f;
-      for (int k = 0; k < gsz; ++k) {
-        S += tot[2 * (g * gsz + k)];
-        Q += tot[2 * (g * gsz + k) + 1];
-      }
-      part[g] = make_float4(tot[2 * COUT] * gsz, S, Q, 0.f);
+    const bool leader = lane < 16 && (lane & (gs - 1)) == 0;
+    if constexpr (WR == 1) {
+      if (leader) {
 #pragma unroll
-      for (int sl = 1; sl < SLOTS; ++sl) part[sl * groups + g] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int c = 0; c < C::NCT; ++c) {
+          const int g = (wc * C::CS + c * 16 + lane) / gs;
+          part[g] = make_float4(cnt, csum[c], csq[c], 0.f);
+#pragma unroll
+          for (int sl = 1; sl < SLOTS; ++sl)
+            part[sl * groups + g] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    } else {
+      // Waves that share columns (WR of them) add their sums in wave-row order.
+      constexpr int GN_OFF = BPP * 16 * ROWB;
+      static_assert(GN_OFF + WR * COUT * 2 * 4 <= C::OFF_P, "group-norm reduction space");
+      float* red = reinterpret_cast<float*>(smem + GN_OFF);
+      if (leader) {
+#pragma unroll
+        for (int c = 0; c < C::NCT; ++c) {
+          const int col = wc * C::CS + c * 16 + lane;
+          red[(wr * COUT + col) * 2] = csum[c];
+          red[(wr * COUT + col) * 2 + 1] = csq[c];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); the row stores may still be in flight
+      __builtin_amdgcn_s_barrier();
+      for (int g = threadIdx.x; g < groups; g += C::THREADS) {
+        float S = 0.f, Q = 0.f;
+        for (int r = 0; r < WR; ++r) {
+          S += red[(r * COUT + g * gs) * 2];
+          Q += red[(r * COUT + g * gs) * 2 + 1];
+        }
+        part[g] = make_float4(cnt, S, Q, 0.f);
+#pragma unroll
+        for (int sl = 1; sl < SLOTS; ++sl) part[sl * groups + g] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
   }
 }
@@ -957,7 +997,7 @@ ssc_status launch_lds(LdsFn fn, int threads, int rows_per_tile, const void* feat
 // Host checks of an epilogue; fills the kernel-side arguments (gn left null: the caller
 // decides whether the kernel sums the statistics itself).
 ssc_status check_epilogue(const ssc_epilogue* e, int64_t n, int cout, Epi* ep) {
-  *ep = Epi{nullptr, nullptr, SSC_ACT_NONE, 0};
+  *ep = Epi{nullptr, nullptr, n, SSC_ACT_NONE, 0};
   if (e == nullptr) return SSC_OK;
   if (e->act < SSC_ACT_NONE || e->act > SSC_ACT_SILU || e->reserved != 0) return SSC_ERR_ARG;
   if (e->residual && !aligned(e->residual, 16)) return SSC_ERR_ARG;
@@ -974,6 +1014,14 @@ ssc_status check_epilogue(const ssc_epilogue* e, int64_t n, int cout, Epi* ep) {
   ep->res = e->residual;
   ep->gn_groups = e->gn_groups;
   return SSC_OK;
+}
+
+// Whether the k=3 kernel sums the group-norm statistics in its epilogue: one batch entry and
+// groups of a power-of-two number of channels up to 16 (a group inside one 16-column tile).
+bool gn_fusable(const ssc_epilogue* e, int cout) {
+  if (e == nullptr || e->gn_partials == nullptr || e->batch != 1) return false;
+  const int gs = cout / e->gn_groups;
+  return gs <= 16 && (gs & (gs - 1)) == 0;
 }
 
 // The group-norm partial sums of out, when the kernel did not sum them in its epilogue.
@@ -1035,7 +1083,7 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
       }
     } else {
       int threads = 0, rows = 0, wcg = 0;
-      const bool fused = epi && epi->gn_partials && epi->batch == 1;
+      const bool fused = gn_fusable(epi, cout);
       if (fused) ep.gn = epi->gn_partials;
       const bool use_epi = fused || ep.act != SSC_ACT_NONE || ep.res != nullptr;
       if (LdsFn fn = pick_lds(cin, cout, out16, ek, &threads, &rows, &wcg, use_epi)) {
@@ -1166,7 +1214,7 @@ extern "C" ssc_status ssc_subm_conv3d_packed_ex(const void* feats, const void* p
   if (const ssc_status st = check_epilogue(epilogue, n, cout, &ep); st != SSC_OK) return st;
   hipStream_t s = as_stream(stream);
   if (n == 0) return gn_after(epilogue, false, out, out_dtype, n, cout, s);
-  const bool fused = epilogue && epilogue->gn_partials && epilogue->batch == 1;
+  const bool fused = gn_fusable(epilogue, cout);
   if (fused) ep.gn = epilogue->gn_partials;
   const bool use_epi = fused || ep.act != SSC_ACT_NONE || ep.res != nullptr;
   LdsFn fn = pick_lds(cin, cout, out_dtype == SSC_BF16, 0, &threads, &rows, &wcg, use_epi);

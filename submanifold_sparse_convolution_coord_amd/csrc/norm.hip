@@ -25,6 +25,7 @@ namespace {
 
 constexpr int kSlotRows = 128;       // rows per partial-sum slot
 constexpr int kPassBatch = 4;        // batch entries one partials pass accumulates
+constexpr int kApplyRows = 8;        // rows each apply thread handles per step
 
 __device__ __forceinline__ float ld_val(const float* p) { return *p; }
 __device__ __forceinline__ float ld_val(const uint16_t* p) { return bf16_to_f32(*p); }
@@ -117,20 +118,24 @@ __device__ __forceinline__ void word_to_f32(const uint4& w, float* f) {
 // words, t / words) owns word w (channels E*w ...) and rows rl, rl + lanes, ... of the slot,
 // all loaded before any is summed; per-channel sums for 4 batch entries per pass, then, one
 // entry at a time, a fixed-order sum over the row lanes and over each group's channels.
+// A block covers spb slots (spb = max(1, 16 / words), so that every thread has about 8 rows)
+// and writes their sum into the first of them and zeros into the rest: finalize adds all.
 template <typename T>
 __global__ __launch_bounds__(256) void k_gn_partials_w(const uint4* __restrict__ x, int64_t n,
                                                        int channels, int groups,
                                                        const int4* __restrict__ coords,
-                                                       int batch, float4* __restrict__ partials) {
+                                                       int batch, int64_t slots,
+                                                       float4* __restrict__ partials) {
   constexpr int E = 16 / sizeof(T);
-  constexpr int MAXR = kSlotRows;              // rows per thread at most (words = 1... 256)
   __shared__ float red[256 * (2 * E + 1)];
   __shared__ float tot[2 * 1024 + 1];
   const int t = threadIdx.x;
-  const int64_t slot = blockIdx.x;
   const int base = blockIdx.y * kPassBatch;
   const int words = channels / E;
   const int lanes = 256 / words;
+  const int spb = words >= 16 ? 1 : 16 / words;
+  const int64_t slot = static_cast<int64_t>(blockIdx.x) * spb;
+  const int MAXR = spb * kSlotRows;            // rows of this block
   const int w = t % words, rl = t / words;
   const bool active = rl < lanes;
   float s[kPassBatch][E], q[kPassBatch][E], cnt[kPassBatch];
@@ -203,6 +208,8 @@ __global__ __launch_bounds__(256) void k_gn_partials_w(const uint4* __restrict__
       }
       partials[(slot * batch + base + k) * groups + g] =
           make_float4(tot[2 * channels] * gs, S, Q, 0.f);
+      for (int j = 1; j < spb && slot + j < slots; ++j)
+        partials[((slot + j) * batch + base + k) * groups + g] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
 }
@@ -285,8 +292,8 @@ __global__ __launch_bounds__(256) void k_gn_apply(const T* x, int64_t n,
   }
 }
 
-// Apply with rows of whole 16-byte words: thread (w, rl) owns word w and 4 rows (rl + u *
-// lanes of its block's 4 * lanes); per channel y = x * a + sh with a = rstd * gamma and
+// Apply with rows of whole 16-byte words: thread (w, rl) owns word w and 8 rows (rl + u *
+// lanes of its block's 8 * lanes); per channel y = x * a + sh with a = rstd * gamma and
 // sh = beta - mean * a, computed once per thread for batch 1 and per row otherwise.
 template <typename T>
 // x and out may be the same buffer (no __restrict__ on either).
@@ -321,16 +328,17 @@ __global__ __launch_bounds__(256) void k_gn_apply_w(const uint4* x, int64_t n,
     }
   };
   if (!coords) coeffs(0);
-  const int64_t step = static_cast<int64_t>(gridDim.x) * 4 * lanes;
-  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * 4 * lanes + rl; r0 < n; r0 += step) {
-    uint4 v[4];
+  const int64_t step = static_cast<int64_t>(gridDim.x) * kApplyRows * lanes;
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * kApplyRows * lanes + rl; r0 < n;
+       r0 += step) {
+    uint4 v[kApplyRows];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kApplyRows; ++u) {
       const int64_t row = r0 + u * lanes;
       if (row < n) v[u] = x[row * words + w];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kApplyRows; ++u) {
       const int64_t row = r0 + u * lanes;
       if (row >= n) break;
       // batch ids outside [0, batch) are invalid input; clamped so the read stays in bounds
@@ -372,12 +380,15 @@ ssc_status gn_partials_launch(const void* x, int32_t dtype, int64_t n, int32_t c
   const int64_t row_bytes = static_cast<int64_t>(channels) * esz;
   if (row_bytes % 16 == 0 && row_bytes / 16 <= 256 && channels <= 1024 && aligned(x, 16)) {
     const auto* x4 = static_cast<const uint4*>(x);
+    const int64_t words = row_bytes / 16, slots = gn_slots(n);
+    const int64_t spb = words >= 16 ? 1 : 16 / words;
+    const dim3 gw(static_cast<unsigned>((slots + spb - 1) / spb), grid.y);
     if (dtype == SSC_F32)
-      k_gn_partials_w<float><<<grid, 256, 0, s>>>(x4, n, channels, groups, c4, batch, p4);
+      k_gn_partials_w<float><<<gw, 256, 0, s>>>(x4, n, channels, groups, c4, batch, slots, p4);
     else if (dtype == SSC_BF16)
-      k_gn_partials_w<uint16_t><<<grid, 256, 0, s>>>(x4, n, channels, groups, c4, batch, p4);
+      k_gn_partials_w<uint16_t><<<gw, 256, 0, s>>>(x4, n, channels, groups, c4, batch, slots, p4);
     else
-      k_gn_partials_w<_Float16><<<grid, 256, 0, s>>>(x4, n, channels, groups, c4, batch, p4);
+      k_gn_partials_w<_Float16><<<gw, 256, 0, s>>>(x4, n, channels, groups, c4, batch, slots, p4);
     return launch_status();
   }
   if (dtype == SSC_F32)
@@ -443,7 +454,7 @@ extern "C" ssc_status ssc_gn_apply(const void* x, int32_t dtype, int64_t n, int3
   const auto* st = reinterpret_cast<const float2*>(stats);
   if (vec && channels * esz / 16 <= 256) {
     const int lanes = 256 / (channels * esz / 16);
-    const int64_t blocks = (n + 4 * lanes - 1) / (4 * lanes);
+    const int64_t blocks = (n + kApplyRows * lanes - 1) / (kApplyRows * lanes);
     const unsigned g = static_cast<unsigned>(std::min<int64_t>(blocks, 65536));
     const auto* x4 = static_cast<const uint4*>(x);
     auto* o4 = static_cast<uint4*>(out);
