@@ -268,6 +268,73 @@ def time_block(ssc, torch, coords, x, plan, batch, dev, reps: int = 50) -> dict:
                 "residual": round(us["conv2_residual"] - us["conv_plain"], 2)}}
 
 
+def time_ablations(ssc, torch, x, wt, bias, plan, nbr, dev, reps: int = 20) -> dict:
+    """The pages' own designs on the same layer (comparison only): the compacted kernel with
+    tap compaction off (every block walks all 27 taps), the dense 27-tap GEMM (gather of the
+    [N, 27*Cin] operand + a library GEMM, bf16 out) and the per-offset gather -> GEMM ->
+    scatter-add (81 launches, replayed from a HIP graph; every replay is checked against the
+    eager result).  Device time per layer."""
+    from submanifold_sparse_convolution_coord_amd import ablations
+    n, cin = x.shape
+    cout = wt.shape[2]
+
+    def t(fn, k=reps):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(k):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k * 1e3
+
+    packed = ssc.pack_weights(wt)
+    y32 = torch.empty((n, cout), dtype=torch.float32, device=dev)
+    compact_us = t(lambda: ssc.subm_conv3d_packed(x, packed, bias, plan, out=y32))
+    ref = y32.clone()
+    dplan = ablations.dense_taps_plan(plan)
+    dense_taps_us = t(lambda: ssc.subm_conv3d_packed(x, packed, bias, dplan, out=y32))
+    same = bool(torch.equal(ref.view(torch.int32), y32.view(torch.int32)))
+    res = {"compacted_us": round(compact_us, 2),
+           "no_compaction_us": round(dense_taps_us, 2), "no_compaction_identical": same}
+    operand = n * 27 * cin * x.element_size()
+    if operand <= (8 << 30):
+        dg = ablations.DenseGemm(nbr, wt)
+        ybf = torch.empty((n, cout), dtype=wt.dtype, device=dev)
+        g_us = t(lambda: dg.gather(x))
+        m_us = t(lambda: dg.gemm(out=ybf))
+        res["dense_gemm"] = {"gather_us": round(g_us, 2), "gemm_us": round(m_us, 2),
+                             "total_us": round(g_us + m_us, 2),
+                             "operand_gb": round(operand / 1e9, 3),
+                             "gather_gbs": round(operand / g_us / 1e3, 1)}
+    po = ablations.PerOffset(nbr, wt)
+    out = torch.empty((n, cout), dtype=torch.float32, device=dev)
+    eager = po(x, bias, out=out).clone()
+    torch.cuda.synchronize()
+    launches = 3 * sum(1 for r in po.rows_out if r.numel() > 0)
+    try:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            po(x, bias, out=out)
+        replays_ok = True
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            replays_ok &= bool(torch.equal(out, eager))
+            out.fill_(0.0)   # eager work between replays
+            torch.cuda.synchronize()
+        po_us = t(graph.replay)
+        res["per_offset"] = {"us": round(po_us, 2), "launches": launches,
+                             "graph_replays_match_eager": replays_ok}
+    except RuntimeError as e:  # capture refused: time the eager loop (host enqueue included)
+        torch.cuda.synchronize()
+        po_us = t(lambda: po(x, bias, out=out))
+        res["per_offset"] = {"us_eager": round(po_us, 2), "launches": launches,
+                             "graph": f"not captured: {e}"[:200]}
+    return res
+
+
 def cpu_baseline(w, m_nbr) -> dict:
     """The CPU oracle as it stands (fp64 dictionary + per-voxel loop), warm: map prebuilt,
     conv over every site of the same workload, repeated for at least a second of wall time;
@@ -439,6 +506,10 @@ def main():
     log(f"[bench] conv kernel, caches flushed: median {flushed['median_us']} us")
 
     resample = time_resample(ssc, torch, coords, x, w, dev)
+    abl = None
+    if x.dtype == torch.bfloat16 and use_packed:
+        abl = time_ablations(ssc, torch, x, wt, bias, plan, nbr, dev)
+        log(f"[bench] ablations {abl}")
     block = None
     if x.dtype == torch.bfloat16 and cin in (32, 64, 128):
         block = time_block(ssc, torch, coords, x, plan, w.batch, dev)
@@ -488,6 +559,7 @@ def main():
         "conv_flushed": flushed,
         "resample": resample,
         "res_block": block,
+        "ablations": abl,
         "cold_index_plan_ms": round(float(np.median(cold)), 4),
         # Algorithmic bytes of the cold path: the index reads the coordinates (16 B per site)
         # and writes the map (27 x 4 B); the plan reads the map and writes the row ids, block

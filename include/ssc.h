@@ -333,6 +333,29 @@ ssc_status ssc_subdivide2(const int32_t* coords, int64_t n, const int32_t* grid,
                           const void* feats, int32_t dtype, int32_t channels,
                           int32_t* out_coords, void* out_feats, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Building blocks of the pages' own convolution designs, for measuring the kernels above
+ * against them (the matrix products in between are plain library GEMMs, not part of this
+ * library).
+ * ------------------------------------------------------------------------------------- */
+
+/* The dense operand of the one-matmul design (LATO.2 MLX port page, "Fleet benchmark"
+ * version history: the 27 neighbour rows of every site side by side, one dense matmul):
+ *   out[i][t][c] = feats[nbr[i][t]][c], or 0 where nbr[i][t] = -1.
+ *   feats [n, channels] dtype (rows a multiple of 16 bytes, else SSC_ERR_UNSUPPORTED),
+ *   nbr [n, 27] int32 from ssc_build_index, out [n, 27 * channels] dtype, 16-byte aligned. */
+ssc_status ssc_gather_taps(const void* feats, int32_t dtype, int64_t n, int32_t channels,
+                           const int32_t* nbr, void* out, void* stream);
+
+/* The scatter of the per-offset design (trellis-mac article, gather-scatter flowchart: per
+ * offset, gather the rows that have the neighbour, multiply by W[t], scatter-add):
+ *   out[idx[k]][c] += part[k][c] for k < p, c < channels (channels a multiple of 4).
+ *   part [p, channels] SSC_F32 or SSC_BF16, idx [p] int32 rows of out (distinct within a
+ *   call; rows outside [0, n) are skipped), out [n, channels] fp32, 16-byte aligned. */
+ssc_status ssc_scatter_add_rows(const void* part, int32_t part_dtype, const int32_t* idx,
+                                int64_t p, int32_t channels, float* out, int64_t n,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -102,6 +102,8 @@ def load_library():
         "ssc_gn_partials": ([p, i32, i64, i32, p, i32, i32, p, sz, p], ctypes.c_int),
         "ssc_gn_finalize": ([p, i64, i32, i32, ctypes.c_float, p, p], ctypes.c_int),
         "ssc_gn_apply": ([p, i32, i64, i32, p, i32, i32, p, p, p, i32, p, p], ctypes.c_int),
+        "ssc_gather_taps": ([p, i32, i64, i32, p, p, p], ctypes.c_int),
+        "ssc_scatter_add_rows": ([p, i32, p, i64, i32, p, i64, p], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
