@@ -108,6 +108,43 @@ def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_m
     print(json.dumps(d))
 
 
+def counter_table(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mb) -> str:
+    """Markdown table of every kernel's HBM bytes per dispatch (median FETCH_SIZE and
+    WRITE_SIZE, scaled by the copy calibration), from rocprofv3 --pmc csv directories."""
+    import csv
+    import glob
+    import re
+
+    def rows(d, counter):
+        per = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r.get("Counter_Name") == counter:
+                    name = r["Kernel_Name"].replace("void ", "").replace(
+                        "ssc::(anonymous namespace)::", "")
+                    m = re.match(r"([A-Za-z_0-9:]+(<[^()]*>)?)", name)
+                    per.setdefault(m.group(1) if m else name[:60], []).append(
+                        float(r["Counter_Value"]))
+        return per
+
+    cf = rows(cal_fetch_dir, "FETCH_SIZE")
+    cw = rows(cal_write_dir, "WRITE_SIZE")
+    copy_f = [v for k, vs in cf.items() if "copy" in k for v in vs]
+    copy_w = [v for k, vs in cw.items() if "copy" in k for v in vs]
+    known = cal_mb * 1024.0
+    fs, ws = known / float(np.median(copy_f)), known / float(np.median(copy_w))
+    f, w = rows(fetch_dir, "FETCH_SIZE"), rows(write_dir, "WRITE_SIZE")
+    out = [f"FETCH_SIZE scale {fs:.3f}, WRITE_SIZE scale {ws:.3f} (plain {cal_mb} MiB copy)", "",
+           "| kernel | dispatches | read MB | write MB | total MB |", "|---|---|---|---|---|"]
+    for k in sorted(f, key=lambda k: -float(np.median(f[k]))):
+        if k not in w:
+            continue
+        rd = float(np.median(f[k])) * 1024 * fs / 1e6
+        wr = float(np.median(w[k])) * 1024 * ws / 1e6
+        out.append(f"| {k[:90]} | {len(f[k])} | {rd:.1f} | {wr:.1f} | {rd + wr:.1f} |")
+    return "\n".join(out)
+
+
 def time_resample(ssc, torch, coords, x, w, dev, reps: int = 20) -> dict:
     """Device time of the downsample (max), its upsample, the spatial-to-channel shuffle and the
     subdivide on the workload's sites and features, called through the C ABI on preallocated
@@ -371,7 +408,14 @@ def main():
     ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR",
                     "CAL_FETCH_DIR", "CAL_WRITE_DIR", "CAL_MIB"),
                     help="write profiles/conv_iid128_counters.json from rocprofv3 --pmc output")
+    ap.add_argument("--counter-table", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR",
+                    "CAL_FETCH_DIR", "CAL_WRITE_DIR", "CAL_MIB"),
+                    help="print every kernel's HBM bytes per dispatch from rocprofv3 --pmc output")
     args = ap.parse_args()
+    if args.counter_table:
+        a = args.counter_table
+        print(counter_table(a[0], a[1], a[2], a[3], int(a[4])))
+        return
     if args.summarize_counters:
         a = args.summarize_counters
         summarize_counters(a[0], a[1], a[2], a[3], int(a[4]),
