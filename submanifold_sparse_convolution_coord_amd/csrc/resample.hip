@@ -265,55 +265,78 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
 
 // Spatial-to-channel in words of 16 bytes (rows a multiple of 16 bytes): thread per (parent,
 // word of E = 16 / ESZ channels).  The children's words land in 8 slot registers (zero for an
-// absent child) and are transposed in registers, so the thread writes the 8 * E values of its
-// channels, 128 contiguous bytes at columns c0*8 .. (c0+E)*8 - 1, as 8 words.
+// absent child) and are transposed in registers into the 8 output words of the thread's E
+// channels (columns c0*8 .. (c0+E)*8 - 1).  A block's 256 items own 256 * 8 consecutive
+// output words, so the words go through LDS (slot e of thread t at t*8 + (e ^ (t & 7)), which
+// spreads 8 neighbouring threads over distinct banks) and leave as consecutive 16-byte
+// stores.  Every thread of a block runs the same number of rounds (the barriers need it).
 template <int ESZ>
-__global__ void k_space2channel_w(const uint4* __restrict__ feats, int32_t words,
-                                  const int4* __restrict__ coords,
-                                  const uint32_t* __restrict__ sorted_sites,
-                                  const int32_t* __restrict__ heads,
-                                  const int64_t* __restrict__ result, int64_t n,
-                                  uint4* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_space2channel_w(const uint4* __restrict__ feats,
+                                                         int32_t words,
+                                                         const int4* __restrict__ coords,
+                                                         const uint32_t* __restrict__ sorted_sites,
+                                                         const int32_t* __restrict__ heads,
+                                                         const int64_t* __restrict__ result,
+                                                         int64_t n, uint4* __restrict__ out) {
+  __shared__ uint4 stage[256 * 8];
+  const int t = threadIdx.x;
   const int64_t m = result[0];
   const int64_t total = m * words;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
-       g += stride) {
-    const int64_t p = g / words;
-    const int w = static_cast<int>(g - p * words);
-    const int64_t r0 = heads[p];
-    const int64_t r1 = p + 1 < m ? heads[p + 1] : n;
-    uint4 v[8];
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * 256; base < total;
+       base += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t g = base + t;
+    uint4 o[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = make_uint4(0u, 0u, 0u, 0u);
-    for (int64_t r = r0; r < r1; ++r) {
-      const int64_t i = sorted_sites[r];
-      const int4 q = coords[i];
-      const int k = ((q.y & 1) << 2) | ((q.z & 1) << 1) | (q.w & 1);
-      const uint4 x = feats[i * words + w];
+    for (int e = 0; e < 8; ++e) o[e] = make_uint4(0u, 0u, 0u, 0u);
+    if (g < total) {
+      const int64_t p = g / words;
+      const int w = static_cast<int>(g - p * words);
+      const int64_t r0 = heads[p];
+      const int64_t r1 = p + 1 < m ? heads[p + 1] : n;
+      uint4 v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j == k) v[j] = x;
-    }
-    uint4* o = out + g * 8;
-    if constexpr (ESZ == 2) {
+      for (int k = 0; k < 8; ++k) v[k] = make_uint4(0u, 0u, 0u, 0u);
+      for (int64_t r = r0; r < r1; ++r) {
+        const int64_t i = sorted_sites[r];
+        const int4 q = coords[i];
+        const int k = ((q.y & 1) << 2) | ((q.z & 1) << 1) | (q.w & 1);
+        const uint4 x = feats[i * words + w];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {  // channel c0 + e: its 8 slots make one word
-        const int sh = (e & 1) * 16;
-        uint32_t d[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          d[h] = ((dword_of(v[2 * h], e >> 1) >> sh) & 0xffffu) |
-                 (((dword_of(v[2 * h + 1], e >> 1) >> sh) & 0xffffu) << 16);
-        o[e] = make_uint4(d[0], d[1], d[2], d[3]);
+        for (int j = 0; j < 8; ++j)
+          if (j == k) v[j] = x;
       }
-    } else {
+      if constexpr (ESZ == 2) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {  // channel c0 + e: slots 0-3, then 4-7
-        o[2 * e] = make_uint4(dword_of(v[0], e), dword_of(v[1], e), dword_of(v[2], e),
-                              dword_of(v[3], e));
-        o[2 * e + 1] = make_uint4(dword_of(v[4], e), dword_of(v[5], e), dword_of(v[6], e),
-                                  dword_of(v[7], e));
+        for (int e = 0; e < 8; ++e) {  // channel c0 + e: its 8 slots make one word
+          const int sh = (e & 1) * 16;
+          uint32_t d[4];
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            d[h] = ((dword_of(v[2 * h], e >> 1) >> sh) & 0xffffu) |
+                   (((dword_of(v[2 * h + 1], e >> 1) >> sh) & 0xffffu) << 16);
+          o[e] = make_uint4(d[0], d[1], d[2], d[3]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {  // channel c0 + e: slots 0-3, then 4-7
+          o[2 * e] = make_uint4(dword_of(v[0], e), dword_of(v[1], e), dword_of(v[2], e),
+                                dword_of(v[3], e));
+          o[2 * e + 1] = make_uint4(dword_of(v[4], e), dword_of(v[5], e), dword_of(v[6], e),
+                                    dword_of(v[7], e));
+        }
+      }
+    }
+    __syncthreads();  // the previous round's words have left the stage
+#pragma unroll
+    for (int e = 0; e < 8; ++e) stage[t * 8 + (e ^ (t & 7))] = o[e];
+    __syncthreads();
+    const int64_t words_here = (total - base < 256 ? total - base : 256) * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = k * 256 + t;  // output word j of the block's run
+      if (j < words_here) {
+        const int src = j >> 3, e = j & 7;
+        out[base * 8 + j] = stage[src * 8 + (e ^ (src & 7))];
       }
     }
   }

@@ -213,24 +213,26 @@ def test_conv_group_norm_statistics(cin, cout, odt):
     assert torch.equal(p2.sums(), ssc.gn_partials(y2, 3, 32, c2).sums())
 
 
-@pytest.mark.parametrize("cin,cout,groups,n_sites", [
-    (64, 128, 4, 700),     # 32 channels a group: statistics pass after the kernel
-    (128, 128, 32, 100),   # second tile all padding
-    (32, 16, 8, 300),      # several wave rows share columns
-    (64, 32, 32, 257),     # one channel a group; ragged last tile
+@pytest.mark.parametrize("cin,cout,groups,n_sites,dtype", [
+    (64, 128, 4, 700, torch.bfloat16),     # 32 channels a group: statistics pass after
+    (128, 128, 32, 100, torch.bfloat16),   # second tile all padding
+    (32, 16, 8, 300, torch.bfloat16),      # several wave rows share columns
+    (64, 32, 32, 257, torch.bfloat16),     # one channel a group; ragged last tile
+    (128, 64, 16, 900, torch.float16),     # fp16 stores summed in the kernel
+    (32, 32, 8, 600, torch.float16),
 ])
-def test_conv_group_norm_statistics_shapes(cin, cout, groups, n_sites):
-    say(f"[gn] conv statistics {cin}->{cout} groups={groups} n={n_sites}")
+def test_conv_group_norm_statistics_shapes(cin, cout, groups, n_sites, dtype):
+    say(f"[gn] conv statistics {cin}->{cout} groups={groups} n={n_sites} {dtype}")
     rng = np.random.default_rng(n_sites)
     coords = workloads.random_sites(rng, 1, (12, 12, 12), n_sites)
     n = len(coords)
-    x = torch.from_numpy(rng.standard_normal((n, cin), dtype=np.float32)).bfloat16().to(DEV)
+    x = torch.from_numpy(rng.standard_normal((n, cin), dtype=np.float32)).to(dtype).to(DEV)
     w = (torch.from_numpy(rng.standard_normal((27, cin, cout), dtype=np.float32)) /
-         np.sqrt(27 * cin)).bfloat16().to(DEV)
+         np.sqrt(27 * cin)).to(dtype).to(DEV)
     b = torch.from_numpy(rng.standard_normal(cout, dtype=np.float32)).to(DEV)
     idx = index(coords, 1, (12, 12, 12))
     parts = ssc.GroupNormPartials(n, 1, groups, DEV)
-    y = ssc.subm_conv3d(x, w, b, idx.plan, torch.bfloat16, act="relu", gn=parts)
+    y = ssc.subm_conv3d(x, w, b, idx.plan, dtype, act="relu", gn=parts)
     fused = ssc.gn_finalize(parts).cpu().numpy().astype(np.float64)
     mean, var = blocks.group_stats(f64(y), np.zeros((n, 4), np.int32), 1, groups)
     assert np.abs(fused[..., 0] - mean).max() <= 1e-5 * np.sqrt(var.max())
