@@ -52,12 +52,10 @@ inline PlanLayout plan_layout(int64_t n) {
   return L;
 }
 
-// Round-to-nearest-even fp32 -> bf16 (ties to even on the upper 16 bits; NaN stays NaN).
+// Round-to-nearest-even fp32 -> bf16 (ties to even; overflow to infinity; NaN stays a quiet
+// NaN): the conversion instruction gfx950 has for it (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
