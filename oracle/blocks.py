@@ -19,6 +19,10 @@ ones (each is also listed among the readings of the design notes):
   epilogue     out = act(conv(x) + bias) + residual.
   res block    pre-norm, identity skip (cin = cout):
                h = conv1(silu(gn1(x))); out = conv2(silu(gn2(h))) + x.
+  layer norm   per site over its C channels: mean and population variance;
+               y = (x - mean) / sqrt(var + eps) * gamma[c] + beta[c].
+  ConvNeXt     h = ln(conv(x)); out = linear2(silu(linear1(h))) + x, linear1 C -> 4C,
+  block        linear2 4C -> C (the inverted-bottleneck MLP after a 3x3x3 SubM conv).
 """
 from __future__ import annotations
 
@@ -108,3 +112,24 @@ def res_block(x, coords, batch: int, nbr, p: dict, groups: int = 32, eps: float 
     h = oracle.conv(h, p["w1"], p["b1"], nbr)
     h = group_norm(h, coords, batch, groups, p["g2"], p["be2"], eps, "silu")
     return conv_epilogue(h, p["w2"], p["b2"], nbr, "none", x)
+
+
+def layer_norm(x, gamma=None, beta=None, eps: float = 1e-6, act: str = "none"):
+    """act(layer norm over each row's channels) in float64; gamma / beta default to 1 / 0."""
+    x = np.asarray(x, dtype=np.float64)
+    m = x.mean(axis=1, keepdims=True)
+    v = ((x - m) ** 2).mean(axis=1, keepdims=True)
+    y = (x - m) / np.sqrt(v + eps)
+    if gamma is not None:
+        y = y * np.asarray(gamma, dtype=np.float64)
+    if beta is not None:
+        y = y + np.asarray(beta, dtype=np.float64)
+    return activation(y, act)
+
+
+def convnext_block(x, nbr, p: dict, eps: float = 1e-6):
+    """p holds w ([27, C, C]), b, ln_g, ln_b ([C]), w1 ([C, 4C]), b1, w2 ([4C, C]), b2."""
+    h = oracle.conv(x, p["w"], p["b"], nbr)
+    h = layer_norm(h, p["ln_g"], p["ln_b"], eps)
+    h = linear_epilogue(h, p["w1"], p["b1"], "silu")
+    return linear_epilogue(h, p["w2"], p["b2"], "none", x)

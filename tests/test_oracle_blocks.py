@@ -139,3 +139,37 @@ def test_res_block_with_zero_convolutions_is_identity():
         p[k] = np.zeros_like(p[k])
     nbr = oracle.build_map(coords, 1, (4, 4, 4))
     np.testing.assert_array_equal(blocks.res_block(x, coords, 1, nbr, p, 4), x)
+
+
+@pytest.mark.parametrize("c,act", [(32, "none"), (128, "silu"), (7, "relu")])
+def test_layer_norm_matches_torch(c, act):
+    rng = np.random.default_rng(c)
+    x = rng.standard_normal((50, c)) * 4.0 + 3.0
+    g, b = rng.standard_normal(c), rng.standard_normal(c)
+    want = F.layer_norm(torch.from_numpy(x), (c,), torch.from_numpy(g), torch.from_numpy(b), 1e-6)
+    want = {"none": want, "silu": F.silu(want), "relu": F.relu(want)}[act]
+    np.testing.assert_allclose(blocks.layer_norm(x, g, b, 1e-6, act), want.numpy(), rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_layer_norm_closed_form():
+    """Row (1, 3): mean 2, population variance 1 -> (-1, 1) with eps 0."""
+    np.testing.assert_allclose(blocks.layer_norm(np.array([[1.0, 3.0]]), eps=0.0), [[-1.0, 1.0]])
+
+
+def test_convnext_block_matches_dense_torch():
+    """torch conv3d on the dense grid, layer_norm, linear, silu, linear, plus the skip."""
+    grid, c = (5, 6, 4), 8
+    coords = sites(11, 1, grid, 0.4)
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((len(coords), c))
+    p = {"w": rng.standard_normal((27, c, c)) * 0.1, "b": rng.standard_normal(c),
+         "ln_g": 1 + 0.1 * rng.standard_normal(c), "ln_b": 0.1 * rng.standard_normal(c),
+         "w1": rng.standard_normal((c, 4 * c)) * 0.3, "b1": rng.standard_normal(4 * c),
+         "w2": rng.standard_normal((4 * c, c)) * 0.2, "b2": rng.standard_normal(c)}
+    got = blocks.convnext_block(x, oracle.build_map(coords, 1, grid), p)
+    h = dense_conv_at_sites(coords, x, p["w"], p["b"], 1, grid)
+    h = F.layer_norm(h, (c,), torch.from_numpy(p["ln_g"]), torch.from_numpy(p["ln_b"]), 1e-6)
+    h = F.silu(h @ torch.from_numpy(p["w1"]) + torch.from_numpy(p["b1"]))
+    h = h @ torch.from_numpy(p["w2"]) + torch.from_numpy(p["b2"])
+    np.testing.assert_allclose(got, (h + torch.from_numpy(x)).numpy(), rtol=1e-11, atol=1e-11)
