@@ -305,6 +305,85 @@ def time_block(ssc, torch, coords, x, plan, batch, dev, reps: int = 50) -> dict:
                 "residual": round(us["conv2_residual"] - us["conv_plain"], 2)}}
 
 
+def time_convnext(ssc, torch, x, plan, dev, reps: int = 50) -> dict:
+    """A ConvNeXt-style block on the workload's sites, C = the input channels (bf16):
+    h = layer_norm(conv(x)); y = linear2(silu(linear1(h))) + x with linear1 C -> 4C and
+    linear2 4C -> C (k=1 layers on the streaming kernel or the tiled GEMM by width).  Launches
+    through the C ABI on preallocated buffers; random weights (seeded); device time per stage
+    and the k=1 layers' algorithmic GB/s (rows in and out, weights)."""
+    import ctypes
+    import math
+    lib = ssc.load_library()
+    n, c = x.shape
+    gen = torch.Generator().manual_seed(4321)
+    bf = torch.bfloat16
+
+    def rnd(*shape, scale=1.0):
+        return torch.randn(*shape, generator=gen) * scale
+
+    w = rnd(27, c, c, scale=1 / math.sqrt(27 * c)).to(bf).to(dev)
+    pw = ssc.pack_weights(w)
+    b = rnd(c, scale=0.1).to(dev)
+    g, be = (1 + rnd(c, scale=0.1)).to(dev), rnd(c, scale=0.1).to(dev)
+    w1 = rnd(c, 4 * c, scale=1 / math.sqrt(c)).to(bf).to(dev)
+    w2 = rnd(4 * c, c, scale=1 / math.sqrt(4 * c)).to(bf).to(dev)
+    b1, b2 = rnd(4 * c, scale=0.1).to(dev), rnd(c, scale=0.1).to(dev)
+    h = torch.empty_like(x)
+    m = torch.empty((n, 4 * c), dtype=bf, device=dev)
+    y = torch.empty_like(x)
+    ws = torch.empty(max(lib.ssc_conv_workspace_bytes(c, 4 * c, ssc.SSC_BF16),
+                         lib.ssc_conv_workspace_bytes(4 * c, c, ssc.SSC_BF16)),
+                     dtype=torch.uint8, device=dev)
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    BF = ssc.SSC_BF16
+    e1 = ssc._Epilogue(act=ssc.ACTS["silu"])
+    e2 = ssc._Epilogue(residual=x.data_ptr())
+
+    def conv():
+        lib.ssc_subm_conv3d_packed(p(x), p(pw.buf), p(b), p(plan.buf), n, c, c, p(h), BF, st)
+
+    def norm():
+        lib.ssc_layer_norm(p(h), BF, n, c, p(g), p(be), 1e-6, 0, p(h), st)
+
+    def lin1():
+        lib.ssc_linear_ex(p(h), BF, p(w1), p(b1), n, c, 4 * c, p(m), BF, ctypes.byref(e1), p(ws),
+                          ws.numel(), st)
+
+    def lin2():
+        lib.ssc_linear_ex(p(m), BF, p(w2), p(b2), n, 4 * c, c, p(y), BF, ctypes.byref(e2), p(ws),
+                          ws.numel(), st)
+
+    def block():
+        conv()
+        norm()
+        lin1()
+        lin2()
+
+    def t(fn):
+        for _ in range(5):
+            fn()
+        e0, e1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1_.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1_) / reps * 1e3
+
+    us = {k: t(f) for k, f in (("block", block), ("conv", conv), ("layer_norm", norm),
+                               ("linear_c_4c_silu", lin1), ("linear_4c_c_residual", lin2))}
+    row = c * 2
+    l1_bytes = n * row + n * 4 * row + c * 4 * c * 2
+    l2_bytes = n * 4 * row + 2 * n * row + c * 4 * c * 2
+    return {"channels": c, "block_us": round(us["block"], 2),
+            "block_mvox_s": round(n / us["block"], 1),
+            "stages_us": {k: round(v, 2) for k, v in us.items() if k != "block"},
+            "linear_gbs": {"c_4c": round(l1_bytes / us["linear_c_4c_silu"] / 1e3, 1),
+                           "4c_c": round(l2_bytes / us["linear_4c_c_residual"] / 1e3, 1)},
+            "layer_norm_gbs": round(2 * n * row / us["layer_norm"] / 1e3, 1)}
+
+
 def time_ablations(ssc, torch, x, wt, bias, plan, nbr, dev, reps: int = 20) -> dict:
     """The pages' own designs on the same layer (comparison only): the compacted kernel with
     tap compaction off (every block walks all 27 taps), the dense 27-tap GEMM (gather of the
@@ -554,10 +633,12 @@ def main():
     if x.dtype == torch.bfloat16 and use_packed:
         abl = time_ablations(ssc, torch, x, wt, bias, plan, nbr, dev)
         log(f"[bench] ablations {abl}")
-    block = None
+    block = convnext = None
     if x.dtype == torch.bfloat16 and cin in (32, 64, 128):
         block = time_block(ssc, torch, coords, x, plan, w.batch, dev)
         log(f"[bench] residual block {block['block_us']} us {block['stages_us']}")
+        convnext = time_convnext(ssc, torch, x, plan, dev)
+        log(f"[bench] convnext block {convnext['block_us']} us {convnext['stages_us']}")
 
     out_bytes = 4 if mid_dt == torch.float32 else 2
     in_bytes = x.element_size()
@@ -603,6 +684,7 @@ def main():
         "conv_flushed": flushed,
         "resample": resample,
         "res_block": block,
+        "convnext_block": convnext,
         "ablations": abl,
         "cold_index_plan_ms": round(float(np.median(cold)), 4),
         # Algorithmic bytes of the cold path: the index reads the coordinates (16 B per site)

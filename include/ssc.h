@@ -173,7 +173,9 @@ ssc_status ssc_subm_conv3d_packed(const void* feats, const void* packed_weight,
                                   int32_t cout, void* out, int32_t out_dtype, void* stream);
 
 /* k=1 SubMConv3d, i.e. the per-voxel linear map out = feats @ weight + bias (LATO.2 page,
- * "Status": SubMConv3d k=1; SparseLinear).  No map is needed.
+ * "Status": SubMConv3d k=1; SparseLinear).  No map is needed.  16-bit inputs run on the
+ * matrix cores: a streaming kernel for cin, cout in {32, 64, 128}, a tiled GEMM for other
+ * multiples of 64 up to 1024 (the ConvNeXt-style MLP's 4C), the vector-ALU kernel otherwise.
  *   feats [n, cin], weight [cin, cout] (the single-tap [1, cin, cout] has the same bytes),
  *   bias [cout] fp32 or NULL, out [n, cout] out_dtype; workspace as for ssc_subm_conv3d. */
 ssc_status ssc_linear(const void* feats, int32_t in_dtype, const void* weight, const float* bias,
@@ -271,6 +273,16 @@ ssc_status ssc_gn_apply(const void* x, int32_t dtype, int64_t n, int32_t channel
                         const int32_t* coords, int32_t batch, int32_t groups,
                         const float* stats, const float* gamma, const float* beta, int32_t act,
                         void* out, void* stream);
+
+/* LayerNorm32 over each site's channels (LATO.2 MLX port page, "Status" and repository
+ * layout: a layer norm with fp32 accumulation), the norm of the ConvNeXt-style block:
+ *   out[i][c] = act((x[i][c] - mean_i) / sqrt(var_i + eps) * gamma[c] + beta[c]),
+ * mean and population variance of row i over its channels, computed in fp32 (the mean first,
+ * then the mean squared deviation).  x [n, channels] SSC_F32 / SSC_BF16 / SSC_F16; out the
+ * same dtype, may be x; gamma / beta fp32 [channels] or NULL (1 / 0). */
+ssc_status ssc_layer_norm(const void* x, int32_t dtype, int64_t n, int32_t channels,
+                          const float* gamma, const float* beta, float eps, int32_t act,
+                          void* out, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Coordinate-changing neighbours: factor-2 downsample (max pool), its paired upsample, and

@@ -25,6 +25,7 @@ import torch
 __all__ = ["SscError", "build_index", "build_plan", "subm_conv3d", "linear", "Plan",
            "PackedWeight", "pack_weights", "subm_conv3d_packed",
            "GroupNormPartials", "gn_partials", "gn_finalize", "gn_apply", "group_norm",
+           "layer_norm",
            "downsample2", "upsample2", "spatial2channel2", "subdivide2",
            "SubMIndex", "cached_index", "library_path", "load_library", "TAPS", "CENTRE_TAP"]
 
@@ -102,6 +103,7 @@ def load_library():
         "ssc_gn_partials": ([p, i32, i64, i32, p, i32, i32, p, sz, p], ctypes.c_int),
         "ssc_gn_finalize": ([p, i64, i32, i32, ctypes.c_float, p, p], ctypes.c_int),
         "ssc_gn_apply": ([p, i32, i64, i32, p, i32, i32, p, p, p, i32, p, p], ctypes.c_int),
+        "ssc_layer_norm": ([p, i32, i64, i32, p, p, ctypes.c_float, i32, p, p], ctypes.c_int),
         "ssc_gather_taps": ([p, i32, i64, i32, p, p, p], ctypes.c_int),
         "ssc_scatter_add_rows": ([p, i32, p, i64, i32, p, i64, p], ctypes.c_int),
     }
@@ -399,6 +401,29 @@ def gn_apply(x: torch.Tensor, stats: torch.Tensor, gamma: Optional[torch.Tensor]
                               groups, _ptr(stats), _ptr(gamma), _ptr(beta), ACTS[act], _ptr(out),
                               _stream(x.device))
     _check(st, "ssc_gn_apply")
+    return out
+
+
+def layer_norm(x: torch.Tensor, gamma: Optional[torch.Tensor] = None,
+               beta: Optional[torch.Tensor] = None, eps: float = 1e-6, act: str = "none",
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """LayerNorm32 over each site's channels (+ activation); ``out`` may be x."""
+    _need_cuda(x, "x")
+    n, c = x.shape
+    for t, name in ((gamma, "gamma"), (beta, "beta")):
+        if t is not None:
+            _need_cuda(t, name)
+            if t.dtype != torch.float32 or t.numel() != c:
+                raise ValueError(f"{name} must be float32 [{c}]")
+    if act not in ACTS:
+        raise ValueError(f"act must be one of {sorted(ACTS)}")
+    if out is None:
+        out = torch.empty_like(x)
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        st = lib.ssc_layer_norm(_ptr(x), _dtype_code(x.dtype, "x"), n, c, _ptr(gamma),
+                                _ptr(beta), float(eps), ACTS[act], _ptr(out), _stream(x.device))
+    _check(st, "ssc_layer_norm")
     return out
 
 

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssc.so")
-SOURCES = ["index.hip", "conv.hip", "resample.hip", "norm.hip", "ablation.hip"]
+SOURCES = ["index.hip", "conv.hip", "resample.hip", "norm.hip", "ablation.hip", "gemm.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

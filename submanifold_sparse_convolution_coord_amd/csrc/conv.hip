@@ -35,6 +35,11 @@ namespace ssc {
 ssc_status gn_partials_launch(const void* x, int32_t dtype, int64_t n, int32_t channels,
                               const int32_t* coords, int32_t batch, int32_t groups,
                               float* partials, hipStream_t s);
+// Matrix-core GEMM for k=1 layers wider than the streaming kernel's (gemm.hip).
+bool gemm_rows_supported(int cin, int cout);
+ssc_status gemm_rows_launch(const void* feats, const uint16_t* wp, const float* bias, int64_t n,
+                            int cin, int cout, void* out, bool out16, int ek, int act,
+                            const void* res, hipStream_t s);
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -1080,6 +1085,14 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
       if (LinFn fn = pick_linear(cin, cout, out16, ek, &wcg, &rows, use_epi)) {
         launch_pack_frag(weight, 1, cin, cout, wcg, 0, wt, s);
         if (const ssc_status st = launch_linear(fn, rows, feats, wt, bias, n, out, ep, s);
+            st != SSC_OK)
+          return st;
+        return gn_after(epi, false, out, out_dtype, n, cout, s);
+      }
+      if (gemm_rows_supported(cin, cout)) {
+        launch_pack_frag(weight, 1, cin, cout, cout / 16, 0, wt, s);  // 16-column tiles
+        if (const ssc_status st = gemm_rows_launch(feats, wt, bias, n, cin, cout, out, out16,
+                                                   ek, ep.act, ep.res, s);
             st != SSC_OK)
           return st;
         return gn_after(epi, false, out, out_dtype, n, cout, s);

@@ -1,0 +1,222 @@
+// k=1 layers wider than the streaming kernel's 128 channels (the C -> 4C -> C MLP of the
+// ConvNeXt-style block; LATO.2 MLX port page, "Status": SparseLinear): out = act(X @ W +
+// bias) + residual for 16-bit X [n, cin] and W, fp32 accumulation on the matrix cores.
+//
+// A workgroup owns 128 rows x CT columns (CT = 64 or 128); its 4 waves own 32 rows each and
+// all CT columns.  The K loop runs in stages of 64: the rows' next stage is loaded into
+// registers while the matrix cores consume this one from LDS (16-byte chunks XOR-swizzled by
+// row), then written to the other LDS buffer; the weight fragments (packed per 16-column
+// tile, 1 KB per fragment) go straight from global memory (L2-resident) into VGPRs, one stage
+// ahead.  Rows past n are read as row n-1 and never stored.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace ssc {
+namespace {
+
+typedef __bf16 g_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 g_f16x8_t __attribute__((ext_vector_type(8)));
+typedef float g_f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t g_u32x4_t __attribute__((ext_vector_type(4)));  // a 16-byte word in registers
+
+template <int EK>
+__device__ __forceinline__ g_f32x4_t gemm_mfma(g_u32x4_t a, g_u32x4_t b, g_f32x4_t c) {
+  if constexpr (EK == 0)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(g_bf16x8_t, a),
+                                                   __builtin_bit_cast(g_bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(g_f16x8_t, a),
+                                                  __builtin_bit_cast(g_f16x8_t, b), c, 0, 0, 0);
+}
+
+template <int EK>
+__device__ __forceinline__ float from16(uint16_t h) {
+  if constexpr (EK == 0) return bf16_to_f32(h);
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+template <int EK>
+__device__ __forceinline__ uint16_t round16(float v) {
+  if constexpr (EK == 0) return f32_to_bf16_rne(v);
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+
+constexpr int kGRows = 128;  // rows per tile
+constexpr int kGK = 64;      // K per stage
+
+template <int CT, bool OUT16, int EK>
+__global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict__ X,
+                                                      const uint16_t* __restrict__ Wp,
+                                                      const float* __restrict__ bias, int64_t n,
+                                                      int cin, int cout, void* Y, int act,
+                                                      const void* res) {
+  constexpr int NCT = CT / 16;  // 16-column tiles (every wave has all of them)
+  constexpr int ESZ = OUT16 ? 2 : 4;
+  constexpr int ROWB = CT * ESZ;          // bytes of a wave's output row
+  constexpr int CHUNKS = ROWB / 16;
+  constexpr int SWM = (CHUNKS < 16 ? CHUNKS : 16) - 1;
+  constexpr int OUT_BYTES = 4 * 32 * ROWB;  // the 4 waves' 32 output rows each
+  constexpr int A_BYTES = 2 * kGRows * kGK * 2;
+  __shared__ __attribute__((aligned(16))) char smem[OUT_BYTES > A_BYTES ? OUT_BYTES : A_BYTES];
+  // two 16 KB stages of 128 rows x 8 chunks of 16 bytes
+  auto* sA = reinterpret_cast<g_u32x4_t (*)[kGRows * kGK / 8]>(smem);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kGRows;
+  const int ct0 = blockIdx.y * NCT;  // first 16-column tile of this workgroup
+  const int ksteps = cin / 32;       // fragment index stride of a column tile
+  const int stages = cin / kGK;
+
+  auto load_a = [&](int st, g_u32x4_t (&r)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = threadIdx.x + k * 256;
+      const int row = idx >> 3, ch = idx & 7;
+      const int64_t g = std::min<int64_t>(row0 + row, n - 1);
+      r[k] = *reinterpret_cast<const g_u32x4_t*>(X + g * cin + st * kGK + ch * 8);
+    }
+  };
+  auto store_a = [&](int buf, const g_u32x4_t (&r)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = threadIdx.x + k * 256;
+      const int row = idx >> 3, ch = idx & 7;
+      sA[buf][row * 8 + (ch ^ (row & 7))] = r[k];
+    }
+  };
+  auto load_b = [&](int st, g_u32x4_t (&b)[2][NCT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+        b[ks][c] = *reinterpret_cast<const g_u32x4_t*>(
+            Wp + (static_cast<int64_t>(ct0 + c) * ksteps + st * 2 + ks) * 512 + lane * 8);
+  };
+
+  g_f32x4_t acc[2][NCT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[rt][c] = g_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  g_u32x4_t ra[4], bw[2][NCT], bn[2][NCT];
+  load_a(0, ra);
+  store_a(0, ra);
+  load_b(0, bw);
+  __syncthreads();
+  for (int st = 0; st < stages; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < stages;
+    if (more) {
+      load_a(st + 1, ra);
+      load_b(st + 1, bn);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int row = wave * 32 + rt * 16 + (lane & 15);
+        const int ch = ks * 4 + (lane >> 4);
+        const g_u32x4_t a = sA[cur][row * 8 + (ch ^ (row & 7))];
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) acc[rt][c] = gemm_mfma<EK>(a, bw[ks][c], acc[rt][c]);
+      }
+    if (more) {
+      store_a(cur ^ 1, ra);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) bw[ks][c] = bn[ks][c];
+    }
+    __syncthreads();
+  }
+  // Epilogue.  Each wave stages its 32 output rows in LDS (16-byte chunks XOR-swizzled by
+  // row), with the residual rows fetched first as whole pieces into the same places, then
+  // writes whole 16-byte pieces of rows.  v = act(acc + bias) + residual, rounded once.
+  // After the loop's last barrier no wave reads the A stages any more.
+  char* sO = smem + wave * 32 * ROWB;
+  const int64_t wrow0 = row0 + wave * 32;
+  const int64_t col0b = static_cast<int64_t>(ct0) * 16 * ESZ;  // byte offset of the tile
+  if (res) {
+#pragma unroll
+    for (int k = 0; k < 32 * CHUNKS / 64; ++k) {
+      const int idx = lane + k * 64;
+      const int r = idx / CHUNKS, ch = idx % CHUNKS;
+      if (wrow0 + r < n)
+        *reinterpret_cast<g_u32x4_t*>(sO + r * ROWB + ((ch ^ (r & SWM)) << 4)) =
+            *reinterpret_cast<const g_u32x4_t*>(static_cast<const char*>(res) +
+                                                (wrow0 + r) * cout * ESZ + col0b + ch * 16);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces are in LDS (only it reads them)
+  }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int col = c * 16 + (lane & 15);  // within the tile
+      const float bc = bias ? bias[ct0 * 16 + col] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rt * 16 + (lane >> 4) * 4 + i;
+        const int byte = col * ESZ;
+        char* dst = sO + r * ROWB + (((byte >> 4) ^ (r & SWM)) << 4) + (byte & 15);
+        float v = apply_act(acc[rt][c][i] + bc, act);
+        if (res) {
+          if constexpr (OUT16)
+            v += from16<EK>(*reinterpret_cast<const uint16_t*>(dst));
+          else
+            v += *reinterpret_cast<const float*>(dst);
+        }
+        if constexpr (OUT16)
+          *reinterpret_cast<uint16_t*>(dst) = round16<EK>(v);
+        else
+          *reinterpret_cast<float*>(dst) = v;
+      }
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's staging writes are done
+#pragma unroll
+  for (int k = 0; k < 32 * CHUNKS / 64; ++k) {
+    const int idx = lane + k * 64;
+    const int r = idx / CHUNKS, ch = idx % CHUNKS;
+    if (wrow0 + r < n)
+      *reinterpret_cast<g_u32x4_t*>(static_cast<char*>(Y) + (wrow0 + r) * cout * ESZ + col0b +
+                                    ch * 16) =
+          *reinterpret_cast<const g_u32x4_t*>(sO + r * ROWB + ((ch ^ (r & SWM)) << 4));
+  }
+}
+
+}  // namespace
+
+// Shapes the GEMM takes: 16-bit inputs, cin a multiple of 64, cout a multiple of 64, both
+// at most 1024.
+bool gemm_rows_supported(int cin, int cout) {
+  return cin >= 64 && cout >= 64 && cin % 64 == 0 && cout % 64 == 0 && cin <= 1024 &&
+         cout <= 1024;
+}
+
+// Weights in wp are packed per 16-column tile (the conv's fragment order with one tap and
+// cout / 16 column groups).
+ssc_status gemm_rows_launch(const void* feats, const uint16_t* wp, const float* bias, int64_t n,
+                            int cin, int cout, void* out, bool out16, int ek, int act,
+                            const void* res, hipStream_t s) {
+  const bool wide = cout % 128 == 0;
+  const dim3 grid(static_cast<unsigned>((n + kGRows - 1) / kGRows),
+                  static_cast<unsigned>(cout / (wide ? 128 : 64)));
+  const auto* x = static_cast<const uint16_t*>(feats);
+#define SSC_GEMM(CT)                                                                       \
+  {                                                                                        \
+    auto fn = out16 ? (ek == 1 ? k_gemm_rows<CT, true, 1> : k_gemm_rows<CT, true, 0>)      \
+                    : (ek == 1 ? k_gemm_rows<CT, false, 1> : k_gemm_rows<CT, false, 0>);   \
+    hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, x, wp, bias, n, cin, cout, out, act, res); \
+  }
+  if (wide)
+    SSC_GEMM(128)
+  else
+    SSC_GEMM(64)
+#undef SSC_GEMM
+  return launch_status();
+}
+
+}  // namespace ssc

@@ -353,6 +353,119 @@ __global__ __launch_bounds__(256) void k_gn_apply_w(const uint4* x, int64_t n,
   }
 }
 
+// Layer norm (LayerNorm32: fp32 statistics) over each row's channels, rows of WORDS 16-byte
+// words (a power of two <= 64): a row is WORDS neighbouring lanes, a wave holds 64 / WORDS
+// rows per group and works on 4 groups at once (their loads in flight together); two
+// butterfly sums give the mean and then the mean squared deviation (every lane of a row ends
+// with the same sums); y = act((x - mean) * rstd * gamma + beta).  x and out may be the same
+// buffer.
+template <typename T, int WORDS>
+__global__ __launch_bounds__(256) void k_layer_norm_w(const uint4* x, int64_t n, int channels,
+                                                      const float* __restrict__ gamma,
+                                                      const float* __restrict__ beta, float eps,
+                                                      int act, uint4* out) {
+  constexpr int E = 16 / sizeof(T);
+  constexpr int RPW = 64 / WORDS;  // rows per group
+  constexpr int G = 4;             // groups a wave keeps in flight
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int w = lane % WORDS, rsub = lane / WORDS;
+  float gm[E], bt[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    gm[e] = 1.f;
+    bt[e] = 0.f;
+  }
+  if (gamma) {
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(gamma + w * E + e);
+      gm[e] = v.x, gm[e + 1] = v.y, gm[e + 2] = v.z, gm[e + 3] = v.w;
+    }
+  }
+  if (beta) {
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(beta + w * E + e);
+      bt[e] = v.x, bt[e + 1] = v.y, bt[e + 2] = v.z, bt[e + 3] = v.w;
+    }
+  }
+  const float inv_c = 1.f / static_cast<float>(channels);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4 * G * RPW;
+  for (int64_t base = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * G * RPW; base < n;
+       base += stride) {  // uniform across the wave: every lane joins the shuffles
+    uint4 v[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int64_t row = base + k * RPW + rsub;
+      v[k] = row < n ? x[row * WORDS + w] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float f[G][E], sum[G], sq[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      word_to_f32<T>(v[k], f[k]);
+      sum[k] = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) sum[k] += f[k][e];
+    }
+#pragma unroll
+    for (int m = 1; m < WORDS; m <<= 1)
+#pragma unroll
+      for (int k = 0; k < G; ++k) sum[k] += __shfl_xor(sum[k], m, 64);
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const float mean = sum[k] * inv_c;
+      sq[k] = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        f[k][e] -= mean;
+        sq[k] = fmaf(f[k][e], f[k][e], sq[k]);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < WORDS; m <<= 1)
+#pragma unroll
+      for (int k = 0; k < G; ++k) sq[k] += __shfl_xor(sq[k], m, 64);
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int64_t row = base + k * RPW + rsub;
+      if (row >= n) continue;
+      const float rstd = 1.f / sqrtf(sq[k] * inv_c + eps);
+      alignas(16) T o[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        st_val(&o[e], apply_act(fmaf(f[k][e] * rstd, gm[e], bt[e]), act));
+      out[row * WORDS + w] = *reinterpret_cast<const uint4*>(o);
+    }
+  }
+}
+
+// Layer norm for any row width: a thread per row, two passes over it.
+template <typename T>
+__global__ __launch_bounds__(256) void k_layer_norm_rows(const T* x, int64_t n, int channels,
+                                                         const float* __restrict__ gamma,
+                                                         const float* __restrict__ beta,
+                                                         float eps, int act, T* out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; row < n;
+       row += stride) {
+    const T* p = x + row * channels;
+    float sum = 0.f;
+    for (int c = 0; c < channels; ++c) sum += ld_val(p + c);
+    const float mean = sum / static_cast<float>(channels);
+    float sq = 0.f;
+    for (int c = 0; c < channels; ++c) {
+      const float d = ld_val(p + c) - mean;
+      sq = fmaf(d, d, sq);
+    }
+    const float rstd = 1.f / sqrtf(sq / static_cast<float>(channels) + eps);
+    for (int c = 0; c < channels; ++c) {
+      float y = (ld_val(p + c) - mean) * rstd;
+      y = fmaf(y, gamma ? gamma[c] : 1.f, beta ? beta[c] : 0.f);
+      st_val(out + row * channels + c, apply_act(y, act));
+    }
+  }
+}
+
 int64_t gn_slots(int64_t n) {
   const int64_t rows = std::max<int64_t>(n, 1);
   return (rows + kPlanRowAlign - 1) / kPlanRowAlign * (kPlanRowAlign / kSlotRows);
@@ -492,5 +605,58 @@ extern "C" ssc_status ssc_gn_apply(const void* x, int32_t dtype, int64_t n, int3
     else
       k_gn_apply<_Float16, 1><<<grid, 256, 0, s>>>(xi, n, channels, groups, c4, batch, st, gamma, beta, act, xo);
   }
+  return launch_status();
+}
+
+extern "C" ssc_status ssc_layer_norm(const void* x, int32_t dtype, int64_t n, int32_t channels,
+                                     const float* gamma, const float* beta, float eps,
+                                     int32_t act, void* out, void* stream) {
+  if (n < 0 || channels < 1 || channels > 65536 || !(eps >= 0.f)) return SSC_ERR_ARG;
+  if (dtype != SSC_F32 && dtype != SSC_BF16 && dtype != SSC_F16) return SSC_ERR_ARG;
+  if (act < SSC_ACT_NONE || act > SSC_ACT_SILU) return SSC_ERR_ARG;
+  if (n == 0) return SSC_OK;
+  if (x == nullptr || out == nullptr || (gamma && !aligned(gamma, 4)) ||
+      (beta && !aligned(beta, 4)))
+    return SSC_ERR_ARG;
+  hipStream_t s = as_stream(stream);
+  const int esz = dtype == SSC_F32 ? 4 : 2;
+  const int64_t row_bytes = static_cast<int64_t>(channels) * esz;
+  const int64_t words = row_bytes / 16;
+  if (row_bytes % 16 == 0 && words <= 64 && (words & (words - 1)) == 0 && aligned(x, 16) &&
+      aligned(out, 16) && (!gamma || aligned(gamma, 16)) && (!beta || aligned(beta, 16))) {
+    const int64_t rpb = 4 * 4 * (64 / words);  // rows per block step: 4 waves x 4 groups
+    const unsigned g =
+        static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>((n + rpb - 1) / rpb, 65536)));
+    const auto* x4 = static_cast<const uint4*>(x);
+    auto* o4 = static_cast<uint4*>(out);
+    auto launch = [&](auto tag) {
+      using T = decltype(tag);
+      switch (words) {
+#define SSC_LN(W) case W: k_layer_norm_w<T, W><<<g, 256, 0, s>>>(x4, n, channels, gamma, beta, eps, act, o4); break;
+        SSC_LN(1) SSC_LN(2) SSC_LN(4) SSC_LN(8) SSC_LN(16) SSC_LN(32) default: SSC_LN(64)
+#undef SSC_LN
+      }
+    };
+    if (dtype == SSC_F32)
+      launch(float{});
+    else if (dtype == SSC_BF16)
+      launch(uint16_t{});
+    else
+      launch(_Float16{});
+    return launch_status();
+  }
+  const unsigned g =
+      static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 65536)));
+  if (dtype == SSC_F32)
+    k_layer_norm_rows<float><<<g, 256, 0, s>>>(static_cast<const float*>(x), n, channels, gamma,
+                                               beta, eps, act, static_cast<float*>(out));
+  else if (dtype == SSC_BF16)
+    k_layer_norm_rows<uint16_t><<<g, 256, 0, s>>>(static_cast<const uint16_t*>(x), n, channels,
+                                                  gamma, beta, eps, act,
+                                                  static_cast<uint16_t*>(out));
+  else
+    k_layer_norm_rows<_Float16><<<g, 256, 0, s>>>(static_cast<const _Float16*>(x), n, channels,
+                                                  gamma, beta, eps, act,
+                                                  static_cast<_Float16*>(out));
   return launch_status();
 }

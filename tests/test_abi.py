@@ -237,3 +237,14 @@ def test_epilogue_and_group_norm_argument_errors(lib):
     assert a(FAKE, 0, 10, 64, None, 1, 32, FAKE, None, None, 7, FAKE, None) == ssc.SSC_ERR_ARG
     assert a(FAKE, 0, 10, 64, None, 1, 32, None, None, None, 0, FAKE, None) == ssc.SSC_ERR_ARG
     assert a(FAKE, 0, 0, 64, None, 1, 32, FAKE, None, None, 0, None, None) == ssc.SSC_OK
+
+
+def test_layer_norm_argument_errors(lib):
+    f = lib.ssc_layer_norm
+    assert f(FAKE, 0, -1, 32, None, None, 1e-6, 0, FAKE, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 0, 10, 0, None, None, 1e-6, 0, FAKE, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 9, 10, 32, None, None, 1e-6, 0, FAKE, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 0, 10, 32, None, None, -1.0, 0, FAKE, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 0, 10, 32, None, None, 1e-6, 5, FAKE, None) == ssc.SSC_ERR_ARG
+    assert f(None, 0, 10, 32, None, None, 1e-6, 0, FAKE, None) == ssc.SSC_ERR_ARG
+    assert f(None, 0, 0, 32, None, None, 1e-6, 0, None, None) == ssc.SSC_OK

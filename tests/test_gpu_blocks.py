@@ -284,3 +284,82 @@ def test_res_block(dtype, batch, c, groups):
     err = rel_err(f64(y), ref)
     say(f"[block]   max|err|/rms = {err:.3e}")
     assert err <= TAU_BLOCK[dtype]
+
+
+@pytest.mark.parametrize("n,cin,cout,dtype,odt,act", [
+    (1000, 128, 512, torch.bfloat16, torch.float32, "silu"),    # tiled GEMM, 128-column tiles
+    (777, 512, 128, torch.bfloat16, torch.bfloat16, "none"),
+    (333, 64, 256, torch.float16, torch.float16, "relu"),
+    (513, 256, 64, torch.bfloat16, torch.float32, "silu"),      # 64-column tiles
+    (129, 192, 192, torch.bfloat16, torch.bfloat16, "none"),
+    (1, 128, 512, torch.bfloat16, torch.float32, "none"),
+])
+def test_wide_linear(n, cin, cout, dtype, odt, act):
+    say(f"[gemm] n={n} {cin}->{cout} {dtype} -> {odt} act={act}")
+    rng = np.random.default_rng(n + cin)
+    x = torch.from_numpy(rng.standard_normal((n, cin), dtype=np.float32)).to(dtype)
+    w = (torch.from_numpy(rng.standard_normal((cin, cout), dtype=np.float32)) / np.sqrt(cin)).to(dtype)
+    b = torch.from_numpy(rng.standard_normal(cout, dtype=np.float32))
+    res = torch.from_numpy(rng.standard_normal((n, cout), dtype=np.float32)).to(odt)
+    y = ssc.linear(x.to(DEV), w.to(DEV), b.to(DEV), odt, act=act, residual=res.to(DEV))
+    y32 = ssc.linear(x.to(DEV), w.to(DEV), b.to(DEV), torch.float32, act=act,
+                     residual=res.float().to(DEV))
+    ref = blocks.linear_epilogue(f64(x), f64(w), b.numpy(), act, f64(res))
+    err = rel_err(f64(y32), ref)
+    say(f"[gemm]   max|err|/rms = {err:.3e}")
+    assert err <= TAU[dtype]
+    assert torch.equal(y.view(torch.uint8), y32.to(odt).view(torch.uint8))
+
+
+@pytest.mark.parametrize("dtype,c,n", [(torch.bfloat16, 128, 3000), (torch.float32, 32, 1001),
+                                       (torch.float16, 512, 257), (torch.bfloat16, 48, 300),
+                                       (torch.float32, 7, 65), (torch.bfloat16, 8, 1)])
+def test_layer_norm(dtype, c, n):
+    say(f"[ln] {dtype} C={c} n={n}")
+    rng = np.random.default_rng(c + n)
+    x = torch.from_numpy((rng.standard_normal((n, c)) * 3.0 + 1.5).astype(np.float32)).to(dtype)
+    g = torch.from_numpy(1 + 0.2 * rng.standard_normal(c).astype(np.float32))
+    be = torch.from_numpy(0.2 * rng.standard_normal(c).astype(np.float32))
+    for act in ("none", "silu"):
+        y = ssc.layer_norm(x.to(DEV), g.to(DEV), be.to(DEV), 1e-6, act)
+        ref = blocks.layer_norm(f64(x), g.numpy(), be.numpy(), 1e-6, act)
+        got = f64(y)
+        say(f"[ln]   act={act} max|err|/rms = {rel_err(got, ref):.3e}")
+        rms = np.sqrt((ref ** 2).mean())
+        assert (np.abs(got - ref) <= ROUND[dtype] * np.abs(ref) + 1e-5 * rms).all()
+    inplace = x.to(DEV).clone()
+    ssc.layer_norm(inplace, g.to(DEV), be.to(DEV), 1e-6, "silu", out=inplace)
+    assert torch.equal(inplace.view(torch.uint8), y.view(torch.uint8))
+
+
+@pytest.mark.parametrize("c", [128, 32, 64])
+def test_convnext_block(c):
+    """conv -> layer norm -> linear C->4C + silu -> linear 4C->C + skip, bf16 through the
+    library (the k=1 layers on the streaming kernel or the tiled GEMM by width)."""
+    say(f"[convnext] C={c}")
+    rng = np.random.default_rng(c)
+    grid = (20, 18, 16)
+    coords = workloads.random_sites(rng, 1, grid, 1500)
+    n = len(coords)
+    bf = torch.bfloat16
+    x = torch.from_numpy(rng.standard_normal((n, c), dtype=np.float32)).to(bf)
+    p = {"w": torch.from_numpy(rng.standard_normal((27, c, c), dtype=np.float32) / np.sqrt(27 * c)).to(bf),
+         "b": torch.from_numpy(0.1 * rng.standard_normal(c).astype(np.float32)),
+         "ln_g": torch.from_numpy(1 + 0.1 * rng.standard_normal(c).astype(np.float32)),
+         "ln_b": torch.from_numpy(0.1 * rng.standard_normal(c).astype(np.float32)),
+         "w1": torch.from_numpy(rng.standard_normal((c, 4 * c), dtype=np.float32) / np.sqrt(c)).to(bf),
+         "b1": torch.from_numpy(0.1 * rng.standard_normal(4 * c).astype(np.float32)),
+         "w2": torch.from_numpy(rng.standard_normal((4 * c, c), dtype=np.float32) / np.sqrt(4 * c)).to(bf),
+         "b2": torch.from_numpy(0.1 * rng.standard_normal(c).astype(np.float32))}
+    pd = {k: v.to(DEV) for k, v in p.items()}
+    idx = ssc.SubMIndex(torch.from_numpy(coords).to(DEV), 1, grid)
+    xd = x.to(DEV)
+    h = ssc.subm_conv3d(xd, pd["w"], pd["b"], idx.plan, bf)
+    h = ssc.layer_norm(h, pd["ln_g"], pd["ln_b"], 1e-6, out=h)
+    h = ssc.linear(h, pd["w1"], pd["b1"], bf, act="silu")
+    y = ssc.linear(h, pd["w2"], pd["b2"], bf, residual=xd)
+    ref = blocks.convnext_block(f64(x), oracle.build_map(coords, 1, grid),
+                                {k: f64(v) for k, v in p.items()}, 1e-6)
+    err = rel_err(f64(y), ref)
+    say(f"[convnext]   max|err|/rms = {err:.3e}")
+    assert err <= TAU_BLOCK[bf]
