@@ -2,8 +2,8 @@
 // ConvNeXt-style block; LATO.2 MLX port page, "Status": SparseLinear): out = act(X @ W +
 // bias) + residual for 16-bit X [n, cin] and W, fp32 accumulation on the matrix cores.
 //
-// A workgroup owns 128 rows x CT columns (CT = 64 or 128); its 4 waves own 32 rows each and
-// all CT columns.  The K loop runs in stages of 64: the rows' next stage is loaded into
+// A workgroup owns 128 rows x 64 columns; its 4 waves own 32 rows each and all 64 columns
+// (128-column tiles need 238 VGPRs, 2 waves per SIMD, and ran 10-20% slower).  The K loop runs in stages of 64: the rows' next stage is loaded into
 // registers while the matrix cores consume this one from LDS (16-byte chunks XOR-swizzled by
 // row), then written to the other LDS buffer; the weight fragments (packed per 16-column
 // tile, 1 KB per fragment) go straight from global memory (L2-resident) into VGPRs, one stage
@@ -87,6 +87,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict
       sA[buf][row * 8 + (ch ^ (row & 7))] = r[k];
     }
   };
+  // Bias of this lane's columns, and the wave's residual rows (whole 16-byte pieces, in the
+  // order the epilogue stages them), loaded before the K loop so that their latency is hidden
+  // behind it.
+  constexpr int RPT = 32 * CHUNKS / 64;  // residual pieces per lane
+  float bcol[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) bcol[c] = bias ? bias[(ct0 + c) * 16 + (lane & 15)] : 0.f;
+  const int64_t wrow0 = row0 + wave * 32;
+  const int64_t col0b = static_cast<int64_t>(ct0) * 16 * ESZ;  // byte offset of the tile
+  g_u32x4_t rres[RPT];
+  if (res) {
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int idx = lane + k * 64;
+      const int r = idx / CHUNKS, ch = idx % CHUNKS;
+      const int64_t g = std::min<int64_t>(wrow0 + r, n - 1);
+      rres[k] = *reinterpret_cast<const g_u32x4_t*>(static_cast<const char*>(res) +
+                                                    g * cout * ESZ + col0b + ch * 16);
+    }
+  }
   auto load_b = [&](int st, g_u32x4_t (&b)[2][NCT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -137,26 +157,22 @@ __global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict
   // writes whole 16-byte pieces of rows.  v = act(acc + bias) + residual, rounded once.
   // After the loop's last barrier no wave reads the A stages any more.
   char* sO = smem + wave * 32 * ROWB;
-  const int64_t wrow0 = row0 + wave * 32;
-  const int64_t col0b = static_cast<int64_t>(ct0) * 16 * ESZ;  // byte offset of the tile
   if (res) {
 #pragma unroll
-    for (int k = 0; k < 32 * CHUNKS / 64; ++k) {
+    for (int k = 0; k < RPT; ++k) {
       const int idx = lane + k * 64;
       const int r = idx / CHUNKS, ch = idx % CHUNKS;
-      if (wrow0 + r < n)
-        *reinterpret_cast<g_u32x4_t*>(sO + r * ROWB + ((ch ^ (r & SWM)) << 4)) =
-            *reinterpret_cast<const g_u32x4_t*>(static_cast<const char*>(res) +
-                                                (wrow0 + r) * cout * ESZ + col0b + ch * 16);
+      *reinterpret_cast<g_u32x4_t*>(sO + r * ROWB + ((ch ^ (r & SWM)) << 4)) = rres[k];
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces are in LDS (only it reads them)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the pieces are in LDS (only this wave
+                                         // reads them)
   }
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       const int col = c * 16 + (lane & 15);  // within the tile
-      const float bc = bias ? bias[ct0 * 16 + col] : 0.f;
+      const float bc = bcol[c];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = rt * 16 + (lane >> 4) * 4 + i;
@@ -201,21 +217,12 @@ bool gemm_rows_supported(int cin, int cout) {
 ssc_status gemm_rows_launch(const void* feats, const uint16_t* wp, const float* bias, int64_t n,
                             int cin, int cout, void* out, bool out16, int ek, int act,
                             const void* res, hipStream_t s) {
-  const bool wide = cout % 128 == 0;
   const dim3 grid(static_cast<unsigned>((n + kGRows - 1) / kGRows),
-                  static_cast<unsigned>(cout / (wide ? 128 : 64)));
+                  static_cast<unsigned>(cout / 64));
   const auto* x = static_cast<const uint16_t*>(feats);
-#define SSC_GEMM(CT)                                                                       \
-  {                                                                                        \
-    auto fn = out16 ? (ek == 1 ? k_gemm_rows<CT, true, 1> : k_gemm_rows<CT, true, 0>)      \
-                    : (ek == 1 ? k_gemm_rows<CT, false, 1> : k_gemm_rows<CT, false, 0>);   \
-    hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, x, wp, bias, n, cin, cout, out, act, res); \
-  }
-  if (wide)
-    SSC_GEMM(128)
-  else
-    SSC_GEMM(64)
-#undef SSC_GEMM
+  auto fn = out16 ? (ek == 1 ? k_gemm_rows<64, true, 1> : k_gemm_rows<64, true, 0>)
+                  : (ek == 1 ? k_gemm_rows<64, false, 1> : k_gemm_rows<64, false, 0>);
+  hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, x, wp, bias, n, cin, cout, out, act, res);
   return launch_status();
 }
 
