@@ -363,3 +363,36 @@ def test_convnext_block(c):
     err = rel_err(f64(y), ref)
     say(f"[convnext]   max|err|/rms = {err:.3e}")
     assert err <= TAU_BLOCK[bf]
+
+
+@pytest.mark.parametrize("n,cin,cout,dtype", [(300, 1024, 1024, torch.bfloat16),
+                                              (50, 1024, 1024, torch.float32),
+                                              (130, 1024, 64, torch.float16)])
+def test_maximum_channels_linear(n, cin, cout, dtype):
+    """1024-channel k=1 layers: the tiled GEMM (16-bit) and the vector-ALU kernel (fp32)."""
+    say(f"[max] k1 n={n} {cin}->{cout} {dtype}")
+    rng = np.random.default_rng(cin + n)
+    x = torch.from_numpy(rng.standard_normal((n, cin), dtype=np.float32)).to(dtype)
+    w = (torch.from_numpy(rng.standard_normal((cin, cout), dtype=np.float32)) / np.sqrt(cin)).to(dtype)
+    b = torch.from_numpy(rng.standard_normal(cout, dtype=np.float32))
+    y = ssc.linear(x.to(DEV), w.to(DEV), b.to(DEV), torch.float32, act="relu")
+    ref = blocks.linear_epilogue(f64(x), f64(w), b.numpy(), "relu")
+    assert rel_err(f64(y), ref) <= TAU[dtype]
+
+
+@pytest.mark.parametrize("c,dtype", [(1024, torch.bfloat16), (4096, torch.float32)])
+def test_wide_layer_norm_and_group_norm(c, dtype):
+    """Rows wider than 64 words take the one-thread-per-row layer norm; the group norm with
+    1024 channels keeps its word kernels."""
+    say(f"[max] norms C={c} {dtype}")
+    rng = np.random.default_rng(c)
+    n = 97
+    x = torch.from_numpy((rng.standard_normal((n, c)) + 0.3).astype(np.float32)).to(dtype)
+    ref = blocks.layer_norm(f64(x), eps=1e-6)
+    got = f64(ssc.layer_norm(x.to(DEV), eps=1e-6))
+    assert (np.abs(got - ref) <= ROUND[dtype] * np.abs(ref) + 1e-5 * np.sqrt((ref ** 2).mean())).all()
+    if c <= 1024:
+        coords = np.zeros((n, 4), np.int32)
+        gref = blocks.group_norm(f64(x), coords, 1, 32, eps=1e-5)
+        ggot = f64(ssc.group_norm(x.to(DEV), 1, 32, eps=1e-5))
+        assert (np.abs(ggot - gref) <= ROUND[dtype] * np.abs(gref) + 1e-5 * np.sqrt((gref ** 2).mean())).all()

@@ -388,3 +388,12 @@ def test_fp16_linear(n, cin, cout):
     ref = oracle.linear(x.float().numpy(), w.float().numpy(), b.numpy())
     assert rel_err(y.cpu().numpy(), ref) <= TAU["f16"]
     assert torch.equal(y16.cpu(), y.cpu().to(torch.float16))
+
+
+@pytest.mark.parametrize("cin,cout,dtype", [(1024, 8, torch.bfloat16), (4, 1024, torch.float32)])
+def test_maximum_channels_conv(cin, cout, dtype):
+    """The largest channel counts the entry points accept (1024), on the vector-ALU path."""
+    say(f"[max] k3 cin={cin} cout={cout} {dtype}")
+    coords, x, w, b = small_case(cin * 3 + cout, 1, (6, 5, 4), 0.5, cin, cout, dtype)
+    check_conv(coords, 1, (6, 5, 4), x, w, b,
+               TAU["f32"] if dtype == torch.float32 else TAU["bf16"])
