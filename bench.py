@@ -537,7 +537,7 @@ def main():
         e0.record()
         nbr = ssc.build_index(coords, w.batch, w.grid, check=False)
         e1.record()
-        plan = ssc.build_plan(nbr)
+        plan = ssc.build_plan(nbr, coords, w.batch, w.grid)
         e2.record()
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e2))
@@ -695,7 +695,10 @@ def main():
             "index_gbs": round(w.n * (16 + 108) / (float(np.median(cold_index)) * 1e-3) / 1e9, 1),
             "plan_ms": round(float(np.median(cold_plan)), 4),
             "plan_gbs": round(w.n * (108 + 4 + 108 + 0.25) / (float(np.median(cold_plan)) * 1e-3)
-                              / 1e9, 1)},
+                              / 1e9, 1),
+            # which site order the plan kept: mask order (interleaved tiles) or spatial order
+            # (one contiguous share of the tiles per XCD)
+            "site_order": "spatial" if plan.schedule() == 1 else "mask"},
         "layer_us_per_call_weight_relayout": round(ms_percall * 1e3, 2),
         "k1_layer_us": None if k1_us is None else round(k1_us, 2),
         "host_enqueue_us_per_step": round(t_host * 1e6, 2),

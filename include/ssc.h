@@ -95,16 +95,29 @@ size_t ssc_plan_workspace_bytes(int64_t n);
 
 /* Reorders the sites for the convolution kernels and stores the neighbour rows in that order
  * (the "prepared device index" the LATO.2 page caches per coordinate set).  The plan holds:
- * the site order (rows stably sorted by the rank of their 26-bit mask of valid non-centre
- * taps read as a reflected Gray code, so that 16-row blocks share which taps are present),
- * each 16-row block's tap mask, and the neighbour rows tap-major in that order.  The plan depends only on nbr; it is valid for any features and
+ * the site order, each 16-row block's tap mask, the neighbour rows tap-major in that order,
+ * and the tile schedule the k=3 matrix-core kernel follows.  It is valid for any features and
  * weights and for every k=3 layer on the same coordinate set.
- *   nbr   [n, 27] int32 from ssc_build_index (or any map with the same meaning).
- *   plan  >= ssc_plan_bytes(n) bytes, 256-byte aligned; written completely.
+ * Site order.  Mask order: rows stably sorted by the rank of their 26-bit mask of valid
+ * non-centre taps read as a reflected Gray code, so that 16-row blocks share which taps are
+ * present.  With coords, when the grid holds at least 8 bricks of 128^3 voxels (batch entries
+ * count separately), the spatial order is tried as well: the mask order stably re-sorted by
+ * brick (batch entry, then Morton code of the brick).  It is kept when its count of (16-row
+ * block, tap present) pairs is at most 21/20 of the mask order's; the kernel then gives each
+ * XCD a contiguous share of the tiles, so that each XCD's L2 holds one region's rows.
+ *   nbr    [n, 27] int32 from ssc_build_index (or any map with the same meaning).
+ *   coords [n, 4] int32 rows (b, x, y, z) that nbr was built from, 16-byte aligned, or NULL
+ *          for the mask order only (batch and grid are then ignored).
+ *   batch, grid  as for ssc_build_index (host int32[3]); used with coords only.
+ *   plan   >= ssc_plan_bytes(n) bytes, 256-byte aligned; written completely.
  *   workspace >= ssc_plan_workspace_bytes(n) bytes, 256-byte aligned, scratch only.
- * Bit-reproducible: the same nbr always yields the same plan. */
-ssc_status ssc_build_plan(const int32_t* nbr, int64_t n, void* plan, size_t plan_bytes,
-                          void* workspace, size_t workspace_bytes, void* stream);
+ * Errors: SSC_ERR_ARG for null or misaligned buffers (or coords without grid),
+ * SSC_ERR_UNSUPPORTED for batch or grid outside [1, 65535] (with coords) or n >= 2^31,
+ * SSC_ERR_WORKSPACE for short buffers.
+ * Bit-reproducible: the same arguments always yield the same plan. */
+ssc_status ssc_build_plan(const int32_t* nbr, const int32_t* coords, int64_t n, int32_t batch,
+                          const int32_t* grid, void* plan, size_t plan_bytes, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Where the parts of a plan for n sites live (for inspection and tests; host only, no GPU).
  * Writes layout[0] = npad (rows, n rounded up to a multiple of 256, at least 256), then byte

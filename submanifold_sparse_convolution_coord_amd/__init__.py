@@ -6,7 +6,7 @@ outputs and workspaces with torch, and passes torch's current HIP stream.  There
 fallback: if libssc.so has not been built, importing works but every call raises.
 
     nbr  = build_index(coords, batch, grid)          # [N, 27] int32, -1 = no neighbour
-    plan = build_plan(nbr)                           # warm payload, reused by every layer
+    plan = build_plan(nbr, coords, batch, grid)      # warm payload, reused by every layer
     y    = subm_conv3d(x, w, b, plan)                # k=3, w [27, Cin, Cout]
     y2   = linear(y.to(torch.bfloat16), w1, b1)      # k=1
 
@@ -80,7 +80,7 @@ def load_library():
         "ssc_build_index": ([p, i64, i32, p, p, p, sz, i32, p], ctypes.c_int),
         "ssc_plan_bytes": ([i64], sz),
         "ssc_plan_workspace_bytes": ([i64], sz),
-        "ssc_build_plan": ([p, i64, p, sz, p, sz, p], ctypes.c_int),
+        "ssc_build_plan": ([p, p, i64, i32, p, p, sz, p, sz, p], ctypes.c_int),
         "ssc_plan_layout": ([i64, p], ctypes.c_int),
         "ssc_conv_workspace_bytes": ([i32, i32, i32], sz),
         "ssc_subm_conv3d": ([p, i32, p, p, p, i64, i32, i32, p, i32, p, sz, p], ctypes.c_int),
@@ -176,7 +176,8 @@ def build_index(coords: torch.Tensor, batch: int, grid: Sequence[int],
 
 
 class Plan:
-    """Warm plan of one coordinate set (sites sorted by tap mask, tap-major neighbour rows)."""
+    """Warm plan of one coordinate set (sites sorted by tap mask, or by 128^3 brick and then
+    tap mask; tap-major neighbour rows)."""
 
     def __init__(self, buf: torch.Tensor, n: int):
         self.buf = buf
@@ -199,18 +200,35 @@ class Plan:
         return (view(o_perm, npad), view(o_bm, npad // 16),
                 view(o_g, TAPS * npad).view(TAPS, npad))
 
+    def schedule(self) -> int:
+        """The tile schedule recorded with the site order: 0 interleaved (mask order), 1 one
+        contiguous share of the tiles per XCD (spatial order).  Reads the device header."""
+        return int(self.buf[:64].view(torch.int64)[4].item())
 
-def build_plan(nbr: torch.Tensor) -> Plan:
+
+def build_plan(nbr: torch.Tensor, coords: Optional[torch.Tensor] = None, batch: int = 1,
+               grid: Optional[Sequence[int]] = None) -> Plan:
+    """Warm plan from the neighbour map; with the coordinates (and their batch and grid) the
+    spatial site order is tried too."""
     _need_cuda(nbr, "nbr")
     if nbr.dtype != torch.int32 or nbr.dim() != 2 or nbr.shape[1] != TAPS:
         raise ValueError("nbr must be int32 [N, 27]")
     lib = load_library()
     dev = nbr.device
     n = nbr.shape[0]
+    g = None
+    if coords is not None:
+        _need_cuda(coords, "coords")
+        if coords.dtype != torch.int32 or coords.shape != (n, 4) or not coords.is_contiguous():
+            raise ValueError("coords must be contiguous int32 [N, 4] matching nbr")
+        if grid is None:
+            raise ValueError("grid is required with coords")
+        g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
     buf = _workspace(lib.ssc_plan_bytes(n), dev)
     ws = _workspace(lib.ssc_plan_workspace_bytes(n), dev)
     with torch.cuda.device(dev):
-        st = lib.ssc_build_plan(_ptr(nbr), n, _ptr(buf), buf.numel(), _ptr(ws), ws.numel(),
+        st = lib.ssc_build_plan(_ptr(nbr), None if coords is None else _ptr(coords), n,
+                                int(batch), g, _ptr(buf), buf.numel(), _ptr(ws), ws.numel(),
                                 _stream(dev))
     _check(st, "ssc_build_plan")
     return Plan(buf, n)
@@ -614,7 +632,7 @@ class SubMIndex:
         self.batch = int(batch)
         self.grid = tuple(int(g) for g in grid)
         self.nbr = build_index(coords, batch, grid, check=check)
-        self.plan = build_plan(self.nbr)
+        self.plan = build_plan(self.nbr, coords, batch, grid)
         self.n = int(coords.shape[0])
 
     def conv(self, x, weight, bias=None, out_dtype=None):

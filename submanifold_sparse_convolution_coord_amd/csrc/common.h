@@ -24,7 +24,8 @@ inline ssc_status launch_status() {
 }
 
 // Plan buffer layout (all offsets 256-byte aligned):
-//   header  int64[8]: magic, n, npad, nblocks, reserved...
+//   header  int64[8]: magic, n, npad, nblocks, tile schedule, reserved...
+//           (tile schedule: kSchedInterleaved or kSchedPerXcd, chosen with the site order)
 //   zero    2048 zero bytes   the source of missing neighbour rows (Cin <= 1024 bf16)
 //   perm    int32[npad]       sorted position -> original row, -1 for padding
 //   bmask   uint32[nblocks]   OR of the tap-validity masks of the 16 rows of each block
@@ -32,6 +33,16 @@ inline ssc_status launch_status() {
 constexpr int64_t kPlanMagic = 0x5353435031LL;  // "SSCP1"
 constexpr int kPlanRowAlign = 256;              // npad is a multiple of this
 constexpr int kBlockRows = 16;                  // rows per MFMA block
+constexpr int kPlanSchedWord = 4;               // header word holding the tile schedule
+// Tile schedules of the k=3 matrix-core kernel (which workgroup takes which tile):
+//   interleaved  workgroup b takes tile T-1-b: the hardware deals consecutive workgroups to
+//                the 8 XCDs in turn, so every XCD sweeps the whole order, heaviest tiles first.
+//   per XCD      XCD x (workgroups b with b % 8 == x) takes the x-th contiguous eighth of the
+//                tiles, in order: with a spatially ordered plan each XCD's L2 then holds the
+//                rows of one region and its halo.
+constexpr int64_t kSchedInterleaved = 0;
+constexpr int64_t kSchedPerXcd = 1;
+constexpr int kXcds = 8;
 
 struct PlanLayout {
   int64_t n, npad, nblocks;

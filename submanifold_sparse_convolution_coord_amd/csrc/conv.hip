@@ -337,7 +337,8 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
     const float* __restrict__ bias, const int32_t* __restrict__ perm,
     const uint32_t* __restrict__ bmask, const int32_t* __restrict__ gidx,
-    const uint16_t* __restrict__ zrow, int64_t npad, void* __restrict__ Y, Epi ep) {
+    const uint16_t* __restrict__ zrow, const int64_t* __restrict__ sched, int64_t npad,
+    void* __restrict__ Y, Epi ep) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_BYTES];
   const char* sA0 = smem;
@@ -351,15 +352,26 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int wr = wave / WC, wc = wave % WC;
   const uint32_t lds0 = lds_addr(smem);
-  // The plan sorts sites by tap mask, so per-tile work grows along the site order (a tile of
-  // near-empty masks has a tap or two, the last tiles a dozen or more).  Launch the heavy
-  // end first so that the workgroups dispatched last are the short ones.
-  const int64_t tile = static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x;
+  // Which tile this workgroup takes follows the plan's schedule.  Interleaved: the mask order
+  // makes per-tile work grow along the sites (a tile of near-empty masks has a tap or two, the
+  // last tiles a dozen or more), so the heavy end goes first and the workgroups dispatched
+  // last are the short ones.  Per XCD: consecutive workgroups go to the 8 XCDs in turn, and
+  // XCD x takes the x-th contiguous eighth of a spatially ordered plan, in order.  Both
+  // candidates' block masks are fetched while the schedule word is read, so choosing costs no
+  // extra round trip.
+  const int64_t tiles = gridDim.x;
+  const int64_t t_il = tiles - 1 - blockIdx.x;
+  const int64_t xcd = blockIdx.x % kXcds, per = tiles / kXcds, extra = tiles % kXcds;
+  const int64_t t_px = xcd * per + (xcd < extra ? xcd : extra) + blockIdx.x / kXcds;
+  const uint32_t bm_il = lane < NB ? bmask[t_il * NB + lane] : 0u;
+  const uint32_t bm_px = lane < NB ? bmask[t_px * NB + lane] : 0u;
+  const bool per_xcd = sched[0] == kSchedPerXcd;
+  const int64_t tile = per_xcd ? t_px : t_il;
   const int64_t row0 = tile * (NB * 16);
 
   // Block tap masks: lane b holds block b's (for the per-tap block sets, one ballot each), and
   // their union U is the set of taps the tile walks.
-  const uint32_t bmv = lane < NB ? bmask[tile * NB + lane] : 0u;
+  const uint32_t bmv = per_xcd ? bm_px : bm_il;
   uint32_t U = bmv;
 #pragma unroll
   for (int off = 1; off < NB; off <<= 1) U |= __shfl_xor(U, off, 64);
@@ -899,7 +911,8 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
 using LinFn = void (*)(const uint16_t*, const uint16_t*, const float*, int64_t, void*, int,
                       const void*);
 using LdsFn = void (*)(const uint16_t*, const uint16_t*, const float*, const int32_t*,
-                       const uint32_t*, const int32_t*, const uint16_t*, int64_t, void*, Epi);
+                       const uint32_t*, const int32_t*, const uint16_t*, const int64_t*,
+                       int64_t, void*, Epi);
 
 // k=1 streaming kernel for the channel counts the matrix-core path is built for.
 template <int CI, int CO, bool O16, int EK>
@@ -998,7 +1011,8 @@ ssc_status launch_lds(LdsFn fn, int threads, int rows_per_tile, const void* feat
                      reinterpret_cast<const int32_t*>(pb + P.off_perm),
                      reinterpret_cast<const uint32_t*>(pb + P.off_bmask),
                      reinterpret_cast<const int32_t*>(pb + P.off_gidx),
-                     reinterpret_cast<const uint16_t*>(pb + P.off_zero), P.npad, out, ep);
+                     reinterpret_cast<const uint16_t*>(pb + P.off_zero),
+                     reinterpret_cast<const int64_t*>(pb) + kPlanSchedWord, P.npad, out, ep);
   return launch_status();
 }
 

@@ -75,13 +75,28 @@ def test_build_index_argument_errors(lib):
 
 def test_build_plan_argument_errors(lib):
     f = lib.ssc_build_plan
-    assert f(FAKE, -1, FAKE, 1 << 30, FAKE, 1 << 30, None) == ssc.SSC_ERR_ARG
-    assert f(None, 10, FAKE, 1 << 30, FAKE, 1 << 30, None) == ssc.SSC_ERR_ARG
-    assert f(FAKE, 10, None, 1 << 30, FAKE, 1 << 30, None) == ssc.SSC_ERR_ARG
-    assert f(FAKE, 10, FAKE, 64, FAKE, 1 << 30, None) == ssc.SSC_ERR_WORKSPACE
-    assert f(FAKE, 10, FAKE, 1 << 30, FAKE, 8, None) == ssc.SSC_ERR_WORKSPACE
-    assert f(FAKE, 10, ctypes.c_void_p((1 << 20) + 16), 1 << 30, FAKE, 1 << 30,
-             None) == ssc.SSC_ERR_ARG
+    big = 1 << 30
+
+    def call(nbr=FAKE, coords=None, n=10, batch=1, grid=GRID, plan=FAKE, pb=big, ws=FAKE,
+             wsb=big):
+        return f(nbr, coords, n, batch, grid, plan, pb, ws, wsb, None)
+
+    assert call(n=-1) == ssc.SSC_ERR_ARG
+    assert call(nbr=None) == ssc.SSC_ERR_ARG
+    assert call(plan=None) == ssc.SSC_ERR_ARG
+    assert call(pb=64) == ssc.SSC_ERR_WORKSPACE
+    assert call(wsb=8) == ssc.SSC_ERR_WORKSPACE
+    assert call(plan=ctypes.c_void_p((1 << 20) + 16)) == ssc.SSC_ERR_ARG
+    # with coordinates: grid required, coords 16-byte aligned, batch and grid in range
+    assert call(coords=FAKE, grid=None) == ssc.SSC_ERR_ARG
+    assert call(coords=ctypes.c_void_p((1 << 20) + 4)) == ssc.SSC_ERR_ARG
+    assert call(coords=FAKE, batch=0) == ssc.SSC_ERR_UNSUPPORTED
+    assert call(coords=FAKE, batch=70000) == ssc.SSC_ERR_UNSUPPORTED
+    assert call(coords=FAKE, grid=(ctypes.c_int32 * 3)(8, 0, 8)) == ssc.SSC_ERR_UNSUPPORTED
+    assert call(coords=FAKE, grid=(ctypes.c_int32 * 3)(8, 65536, 8)) == ssc.SSC_ERR_UNSUPPORTED
+    assert call(coords=FAKE, wsb=8) == ssc.SSC_ERR_WORKSPACE
+    # without coordinates, batch and grid are not looked at
+    assert call(batch=0, grid=None, wsb=8) == ssc.SSC_ERR_WORKSPACE
 
 
 def test_conv_argument_errors(lib):

@@ -322,15 +322,41 @@ def gray_rank_keys(nbr: np.ndarray) -> np.ndarray:
     return rank
 
 
-@pytest.mark.parametrize("name", ["tiny", "batch4", "iid128"])
-def test_plan_structure(name):
-    """The plan is a stable sort of the sites by Gray rank of their tap mask, with every
-    part (row ids, block masks, tap-major neighbour rows) consistent with the map."""
-    say(f"[plan] {name}")
-    w, m = workload_case(name)
-    idx = run_gpu(w.coords, w.batch, w.grid)
-    nbr = idx.nbr.cpu().numpy()
-    np.testing.assert_array_equal(nbr, m)
+def morton3(bx, by, bz, bits):
+    key = np.zeros(len(bx), np.int64)
+    for k in range(bits):
+        key |= ((bx >> k) & 1) << (3 * k + 2)
+        key |= ((by >> k) & 1) << (3 * k + 1)
+        key |= ((bz >> k) & 1) << (3 * k)
+    return key
+
+
+def block_tap_pairs(nbr_sorted: np.ndarray) -> int:
+    """(16-row block, non-centre tap present) pairs of a site order."""
+    valid = np.delete(nbr_sorted >= 0, 13, axis=1)
+    pad = (-len(valid)) % 16
+    valid = np.concatenate([valid, np.zeros((pad, 26), bool)]).reshape(-1, 16, 26)
+    return int(valid.any(axis=1).sum())
+
+
+def expected_site_order(coords, batch, grid, m):
+    """The plan's site order from its definition: the mask order (stable sort by Gray rank);
+    when the grid holds >= 8 bricks of 128^3 (batch entries apart), also the brick order (the
+    mask order stably re-sorted by (entry, Morton code of the brick)), kept when its
+    (block, tap) pairs are at most 21/20 of the mask order's.  Returns (order, spatial)."""
+    mask_order = np.argsort(gray_rank_keys(m), kind="stable")
+    per_axis = [(g - 1) // 128 + 1 for g in grid]
+    if batch * np.prod(per_axis) < 8:
+        return mask_order, False
+    bits = max(int(np.ceil(np.log2(p))) if p > 1 else 0 for p in per_axis)
+    c = coords.astype(np.int64)[mask_order]
+    key = (c[:, 0] << (3 * bits)) | morton3(c[:, 1] >> 7, c[:, 2] >> 7, c[:, 3] >> 7, bits)
+    brick_order = mask_order[np.argsort(key, kind="stable")]
+    spatial = block_tap_pairs(m[brick_order]) * 20 <= block_tap_pairs(m[mask_order]) * 21
+    return (brick_order if spatial else mask_order), spatial
+
+
+def check_plan(idx, coords, batch, grid, m):
     perm, bmask, gidx = (t.cpu().numpy() for t in idx.plan.parts())
     n, npad = len(m), perm.shape[0]
     assert npad % 256 == 0 and npad >= n
@@ -339,10 +365,52 @@ def test_plan_structure(name):
     bits = ((gidx >= 0).astype(np.int64) << np.arange(27)[:, None]).reshape(27, -1, 16)
     want = np.bitwise_or.reduce(np.bitwise_or.reduce(bits, axis=2), axis=0)
     assert np.array_equal(bmask.astype(np.uint32).astype(np.int64), want)
-    keys = gray_rank_keys(m)[perm[:n]]
-    assert (np.diff(keys) >= 0).all()
-    same = np.diff(keys) == 0
-    assert (np.diff(perm[:n])[same] > 0).all()          # stable among equal keys
+    order, spatial = expected_site_order(coords, batch, grid, m)
+    assert np.array_equal(perm[:n], order)
+    assert idx.plan.schedule() == (1 if spatial else 0)
+    return spatial
+
+
+@pytest.mark.parametrize("name,spatial", [("tiny", False), ("batch4", False), ("iid128", False),
+                                          ("shell256", True), ("shell512", True)])
+def test_plan_structure(name, spatial):
+    """The plan's site order is the stable sort by Gray rank of the tap mask, or (surfaces on
+    grids of 8 or more 128^3 bricks) that order re-sorted by brick, with every part (row ids,
+    block masks, tap-major neighbour rows, tile schedule) consistent with the map."""
+    say(f"[plan] {name}")
+    w, m = workload_case(name)
+    idx = run_gpu(w.coords, w.batch, w.grid)
+    np.testing.assert_array_equal(idx.nbr.cpu().numpy(), m)
+    assert check_plan(idx, w.coords, w.batch, w.grid, m) == spatial
+    if not spatial:
+        keys = gray_rank_keys(m)[idx.plan.parts()[0][:w.n].cpu().numpy()]
+        assert (np.diff(keys) >= 0).all()
+
+
+def test_plan_spatial_candidate_rejected_and_batched():
+    """Sparse i.i.d. sites on a grid of 8 bricks: the brick order costs far more than 5% extra
+    (block, tap) pairs, so the mask order stays; a batch of 8 small surfaces counts 8 bricks
+    and takes the spatial order.  Both plans convolve to the oracle's result."""
+    rng = np.random.default_rng(41)
+    coords = workloads.random_sites(rng, 1, (256, 256, 256), 200000)
+    m = oracle.build_map(coords, 1, (256, 256, 256))
+    idx = run_gpu(coords, 1, (256, 256, 256))
+    assert not check_plan(idx, coords, 1, (256, 256, 256), m)
+    occ = np.zeros((8, 48, 48, 48), bool)
+    g = np.indices((48, 48, 48)) - 23.5
+    for b in range(8):
+        r = np.sqrt(((g / (np.array([15, 17, 19]) + b % 3)[:, None, None, None]) ** 2).sum(0))
+        occ[b] = np.abs(r - 1.0) < 0.12
+    coords = np.ascontiguousarray(np.argwhere(occ), dtype=np.int32)
+    m = oracle.build_map(coords, 8, (48, 48, 48))
+    idx = run_gpu(coords, 8, (48, 48, 48))
+    assert check_plan(idx, coords, 8, (48, 48, 48), m)
+    x = torch.from_numpy(rng.standard_normal((len(coords), 64), dtype=np.float32)).bfloat16()
+    wt = (torch.from_numpy(rng.standard_normal((27, 64, 64), dtype=np.float32)) / 40).bfloat16()
+    y = idx.conv(x.to(DEV), wt.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.conv(x.float().numpy(), wt.float().numpy(), None, m)
+    assert rel_err(y.cpu().numpy(), ref) <= TAU["bf16"]
 
 
 @pytest.mark.parametrize("cin,cout", [(32, 16), (64, 64), (128, 128), (64, 128), (128, 32)])
