@@ -9,7 +9,8 @@
 // page, version history).  Here the whole layer is ONE kernel, output-stationary:
 //
 //   * a workgroup owns a tile of NB 16-row blocks of the plan's site order (sites sorted by
-//     their tap-validity mask, so a block's rows mostly share which taps exist);
+//     their tap-validity mask, so a block's rows mostly share which taps exist; on surfaces
+//     first by 128^3 brick, with the tiles dealt to the XCDs in contiguous shares);
 //   * for every tap present in the tile, each wave loads its slice of W[t] into registers as
 //     matrix-core B fragments, then, for each block whose mask has tap t, gathers the 16
 //     neighbour rows straight from HBM/L2 into A fragments (a missing neighbour is a zero row,
@@ -936,13 +937,15 @@ LinFn pick_linear(int cin, int cout, bool out16, int ek, int* wc_groups, int* ro
   return nullptr;
 }
 
-// k=3 pipelined kernel: 4 waves as WR x WC, tile of NB blocks (NB = 8 keeps two gather
-// stages plus the indices under 80 KB of LDS, so two workgroups share a CU).
+// k=3 pipelined kernel: 4 waves as WR x WC, tile of NB = 8 blocks.  At Cin = 128 that keeps
+// two gather stages plus the indices under 80 KB of LDS, so two workgroups share a CU;
+// narrower rows leave room for more, and at Cin = 32 the extra workgroups keep more gathers
+// in flight than 16-block tiles did (512^3 surface, C 32: 159 -> 130 us).
 template <int CI, int CO>
 struct LdsPick {
   static constexpr int WC = CO >= 64 ? 4 : CO / 16;
   static constexpr int WR = 4 / WC;
-  static constexpr int NB = (CI >= 64 || CO > 64) ? 8 : 16;
+  static constexpr int NB = 8;
 };
 
 template <int CI, int CO, bool O16, int EK>
