@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ Wp,
                                                       const float* __restrict__ bias, int64_t n,
                                                       int cin, int cout, void* Y, int act,
-                                                      const void* res) {
+                                                      const void* res, int64_t row_tiles) {
   constexpr int NCT = CT / 16;  // 16-column tiles (every wave has all of them)
   constexpr int ESZ = OUT16 ? 2 : 4;
   constexpr int ROWB = CT * ESZ;          // bytes of a wave's output row
@@ -63,10 +63,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict
   __shared__ __attribute__((aligned(16))) char smem[OUT_BYTES > A_BYTES ? OUT_BYTES : A_BYTES];
   // two 16 KB stages of 128 rows x 8 chunks of 16 bytes
   auto* sA = reinterpret_cast<g_u32x4_t (*)[kGRows * kGK / 8]>(smem);
+  // Workgroup -> (row tile, column tile).  The hardware deals consecutive workgroups to the
+  // 8 XCDs in turn; XCD x takes row tiles x, x + 8, ... and each with all its column tiles
+  // back to back, so the workgroups that read the same 128 input rows run together on one
+  // XCD and share its L2 (spread over the XCDs, every XCD fetched the rows again; C -> 4C at
+  // 128 channels and 209K rows: 111 -> 108 us).
+  const int col_tiles = cout / CT;
+  const int64_t xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int64_t rt = (j / col_tiles) * 8 + xcd;
+  if (rt >= row_tiles) return;  // the grid is rounded up to whole groups of 8 row tiles
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kGRows;
-  const int ct0 = blockIdx.y * NCT;  // first 16-column tile of this workgroup
+  const int64_t row0 = rt * kGRows;
+  const int ct0 = static_cast<int>(j % col_tiles) * NCT;  // first 16-column tile
   const int ksteps = cin / 32;       // fragment index stride of a column tile
   const int stages = cin / kGK;
 
@@ -217,12 +226,13 @@ bool gemm_rows_supported(int cin, int cout) {
 ssc_status gemm_rows_launch(const void* feats, const uint16_t* wp, const float* bias, int64_t n,
                             int cin, int cout, void* out, bool out16, int ek, int act,
                             const void* res, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((n + kGRows - 1) / kGRows),
-                  static_cast<unsigned>(cout / 64));
+  const int64_t row_tiles = (n + kGRows - 1) / kGRows;
   const auto* x = static_cast<const uint16_t*>(feats);
+  const int64_t grid = (row_tiles + 7) / 8 * 8 * (cout / 64);
   auto fn = out16 ? (ek == 1 ? k_gemm_rows<64, true, 1> : k_gemm_rows<64, true, 0>)
                   : (ek == 1 ? k_gemm_rows<64, false, 1> : k_gemm_rows<64, false, 0>);
-  hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, x, wp, bias, n, cin, cout, out, act, res);
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, x, wp, bias, n, cin,
+                     cout, out, act, res, row_tiles);
   return launch_status();
 }
 

@@ -287,12 +287,14 @@ def test_res_block(dtype, batch, c, groups):
 
 
 @pytest.mark.parametrize("n,cin,cout,dtype,odt,act", [
-    (1000, 128, 512, torch.bfloat16, torch.float32, "silu"),    # tiled GEMM, 128-column tiles
+    (1000, 128, 512, torch.bfloat16, torch.float32, "silu"),    # 8 column tiles per row tile
     (777, 512, 128, torch.bfloat16, torch.bfloat16, "none"),
     (333, 64, 256, torch.float16, torch.float16, "relu"),
-    (513, 256, 64, torch.bfloat16, torch.float32, "silu"),      # 64-column tiles
+    (513, 256, 64, torch.bfloat16, torch.float32, "silu"),
     (129, 192, 192, torch.bfloat16, torch.bfloat16, "none"),
     (1, 128, 512, torch.bfloat16, torch.float32, "none"),
+    (4097, 64, 1024, torch.bfloat16, torch.bfloat16, "silu"),   # 16 column tiles
+    (255, 128, 192, torch.float16, torch.float32, "none"),      # 3 column tiles, 2 row tiles
 ])
 def test_wide_linear(n, cin, cout, dtype, odt, act):
     say(f"[gemm] n={n} {cin}->{cout} {dtype} -> {odt} act={act}")
