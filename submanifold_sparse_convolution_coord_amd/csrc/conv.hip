@@ -322,7 +322,7 @@ struct Epi {
   int gn_groups;     // with gn: groups of cout / gn_groups channels, a power of two <= 16
 };
 
-// One output value of a residual row (the output's own type).
+// One value of the output's own type (a residual element, here read where it is staged).
 template <bool OUT16, int EK>
 __device__ __forceinline__ float load_out(const void* p, int64_t i) {
   if constexpr (!OUT16) return static_cast<const float*>(p)[i];
@@ -762,11 +762,15 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ X, cons
 // Per tile: the next tile's rows are copied into the other LDS buffer (direct global->LDS
 // loads, whole 1 KB copies) while the matrix cores work on this one; the outputs plus bias
 // are staged in LDS and leave as contiguous 16-byte stores of whole rows.
-// The only vector-memory operations in the loop are those copies and the output stores, and
-// both retire in issue order, so "this tile's copies have landed" is "at most STORES (the
-// previous tile's stores, issued after them) are outstanding": the loop waits for exactly
-// that, not for the stores.  Only the last tile of the layer can be partial, and it is the
-// last tile its workgroup handles; rows past n are copied from row n-1 and never stored.
+// The only vector-memory operations in the loop are those copies, the residual's copies and
+// the output stores, and they retire in issue order, so "this tile's copies have landed" is
+// "at most STORES (the previous tile's stores, issued after them) are outstanding": the loop
+// waits for exactly that, not for the stores.  A residual is copied the same way, straight
+// into the output staging tile (before the next tile's rows, so waiting for it leaves those
+// in flight), and added where each output is staged; a per-element global load there would
+// make the compiler drain every copy in flight before it.  Only the last tile of the layer
+// can be partial, and it is the last tile its workgroup handles; rows past n are copied from
+// row n-1 and never stored.
 // ------------------------------------------------------------------------------------------
 template <int CIN, int COUT, bool OUT16>
 struct LinCfg {
@@ -815,6 +819,27 @@ __device__ __forceinline__ void linear_copies(int64_t tile, int64_t n,
   }
 }
 
+// The residual rows of a tile into the output staging tile, in its swizzled layout: lane l of
+// copy j fills 16 bytes at j * 1024 + 16 l, i.e. physical chunk p of some row, so it reads
+// that row's logical chunk p ^ (row & SWM).
+template <int CIN, int COUT, bool OUT16>
+__device__ __forceinline__ void residual_copies(int64_t row0, int64_t n, const void* res,
+                                                char* sOut, int wave, int lane) {
+  using L = LinCfg<CIN, COUT, OUT16>;
+  constexpr int RCPW = L::OBUF / 1024 / L::C::WAVES;
+  static_assert(L::OBUF % (1024 * L::C::WAVES) == 0, "residual copy shape");
+#pragma unroll
+  for (int i = 0; i < RCPW; ++i) {
+    const int j = i * L::C::WAVES + wave;
+    const int o = j * 1024 + lane * 16;
+    const int row = o / L::ROWB, p = (o % L::ROWB) >> 4;
+    const int ch = p ^ (row & L::SWM);
+    int64_t g = row0 + row;
+    g = g < n ? g : n - 1;
+    dma16(static_cast<const char*>(res) + g * L::ROWB + ch * 16, lds_addr(sOut + j * 1024));
+  }
+}
+
 template <int CIN, int COUT, bool OUT16, int EK, bool EPI>
 __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __restrict__ X,
                                                           const uint16_t* __restrict__ Wp,
@@ -852,6 +877,10 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
       wait_vm_n_lgkm0<L::STORES>();
     __builtin_amdgcn_s_barrier();
     char* cur = (k & 1) ? sX1 : sX0;
+    const int64_t row0 = tile * L::TR;
+    // The staging tile is free: the previous tile's reads of it finished before the barrier.
+    if constexpr (EPI)
+      if (res) residual_copies<CIN, COUT, OUT16>(row0, n, res, sOut, wave, lane);
     const int64_t next = tile + gridDim.x;
     if (next < tiles) linear_copies<CIN, COUT, OUT16>(next, n, X, (k & 1) ? sX0 : sX1, wave, lane);
 
@@ -870,8 +899,17 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
           acc[bl][c] = mfma16x16x32<EK>(a[s], bw[c][s], acc[bl][c]);
       }
     }
-    // Stage the outputs: act(acc + bias) + residual (16-byte chunks XOR-swizzled by row).
-    const int64_t row0 = tile * L::TR;
+    // Stage the outputs: act(acc + bias) + residual (16-byte chunks XOR-swizzled by row).  The
+    // residual copies were issued before the next tile's, so these are waited for alone.
+    if constexpr (EPI) {
+      if (res) {
+        if (next < tiles)
+          wait_vm_n_lgkm0<L::CPW>();
+        else
+          wait_vm_lgkm0();
+        __builtin_amdgcn_s_barrier();
+      }
+    }
 #pragma unroll
     for (int bl = 0; bl < C::BPW; ++bl) {
       const int b = bl * L::WR + wr;
@@ -886,7 +924,7 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
           float v = acc[bl][c][i] + bv[c];
           if constexpr (EPI) {
             v = apply_act(v, act);
-            if (res && row0 + row < n) v += load_out<OUT16, EK>(res, (row0 + row) * COUT + col);
+            if (res) v += load_out<OUT16, EK>(dst, 0);  // the staged residual value
           }
           if (OUT16)
             *reinterpret_cast<uint16_t*>(dst) = to16<EK>(v);
@@ -995,9 +1033,12 @@ int device_cu_count() {
 
 ssc_status launch_linear(LinFn fn, int rows_per_tile, const void* feats, const uint16_t* wp,
                          const float* bias, int64_t n, void* out, const Epi& ep, hipStream_t s) {
-  // Persistent: two resident workgroups per compute unit, each walking tiles with a stride.
+  // Persistent: four resident workgroups per compute unit, each walking tiles with a stride.
+  // Two keep HBM as busy for the plain map; a silu epilogue (an exp and a reciprocal per
+  // output) needs the other two to overlap with the copies (1.2M rows, 32 -> 128 + silu:
+  // 119 -> 84 us).
   const int64_t tiles = (n + rows_per_tile - 1) / rows_per_tile;
-  const int64_t grid = std::min<int64_t>(tiles, 2 * static_cast<int64_t>(device_cu_count()));
+  const int64_t grid = std::min<int64_t>(tiles, 4 * static_cast<int64_t>(device_cu_count()));
   hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(feats), wp, bias, n, out, ep.act, ep.res);
   return launch_status();

@@ -117,6 +117,9 @@ def test_packed_epilogue_equals_per_call(cin, cout):
     (4097, 128, 128, torch.bfloat16, torch.bfloat16, "relu"),
     (333, 32, 64, torch.float16, torch.float16, "silu"),
     (77, 16, 16, torch.float32, torch.float32, "silu"),          # vector-ALU path
+    (200000, 128, 32, torch.bfloat16, torch.bfloat16, "none"),   # several tiles per workgroup
+    (70001, 32, 16, torch.float16, torch.float32, "relu"),       # 128-row tiles, ragged end
+    (1, 64, 64, torch.bfloat16, torch.bfloat16, "silu"),
 ])
 def test_linear_epilogue(n, cin, cout, dtype, odt, act):
     say(f"[epi] linear n={n} {cin}->{cout} {dtype} act={act}")
