@@ -244,6 +244,35 @@ def test_conv_group_norm_statistics_shapes(cin, cout, groups, n_sites, dtype):
         assert torch.equal(parts.sums(), ssc.gn_partials(y, 1, groups).sums())
 
 
+def test_spatial_plan_epilogue_and_statistics():
+    """A surface on a 256^3 grid takes the spatial site order and the per-XCD tile
+    schedule; the fused epilogue (silu, residual) and the group-norm statistics summed in the
+    kernel (slots indexed by tile) hold there as on the interleaved schedule."""
+    say("[gn] spatial plan: epilogue and fused statistics")
+    rng = np.random.default_rng(77)
+    occ, _ = workloads.shell_occupancy(rng, 256, 40.0, 60.0, 1.0)
+    coords = workloads.coords_from_occupancy([occ])
+    n = len(coords)
+    idx = index(coords, 1, (256, 256, 256))
+    assert idx.plan.schedule() == 1
+    x = torch.from_numpy(rng.standard_normal((n, 64), dtype=np.float32)).bfloat16()
+    w = (torch.from_numpy(rng.standard_normal((27, 64, 64), dtype=np.float32)) / 40).bfloat16()
+    b = torch.from_numpy(rng.standard_normal(64, dtype=np.float32) * 0.5)
+    res = torch.from_numpy(rng.standard_normal((n, 64), dtype=np.float32))
+    parts = ssc.GroupNormPartials(n, 1, 32, DEV)
+    y = ssc.subm_conv3d(x.to(DEV), w.to(DEV), b.to(DEV), idx.plan, torch.float32, act="silu",
+                        residual=res.to(DEV), gn=parts)
+    m = oracle.build_map(coords, 1, (256, 256, 256))
+    ref = blocks.conv_epilogue(f64(x), f64(w), b.numpy(), m, "silu", f64(res))
+    err = rel_err(f64(y), ref)
+    say(f"[gn]   n={n} max|err|/rms = {err:.3e}")
+    assert err <= TAU[torch.bfloat16]
+    fused = ssc.gn_finalize(parts).cpu().numpy().astype(np.float64)
+    mean, var = blocks.group_stats(f64(y), np.zeros((n, 4), np.int32), 1, 32)
+    assert np.abs(fused[..., 0] - mean).max() <= 1e-5 * np.sqrt(var.max())
+    np.testing.assert_allclose(fused[..., 1], 1 / np.sqrt(var + 1e-5), rtol=2e-5)
+
+
 def res_block_gpu(x, coords_d, batch, plan, p, groups, eps, packed=False):
     """The pre-norm residual block through the library: statistics + apply for the first
     norm, conv1 summing the second norm's statistics in its epilogue, apply, conv2 adding
