@@ -166,9 +166,11 @@ __global__ void k_plan_header(int64_t* __restrict__ header, int64_t n, int64_t n
 constexpr int kKeyBits = 26;                     // the plan's sort key (Gray rank of the mask)
 constexpr int kBrickShift = 7;                   // spatial order: bricks of 128^3 voxels
 constexpr int64_t kMinBricks = 8;                // ... tried when the grid holds this many
+constexpr int kCountSlots = 64;                  // (block, tap) counts: slots of partial sums
 
 // The plan's scratch: the mask-order sort (32-bit keys), the brick sort (64-bit keys), each
-// site's tap mask, and the two orders' (block, tap) counts.
+// site's tap mask, and the two orders' (block, tap) counts in kCountSlots slots each (one
+// counter took every wave's atomic add and serialised them: 0.46 ms at 1.2M sites).
 struct PlanWork {
   SortLayout<uint32_t> g;
   SortLayout<uint64_t> b;
@@ -180,18 +182,18 @@ inline PlanWork plan_work_layout(int64_t n) {
   W.b = sort_layout<uint64_t>(n, W.g.total);
   W.off_mask = align_up(W.b.total);
   W.off_count = align_up(W.off_mask + sizeof(uint32_t) * (n > 0 ? n : 1));
-  W.total = align_up(W.off_count + 2 * sizeof(unsigned long long));
+  W.total = align_up(W.off_count + 2 * kCountSlots * sizeof(unsigned long long));
   return W;
 }
 
 // Sort key of a site: bit (t < 13 ? t : t - 1) set when non-centre tap t has a neighbour.
-// With masks non-null the plain mask is kept too, and block 0 clears the two counters.
+// With masks non-null the plain mask is kept too, and block 0 clears the count slots.
 __global__ void k_mask_keys(const int32_t* __restrict__ nbr, int64_t n, uint32_t* __restrict__ keys,
                             uint32_t* __restrict__ vals, uint32_t* __restrict__ totals,
                             uint32_t* __restrict__ masks, unsigned long long* __restrict__ counts) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (blockIdx.x == 0 && threadIdx.x < kDigits) totals[threadIdx.x] = 0;
-  if (masks != nullptr && blockIdx.x == 0 && threadIdx.x < 2) counts[threadIdx.x] = 0;
+  if (masks != nullptr && blockIdx.x == 0 && threadIdx.x < 2 * kCountSlots) counts[threadIdx.x] = 0;
   if (i >= n) return;
   const int32_t* row = nbr + i * kTaps;
   uint32_t m = 0;
@@ -242,8 +244,9 @@ __global__ void k_brick_keys(const int4* __restrict__ coords, const uint32_t* __
 }
 
 // (block, tap) pairs of the two candidate orders: for every 16-position block, the number of
-// non-centre taps present in any of its sites, summed into counts[0] (mask order) and
-// counts[1] (brick order).  One wave covers 4 blocks of each order.
+// non-centre taps present in any of its sites.  One wave covers 4 blocks of each order; the
+// workgroup's sums go to slot blockIdx % kCountSlots (counts[2 s] mask order, counts[2 s + 1]
+// brick order).
 __global__ __launch_bounds__(256) void k_block_taps(const uint32_t* __restrict__ rows_mask,
                                                     const uint32_t* __restrict__ rows_brick,
                                                     const uint32_t* __restrict__ masks, int64_t n,
@@ -264,9 +267,18 @@ __global__ __launch_bounds__(256) void k_block_taps(const uint32_t* __restrict__
     cg += __shfl_xor(cg, off, 64);
     cb += __shfl_xor(cb, off, 64);
   }
+  __shared__ uint32_t wsum[2][4];
+  const int wave = threadIdx.x >> 6;
   if (lane == 0) {
-    atomicAdd(&counts[0], static_cast<unsigned long long>(cg));
-    atomicAdd(&counts[1], static_cast<unsigned long long>(cb));
+    wsum[0][wave] = cg;
+    wsum[1][wave] = cb;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const uint32_t t = wsum[threadIdx.x][0] + wsum[threadIdx.x][1] + wsum[threadIdx.x][2] +
+                       wsum[threadIdx.x][3];
+    atomicAdd(&counts[2 * (blockIdx.x % kCountSlots) + threadIdx.x],
+              static_cast<unsigned long long>(t));
   }
 }
 
@@ -289,7 +301,14 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ n
                                          // wave's column reads hit distinct banks
   __shared__ int32_t src[256];
   const int tid = threadIdx.x;
-  const bool spatial = counts != nullptr && counts[1] * 20 <= counts[0] * 21;
+  __shared__ unsigned long long total[2];
+  if (counts != nullptr && tid < 2) {
+    unsigned long long t = 0;
+    for (int k = 0; k < kCountSlots; ++k) t += counts[2 * k + tid];
+    total[tid] = t;
+  }
+  __syncthreads();
+  const bool spatial = counts != nullptr && total[1] * 20 <= total[0] * 21;
   const uint32_t* sorted_rows = spatial ? brick_rows : mask_rows;
   if (blockIdx.x == 0 && tid == 0)
     header[kPlanSchedWord] = spatial ? kSchedPerXcd : kSchedInterleaved;
