@@ -85,4 +85,35 @@ __device__ __forceinline__ float apply_act(float v, int act) {
   return v;
 }
 
+// LDS byte address of a __shared__ location (wave-uniform in every use).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// One direct global->LDS copy (global_load_lds_dwordx4): every active lane fetches 16 bytes
+// from its own global address and the hardware writes them to LDS at lds_base + 16*lane.
+// Written as inline asm, not the builtin, on purpose: the compiler then does not treat the
+// copy as a pending write to every LDS location, which would otherwise make it drain all
+// copies (vmcnt 0) before each LDS read and serialize the pipeline.  The instruction has no
+// destination register (the data goes to LDS; the address VGPRs are read at issue), and
+// every wait for these copies is explicit in the kernel (wait_vm_lgkm0 before each barrier).
+// m0 (which holds the LDS base) is saved and restored inside the statement, so the compiler's
+// view of every register is unchanged by it.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+// s_waitcnt vmcnt(0) lgkmcnt(0): every global load / direct copy and every LDS access issued
+// by this wave has completed.
+__device__ __forceinline__ void wait_vm_lgkm0() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
 }  // namespace ssc

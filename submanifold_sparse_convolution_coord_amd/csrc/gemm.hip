@@ -3,11 +3,13 @@
 // bias) + residual for 16-bit X [n, cin] and W, fp32 accumulation on the matrix cores.
 //
 // A workgroup owns 128 rows x 64 columns; its 4 waves own 32 rows each and all 64 columns
-// (128-column tiles need 238 VGPRs, 2 waves per SIMD, and ran 10-20% slower).  The K loop runs in stages of 64: the rows' next stage is loaded into
-// registers while the matrix cores consume this one from LDS (16-byte chunks XOR-swizzled by
-// row), then written to the other LDS buffer; the weight fragments (packed per 16-column
-// tile, 1 KB per fragment) go straight from global memory (L2-resident) into VGPRs, one stage
-// ahead.  Rows past n are read as row n-1 and never stored.
+// (128-column tiles need 238 VGPRs, 2 waves per SIMD, and ran 10-20% slower).  For Cin of 192
+// and more the K loop runs in stages of 64: the rows' next stage is loaded into registers
+// while the matrix cores consume this one from LDS (16-byte chunks XOR-swizzled by row), then
+// written to the other LDS buffer; the weight fragments (packed per 16-column tile, 1 KB per
+// fragment) go straight from global memory (L2-resident) into VGPRs, one stage ahead.  Cin of
+// 64 and 128 takes a one-pass kernel (k_gemm_rows_narrow).  Rows past n are read as row n-1
+// and never stored.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -212,6 +214,135 @@ __global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict
   }
 }
 
+// Cin 64 or 128: the tile's 128 rows, all of K, go to LDS in one batch of direct
+// global->LDS copies (no registers held, one wait), with the weight fragments and the
+// residual pieces loading alongside; then one pass of matrix work and the same epilogue.
+// With only 2 or 4 k-steps there is nothing to pipeline, and the two-stage register path
+// above spends its time in the latency of its stages (128 -> 512 at 209K rows: 109 -> 87
+// us; 64 -> 256 at 268K rows: 57 -> 42 us, bit-identical results).  Copy k of a wave fills
+// LDS bytes [k*1024, (k+1)*1024): lane l writes slot (row, p) = divmod(64 k + l, CPR), which
+// holds the row's chunk p ^ (row & 7), the swizzle the fragment reads expect.
+template <int KS, bool OUT16, int EK>
+__global__ __launch_bounds__(256, (OUT16 || KS < 4) ? 4 : 3) void k_gemm_rows_narrow(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
+    const float* __restrict__ bias, int64_t n, int cout, void* Y, int act, const void* res,
+    int64_t row_tiles) {
+  constexpr int CIN = KS * 32;
+  constexpr int CPR = CIN / 8;
+  constexpr int NCT = 4;
+  constexpr int ESZ = OUT16 ? 2 : 4;
+  constexpr int ROWB = 64 * ESZ;
+  constexpr int CHUNKS = ROWB / 16;
+  constexpr int SWM = CHUNKS - 1;
+  constexpr int RPT = 32 * CHUNKS / 64;
+  constexpr int A_BYTES = kGRows * CIN * 2;
+  constexpr int OUT_BYTES = 4 * 32 * ROWB;
+  __shared__ __attribute__((aligned(1024))) char smem[A_BYTES > OUT_BYTES ? A_BYTES : OUT_BYTES];
+  // (row tile, column tile) as in k_gemm_rows: a row tile's column tiles together on one XCD
+  const int col_tiles = cout / 64;
+  const int64_t xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int64_t rt = (j / col_tiles) * 8 + xcd;
+  if (rt >= row_tiles) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row0 = rt * kGRows;
+  const int ct0 = static_cast<int>(j % col_tiles) * NCT;
+  constexpr int COPIES = A_BYTES / 1024 / 4;  // per wave
+#pragma unroll
+  for (int i = 0; i < COPIES; ++i) {
+    const int k = i * 4 + wave;
+    const int slot = k * 64 + lane;
+    const int r = slot / CPR, p = slot % CPR;
+    const int64_t g = std::min<int64_t>(row0 + r, n - 1);
+    dma16(X + g * CIN + (p ^ (r & 7)) * 8, lds_addr(smem + k * 1024));
+  }
+  g_u32x4_t bw[KS][NCT];
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+      bw[k][c] = *reinterpret_cast<const g_u32x4_t*>(
+          Wp + (static_cast<int64_t>(ct0 + c) * KS + k) * 512 + lane * 8);
+  float bcol[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) bcol[c] = bias ? bias[(ct0 + c) * 16 + (lane & 15)] : 0.f;
+  const int64_t wrow0 = row0 + wave * 32;
+  const int64_t col0b = static_cast<int64_t>(ct0) * 16 * ESZ;
+  g_u32x4_t rres[RPT];
+  if (res) {
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int idx = lane + k * 64;
+      const int r = idx / CHUNKS, ch = idx % CHUNKS;
+      const int64_t g = std::min<int64_t>(wrow0 + r, n - 1);
+      rres[k] = *reinterpret_cast<const g_u32x4_t*>(static_cast<const char*>(res) +
+                                                    g * cout * ESZ + col0b + ch * 16);
+    }
+  }
+  wait_vm_lgkm0();  // the copies (and the loads) have landed
+  __syncthreads();
+  g_f32x4_t acc[2][NCT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[t][c] = g_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const auto* sA = reinterpret_cast<const g_u32x4_t*>(smem);
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = wave * 32 + t * 16 + (lane & 15);
+      const int ch = k * 4 + (lane >> 4);
+      const g_u32x4_t a = sA[row * CPR + (ch ^ (row & 7))];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) acc[t][c] = gemm_mfma<EK>(a, bw[k][c], acc[t][c]);
+    }
+  __syncthreads();  // every wave is past its A reads: the area becomes the output staging
+  char* sO = smem + wave * 32 * ROWB;
+  if (res) {
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int idx = lane + k * 64;
+      const int r = idx / CHUNKS, ch = idx % CHUNKS;
+      *reinterpret_cast<g_u32x4_t*>(sO + r * ROWB + ((ch ^ (r & SWM)) << 4)) = rres[k];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int col = c * 16 + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = t * 16 + (lane >> 4) * 4 + i;
+        const int byte = col * ESZ;
+        char* dst = sO + r * ROWB + (((byte >> 4) ^ (r & SWM)) << 4) + (byte & 15);
+        float v = apply_act(acc[t][c][i] + bcol[c], act);
+        if (res) {
+          if constexpr (OUT16)
+            v += from16<EK>(*reinterpret_cast<const uint16_t*>(dst));
+          else
+            v += *reinterpret_cast<const float*>(dst);
+        }
+        if constexpr (OUT16)
+          *reinterpret_cast<uint16_t*>(dst) = round16<EK>(v);
+        else
+          *reinterpret_cast<float*>(dst) = v;
+      }
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's staging writes are done
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const int idx = lane + k * 64;
+    const int r = idx / CHUNKS, ch = idx % CHUNKS;
+    if (wrow0 + r < n)
+      *reinterpret_cast<g_u32x4_t*>(static_cast<char*>(Y) + (wrow0 + r) * cout * ESZ + col0b +
+                                    ch * 16) =
+          *reinterpret_cast<const g_u32x4_t*>(sO + r * ROWB + ((ch ^ (r & SWM)) << 4));
+  }
+}
+
 }  // namespace
 
 // Shapes the GEMM takes: 16-bit inputs, cin a multiple of 64, cout a multiple of 64, both
@@ -229,6 +360,20 @@ ssc_status gemm_rows_launch(const void* feats, const uint16_t* wp, const float* 
   const int64_t row_tiles = (n + kGRows - 1) / kGRows;
   const auto* x = static_cast<const uint16_t*>(feats);
   const int64_t grid = (row_tiles + 7) / 8 * 8 * (cout / 64);
+  if (cin == 64 || cin == 128) {
+    using Fn = void (*)(const uint16_t*, const uint16_t*, const float*, int64_t, int, void*, int,
+                        const void*, int64_t);
+    Fn f;
+    if (cin == 64)
+      f = out16 ? (ek == 1 ? k_gemm_rows_narrow<2, true, 1> : k_gemm_rows_narrow<2, true, 0>)
+                : (ek == 1 ? k_gemm_rows_narrow<2, false, 1> : k_gemm_rows_narrow<2, false, 0>);
+    else
+      f = out16 ? (ek == 1 ? k_gemm_rows_narrow<4, true, 1> : k_gemm_rows_narrow<4, true, 0>)
+                : (ek == 1 ? k_gemm_rows_narrow<4, false, 1> : k_gemm_rows_narrow<4, false, 0>);
+    hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, x, wp, bias, n,
+                       cout, out, act, res, row_tiles);
+    return launch_status();
+  }
   auto fn = out16 ? (ek == 1 ? k_gemm_rows<64, true, 1> : k_gemm_rows<64, true, 0>)
                   : (ek == 1 ? k_gemm_rows<64, false, 1> : k_gemm_rows<64, false, 0>);
   hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, x, wp, bias, n, cin,
