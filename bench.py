@@ -610,6 +610,21 @@ def main():
     if two:
         k1_us = timed(lambda: ssc.linear(y1, w2, b2, odt, out=y2), args.steps) * 1e3
         log(f"[bench] k=1 layer {k1_us:.1f} us")
+    # Single launches, each between its own pair of events (warm caches): the spread of one
+    # call, beside the back-to-back mean above.
+    warm = []
+    for _ in range(min(args.steps, 200)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        conv()
+        e1.record()
+        torch.cuda.synchronize()
+        warm.append(e0.elapsed_time(e1) * 1e3)
+    single_warm = {"median_us": round(float(np.median(warm)), 2),
+                   "p10_us": round(float(np.percentile(warm, 10)), 2),
+                   "p90_us": round(float(np.percentile(warm, 90)), 2), "calls": len(warm)}
+    log(f"[bench] conv kernel, single warm calls: median {single_warm['median_us']} us "
+        f"(p10 {single_warm['p10_us']}, p90 {single_warm['p90_us']})")
     # Single launches with the caches flushed: a 512 MiB fill runs between calls (outside the
     # events), so the conv's inputs come from HBM, not from the 256 MB MALL.
     flush = torch.empty(512 * 262144, dtype=torch.float32, device=dev)
@@ -681,6 +696,7 @@ def main():
                  "effective_tflops_step": round(tflops_step, 2),
                  "frac_bf16_peak_step": round(tflops_step / PEAK_BF16_TFLOPS, 5),
                  "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": flops},
+        "conv_single_warm": single_warm,
         "conv_flushed": flushed,
         "resample": resample,
         "res_block": block,
