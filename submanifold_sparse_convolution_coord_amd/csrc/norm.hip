@@ -568,7 +568,9 @@ extern "C" ssc_status ssc_gn_apply(const void* x, int32_t dtype, int64_t n, int3
   if (vec && channels * esz / 16 <= 256) {
     const int lanes = 256 / (channels * esz / 16);
     const int64_t blocks = (n + kApplyRows * lanes - 1) / (kApplyRows * lanes);
-    const unsigned g = static_cast<unsigned>(std::min<int64_t>(blocks, 65536));
+    // At most 1024 workgroups (4 per CU), each striding over the rows, so that one
+    // workgroup's stores overlap another's loads (128 channels, 209K rows: 30.6 -> 26.5 us).
+    const unsigned g = static_cast<unsigned>(std::min<int64_t>(blocks, 1024));
     const auto* x4 = static_cast<const uint4*>(x);
     auto* o4 = static_cast<uint4*>(out);
     if (dtype == SSC_F32)
