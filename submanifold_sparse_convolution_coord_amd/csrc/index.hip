@@ -23,7 +23,7 @@
 // by 128^3 brick (batch entry, then the Morton code of the brick), which keeps the rows a tile
 // gathers within one region.  It is kept when it costs at most 5% more (block, tap) pairs
 // than the mask order, and the k=3 kernel then gives each XCD a contiguous share of the tiles
-// so that its L2 serves one region (surfaces: 25-30% faster convolutions).  Point clouds
+// so that its L2 serves one region (surfaces: 25-32% faster convolutions).  Point clouds
 // without spatial coherence (i.i.d. sites) lose more than 5% and keep the mask order.
 #include <hip/hip_runtime.h>
 
@@ -225,7 +225,8 @@ __device__ __forceinline__ unsigned long long spread3(uint32_t v, int bits) {
 
 // Brick sort input: position p of the mask order holds site r = rows[p]; its key is
 // (batch entry << 3L) | Morton code of its 128^3 brick (L bits per axis).  Out-of-range
-// coordinates only give odd keys (the map already leaves such sites without neighbours).
+// coordinates only give meaningless keys, never an out-of-bounds access (the map already
+// leaves such sites without neighbours).
 __global__ void k_brick_keys(const int4* __restrict__ coords, const uint32_t* __restrict__ rows,
                              int64_t n, int axis_bits, unsigned long long* __restrict__ keys,
                              uint32_t* __restrict__ vals, uint32_t* __restrict__ totals) {
