@@ -216,6 +216,31 @@ def test_conv_group_norm_statistics(cin, cout, odt):
     assert torch.equal(p2.sums(), ssc.gn_partials(y2, 3, 32, c2).sums())
 
 
+@pytest.mark.parametrize("cin,cout,odt", [(128, 128, torch.bfloat16), (64, 64, torch.float32),
+                                          (32, 32, torch.bfloat16)])
+def test_conv_residual_with_group_norm_statistics(cin, cout, odt):
+    """The epilogue that closes a residual block and opens the next one: the skip added and
+    the next norm's statistics summed from the stored values, in one kernel."""
+    say(f"[gn] residual + statistics {cin}->{cout} {odt}")
+    coords, x, w, b, rng = case(300 + cin, 1, (14, 13, 15), 0.4, cin, cout, torch.bfloat16)
+    n = len(coords)
+    res = torch.from_numpy(rng.standard_normal((n, cout), dtype=np.float32)).to(odt)
+    idx = index(coords, 1, (14, 13, 15))
+    parts = ssc.GroupNormPartials(n, 1, 32, DEV)
+    y = ssc.subm_conv3d(x.to(DEV), w.to(DEV), b.to(DEV), idx.plan, odt, residual=res.to(DEV),
+                        gn=parts)
+    y32 = ssc.subm_conv3d(x.to(DEV), w.to(DEV), b.to(DEV), idx.plan, torch.float32,
+                          residual=res.float().to(DEV))
+    m = oracle.build_map(coords, 1, (14, 13, 15))
+    ref = blocks.conv_epilogue(f64(x), f64(w), b.numpy(), m, "none", f64(res))
+    assert rel_err(f64(y32), ref) <= TAU[torch.bfloat16]
+    assert torch.equal(y.view(torch.uint8), y32.to(odt).view(torch.uint8))
+    fused = ssc.gn_finalize(parts).cpu().numpy().astype(np.float64)
+    mean, var = blocks.group_stats(f64(y), np.zeros((n, 4), np.int32), 1, 32)
+    assert np.abs(fused[..., 0] - mean).max() <= 1e-5 * np.sqrt(var.max())
+    np.testing.assert_allclose(fused[..., 1], 1 / np.sqrt(var + 1e-5), rtol=2e-5)
+
+
 @pytest.mark.parametrize("cin,cout,groups,n_sites,dtype", [
     (64, 128, 4, 700, torch.bfloat16),     # 32 channels a group: statistics pass after
     (128, 128, 32, 100, torch.bfloat16),   # second tile all padding
