@@ -249,6 +249,11 @@ def time_block(ssc, torch, coords, x, plan, batch, dev, reps: int = 50) -> dict:
     epi1 = ssc._Epilogue(gn_groups=groups, batch=batch, coords=None if cd is None else cd.data_ptr(),
                          gn_partials=parts1.buf.data_ptr(), gn_partials_bytes=nb)
     epi2 = ssc._Epilogue(residual=x.data_ptr())
+    # In a chain of blocks, conv2 also sums the next block's first-norm statistics, so that
+    # norm1 of every block but the first is finalize + apply only.
+    epi2_chain = ssc._Epilogue(residual=x.data_ptr(), gn_groups=groups, batch=batch,
+                               coords=None if cd is None else cd.data_ptr(),
+                               gn_partials=parts0.buf.data_ptr(), gn_partials_bytes=nb)
 
     def norm1():
         lib.ssc_gn_partials(p(x), BF, n, c, p(cd), batch, groups, p(parts0.buf), nb, st)
@@ -272,11 +277,26 @@ def time_block(ssc, torch, coords, x, plan, batch, dev, reps: int = 50) -> dict:
     def plain_conv():
         lib.ssc_subm_conv3d_packed(p(h), p(pw1.buf), p(b1), p(plan.buf), n, c, c, p(h1), BF, st)
 
+    def norm1_chained():
+        lib.ssc_gn_finalize(p(parts0.buf), n, batch, groups, eps, p(stats0), st)
+        lib.ssc_gn_apply(p(x), BF, n, c, p(cd), batch, groups, p(stats0), p(g1), p(be1), SILU,
+                         p(h), st)
+
+    def conv2_chained():
+        lib.ssc_subm_conv3d_packed_ex(p(h1), p(pw2.buf), p(b2), p(plan.buf), n, c, c, p(y), BF,
+                                      ctypes.byref(epi2_chain), st)
+
     def block():
         norm1()
         conv1()
         norm2()
         conv2()
+
+    def block_chained():
+        norm1_chained()
+        conv1()
+        norm2()
+        conv2_chained()
 
     def t(fn):
         for _ in range(5):
@@ -289,8 +309,11 @@ def time_block(ssc, torch, coords, x, plan, batch, dev, reps: int = 50) -> dict:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e3
 
-    us = {k: t(f) for k, f in (("block", block), ("norm1", norm1), ("conv1_gn_stats", conv1),
+    norm1()  # the chained block's first finalize reads statistics that exist
+    us = {k: t(f) for k, f in (("block", block), ("block_chained", block_chained),
+                               ("norm1", norm1), ("conv1_gn_stats", conv1),
                                ("norm2", norm2), ("conv2_residual", conv2),
+                               ("conv2_residual_gn_stats", conv2_chained),
                                ("conv_plain", plain_conv))}
     row = c * 2
     # algorithmic bytes of the two norms: read x twice (statistics, apply) and write h; read
@@ -298,7 +321,11 @@ def time_block(ssc, torch, coords, x, plan, batch, dev, reps: int = 50) -> dict:
     norm_bytes = n * row * 3 + n * row * 2
     return {"channels": c, "groups": groups, "batch": batch,
             "block_us": round(us["block"], 2), "block_mvox_s": round(n / us["block"], 1),
-            "stages_us": {k: round(v, 2) for k, v in us.items() if k != "block"},
+            # a block inside a chain: its first norm's statistics come from the previous
+            # block's last conv
+            "block_chained_us": round(us["block_chained"], 2),
+            "stages_us": {k: round(v, 2) for k, v in us.items()
+                          if k not in ("block", "block_chained")},
             "norm_gbs": round(norm_bytes / (us["norm1"] + us["norm2"]) / 1e3, 1),
             "epilogue_overhead_us": {
                 "gn_stats": round(us["conv1_gn_stats"] - us["conv_plain"], 2),
@@ -651,7 +678,8 @@ def main():
     block = convnext = None
     if x.dtype == torch.bfloat16 and cin in (32, 64, 128):
         block = time_block(ssc, torch, coords, x, plan, w.batch, dev)
-        log(f"[bench] residual block {block['block_us']} us {block['stages_us']}")
+        log(f"[bench] residual block {block['block_us']} us (chained {block['block_chained_us']} us) "
+            f"{block['stages_us']}")
         convnext = time_convnext(ssc, torch, x, plan, dev)
         log(f"[bench] convnext block {convnext['block_us']} us {convnext['stages_us']}")
 
