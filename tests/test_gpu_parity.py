@@ -68,6 +68,10 @@ def test_workload_parity(name, shuffle):
     b = layer.bias.to(DEV)
     y32 = idx.conv(x, wt, b, out_dtype=torch.float32)
     ybf = idx.conv(x, wt, b, out_dtype=torch.bfloat16)
+    if x.dtype == torch.bfloat16:
+        # the launch configuration the benchmark times: weights packed once, then the layer
+        yp = ssc.subm_conv3d_packed(x, ssc.pack_weights(wt), b, idx.plan, torch.float32)
+        assert torch.equal(yp, y32)
     torch.cuda.synchronize()
     ref = oracle.conv(w.feats.float().numpy(), layer.weight.float().numpy(),
                       layer.bias.numpy(), m)
