@@ -18,9 +18,10 @@
  * Conventions shared by every entry point:
  *   - All array pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) unless
  *     marked "host".  Arrays are contiguous and row-major.  The caller owns every buffer,
- *     including outputs and workspaces; the library never allocates device memory and keeps
- *     no mutable global state, so calls on different streams with different buffers are
- *     independent.
+ *     including outputs and workspaces; the library never allocates device memory.  Its only
+ *     host-side state is a per-device cache of the compute-unit count (an array of atomics,
+ *     written once per device with the value the runtime reports), so calls on different
+ *     streams with different buffers are independent.
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued on it and
  *     the call returns without waiting, except ssc_build_index with check != 0, which waits
  *     for its own work to read two error counters back.
@@ -59,6 +60,10 @@ int ssc_version(void);
 
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* ssc_status_string(int status);
+
+/* Digest (16 hex digits, static storage) of the sources the library was built from; the
+ * Python binding refuses a library whose digest differs from the sources beside it. */
+const char* ssc_source_digest(void);
 
 /* ---------------------------------------------------------------------------------------
  * Coordinate index (cold path, once per coordinate set)
@@ -132,34 +137,59 @@ ssc_status ssc_plan_layout(int64_t n, int64_t* layout);
  * Convolution (warm path)
  * ------------------------------------------------------------------------------------- */
 
-/* Bytes of scratch workspace ssc_subm_conv3d needs (the weights re-laid out for the matrix
- * cores; 0 for the fp32 path). */
+/* SubMConv3d, k=3, stride 1, on the neighbour map of a coordinate set:
+ *   out[i][o] = bias[o] + sum_{t : nbr[i][t] != -1} sum_c feats[nbr[i][t]][c] * weight[t][c][o]
+ * (cross-correlation; LATO.2 MLX port page, "Correctness"; the gather per kernel offset from
+ * the neighbour map, trellis-mac article, gather-scatter flowchart).
+ *   feats    [n, cin], in_dtype (SSC_F32, SSC_BF16 or SSC_F16); rows in coords order.
+ *   weight   [27, cin, cout], same dtype as feats (Pixal3D MLX port README, "Status").
+ *   bias     [cout] fp32, or NULL for none.
+ *   nbr      [n, 27] int32 neighbour map from ssc_build_index (or any map with its meaning).
+ *   out      [n, cout], out_dtype; rows in coords order; must not alias feats.
+ *   workspace >= ssc_subm_conv3d_workspace_bytes(n, cin, cout, in_dtype) bytes, 256-byte
+ *            aligned, scratch only: every call builds the warm plan of the map into it
+ *            (ssc_build_plan, mask order) and re-lays the weights out, then runs the same
+ *            kernels as ssc_subm_conv3d_plan.  Callers that run several layers on one
+ *            coordinate set build the plan once (ssc_build_plan) and call
+ *            ssc_subm_conv3d_plan or ssc_subm_conv3d_packed instead: that is the warm path.
+ * Accumulation is fp32 (bf16 and fp16 products are exact in fp32).  out_dtype is SSC_F32 or
+ * a 16-bit type: each 16-bit output is the round-to-nearest-even value of the fp32 result
+ * the SSC_F32 output holds.  Results are bit-identical from run to run (no atomics in the
+ * accumulation) and equal, bit for bit, to ssc_subm_conv3d_plan on a plan of the same map.
+ * Shapes and errors as for ssc_subm_conv3d_plan; every host-detectable error returns before
+ * anything is launched; n = 0 launches nothing. */
+size_t ssc_subm_conv3d_workspace_bytes(int64_t n, int32_t cin, int32_t cout, int32_t in_dtype);
+ssc_status ssc_subm_conv3d(const void* feats, int32_t in_dtype, const void* weight,
+                           const float* bias, const int32_t* nbr, int64_t n, int32_t cin,
+                           int32_t cout, void* out, int32_t out_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Bytes of scratch workspace ssc_subm_conv3d_plan and ssc_linear need (the weights re-laid out
+ * for the matrix cores; 0 for the fp32 path). */
 size_t ssc_conv_workspace_bytes(int32_t cin, int32_t cout, int32_t in_dtype);
 
-/* SubMConv3d, k=3, stride 1, over the plan of a coordinate set:
- *   out[i][o] = bias[o] + sum_{t : nbr[i][t] != -1} sum_c feats[nbr[i][t]][c] * weight[t][c][o]
- * (cross-correlation; LATO.2 MLX port page, "Correctness").
+/* SubMConv3d, k=3, stride 1, over the warm plan of a coordinate set (the same sum as
+ * ssc_subm_conv3d):
  *   feats    [n, cin], in_dtype (SSC_F32, SSC_BF16 or SSC_F16); rows in coords order.
  *   weight   [27, cin, cout], same dtype as feats.
  *   bias     [cout] fp32, or NULL for none.
  *   plan     from ssc_build_plan for the same n.
  *   out      [n, cout], out_dtype; rows in coords order; must not alias feats.
  *   workspace >= ssc_conv_workspace_bytes(cin, cout, in_dtype) bytes, 256-byte aligned.
- * Accumulation is fp32 (bf16 and fp16 products are exact in fp32).  out_dtype is SSC_F32 or
- * a 16-bit type: each 16-bit output is the round-to-nearest-even value of the fp32 result
- * the SSC_F32 output holds.  fp16 is the checkpoints' source precision (trellis2-mlx-8bit
- * page); the matrix-core kernels store fp32 or the input's own 16-bit type.
- * Results are bit-identical from run to run (no atomics in the accumulation).
+ * fp16 is the checkpoints' source precision (trellis2-mlx-8bit page); the matrix-core kernels
+ * store fp32 or the input's own 16-bit type.
  * Shapes: 1 <= cin, cout <= 1024.  bf16 or fp16 with cin in {32, 64, 128} and cout in
  * {16, 32, 64, 128} (and out_dtype fp32 or the input's type) runs on the matrix cores; the
- * rest runs a vector-ALU kernel with the same numerics contract. */
-ssc_status ssc_subm_conv3d(const void* feats, int32_t in_dtype, const void* weight,
-                           const float* bias, const void* plan, int64_t n, int32_t cin,
-                           int32_t cout, void* out, int32_t out_dtype, void* workspace,
-                           size_t workspace_bytes, void* stream);
+ * rest runs a vector-ALU kernel with the same numerics contract.
+ * Errors: SSC_ERR_ARG (null or misaligned buffers, bad dtype, n < 0), SSC_ERR_UNSUPPORTED
+ * (channels outside [1, 1024], n >= 2^31), SSC_ERR_WORKSPACE (short workspace). */
+ssc_status ssc_subm_conv3d_plan(const void* feats, int32_t in_dtype, const void* weight,
+                                const float* bias, const void* plan, int64_t n, int32_t cin,
+                                int32_t cout, void* out, int32_t out_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Weights re-laid out once for the matrix cores, for callers that keep a layer's weights
- * (the same re-layout ssc_subm_conv3d performs into its workspace on every call).
+ * (the same re-layout ssc_subm_conv3d_plan performs into its workspace on every call).
  *   weight  [27, cin, cout] bf16.
  *   packed  >= ssc_packed_weight_bytes(27, cin, cout) bytes, 256-byte aligned; receives the
  *           weights in the k=3 kernel's fragment order (an opaque layout of the same bytes
@@ -178,8 +208,8 @@ ssc_status ssc_pack_weights(const void* weight, int32_t taps, int32_t cin, int32
 ssc_status ssc_pack_weights_ex(const void* weight, int32_t taps, int32_t cin, int32_t cout,
                                int32_t flags, void* packed, size_t packed_bytes, void* stream);
 
-/* ssc_subm_conv3d with weights from ssc_pack_weights (taps = 27): one kernel launch, no
- * workspace.  Same results, bit for bit, as ssc_subm_conv3d on the unpacked weights.
+/* ssc_subm_conv3d_plan with weights from ssc_pack_weights (taps = 27): one kernel launch, no
+ * workspace.  Same results, bit for bit, as ssc_subm_conv3d_plan on the unpacked weights.
  * bf16 inputs and the shapes ssc_pack_weights accepts only. */
 ssc_status ssc_subm_conv3d_packed(const void* feats, const void* packed_weight,
                                   const float* bias, const void* plan, int64_t n, int32_t cin,
@@ -190,7 +220,7 @@ ssc_status ssc_subm_conv3d_packed(const void* feats, const void* packed_weight,
  * matrix cores: a streaming kernel for cin, cout in {32, 64, 128}, a tiled GEMM for other
  * multiples of 64 up to 1024 (the ConvNeXt-style MLP's 4C), the vector-ALU kernel otherwise.
  *   feats [n, cin], weight [cin, cout] (the single-tap [1, cin, cout] has the same bytes),
- *   bias [cout] fp32 or NULL, out [n, cout] out_dtype; workspace as for ssc_subm_conv3d. */
+ *   bias [cout] fp32 or NULL, out [n, cout] out_dtype; workspace as for ssc_subm_conv3d_plan. */
 ssc_status ssc_linear(const void* feats, int32_t in_dtype, const void* weight, const float* bias,
                       int64_t n, int32_t cin, int32_t cout, void* out, int32_t out_dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
@@ -242,14 +272,14 @@ typedef struct ssc_epilogue {
   size_t gn_partials_bytes;
 } ssc_epilogue;
 
-/* ssc_subm_conv3d, ssc_subm_conv3d_packed and ssc_linear with an epilogue (NULL = none);
+/* ssc_subm_conv3d_plan, ssc_subm_conv3d_packed and ssc_linear with an epilogue (NULL = none);
  * other arguments, shapes and errors as there.  Bad epilogue fields return SSC_ERR_ARG, a
  * short gn_partials buffer SSC_ERR_WORKSPACE. */
-ssc_status ssc_subm_conv3d_ex(const void* feats, int32_t in_dtype, const void* weight,
-                              const float* bias, const void* plan, int64_t n, int32_t cin,
-                              int32_t cout, void* out, int32_t out_dtype,
-                              const ssc_epilogue* epilogue, void* workspace,
-                              size_t workspace_bytes, void* stream);
+ssc_status ssc_subm_conv3d_plan_ex(const void* feats, int32_t in_dtype, const void* weight,
+                                   const float* bias, const void* plan, int64_t n,
+                                   int32_t cin, int32_t cout, void* out, int32_t out_dtype,
+                                   const ssc_epilogue* epilogue, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 ssc_status ssc_subm_conv3d_packed_ex(const void* feats, const void* packed_weight,
                                      const float* bias, const void* plan, int64_t n,
                                      int32_t cin, int32_t cout, void* out, int32_t out_dtype,

@@ -105,13 +105,35 @@ def linear_epilogue(x, w, bias, act: str = "none", residual=None):
     return y
 
 
-def res_block(x, coords, batch: int, nbr, p: dict, groups: int = 32, eps: float = 1e-5):
+def round_bf16(x):
+    """Each value rounded to bfloat16 (round to nearest, ties to even) and returned as float64:
+    first to float32 (numpy's round to nearest even), then to the 8-bit significand of bf16 on
+    the float32 bits.  This is where a layer that stores bf16 rounds its float32 result."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    nan = np.isnan(f)
+    out = r.astype(np.uint32).view(np.float32).astype(np.float64)
+    out[nan] = np.nan
+    return out
+
+
+def _keep(x):
+    return x
+
+
+def res_block(x, coords, batch: int, nbr, p: dict, groups: int = 32, eps: float = 1e-5,
+              store=None):
     """The pre-norm residual block: p holds w1, b1, w2, b2 ([27, C, C] / [C]) and the norms'
-    g1, be1, g2, be2 ([C])."""
-    h = group_norm(x, coords, batch, groups, p["g1"], p["be1"], eps, "silu")
-    h = oracle.conv(h, p["w1"], p["b1"], nbr)
-    h = group_norm(h, coords, batch, groups, p["g2"], p["be2"], eps, "silu")
-    return conv_epilogue(h, p["w2"], p["b2"], nbr, "none", x)
+    g1, be1, g2, be2 ([C]).  ``store`` rounds a layer's result where a chain keeps it in a
+    narrower type (round_bf16 for bf16 storage: after each norm, after each convolution);
+    None keeps float64 throughout."""
+    st = store or _keep
+    h = st(group_norm(x, coords, batch, groups, p["g1"], p["be1"], eps, "silu"))
+    h = st(oracle.conv(h, p["w1"], p["b1"], nbr))
+    h = st(group_norm(h, coords, batch, groups, p["g2"], p["be2"], eps, "silu"))
+    return st(conv_epilogue(h, p["w2"], p["b2"], nbr, "none", x))
 
 
 def layer_norm(x, gamma=None, beta=None, eps: float = 1e-6, act: str = "none"):
@@ -127,9 +149,11 @@ def layer_norm(x, gamma=None, beta=None, eps: float = 1e-6, act: str = "none"):
     return activation(y, act)
 
 
-def convnext_block(x, nbr, p: dict, eps: float = 1e-6):
-    """p holds w ([27, C, C]), b, ln_g, ln_b ([C]), w1 ([C, 4C]), b1, w2 ([4C, C]), b2."""
-    h = oracle.conv(x, p["w"], p["b"], nbr)
-    h = layer_norm(h, p["ln_g"], p["ln_b"], eps)
-    h = linear_epilogue(h, p["w1"], p["b1"], "silu")
-    return linear_epilogue(h, p["w2"], p["b2"], "none", x)
+def convnext_block(x, nbr, p: dict, eps: float = 1e-6, store=None):
+    """p holds w ([27, C, C]), b, ln_g, ln_b ([C]), w1 ([C, 4C]), b1, w2 ([4C, C]), b2.
+    ``store`` as for res_block: applied after the convolution, the norm and each linear."""
+    st = store or _keep
+    h = st(oracle.conv(x, p["w"], p["b"], nbr))
+    h = st(layer_norm(h, p["ln_g"], p["ln_b"], eps))
+    h = st(linear_epilogue(h, p["w1"], p["b1"], "silu"))
+    return st(linear_epilogue(h, p["w2"], p["b2"], "none", x))

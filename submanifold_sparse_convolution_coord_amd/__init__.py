@@ -6,8 +6,9 @@ outputs and workspaces with torch, and passes torch's current HIP stream.  There
 fallback: if libssc.so has not been built, importing works but every call raises.
 
     nbr  = build_index(coords, batch, grid)          # [N, 27] int32, -1 = no neighbour
+    y    = subm_conv3d(x, w, b, nbr)                 # k=3 on the map (plans it every call)
     plan = build_plan(nbr, coords, batch, grid)      # warm payload, reused by every layer
-    y    = subm_conv3d(x, w, b, plan)                # k=3, w [27, Cin, Cout]
+    y    = subm_conv3d(x, w, b, plan)                # k=3, w [27, Cin, Cout], warm path
     y2   = linear(y.to(torch.bfloat16), w1, b1)      # k=1
 
 ``SubMIndex`` bundles the map and the plan of one coordinate set, and ``cached_index``
@@ -72,9 +73,20 @@ def load_library():
         raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
                            "submanifold_sparse_convolution_coord_amd.build.build()")
     lib = ctypes.CDLL(_LIB_PATH)
+    # Refuse a library built from other sources than the ones on disk (a failed or skipped
+    # rebuild would otherwise run stale kernels).
+    from . import build as _build
+    lib.ssc_source_digest.argtypes = []
+    lib.ssc_source_digest.restype = ctypes.c_char_p
+    built, current = lib.ssc_source_digest().decode(), _build.source_digest()
+    if built != current:
+        raise RuntimeError(f"{_LIB_PATH} was built from other sources (digest {built}, sources "
+                           f"{current}): rebuild it with "
+                           "submanifold_sparse_convolution_coord_amd.build.build()")
     p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sig = {
         "ssc_version": ([], ctypes.c_int),
+        "ssc_source_digest": ([], ctypes.c_char_p),
         "ssc_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "ssc_index_workspace_bytes": ([i64], sz),
         "ssc_build_index": ([p, i64, i32, p, p, p, sz, i32, p], ctypes.c_int),
@@ -83,7 +95,10 @@ def load_library():
         "ssc_build_plan": ([p, p, i64, i32, p, p, sz, p, sz, p], ctypes.c_int),
         "ssc_plan_layout": ([i64, p], ctypes.c_int),
         "ssc_conv_workspace_bytes": ([i32, i32, i32], sz),
+        "ssc_subm_conv3d_workspace_bytes": ([i64, i32, i32, i32], sz),
         "ssc_subm_conv3d": ([p, i32, p, p, p, i64, i32, i32, p, i32, p, sz, p], ctypes.c_int),
+        "ssc_subm_conv3d_plan": ([p, i32, p, p, p, i64, i32, i32, p, i32, p, sz, p],
+                                 ctypes.c_int),
         "ssc_linear": ([p, i32, p, p, i64, i32, i32, p, i32, p, sz, p], ctypes.c_int),
         "ssc_packed_weight_bytes": ([i32, i32, i32], sz),
         "ssc_pack_weights": ([p, i32, i32, i32, p, sz, p], ctypes.c_int),
@@ -95,8 +110,8 @@ def load_library():
         "ssc_spatial2channel2": ([p, i64, i32, p, p, i32, i32, p, p, p, p, p, sz, p],
                                  ctypes.c_int),
         "ssc_subdivide2": ([p, i64, p, p, i32, i32, p, p, p], ctypes.c_int),
-        "ssc_subm_conv3d_ex": ([p, i32, p, p, p, i64, i32, i32, p, i32, p, p, sz, p],
-                               ctypes.c_int),
+        "ssc_subm_conv3d_plan_ex": ([p, i32, p, p, p, i64, i32, i32, p, i32, p, p, sz, p],
+                                    ctypes.c_int),
         "ssc_subm_conv3d_packed_ex": ([p, p, p, p, i64, i32, i32, p, i32, p, p], ctypes.c_int),
         "ssc_linear_ex": ([p, i32, p, p, i64, i32, i32, p, i32, p, p, sz, p], ctypes.c_int),
         "ssc_gn_partials_bytes": ([i64, i32, i32], sz),
@@ -301,34 +316,57 @@ def _epilogue(n, cout, out_dtype, act, residual, gn):
     return e
 
 
-def subm_conv3d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor], plan: Plan,
+def subm_conv3d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor], index,
                 out_dtype: Optional[torch.dtype] = None,
                 out: Optional[torch.Tensor] = None, act: str = "none",
                 residual: Optional[torch.Tensor] = None,
                 gn: Optional[GroupNormPartials] = None) -> torch.Tensor:
     """k=3 SubMConv3d: out[i] = bias + sum_t x[nbr[i][t]] @ weight[t] (cross-correlation).
     ``weight`` is [27, Cin, Cout] with the dtype of ``x``; output fp32 unless ``out_dtype``.
-    Epilogue: out = act(conv + bias) + residual, and with ``gn`` the group-norm partial sums
-    of the stored output."""
+    ``index`` is the neighbour map (int32 [N, 27] from build_index: ssc_subm_conv3d, which builds
+    the warm plan of the map on every call), or a Plan / SubMIndex of it (ssc_subm_conv3d_plan:
+    the warm path).  Epilogue (plan path): out = act(conv + bias) + residual, and with ``gn``
+    the group-norm partial sums of the stored output."""
     n, cin, cout, din, dout, odt = _conv_args(x, weight, bias, TAPS, out_dtype)
-    if plan.n != n:
-        raise ValueError(f"plan is for {plan.n} sites, x has {n}")
     lib = load_library()
     dev = x.device
+    if isinstance(index, SubMIndex):
+        index = index.plan
+    if isinstance(index, torch.Tensor):
+        nbr = index
+        _need_cuda(nbr, "nbr")
+        if nbr.dtype != torch.int32 or tuple(nbr.shape) != (n, TAPS):
+            raise ValueError(f"nbr must be int32 [{n}, {TAPS}]")
+        if act != "none" or residual is not None or gn is not None:
+            raise ValueError("epilogues take a Plan (build_plan) or a SubMIndex")
+        if out is None:
+            out = torch.empty((n, cout), dtype=odt, device=dev)
+        ws = _workspace(lib.ssc_subm_conv3d_workspace_bytes(n, cin, cout, din), dev)
+        with torch.cuda.device(dev):
+            st = lib.ssc_subm_conv3d(_ptr(x), din, _ptr(weight), _ptr(bias), _ptr(nbr), n, cin,
+                                     cout, _ptr(out), dout, _ptr(ws), ws.numel(), _stream(dev))
+        _check(st, "ssc_subm_conv3d")
+        return out
+    plan = index
+    if not isinstance(plan, Plan):
+        raise TypeError("index must be an int32 [N, 27] map, a Plan or a SubMIndex")
+    if plan.n != n:
+        raise ValueError(f"plan is for {plan.n} sites, x has {n}")
     if out is None:
         out = torch.empty((n, cout), dtype=odt, device=dev)
     epi = _epilogue(n, cout, odt, act, residual, gn)
     ws = _workspace(lib.ssc_conv_workspace_bytes(cin, cout, din), dev)
     with torch.cuda.device(dev):
         if epi is None:
-            st = lib.ssc_subm_conv3d(_ptr(x), din, _ptr(weight), _ptr(bias), _ptr(plan.buf), n,
-                                     cin, cout, _ptr(out), dout, _ptr(ws), ws.numel(),
-                                     _stream(dev))
+            st = lib.ssc_subm_conv3d_plan(_ptr(x), din, _ptr(weight), _ptr(bias), _ptr(plan.buf),
+                                          n, cin, cout, _ptr(out), dout, _ptr(ws), ws.numel(),
+                                          _stream(dev))
         else:
-            st = lib.ssc_subm_conv3d_ex(_ptr(x), din, _ptr(weight), _ptr(bias), _ptr(plan.buf),
-                                        n, cin, cout, _ptr(out), dout, ctypes.byref(epi),
-                                        _ptr(ws), ws.numel(), _stream(dev))
-    _check(st, "ssc_subm_conv3d")
+            st = lib.ssc_subm_conv3d_plan_ex(_ptr(x), din, _ptr(weight), _ptr(bias),
+                                             _ptr(plan.buf), n, cin, cout, _ptr(out), dout,
+                                             ctypes.byref(epi), _ptr(ws), ws.numel(),
+                                             _stream(dev))
+    _check(st, "ssc_subm_conv3d_plan")
     return out
 
 
@@ -645,7 +683,10 @@ _CACHE_MAX = 16
 
 def cached_index(coords: torch.Tensor, batch: int, grid: Sequence[int]) -> SubMIndex:
     """SubMIndex of ``coords``, rebuilt only when the tensor object, its storage, shape or
-    in-place version counter changes."""
+    in-place version counter, or the batch or grid, changes (the per-tensor cache of the
+    trellis-mac article's flowchart; the LATO.2 page rebuilds the map whenever coordinates
+    change).  Entries whose tensor has been freed are dropped before the oldest live entry is
+    evicted, so at most _CACHE_MAX indices stay alive."""
     key = (coords.data_ptr(), tuple(coords.shape), coords.device, int(batch),
            tuple(int(g) for g in grid))
     hit = _CACHE.get(key)
@@ -653,8 +694,11 @@ def cached_index(coords: torch.Tensor, batch: int, grid: Sequence[int]) -> SubMI
         ref, version, idx = hit
         if ref() is coords and version == coords._version:
             return idx
+        del _CACHE[key]
     idx = SubMIndex(coords, batch, grid)
-    if len(_CACHE) >= _CACHE_MAX:
+    for k in [k for k, (r, _, _) in _CACHE.items() if r() is None]:
+        del _CACHE[k]
+    while len(_CACHE) >= _CACHE_MAX:
         _CACHE.pop(next(iter(_CACHE)))
     _CACHE[key] = (weakref.ref(coords), coords._version, idx)
     return idx

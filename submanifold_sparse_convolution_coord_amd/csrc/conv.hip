@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -60,7 +61,10 @@ __device__ __forceinline__ bf16x8_t zero_bf16x8() {
 //   B (32 x 16): lane l holds column (l & 15), k = 8*(l >> 4) .. +7
 //   D (16 x 16): lane l holds column (l & 15), rows 4*(l >> 4) .. +3
 // Both operands use the same (lane, element) -> k assignment, so the product is the full
-// k-sum whatever order the hardware walks k in.
+// k-sum whatever order the hardware walks k in.  A weight fragment (lane l: output channel
+// l & 15, 8 input channels) is therefore also a valid A operand and a gathered-row fragment
+// (lane l: site l & 15, 8 input channels) a valid B operand: the k=3 kernel multiplies them
+// in that order, so its D holds output channels as rows and sites as columns.
 
 
 // ------------------------------------------------------------------------------------------
@@ -83,7 +87,8 @@ __device__ __forceinline__ bf16x8_t zero_bf16x8() {
 // fall in distinct banks.  Waves are WR x WC: column group wc owns COUT/WC output columns,
 // row group wr owns blocks wr, wr+WR, ...; fp32 accumulators stay in VGPRs.
 // The epilogue adds the bias, stages the tile's output rows in LDS (over the dead gather
-// buffers) and writes every row with 16-byte stores at its original index.
+// buffers; each lane writes its four consecutive channels of a site as one piece) and writes
+// every row with 16-byte stores at its original index.
 // ------------------------------------------------------------------------------------------
 template <int CIN, int COUT, int NB, int WR, int WC>
 struct LdsCfg {
@@ -108,6 +113,18 @@ struct LdsCfg {
   static_assert(16 % WAVES == 0 && A_LANES <= 64 && A_LANES > 0, "block copy shape");
   static_assert(CIN % 32 == 0 && COUT % (16 * WC) == 0 && NB % WR == 0, "tile shape");
   static_assert(NB * 4 <= 64 && 64 % (NB * 4) == 0, "index copy shape");
+  // Every LDS access stays inside its region (the kernel's index arithmetic, bound by bound):
+  //   gather copies: block b < NB, piece offset + 64 lanes x 16 B within one block slot;
+  static_assert(CIN < 128 ? (64 / CPR) * CIN * 2 * (16 / (64 / CPR)) == A_BLOCK * 2
+                          : RPW * CIN * 2 * WAVES == A_BLOCK * 2 && RPW * CPR == 64,
+                "copies tile a block slot exactly");
+  //   A fragments: row (l & 15) and chunk (l >> 4) + 4 s < CPR stay in the block slot;
+  static_assert(16 * CPR * 16 == A_BLOCK * 2 && 3 + 4 * (KS - 1) < CPR,
+                "fragment reads inside a block slot");
+  //   neighbour indices: at most 27 taps x NB * 16 rows, then NB * 16 row ids.
+  static_assert(OFF_G + kTaps * NB * 16 * 4 == OFF_P && OFF_P + NB * 16 * 4 == SMEM_BYTES &&
+                OFF_G == 2 * ABUF_BYTES, "index and row-id regions");
+  static_assert(SMEM_BYTES <= 160 * 1024, "LDS of one workgroup");
 };
 
 // Fragment-major packed weights for WC column groups: element
@@ -260,25 +277,36 @@ __device__ __forceinline__ void a_frag_offsets(int lane, uint32_t (&off)[CIN / 3
   }
 }
 
+// Matrix work of one stage.  The product is computed transposed, D = W^T X^T (the weight
+// fragment as the A operand, the gathered rows as the B operand: the same registers, the
+// roles swapped), so that each lane's four accumulators are four consecutive output channels
+// of one site (lane l: site row l & 15, channels 4 (l >> 4) .. +3 of the 16-column tile), which
+// the epilogue stores as one 16-byte (fp32) or 8-byte (16-bit) piece.  The A fragments of this
+// wave's blocks are read from LDS one block ahead of the MFMAs that use them (register set
+// bl & 1), so the LDS latency of a block hides behind the previous block's matrix work.
 template <int CIN, int COUT, int NB, int WR, int WC, int EK>
 __device__ __forceinline__ void compute_stage(uint32_t act, const char* sA,
                                               const bf16x8_t (&bw)[COUT / WC / 16][CIN / 32],
                                               const uint32_t (&aoff)[CIN / 32], int wr,
                                               f32x4_t (&acc)[NB / WR][COUT / WC / 16]) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
+  bf16x8_t a[2][C::KS];
+#pragma unroll
+  for (int s = 0; s < C::KS; ++s) a[0][s] = lds_read16(sA + wr * (C::A_BLOCK * 2) + aoff[s]);
 #pragma unroll
   for (int bl = 0; bl < C::BPW; ++bl) {
+    if (bl + 1 < C::BPW) {
+      const char* nblk = sA + ((bl + 1) * WR + wr) * (C::A_BLOCK * 2);
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) a[(bl + 1) & 1][s] = lds_read16(nblk + aoff[s]);
+    }
     const int b = bl * WR + wr;
     if (!((act >> b) & 1u)) continue;
-    const char* blk = sA + b * (C::A_BLOCK * 2);
-    bf16x8_t a[C::KS];
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) a[s] = lds_read16(blk + aoff[s]);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s)
 #pragma unroll
       for (int c = 0; c < C::NCT; ++c)
-        acc[bl][c] = mfma16x16x32<EK>(a[s], bw[c][s], acc[bl][c]);
+        acc[bl][c] = mfma16x16x32<EK>(bw[c][s], a[bl & 1][s], acc[bl][c]);
   }
 }
 
@@ -379,9 +407,12 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   // The tile's original row indices -> sP (read by the epilogue), by the last wave.
   if (wave == C::WAVES - 1 && lane < NB * 4) dma16(perm + row0 + lane * 4, lds0 + C::OFF_P);
   // Bias of this lane's columns, loaded now so the epilogue issues no global loads.
-  float bv[C::NCT];
+  f32x4_t bv[C::NCT];
 #pragma unroll
-  for (int c = 0; c < C::NCT; ++c) bv[c] = bias ? bias[wc * C::CS + c * 16 + (lane & 15)] : 0.f;
+  for (int c = 0; c < C::NCT; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // bias needs only 4-byte alignment: scalar loads
+      bv[c][i] = bias ? bias[wc * C::CS + c * 16 + 4 * (lane >> 4) + i] : 0.f;
   wait_vm_lgkm0();
   __builtin_amdgcn_s_barrier();
 
@@ -395,6 +426,10 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   // is full and covers rows [p0*16, (p0+BPP)*16) of the tile exactly).
   constexpr int BPP = BPP_RAW >= NB ? NB : BPP_RAW >= 8 ? 8 : BPP_RAW >= 4 ? 4 : BPP_RAW >= 2 ? 2 : 1;
   static_assert(BPP_RAW >= 1 && NB % BPP == 0, "output staging space");
+  // A pass stages rows [p0 * 16, (p0 + BPP) * 16) of the tile: the staging tile and the row
+  // ids it reads (sP[p0 * 16 + row], row < BPP * 16) stay in range for every pass.
+  static_assert(BPP * 16 * ROWB <= C::STAGE_BYTES && (NB / BPP) * BPP * 16 == NB * 16,
+                "staging passes inside the arena and the tile");
   // Residual rows: when the tile leaves in one pass and each thread's share is at most 8
   // pieces, they are loaded now, in flight with the first gather, and held in registers.
   constexpr int RPT = BPP * 16 * CHUNKS / C::THREADS;
@@ -480,9 +515,9 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   char* sOut = smem;
   // Group-norm statistics of the stored values: each lane sums its own columns (NCT of
   // them) over the rows it stages that hold a site.
-  float csum[C::NCT], csq[C::NCT];
+  f32x4_t csum[C::NCT], csq[C::NCT];
 #pragma unroll
-  for (int c = 0; c < C::NCT; ++c) csum[c] = csq[c] = 0.f;
+  for (int c = 0; c < C::NCT; ++c) csum[c] = csq[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int64_t site_rows = EPI ? ep.rows - row0 : 0;  // rows of this tile holding a site
   // The epilogue, one copy per combination of its options (activation, residual, group-norm
   // statistics), chosen once per tile, so that no element pays a branch for them.
@@ -525,35 +560,47 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
         if (b < p0 || b >= p0 + BPP) continue;
 #pragma unroll
         for (int c = 0; c < C::NCT; ++c) {
-          const int col = wc * C::CS + c * 16 + (lane & 15);
+          // This lane's piece: channels col .. col + 3 of one site row.
+          const int col = wc * C::CS + c * 16 + 4 * (lane >> 4);
+          const int row = (b - p0) * 16 + (lane & 15);
+          const int byte = col * ESZ;
+          char* dst = sOut + row * ROWB + (((byte >> 4) ^ (row & SWM)) << 4) + (byte & 15);
+          float v[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = (b - p0) * 16 + (lane >> 4) * 4 + i;
-            const int byte = col * ESZ;
-            char* dst = sOut + row * ROWB + (((byte >> 4) ^ (row & SWM)) << 4) + (byte & 15);
-            float v = apply_act(acc[bl][c][i] + bv[c], ACT);
-            if constexpr (RES) {
+          for (int i = 0; i < 4; ++i) v[i] = apply_act(acc[bl][c][i] + bv[c][i], ACT);
+          if constexpr (RES) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
               if constexpr (!OUT16)
-                v += *reinterpret_cast<const float*>(dst);
+                v[i] += reinterpret_cast<const float*>(dst)[i];
               else if constexpr (EK == 0)
-                v += bf16_to_f32(*reinterpret_cast<const uint16_t*>(dst));
+                v[i] += bf16_to_f32(reinterpret_cast<const uint16_t*>(dst)[i]);
               else
-                v += static_cast<float>(*reinterpret_cast<const _Float16*>(dst));
+                v[i] += static_cast<float>(reinterpret_cast<const _Float16*>(dst)[i]);
             }
-            float stored = v;
-            if constexpr (OUT16) {
-              const uint16_t h = to16<EK>(v);
-              *reinterpret_cast<uint16_t*>(dst) = h;
+          }
+          float stored[4] = {v[0], v[1], v[2], v[3]};
+          if constexpr (OUT16) {
+            uint16_t h[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              h[i] = to16<EK>(v[i]);
               if constexpr (GN)
-                stored = EK == 0 ? bf16_to_f32(h)
-                                 : static_cast<float>(__builtin_bit_cast(_Float16, h));
-            } else {
-              *reinterpret_cast<float*>(dst) = v;
+                stored[i] = EK == 0 ? bf16_to_f32(h[i])
+                                    : static_cast<float>(__builtin_bit_cast(_Float16, h[i]));
             }
-            if constexpr (GN) {
-              if (b * 16 + (lane >> 4) * 4 + i < site_rows) {
-                csum[c] += stored;
-                csq[c] = fmaf(stored, stored, csq[c]);
+            *reinterpret_cast<uint2*>(dst) =
+                make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16),
+                           h[2] | (static_cast<uint32_t>(h[3]) << 16));
+          } else {
+            *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v[0], v[1], v[2], v[3]};
+          }
+          if constexpr (GN) {
+            if (b * 16 + (lane & 15) < site_rows) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                csum[c][i] += stored[i];
+                csq[c][i] = fmaf(stored[i], stored[i], csq[c][i]);
               }
             }
           }
@@ -605,36 +652,57 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     }
   }
   if (EPI && ep.gn) {
-    // Fixed-order reduction, every step a butterfly (all lanes end with the same sums): over
-    // the four row quads of a column (lane bits 4, 5), then over the gs columns of a group
-    // (lane bits below log2 gs; a group never leaves a 16-column tile).  The tile's count is
-    // its rows that hold a site.  One or two 128-row slots per tile.
+    // Fixed-order reduction, every step a butterfly (all lanes end with the same sums): each
+    // lane holds four consecutive channels of one site row; first over the 16 site rows of a
+    // tile (lane bits 0-3), then over the gs channels of a group: within the lane's four (gs <= 4)
+    // and over lane bits 4, 5 (gs = 8, 16; a group never leaves a 16-column tile).  The tile's
+    // count is its rows that hold a site.  One or two 128-row slots per tile.
     const int groups = ep.gn_groups, gs = COUT / groups;
+    const int per_lane = gs >= 4 ? 1 : 4 / gs;  // groups among a lane's four channels
+    float S[C::NCT][4], Q[C::NCT][4];
 #pragma unroll
     for (int c = 0; c < C::NCT; ++c) {
-      csum[c] += __shfl_xor(csum[c], 16, 64);
-      csq[c] += __shfl_xor(csq[c], 16, 64);
-      csum[c] += __shfl_xor(csum[c], 32, 64);
-      csq[c] += __shfl_xor(csq[c], 32, 64);
-      for (int m = 1; m < gs; m <<= 1) {
-        csum[c] += __shfl_xor(csum[c], m, 64);
-        csq[c] += __shfl_xor(csq[c], m, 64);
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          csum[c][i] += __shfl_xor(csum[c][i], m, 64);
+          csq[c][i] += __shfl_xor(csq[c][i], m, 64);
+        }
+      if (gs == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[c][i] = csum[c][i], Q[c][i] = csq[c][i];
+      } else if (gs == 2) {
+        S[c][0] = csum[c][0] + csum[c][1];
+        Q[c][0] = csq[c][0] + csq[c][1];
+        S[c][1] = csum[c][2] + csum[c][3];
+        Q[c][1] = csq[c][2] + csq[c][3];
+      } else {
+        S[c][0] = (csum[c][0] + csum[c][1]) + (csum[c][2] + csum[c][3]);
+        Q[c][0] = (csq[c][0] + csq[c][1]) + (csq[c][2] + csq[c][3]);
+        for (int m = 16; m < 16 * (gs / 4); m <<= 1) {
+          S[c][0] += __shfl_xor(S[c][0], m, 64);
+          Q[c][0] += __shfl_xor(Q[c][0], m, 64);
+        }
       }
     }
     const float cnt = static_cast<float>(
         site_rows < 0 ? 0 : site_rows > NB * 16 ? NB * 16 : site_rows) * static_cast<float>(gs);
     constexpr int SLOTS = NB * 16 / 128;
     float4* part = reinterpret_cast<float4*>(ep.gn) + tile * SLOTS * groups;
-    const bool leader = lane < 16 && (lane & (gs - 1)) == 0;
+    const int quad = lane >> 4;  // channels 4 quad .. +3 of each 16-column tile
+    const bool leader = (lane & 15) == 0 && (gs < 8 || (quad & (gs / 4 - 1)) == 0);
     if constexpr (WR == 1) {
       if (leader) {
 #pragma unroll
         for (int c = 0; c < C::NCT; ++c) {
-          const int g = (wc * C::CS + c * 16 + lane) / gs;
-          part[g] = make_float4(cnt, csum[c], csq[c], 0.f);
+          const int g0 = (wc * C::CS + c * 16 + 4 * quad) / gs;
+          for (int k = 0; k < per_lane; ++k) {
+            part[g0 + k] = make_float4(cnt, S[c][k], Q[c][k], 0.f);
 #pragma unroll
-          for (int sl = 1; sl < SLOTS; ++sl)
-            part[sl * groups + g] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int sl = 1; sl < SLOTS; ++sl)
+              part[sl * groups + g0 + k] = make_float4(0.f, 0.f, 0.f, 0.f);
+          }
         }
       }
     } else {
@@ -645,20 +713,22 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
       if (leader) {
 #pragma unroll
         for (int c = 0; c < C::NCT; ++c) {
-          const int col = wc * C::CS + c * 16 + lane;
-          red[(wr * COUT + col) * 2] = csum[c];
-          red[(wr * COUT + col) * 2 + 1] = csq[c];
+          const int g0 = (wc * C::CS + c * 16 + 4 * quad) / gs;
+          for (int k = 0; k < per_lane; ++k) {
+            red[(wr * groups + g0 + k) * 2] = S[c][k];
+            red[(wr * groups + g0 + k) * 2 + 1] = Q[c][k];
+          }
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); the row stores may still be in flight
       __builtin_amdgcn_s_barrier();
       for (int g = threadIdx.x; g < groups; g += C::THREADS) {
-        float S = 0.f, Q = 0.f;
+        float Ssum = 0.f, Qsum = 0.f;
         for (int r = 0; r < WR; ++r) {
-          S += red[(r * COUT + g * gs) * 2];
-          Q += red[(r * COUT + g * gs) * 2 + 1];
+          Ssum += red[(r * groups + g) * 2];
+          Qsum += red[(r * groups + g) * 2 + 1];
         }
-        part[g] = make_float4(cnt, S, Q, 0.f);
+        part[g] = make_float4(cnt, Ssum, Qsum, 0.f);
 #pragma unroll
         for (int sl = 1; sl < SLOTS; ++sl) part[sl * groups + g] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
@@ -986,19 +1056,21 @@ bool valid_dtype(int d) { return d == SSC_F32 || d == SSC_BF16 || d == SSC_F16; 
 // Element kind of a 16-bit feature type for the matrix-core kernels (-1: none).
 int elem_kind(int d) { return d == SSC_BF16 ? 0 : d == SSC_F16 ? 1 : -1; }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device, cached per device id.  The cache is a table of
+// atomics: concurrent first calls on one device may both query the attribute, and each
+// stores the same value, so every reader sees 0 (not cached yet) or the device's count.
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cus;
 }
 
 ssc_status launch_linear(LinFn fn, int rows_per_tile, const void* feats, const uint16_t* wp,
@@ -1172,21 +1244,72 @@ extern "C" size_t ssc_conv_workspace_bytes(int32_t cin, int32_t cout, int32_t in
   return align_up(static_cast<size_t>(kTaps) * cin * cout * sizeof(uint16_t));
 }
 
-extern "C" ssc_status ssc_subm_conv3d(const void* feats, int32_t in_dtype, const void* weight,
-                                      const float* bias, const void* plan, int64_t n, int32_t cin,
-                                      int32_t cout, void* out, int32_t out_dtype, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+extern "C" ssc_status ssc_subm_conv3d_plan(const void* feats, int32_t in_dtype,
+                                           const void* weight, const float* bias,
+                                           const void* plan, int64_t n, int32_t cin,
+                                           int32_t cout, void* out, int32_t out_dtype,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream) {
   return run_conv(false, feats, in_dtype, weight, bias, plan, n, cin, cout, out, out_dtype,
                   nullptr, workspace, workspace_bytes, stream);
 }
 
-extern "C" ssc_status ssc_subm_conv3d_ex(const void* feats, int32_t in_dtype, const void* weight,
-                                         const float* bias, const void* plan, int64_t n,
-                                         int32_t cin, int32_t cout, void* out, int32_t out_dtype,
-                                         const ssc_epilogue* epilogue, void* workspace,
-                                         size_t workspace_bytes, void* stream) {
+extern "C" ssc_status ssc_subm_conv3d_plan_ex(const void* feats, int32_t in_dtype,
+                                              const void* weight, const float* bias,
+                                              const void* plan, int64_t n, int32_t cin,
+                                              int32_t cout, void* out, int32_t out_dtype,
+                                              const ssc_epilogue* epilogue, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
   return run_conv(false, feats, in_dtype, weight, bias, plan, n, cin, cout, out, out_dtype,
                   epilogue, workspace, workspace_bytes, stream);
+}
+
+// The map-taking call: the workspace holds [plan][plan scratch][re-laid-out weights], each
+// part 256-byte aligned.
+namespace {
+struct MapWork {
+  size_t off_plan, off_scratch, off_weights, total;
+};
+MapWork map_work(int64_t n, int32_t cin, int32_t cout, int32_t in_dtype) {
+  MapWork M;
+  M.off_plan = 0;
+  M.off_scratch = align_up(ssc_plan_bytes(n));
+  M.off_weights = M.off_scratch + align_up(ssc_plan_workspace_bytes(n));
+  M.total = M.off_weights + ssc_conv_workspace_bytes(cin, cout, in_dtype);
+  return M;
+}
+}  // namespace
+
+extern "C" size_t ssc_subm_conv3d_workspace_bytes(int64_t n, int32_t cin, int32_t cout,
+                                                  int32_t in_dtype) {
+  if (n < 0 || cin < 1 || cout < 1) return 0;
+  return map_work(n, cin, cout, in_dtype).total;
+}
+
+extern "C" ssc_status ssc_subm_conv3d(const void* feats, int32_t in_dtype, const void* weight,
+                                      const float* bias, const int32_t* nbr, int64_t n,
+                                      int32_t cin, int32_t cout, void* out, int32_t out_dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (n < 0 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSC_ERR_ARG;
+  if (cin < 1 || cout < 1 || cin > 1024 || cout > 1024) return SSC_ERR_UNSUPPORTED;
+  if (n >= (int64_t(1) << 31)) return SSC_ERR_UNSUPPORTED;
+  if (weight == nullptr || (n > 0 && nbr == nullptr)) return SSC_ERR_ARG;
+  if (n == 0) return SSC_OK;
+  // Every host-detectable error is reported before the plan kernels are enqueued.
+  if (feats == nullptr || out == nullptr || workspace == nullptr) return SSC_ERR_ARG;
+  if (!aligned(weight, 16) || !aligned(feats, 16) || !aligned(out, 16) || !aligned(nbr, 4) ||
+      !aligned(workspace, kAlign) || (bias && !aligned(bias, 4)))
+    return SSC_ERR_ARG;
+  const MapWork M = map_work(n, cin, cout, in_dtype);
+  if (workspace_bytes < M.total) return SSC_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  if (const ssc_status st =
+          ssc_build_plan(nbr, nullptr, n, 1, nullptr, ws + M.off_plan, M.off_scratch,
+                         ws + M.off_scratch, M.off_weights - M.off_scratch, stream);
+      st != SSC_OK)
+    return st;
+  return run_conv(false, feats, in_dtype, weight, bias, ws + M.off_plan, n, cin, cout, out,
+                  out_dtype, nullptr, ws + M.off_weights, M.total - M.off_weights, stream);
 }
 
 extern "C" ssc_status ssc_linear(const void* feats, int32_t in_dtype, const void* weight,
@@ -1268,19 +1391,4 @@ extern "C" ssc_status ssc_subm_conv3d_packed_ex(const void* feats, const void* p
       st != SSC_OK)
     return st;
   return gn_after(epilogue, fused, out, out_dtype, n, cout, s);
-}
-
-extern "C" int ssc_version(void) { return 100; }
-
-extern "C" const char* ssc_status_string(int status) {
-  switch (status) {
-    case SSC_OK: return "ok";
-    case SSC_ERR_ARG: return "invalid argument (null, negative size, bad dtype or misaligned)";
-    case SSC_ERR_COORD_RANGE: return "coordinate outside [0,batch) x [0,grid)";
-    case SSC_ERR_DUPLICATE: return "duplicate coordinate";
-    case SSC_ERR_UNSUPPORTED: return "unsupported shape";
-    case SSC_ERR_WORKSPACE: return "workspace or plan buffer too small";
-    case SSC_ERR_HIP: return "HIP runtime error";
-    default: return "unknown status";
-  }
 }

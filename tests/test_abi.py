@@ -50,6 +50,13 @@ def test_workspace_sizes(lib):
     assert lib.ssc_plan_workspace_bytes(1000) >= 1000 * 16
     assert lib.ssc_conv_workspace_bytes(128, 128, ssc.SSC_BF16) >= 27 * 128 * 128 * 2
     assert lib.ssc_conv_workspace_bytes(16, 16, ssc.SSC_F32) == 0
+    # the map-taking conv: plan + plan scratch + re-laid-out weights
+    for n in (1, 1000, 209473):
+        m = lib.ssc_subm_conv3d_workspace_bytes(n, 128, 128, ssc.SSC_BF16)
+        assert m >= (lib.ssc_plan_bytes(n) + lib.ssc_plan_workspace_bytes(n)
+                     + lib.ssc_conv_workspace_bytes(128, 128, ssc.SSC_BF16))
+    assert lib.ssc_subm_conv3d_workspace_bytes(-1, 128, 128, ssc.SSC_BF16) == 0
+    assert lib.ssc_subm_conv3d_workspace_bytes(10, 0, 128, ssc.SSC_BF16) == 0
 
 
 FAKE = ctypes.c_void_p(1 << 20)       # aligned, never dereferenced: every call below returns
@@ -100,7 +107,7 @@ def test_build_plan_argument_errors(lib):
 
 
 def test_conv_argument_errors(lib):
-    f = lib.ssc_subm_conv3d
+    f = lib.ssc_subm_conv3d_plan
     big = 1 << 30
     ok = dict(x=FAKE, din=ssc.SSC_BF16, w=FAKE, b=None, plan=FAKE, n=0, cin=64, cout=64, y=FAKE,
               dout=ssc.SSC_F32, ws=FAKE, wsb=big)
@@ -127,6 +134,52 @@ def test_conv_argument_errors(lib):
               None) == ssc.SSC_OK
     assert lf(FAKE, 3, FAKE, None, 10, 64, 64, FAKE, ssc.SSC_F32, FAKE, big,
               None) == ssc.SSC_ERR_ARG
+
+
+def test_map_conv_argument_errors(lib):
+    # ssc_subm_conv3d(feats, in_dtype, weight, bias, nbr, n, cin, cout, out, out_dtype,
+    #                 workspace, workspace_bytes, stream): every error before any launch
+    f = lib.ssc_subm_conv3d
+    big = 1 << 30
+    ok = dict(x=FAKE, din=ssc.SSC_BF16, w=FAKE, b=None, nbr=FAKE, n=10, cin=128, cout=128,
+              y=FAKE, dout=ssc.SSC_F32, ws=FAKE, wsb=big)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["din"], a["w"], a["b"], a["nbr"], a["n"], a["cin"], a["cout"], a["y"],
+                 a["dout"], a["ws"], a["wsb"], None)
+
+    assert call(n=0, nbr=None, ws=None, wsb=0) == ssc.SSC_OK      # n = 0 launches nothing
+    assert call(n=-1) == ssc.SSC_ERR_ARG
+    assert call(din=9) == ssc.SSC_ERR_ARG
+    assert call(dout=9) == ssc.SSC_ERR_ARG
+    assert call(cin=0) == ssc.SSC_ERR_UNSUPPORTED
+    assert call(cout=2048) == ssc.SSC_ERR_UNSUPPORTED
+    assert call(nbr=None) == ssc.SSC_ERR_ARG
+    assert call(w=None) == ssc.SSC_ERR_ARG
+    assert call(x=None) == ssc.SSC_ERR_ARG
+    assert call(y=None) == ssc.SSC_ERR_ARG
+    assert call(ws=None) == ssc.SSC_ERR_ARG
+    assert call(x=ctypes.c_void_p((1 << 20) + 2)) == ssc.SSC_ERR_ARG
+    assert call(nbr=ctypes.c_void_p((1 << 20) + 2)) == ssc.SSC_ERR_ARG
+    assert call(ws=ctypes.c_void_p((1 << 20) + 64)) == ssc.SSC_ERR_ARG
+    assert call(b=ctypes.c_void_p((1 << 20) + 2)) == ssc.SSC_ERR_ARG
+    need = lib.ssc_subm_conv3d_workspace_bytes(10, 128, 128, ssc.SSC_BF16)
+    assert call(wsb=need - 1) == ssc.SSC_ERR_WORKSPACE
+
+
+def test_library_digest_matches_sources(lib):
+    from submanifold_sparse_convolution_coord_amd import build
+    assert lib.ssc_source_digest().decode() == build.source_digest()
+
+
+def test_stale_library_is_refused(monkeypatch):
+    # A library built from other sources than those on disk is never loaded.
+    from submanifold_sparse_convolution_coord_amd import build
+    monkeypatch.setattr(build, "source_digest", lambda: "0000000000000000")
+    monkeypatch.setattr(ssc, "_lib", None)
+    with pytest.raises(RuntimeError, match="other sources"):
+        ssc.load_library()
 
 
 def test_pack_weights_argument_errors(lib):
@@ -213,7 +266,7 @@ def test_epilogue_and_group_norm_argument_errors(lib):
     E = ssc._Epilogue
 
     def conv(epi, n=10, cout=64):
-        return lib.ssc_subm_conv3d_ex(FAKE, ssc.SSC_BF16, FAKE, None, FAKE, n, 64, cout, FAKE,
+        return lib.ssc_subm_conv3d_plan_ex(FAKE, ssc.SSC_BF16, FAKE, None, FAKE, n, 64, cout, FAKE,
                                       ssc.SSC_F32, ctypes.byref(epi), FAKE, big, None)
 
     assert conv(E(act=3)) == ssc.SSC_ERR_ARG                               # unknown activation

@@ -5,8 +5,10 @@ Bars: conv outputs as for the plain convolution (the fp32-stored output max|err|
 RMS(oracle), tau 1e-4 for fp32 / fp16 inputs, 2e-2 for bf16 inputs; a 16-bit store is the
 round-to-nearest-even of the fp32 one, bit for bit); group-norm statistics within fp32
 summation error; normalised outputs within one rounding to the stored type per element (plus
-1e-5 * RMS of fp32 arithmetic); the residual block (four bf16 roundings in a
-chain) 3e-2 * RMS for bf16, 1e-4 for fp32.  Everything that runs twice must agree bit for bit.
+1e-5 * RMS of fp32 arithmetic); the residual and ConvNeXt-style blocks in bf16 against an
+oracle chain that rounds to bf16 wherever the library stores bf16 (after every layer):
+max|err| <= 2e-2 * RMS, and per element at most one bf16 step of the value (2^-7 |v|) plus
+2e-3 * RMS; in fp32 1e-4 * RMS.  Everything that runs twice must agree bit for bit.
 """
 import sys
 
@@ -25,7 +27,22 @@ TAU = {torch.float32: 1e-4, torch.bfloat16: 2e-2, torch.float16: 1e-4}
 # group norm outputs, per element: one rounding to the stored type (half an ulp: 2^-8 |v| for
 # bf16, 2^-11 |v| for fp16) plus fp32 arithmetic on O(1) values
 ROUND = {torch.float32: 0.0, torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
-TAU_BLOCK = {torch.float32: 1e-4, torch.bfloat16: 3e-2}
+TAU_BLOCK = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+# bf16 chains: where the oracle and the library round the same float32-vs-float64 value to
+# different neighbours, the stored values differ by one bf16 step (at most 2^-7 |v|); the
+# steps of earlier layers reach the output through the convolutions as small sums.
+STEP_BF16 = 2.0 ** -7
+TAU_CHAIN = 2e-3
+
+
+def check_chain(y, ref, dtype):
+    err = rel_err(y, ref)
+    assert err <= TAU_BLOCK[dtype], err
+    if dtype == torch.bfloat16:
+        rms = np.sqrt((ref ** 2).mean())
+        bad = np.abs(y - ref) > STEP_BF16 * np.abs(ref) + TAU_CHAIN * rms
+        assert not bad.any(), (int(bad.sum()), float(np.abs(y - ref)[bad].max() / rms))
+    return err
 
 
 def say(msg):
@@ -337,10 +354,10 @@ def test_res_block(dtype, batch, c, groups):
     y_again = res_block_gpu(x.to(DEV), cd, batch, idx.plan, pd, groups, 1e-5)
     assert torch.equal(y.view(torch.uint8), y_again.view(torch.uint8))
     ref = blocks.res_block(f64(x), coords, batch, oracle.build_map(coords, batch, grid),
-                           {k: f64(v) for k, v in p.items()}, groups, 1e-5)
-    err = rel_err(f64(y), ref)
+                           {k: f64(v) for k, v in p.items()}, groups, 1e-5,
+                           store=blocks.round_bf16 if dtype == torch.bfloat16 else None)
+    err = check_chain(f64(y), ref, dtype)
     say(f"[block]   max|err|/rms = {err:.3e}")
-    assert err <= TAU_BLOCK[dtype]
 
 
 @pytest.mark.parametrize("n,cin,cout,dtype,odt,act", [
@@ -418,10 +435,9 @@ def test_convnext_block(c):
     h = ssc.linear(h, pd["w1"], pd["b1"], bf, act="silu")
     y = ssc.linear(h, pd["w2"], pd["b2"], bf, residual=xd)
     ref = blocks.convnext_block(f64(x), oracle.build_map(coords, 1, grid),
-                                {k: f64(v) for k, v in p.items()}, 1e-6)
-    err = rel_err(f64(y), ref)
+                                {k: f64(v) for k, v in p.items()}, 1e-6, store=blocks.round_bf16)
+    err = check_chain(f64(y), ref, bf)
     say(f"[convnext]   max|err|/rms = {err:.3e}")
-    assert err <= TAU_BLOCK[bf]
 
 
 @pytest.mark.parametrize("n,cin,cout,dtype", [(300, 1024, 1024, torch.bfloat16),

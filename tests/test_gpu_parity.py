@@ -20,6 +20,11 @@ pytestmark = pytest.mark.gpu
 # fp16 inputs: products of two fp16 values are exact in fp32 and accumulation is fp32, as for
 # fp32 inputs, so the fp32-input bound applies (the 2e-2 bf16 bound is for bf16 inputs).
 TAU = {"f32": 1e-4, "bf16": 2e-2, "f16": 1e-4}
+# Second bar on every fp32-stored convolution: 16-bit products are exact in fp32 and the sum
+# has at most 27 * Cin terms, so an fp32 accumulator stays within ~1e-6 of RMS (measured
+# 2e-7 to 8e-7); 1e-5 leaves a margin of 10x and still fails an accumulator that rounds to
+# 16 bits per tap (~4e-3 of RMS).
+TAU_ACC = 1e-5
 DEV = torch.device("cuda:0")
 
 
@@ -78,6 +83,7 @@ def test_workload_parity(name, shuffle):
     err = rel_err(y32.cpu().numpy(), ref)
     say(f"[parity] {name} n={w.n} k3 max|err|/rms = {err:.3e}")
     assert err <= TAU[w.dtype]
+    assert err <= TAU_ACC
     assert torch.equal(ybf.cpu().view(torch.int16), rne_bf16(y32.cpu()).view(torch.int16))
 
     if len(w.layers) > 1:  # batch4: k=1 128->128 on the bf16 k=3 output
@@ -116,6 +122,7 @@ def check_conv(coords, batch, grid, x, w, b, tau):
     ref = oracle.conv(x.float().numpy(), w.float().numpy(), None if b is None else b.numpy(), m)
     err = rel_err(y.cpu().numpy(), ref)
     assert err <= tau, err
+    assert err <= TAU_ACC, err
     return idx, y
 
 
@@ -470,3 +477,78 @@ def test_maximum_channels_conv(cin, cout, dtype):
     coords, x, w, b = small_case(cin * 3 + cout, 1, (6, 5, 4), 0.5, cin, cout, dtype)
     check_conv(coords, 1, (6, 5, 4), x, w, b,
                TAU["f32"] if dtype == torch.float32 else TAU["bf16"])
+
+
+def test_map_entry_matches_plan_and_oracle():
+    """ssc_subm_conv3d takes the neighbour map itself (it plans the map on every call): on the
+    128^3 benchmark workload it equals the warm plan path bit for bit and the oracle within
+    the bars."""
+    say("[map entry] iid128")
+    w, m = workload_case("iid128")
+    layer = w.layers[0]
+    c = torch.from_numpy(w.coords).to(DEV)
+    nbr = ssc.build_index(c, w.batch, w.grid)
+    x, wt, b = w.feats.to(DEV), layer.weight.to(DEV), layer.bias.to(DEV)
+    y_map = ssc.subm_conv3d(x, wt, b, nbr)
+    y_map16 = ssc.subm_conv3d(x, wt, b, nbr, out_dtype=torch.bfloat16)
+    plan = ssc.build_plan(nbr)  # the map entry's own plan: mask order, no coordinates
+    y_plan = ssc.subm_conv3d(x, wt, b, plan)
+    torch.cuda.synchronize()
+    assert torch.equal(y_map, y_plan)
+    assert torch.equal(y_map16.cpu().view(torch.int16), rne_bf16(y_map.cpu()).view(torch.int16))
+    ref = oracle.conv(w.feats.float().numpy(), layer.weight.float().numpy(), layer.bias.numpy(), m)
+    err = rel_err(y_map.cpu().numpy(), ref)
+    say(f"[map entry] max|err|/rms = {err:.3e}")
+    assert err <= TAU["bf16"] and err <= TAU_ACC
+
+
+def test_map_entry_small_and_fp32():
+    say("[map entry] ragged bf16 and fp32")
+    for dtype, tau in ((torch.bfloat16, TAU["bf16"]), (torch.float32, TAU["f32"])):
+        coords, x, w, b = small_case(77, 2, (14, 14, 14), 0.12, 32, 64, dtype)
+        m = oracle.build_map(coords, 2, (14, 14, 14))
+        nbr = ssc.build_index(torch.from_numpy(coords).to(DEV), 2, (14, 14, 14))
+        y = ssc.subm_conv3d(x.to(DEV), w.to(DEV), b.to(DEV), nbr)
+        torch.cuda.synchronize()
+        ref = oracle.conv(x.float().numpy(), w.float().numpy(), b.numpy(), m)
+        err = rel_err(y.cpu().numpy(), ref)
+        assert err <= tau and err <= TAU_ACC, (dtype, err)
+
+
+def test_cached_index_reuse_and_invalidation():
+    """cached_index returns the cached SubMIndex while the coordinate tensor is the same object
+    with the same version, and rebuilds after an in-place edit, for a new tensor with equal
+    contents, and for another grid or batch; freed tensors' entries are dropped."""
+    say("[cache]")
+    rng = np.random.default_rng(31)
+    grid = (16, 16, 16)
+    coords = workloads.random_sites(rng, 2, grid, 700)
+    c = torch.from_numpy(coords).to(DEV)
+    i1 = ssc.cached_index(c, 2, grid)
+    assert ssc.cached_index(c, 2, grid) is i1                      # hit
+    assert np.array_equal(i1.nbr.cpu().numpy(), oracle.build_map(coords, 2, grid))
+    # in-place edit: move every site one voxel in x inside the grid (bumps the version)
+    keep = coords[:, 1] < grid[0] - 1
+    c = torch.from_numpy(coords[keep]).to(DEV)
+    i2 = ssc.cached_index(c, 2, grid)
+    c[:, 1] += 1
+    i3 = ssc.cached_index(c, 2, grid)
+    assert i3 is not i2
+    moved = coords[keep].copy()
+    moved[:, 1] += 1
+    assert np.array_equal(i3.nbr.cpu().numpy(), oracle.build_map(moved, 2, grid))
+    assert ssc.cached_index(c, 2, grid) is i3                      # hit again after rebuild
+    c2 = c.clone()                                                 # equal contents, new tensor
+    i4 = ssc.cached_index(c2, 2, grid)
+    assert i4 is not i3 and torch.equal(i4.nbr, i3.nbr)
+    i5 = ssc.cached_index(c2, 2, (17, 16, 16))                     # another grid
+    assert i5 is not i4 and torch.equal(i5.nbr, i4.nbr)
+    i6 = ssc.cached_index(c2, 3, grid)                             # another batch
+    assert i6 is not i4 and i6 is not i5
+    # entries of freed tensors do not pile up beyond the cache's bound
+    for k in range(ssc._CACHE_MAX + 4):
+        t = torch.from_numpy(workloads.random_sites(rng, 1, (8, 8, 8), 50 + k)).to(DEV)
+        ssc.cached_index(t, 1, (8, 8, 8))
+        del t
+    assert len(ssc._CACHE) <= ssc._CACHE_MAX
+    torch.cuda.synchronize()

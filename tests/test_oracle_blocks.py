@@ -173,3 +173,40 @@ def test_convnext_block_matches_dense_torch():
     h = F.silu(h @ torch.from_numpy(p["w1"]) + torch.from_numpy(p["b1"]))
     h = h @ torch.from_numpy(p["w2"]) + torch.from_numpy(p["b2"])
     np.testing.assert_allclose(got, (h + torch.from_numpy(x)).numpy(), rtol=1e-11, atol=1e-11)
+
+
+def test_round_bf16_matches_torch_cast():
+    """The oracle's bf16 storage rounding against torch's float32 -> bfloat16 cast (round to
+    nearest, ties to even) on random values, exact ties, subnormals, signed zeros, overflow."""
+    import torch
+    rng = np.random.default_rng(5)
+    ties = np.array([1 + k * 2.0 ** -8 for k in range(1, 16, 2)])            # halfway cases
+    vals = np.concatenate([rng.standard_normal(200000) * 7, rng.standard_normal(1000) * 1e-39,
+                           ties, -ties, [0.0, -0.0, 3.39e38, -3.39e38, 1e-45, 65504.0]])
+    got = blocks.round_bf16(vals)
+    want = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    # ties go to the even significand: 1 + 2^-8 -> 1, 1 + 3 * 2^-8 -> 1 + 2^-6
+    assert blocks.round_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
+    assert blocks.round_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
+
+
+def test_blocks_store_hook_defaults_to_float64():
+    """Without a storage rounding the blocks are unchanged; with it every stored layer output
+    is representable in bf16 (a fixed point of the rounding)."""
+    rng = np.random.default_rng(8)
+    coords = np.array([[0, x, y, z] for x in range(3) for y in range(3) for z in range(2)],
+                      np.int32)
+    nbr = oracle.build_map(coords, 1, (3, 3, 2))
+    c = 8
+    p = {k: rng.standard_normal((27, c, c)) / np.sqrt(27 * c) for k in ("w1", "w2")}
+    p.update({k: 0.1 * rng.standard_normal(c) for k in ("b1", "b2", "be1", "be2")})
+    p.update({k: 1 + 0.1 * rng.standard_normal(c) for k in ("g1", "g2")})
+    x = rng.standard_normal((len(coords), c))
+    a = blocks.res_block(x, coords, 1, nbr, p, 4, 1e-5)
+    b = blocks.res_block(x, coords, 1, nbr, p, 4, 1e-5, store=None)
+    assert np.array_equal(a, b)
+    r = blocks.res_block(x, coords, 1, nbr, p, 4, 1e-5, store=blocks.round_bf16)
+    assert np.array_equal(r, blocks.round_bf16(r))
+    assert np.abs(r - a).max() <= 0.05 * np.sqrt((a ** 2).mean())
