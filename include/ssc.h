@@ -188,6 +188,23 @@ ssc_status ssc_subm_conv3d_plan(const void* feats, int32_t in_dtype, const void*
                                 int32_t cout, void* out, int32_t out_dtype, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* ssc_subm_conv3d_plan for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): no workspace argument; the
+ * weights are re-laid out into a static device array of SSC_STATIC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  The call allocates nothing
+ * (no hipMalloc, no library allocation); its first call on a device looks the array's address
+ * up once.  Limit: ssc_conv_workspace_bytes(cin, cout, in_dtype) <= SSC_STATIC_SCRATCH_BYTES
+ * (every matrix-core shape, cin and cout <= 128, fits; larger 16-bit layers return
+ * SSC_ERR_WORKSPACE before anything is launched).  All calls on one GPU share that GPU's
+ * array: calls that overlap on one GPU (concurrent streams, threads) race; calls in order on
+ * one stream do not.  Other arguments, results (bit for bit) and errors as for
+ * ssc_subm_conv3d_plan; SSC_ERR_HIP if the runtime cannot give the array's address. */
+#define SSC_STATIC_SCRATCH_BYTES (1u << 20)
+ssc_status ssc_subm_conv3d_plan_static(const void* feats, int32_t in_dtype, const void* weight,
+                                       const float* bias, const void* plan, int64_t n,
+                                       int32_t cin, int32_t cout, void* out, int32_t out_dtype,
+                                       void* stream);
+
 /* Weights re-laid out once for the matrix cores, for callers that keep a layer's weights
  * (the same re-layout ssc_subm_conv3d_plan performs into its workspace on every call).
  *   weight  [27, cin, cout] bf16.

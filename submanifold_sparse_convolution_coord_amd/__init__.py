@@ -99,6 +99,8 @@ def load_library():
         "ssc_subm_conv3d": ([p, i32, p, p, p, i64, i32, i32, p, i32, p, sz, p], ctypes.c_int),
         "ssc_subm_conv3d_plan": ([p, i32, p, p, p, i64, i32, i32, p, i32, p, sz, p],
                                  ctypes.c_int),
+        "ssc_subm_conv3d_plan_static": ([p, i32, p, p, p, i64, i32, i32, p, i32, p],
+                                        ctypes.c_int),
         "ssc_linear": ([p, i32, p, p, i64, i32, i32, p, i32, p, sz, p], ctypes.c_int),
         "ssc_packed_weight_bytes": ([i32, i32, i32], sz),
         "ssc_pack_weights": ([p, i32, i32, i32, p, sz, p], ctypes.c_int),

@@ -1312,6 +1312,48 @@ extern "C" ssc_status ssc_subm_conv3d(const void* feats, int32_t in_dtype, const
                   out_dtype, nullptr, ws + M.off_weights, M.total - M.off_weights, stream);
 }
 
+// ------------------------------------------------------------------------------------------
+// Allocation-free variant of ssc_subm_conv3d_plan: the re-laid-out weights go to a static
+// device array instead of a caller workspace.  Its device address is looked up once per
+// device (the runtime's address of this device's copy of the array) and kept; host code uses
+// that address, never the array's name.
+// ------------------------------------------------------------------------------------------
+namespace ssc {
+namespace {
+static __device__ __align__(256) unsigned char scratch[SSC_STATIC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[64];
+
+// This device's copy of the static scratch, or null if the runtime cannot give its address.
+void* static_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+      return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);  // same value on every race
+    p = q;
+  }
+  return p;
+}
+}  // namespace
+}  // namespace ssc
+
+extern "C" ssc_status ssc_subm_conv3d_plan_static(const void* feats, int32_t in_dtype,
+                                                  const void* weight, const float* bias,
+                                                  const void* plan, int64_t n, int32_t cin,
+                                                  int32_t cout, void* out, int32_t out_dtype,
+                                                  void* stream) {
+  if (!valid_dtype(in_dtype)) return SSC_ERR_ARG;
+  const size_t need = ssc_conv_workspace_bytes(cin, cout, in_dtype);
+  if (need > SSC_STATIC_SCRATCH_BYTES) return SSC_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && (ws = static_scratch()) == nullptr) return SSC_ERR_HIP;
+  return run_conv(false, feats, in_dtype, weight, bias, plan, n, cin, cout, out, out_dtype,
+                  nullptr, ws, ws ? need : 0, stream);
+}
+
 extern "C" ssc_status ssc_linear(const void* feats, int32_t in_dtype, const void* weight,
                                  const float* bias, int64_t n, int32_t cin, int32_t cout, void* out,
                                  int32_t out_dtype, void* workspace, size_t workspace_bytes,
