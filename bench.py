@@ -4,13 +4,18 @@ Workload (the pages' benchmark shape, LATO.2 MLX port page, "Fleet benchmark"): 
 128^3 grid, i.i.d. occupancy 10 %, Cin = Cout = 128, k=3, bf16 features and weights, fp32
 accumulation, neighbour map and plan built once before the timed region (warm).  A step is one
 SubMConv3d layer call on resident inputs with the layer's weights re-laid out once at load time
-(the per-call re-layout variant is reported beside it); the two-layer workload adds its k=1
-layer.
+(the per-call entries are reported beside it); the two-layer workload adds its k=1 layer.
+
+Timing: after the warm-up steps, windows of --steps back-to-back steps are timed with HIP
+events on the kernels' stream until there are at least 25 windows and about 0.25 s of GPU
+work; ms_per_step is the median window / steps, and the k=3 kernel's time comes from the same
+windows (the step itself for one layer; events after each k=3 launch for two), so the kernel
+never exceeds the step.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload iid128]
-                    [--out-dtype f32|bf16] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload iid128]
+                    [--out-dtype f32|bf16] [--no-cpu-baseline] [--extras]
 """
 from __future__ import annotations
 
@@ -51,10 +56,14 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def counters_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"conv_{workload}_counters.json")
+
+
 def counted_traffic(kernel: str, digest: str, workload: str, out_dtype: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
     the current kernel sources for this kernel, workload and output type; else None."""
-    path = os.path.join(ROOT, "profiles", "conv_iid128_counters.json")
+    path = counters_path(workload)
     try:
         d = json.load(open(path))
     except (OSError, ValueError):
@@ -78,13 +87,25 @@ def _counter_rows(d: str, kernel_substr: str, counter: str):
     return vals
 
 
+def conv_kernel_name(cin: int, cout: int, out16: bool) -> str:
+    """The plain k=3 kernel instantiation a workload's timed layer runs (bf16 inputs)."""
+    wc = 4 if cout >= 64 else cout // 16
+    return (f"k_subm_lds<{cin}, {cout}, 8, {4 // wc}, {wc}, {'true' if out16 else 'false'}, 0, "
+            f"false>")
+
+
 def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mb, out_path,
-                       kernel="k_subm_lds<128, 128, 8, 1, 4, false, 0, false>",
-                       label="k_subm_lds<128,128>", workload="iid128"):
+                       workload="iid128", out_dtype="f32"):
     """HBM traffic of one kernel per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
-    the median over the dispatches: the benchmark's few cache-flushed launches are outliers)
-    scaled by what the same counters read for a plain device copy of cal_mb MiB.  The kernel
-    filter names the plain fp32-output variant the headline figure times."""
+    the median over the dispatches) scaled by what the same counters read for a plain device
+    copy of cal_mb MiB.  The kernel filter names the plain variant the workload's timed layer
+    runs (its output type as stored between layers: bf16 for the two-layer workload)."""
+    import workloads
+    layer = workloads.make(workload).layers
+    two = len(layer) > 1
+    out16 = two or out_dtype == "bf16"
+    kernel = conv_kernel_name(layer[0].cin, layer[0].cout, out16)
+    label = f"k_subm_lds<{layer[0].cin},{layer[0].cout}>"
     copy = "copy"  # torch's elementwise copy kernel
     f = _counter_rows(fetch_dir, kernel, "FETCH_SIZE")
     w = _counter_rows(write_dir, kernel, "WRITE_SIZE")
@@ -97,7 +118,8 @@ def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_m
     write_scale = known / float(np.median(cw))
     fetch_b = float(np.median(f)) * 1024.0 * fetch_scale
     write_b = float(np.median(w)) * 1024.0 * write_scale
-    d = {"kernel": label, "workload": workload, "out_dtype": "f32", "source_digest": source_digest(),
+    d = {"kernel": label, "kernel_instance": kernel, "workload": workload,
+         "out_dtype": "bf16" if out16 else "f32", "source_digest": source_digest(),
          "fetch_kib_per_dispatch": float(np.median(f)), "write_kib_per_dispatch": float(np.median(w)),
          "dispatches": [len(f), len(w)],
          "copy_calibration_mib": cal_mb, "copy_fetch_kib": float(np.median(cf)),
@@ -478,42 +500,112 @@ def time_ablations(ssc, torch, x, wt, bias, plan, nbr, dev, reps: int = 20) -> d
     return res
 
 
-def cpu_baseline(w, m_nbr) -> dict:
-    """The CPU oracle as it stands (fp64 dictionary + per-voxel loop), warm: map prebuilt,
-    conv over every site of the same workload, repeated for at least a second of wall time;
-    median run."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w) -> dict:
+    """The CPU oracle as it stands (fp64 dictionary + per-voxel loop) on the same workload,
+    timed on this host's cores: cold (dictionary + 27-tap map) and warm (the convolution over
+    every site, map prebuilt), with all threads and with one.  Each phase repeats until it has
+    at least 3 runs and about 3 s of work (one-thread warm: 3 runs); the median run is kept.
+    ``value`` is the warm all-thread throughput, the counterpart of the GPU's warm-map metric.
+    About 10-30 s in all on a many-core host."""
     import oracle
     x = w.feats.float().numpy()
     wt = w.layers[0].weight.float().numpy()
     b = w.layers[0].bias.numpy()
-    ts = []
-    # About 10 s of oracle work (at least 3 runs, at most 30 s).
-    while len(ts) < 3 or sum(ts) < 10.0:
-        t0 = time.perf_counter()
-        oracle.conv(x, wt, b, m_nbr)
-        ts.append(time.perf_counter() - t0)
-        if sum(ts) > 30:
-            break
-    t = float(np.median(ts))
-    return {"value": round(mvox_per_s(w.n, t), 4), "unit": "Mvox/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"full workload, all {w.n} sites, warm (map prebuilt), fp64, "
-                      f"median of {len(ts)} runs of {t:.3f} s ({sum(ts):.1f} s wall)"}
+    all_threads = oracle.num_threads()
+
+    def phase(fn, min_runs, min_s, max_s):
+        ts = []
+        while len(ts) < min_runs or (sum(ts) < min_s and sum(ts) < max_s):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)), len(ts)
+
+    m = oracle.build_map(w.coords, w.batch, w.grid)
+    out = {}
+    for threads in (all_threads, 1):
+        oracle.set_num_threads(threads)
+        tag = "all" if threads == all_threads else "1"
+        t, k = phase(lambda: oracle.build_map(w.coords, w.batch, w.grid), 3, 2.0, 6.0)
+        out[f"cold_{tag}"] = {"threads": threads, "median_s": round(t, 4), "runs": k,
+                              "mvox_s": round(mvox_per_s(w.n, t), 3)}
+        t, k = phase(lambda: oracle.conv(x, wt, b, m), 3, 3.0 if threads > 1 else 0.0, 12.0)
+        out[f"warm_{tag}"] = {"threads": threads, "median_s": round(t, 4), "runs": k,
+                              "mvox_s": round(mvox_per_s(w.n, t), 3)}
+        log(f"[bench] oracle {threads} thread(s): cold {out[f'cold_{tag}']['median_s']} s, "
+            f"warm {out[f'warm_{tag}']['median_s']} s")
+    oracle.set_num_threads(all_threads)
+    return {"value": out["warm_all"]["mvox_s"], "unit": "Mvox/s", "cores": all_threads,
+            "kind": "oracle", "cpu": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": (f"full workload, all {w.n} sites, fp64; value = warm conv (map prebuilt) "
+                       f"on {all_threads} threads, median of {out['warm_all']['runs']} runs; "
+                       f"phases: cold = dictionary + 27-tap map, warm = conv only, "
+                       f"each on all threads and on 1"),
+            "phases": out}
+
+
+class Windows:
+    """Device time of ``k`` back-to-back steps per window, over many windows: events on the
+    stream the kernels run on (torch's current stream) before the first step, after every
+    step and, with ``mid``, after the first kernel of every step.  Windows repeat until there
+    are at least ``min_windows`` and about ``min_s`` seconds of timed GPU work (at most
+    ``max_windows``); each window is synchronised before the next starts."""
+
+    def __init__(self, torch, step, k, mid=False, min_windows=25, min_s=0.25, max_windows=400):
+        self.step_ms, self.first_ms, self.windows = [], [], 0
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        starts = [ev() for _ in range(k + 1)]
+        mids = [ev() for _ in range(k)] if mid else None
+        total = 0.0
+        while self.windows < min_windows or (total < min_s * 1e3 and
+                                             self.windows < max_windows):
+            starts[0].record()
+            for j in range(k):
+                step(mids[j] if mid else None)
+                starts[j + 1].record()
+            torch.cuda.synchronize()
+            win = starts[0].elapsed_time(starts[k])
+            total += win
+            self.step_ms.append(win / k)
+            self.first_ms.append(
+                float(np.mean([starts[j].elapsed_time(mids[j]) for j in range(k)])) if mid
+                else win / k)
+            self.windows += 1
+        self.k = k
+
+    def summary(self, values):
+        v = np.asarray(values)
+        return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)),
+                "p90": float(np.percentile(v, 90)), "first": float(v[0])}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="iid128")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time single warm and cache-flushed calls and the pages' designs "
+                         "(ablations); these launch the headline kernel under other conditions")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter calibration)")
     ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR",
                     "CAL_FETCH_DIR", "CAL_WRITE_DIR", "CAL_MIB"),
-                    help="write profiles/conv_iid128_counters.json from rocprofv3 --pmc output")
+                    help="write the conv counter summary of --workload from rocprofv3 --pmc "
+                         "output")
     ap.add_argument("--counter-table", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR",
                     "CAL_FETCH_DIR", "CAL_WRITE_DIR", "CAL_MIB"),
                     help="print every kernel's HBM bytes per dispatch from rocprofv3 --pmc output")
@@ -524,8 +616,8 @@ def main():
         return
     if args.summarize_counters:
         a = args.summarize_counters
-        summarize_counters(a[0], a[1], a[2], a[3], int(a[4]),
-                           os.path.join(ROOT, "profiles", "conv_iid128_counters.json"))
+        summarize_counters(a[0], a[1], a[2], a[3], int(a[4]), counters_path(args.workload),
+                           workload=args.workload, out_dtype=args.out_dtype)
         return
     if args.copy_calibration:
         import torch
@@ -559,7 +651,7 @@ def main():
 
     # Cold path, timed on its own: neighbour map + plan (once per coordinate set).
     cold, cold_index, cold_plan = [], [], []
-    for _ in range(5):
+    for _ in range(7):
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         e0.record()
         nbr = ssc.build_index(coords, w.batch, w.grid, check=False)
@@ -570,6 +662,7 @@ def main():
         cold.append(e0.elapsed_time(e2))
         cold_index.append(e0.elapsed_time(e1))
         cold_plan.append(e1.elapsed_time(e2))
+    cold, cold_index, cold_plan = cold[2:], cold_index[2:], cold_plan[2:]
     pairs = int((nbr >= 0).sum().item())
     log(f"[bench] n={w.n} valid_pairs={pairs} cold index+plan median {np.median(cold):.3f} ms "
         f"(index {np.median(cold_index):.3f}, plan {np.median(cold_plan):.3f})")
@@ -579,7 +672,7 @@ def main():
     # layer calls on resident inputs: the k=3 SubMConv3d, and for the two-layer workload the
     # k=1 layer on its bf16 output.
     mfma_shapes = (16, 32, 64, 128)
-    use_packed = (wt.dtype == torch.bfloat16 and cin in mfma_shapes and cout in mfma_shapes)
+    use_packed = (wt.dtype == torch.bfloat16 and cin in (32, 64, 128) and cout in mfma_shapes)
     packed = ssc.pack_weights(wt) if use_packed else None
     two = len(w.layers) > 1
     mid_dt = torch.bfloat16 if two else odt
@@ -597,10 +690,36 @@ def main():
         else:
             ssc.subm_conv3d(x, wt, bias, plan, mid_dt, out=y1)
 
-    def step():
+    def step(mid=None):
         conv()
+        if mid is not None:
+            mid.record()
         if two:
             ssc.linear(y1, w2, b2, odt, out=y2)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    win = Windows(torch, step, args.steps)
+    t_wall = time.perf_counter() - t_wall
+    st = win.summary(win.step_ms)
+    # Two layers: the k=3 kernel's share comes from windows that also record an event after
+    # each k=3 launch (the event between the layers lengthens those steps a little, so the
+    # step itself is taken from the plain windows above).
+    kwin = Windows(torch, step, args.steps, mid=True) if two else win
+    kt = kwin.summary(kwin.first_ms)
+    ms_step, ms_kernel = st["median"], kt["median"]
+    log(f"[bench] {win.windows} windows of {args.steps} steps ({t_wall:.2f} s wall): step "
+        f"median {ms_step * 1e3:.2f} us (p10 {st['p10'] * 1e3:.2f}, p90 {st['p90'] * 1e3:.2f}, "
+        f"first window {st['first'] * 1e3:.2f}); k=3 kernel {ms_kernel * 1e3:.2f} us")
+    # Host cost of enqueueing one step through the binding (no wait): the step is GPU-bound
+    # while this stays below ms_per_step.
+    t_host = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    t_host = (time.perf_counter() - t_host) / args.steps
+    torch.cuda.synchronize()
 
     def timed(fn, k):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -611,70 +730,48 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / k
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    ms_step = timed(step, args.steps)
-    t_wall = time.perf_counter() - t_wall
-    log(f"[bench] step {ms_step * 1e3:.1f} us (wall {t_wall / args.steps * 1e6:.1f} us)")
-    # Host cost of enqueueing one step through the binding (no wait): the step is GPU-bound
-    # while this stays below ms_per_step.
-    t_host = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    t_host = (time.perf_counter() - t_host) / args.steps
-    torch.cuda.synchronize()
-
-    # Dominant kernel alone: the k=3 conv kernel, one launch per call, events on the stream
-    # it runs on (torch's current stream).
-    ms_kernel = timed(conv, args.steps)
-    log(f"[bench] conv kernel {ms_kernel * 1e3:.1f} us per launch")
-    # The same layer when the weights are re-laid out on every call (two launches).
+    # The same layer through the per-call entries: the weights re-laid out on every call
+    # (ssc_subm_conv3d_plan: two launches), and on the neighbour map alone (ssc_subm_conv3d:
+    # the plan of the map is built on every call too).
     ms_percall = timed(lambda: ssc.subm_conv3d(x, wt, bias, plan, mid_dt, out=y1), args.steps)
-    log(f"[bench] layer with per-call weight re-layout {ms_percall * 1e3:.1f} us")
-    k1_us = None
-    if two:
-        k1_us = timed(lambda: ssc.linear(y1, w2, b2, odt, out=y2), args.steps) * 1e3
-        log(f"[bench] k=1 layer {k1_us:.1f} us")
-    # Single launches, each between its own pair of events (warm caches): the spread of one
-    # call, beside the back-to-back mean above.
-    warm = []
-    for _ in range(min(args.steps, 200)):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        conv()
-        e1.record()
-        torch.cuda.synchronize()
-        warm.append(e0.elapsed_time(e1) * 1e3)
-    single_warm = {"median_us": round(float(np.median(warm)), 2),
-                   "p10_us": round(float(np.percentile(warm, 10)), 2),
-                   "p90_us": round(float(np.percentile(warm, 90)), 2), "calls": len(warm)}
-    log(f"[bench] conv kernel, single warm calls: median {single_warm['median_us']} us "
-        f"(p10 {single_warm['p10_us']}, p90 {single_warm['p90_us']})")
-    # Single launches with the caches flushed: a 512 MiB fill runs between calls (outside the
-    # events), so the conv's inputs come from HBM, not from the 256 MB MALL.
-    flush = torch.empty(512 * 262144, dtype=torch.float32, device=dev)
-    single = []
-    for _ in range(min(args.steps, 100)):
-        flush.fill_(1.0)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        conv()
-        e1.record()
-        torch.cuda.synchronize()
-        single.append(e0.elapsed_time(e1) * 1e3)
-    del flush
-    flushed = {"median_us": round(float(np.median(single)), 2),
-               "p10_us": round(float(np.percentile(single, 10)), 2),
-               "p90_us": round(float(np.percentile(single, 90)), 2), "calls": len(single)}
-    log(f"[bench] conv kernel, caches flushed: median {flushed['median_us']} us")
+    ms_map = timed(lambda: ssc.subm_conv3d(x, wt, bias, nbr, mid_dt, out=y1), args.steps)
+    log(f"[bench] layer with per-call weight re-layout {ms_percall * 1e3:.1f} us; "
+        f"on the map alone {ms_map * 1e3:.1f} us")
+
+    extras = {}
+    if args.extras:
+        # Single launches, each between its own pair of events (warm caches), and with the
+        # caches flushed (a 512 MiB fill between calls, outside the events).
+        warm = []
+        for _ in range(200):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            conv()
+            e1.record()
+            torch.cuda.synchronize()
+            warm.append(e0.elapsed_time(e1) * 1e3)
+        flush = torch.empty(512 * 262144, dtype=torch.float32, device=dev)
+        single = []
+        for _ in range(100):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            conv()
+            e1.record()
+            torch.cuda.synchronize()
+            single.append(e0.elapsed_time(e1) * 1e3)
+        del flush
+        q = lambda v: {"median_us": round(float(np.median(v)), 2),
+                       "p10_us": round(float(np.percentile(v, 10)), 2),
+                       "p90_us": round(float(np.percentile(v, 90)), 2), "calls": len(v)}
+        extras["conv_single_warm"], extras["conv_flushed"] = q(warm), q(single)
+        log(f"[bench] single warm calls {extras['conv_single_warm']}, flushed "
+            f"{extras['conv_flushed']}")
+        if x.dtype == torch.bfloat16 and use_packed:
+            extras["ablations"] = time_ablations(ssc, torch, x, wt, bias, plan, nbr, dev)
+            log(f"[bench] ablations {extras['ablations']}")
 
     resample = time_resample(ssc, torch, coords, x, w, dev)
-    abl = None
-    if x.dtype == torch.bfloat16 and use_packed:
-        abl = time_ablations(ssc, torch, x, wt, bias, plan, nbr, dev)
-        log(f"[bench] ablations {abl}")
     block = convnext = None
     if x.dtype == torch.bfloat16 and cin in (32, 64, 128):
         block = time_block(ssc, torch, coords, x, plan, w.batch, dev)
@@ -695,7 +792,8 @@ def main():
     value = mvox_per_s(w.n, ms_step * 1e-3)
     kname = f"k_subm_lds<{cin},{cout}>" if use_packed else "k_conv_valu"
     digest = source_digest()
-    traffic = counted_traffic(kname, digest, args.workload, args.out_dtype)
+    traffic = counted_traffic(kname, digest, args.workload, "f32" if out_bytes == 4 else "bf16")
+    rnd = lambda d, k=1e3, nd=2: {a: round(v * k, nd) for a, v in d.items()}
 
     res = {
         "metric": METRIC,
@@ -707,6 +805,7 @@ def main():
         "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
+        # the pages' figure for this workload (M3 Ultra, LATO.2 page): context, other hardware
         "vs_baseline": round(value / PAGES_MVOX_PER_S, 2) if args.workload == "iid128" else None,
         "dtype": "bf16" if in_bytes == 2 else "f32",
         "data": "synthetic (seeded i.i.d. occupancy, N(0,1) features, fan-in-scaled weights)",
@@ -716,20 +815,24 @@ def main():
                    "weights": ("re-laid out once at load time (packed)" if use_packed
                                else "read as given ([27, Cin, Cout])"),
                    "parallelism": "single GPU"},
+        "timing": {"windows": win.windows, "steps_per_window": args.steps,
+                   "step_us": rnd(st), "kernel_us": rnd(kt),
+                   "note": "median over windows of back-to-back steps; kernel_us: the step "
+                           "itself for one layer (same windows), for two layers the k=3 share "
+                           "of windows with an event after each k=3 launch"},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel": kname,
                      "bytes_alg_per_launch": bytes_alg, "kernel_us": round(ms_kernel * 1e3, 2)},
         "mfma": {"effective_tflops_kernel": round(tflops_kernel, 2),
+                 "frac_bf16_peak_kernel": round(tflops_kernel / PEAK_BF16_TFLOPS, 5),
                  "effective_tflops_step": round(tflops_step, 2),
                  "frac_bf16_peak_step": round(tflops_step / PEAK_BF16_TFLOPS, 5),
                  "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": flops},
-        "conv_single_warm": single_warm,
-        "conv_flushed": flushed,
-        "resample": resample,
-        "res_block": block,
-        "convnext_block": convnext,
-        "ablations": abl,
+        "pages_context": {"mvox_s": PAGES_MVOX_PER_S, "hardware": "Apple M3 Ultra (80 GPU cores)",
+                          "source": "LATO.2 MLX port page, Fleet benchmark table"},
+        "layer_us_per_call_weight_relayout": round(ms_percall * 1e3, 2),
+        "layer_us_on_map_alone": round(ms_map * 1e3, 2),
         "cold_index_plan_ms": round(float(np.median(cold)), 4),
         # Algorithmic bytes of the cold path: the index reads the coordinates (16 B per site)
         # and writes the map (27 x 4 B); the plan reads the map and writes the row ids, block
@@ -743,16 +846,16 @@ def main():
             # which site order the plan kept: mask order (interleaved tiles) or spatial order
             # (one contiguous share of the tiles per XCD)
             "site_order": "spatial" if plan.schedule() == 1 else "mask"},
-        "layer_us_per_call_weight_relayout": round(ms_percall * 1e3, 2),
-        "k1_layer_us": None if k1_us is None else round(k1_us, 2),
+        "resample": resample,
+        "res_block": block,
+        "convnext_block": convnext,
         "host_enqueue_us_per_step": round(t_host * 1e6, 2),
         "source_digest": digest,
     }
+    res.update(extras)
     if not args.no_cpu_baseline:
-        import oracle
-        log("[bench] CPU oracle baseline (map + conv on the host)")
-        m = oracle.build_map(w.coords, w.batch, w.grid)
-        res["cpu_baseline"] = cpu_baseline(w, m)
+        log("[bench] CPU oracle baseline (cold: dictionary + map; warm: conv)")
+        res["cpu_baseline"] = cpu_baseline(w)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -49,6 +49,8 @@ def _load():
         p = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int32
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         lib.oracle_build_map.argtypes = [p, i64, i32, i32, i32, i32, i32, p]
         lib.oracle_build_map.restype = ctypes.c_int
         lib.oracle_conv.argtypes = [p, p, p, p, i64, i32, i32, i32, i32, p]
@@ -61,6 +63,11 @@ def _load():
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (n >= 1)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _ptr(a: np.ndarray):

@@ -68,6 +68,11 @@ extern "C" {
 // Number of OpenMP threads the oracle's parallel loops use.
 int oracle_num_threads() { return omp_get_max_threads(); }
 
+// Sets that number (for timing the oracle on one core and on all of them).
+void oracle_set_num_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+
 // Neighbour map of a set of active sites.
 //   coords  [n, 4] int32 rows (b, x, y, z)
 //   ksize   3 (27 taps) or 1 (one tap, the site itself)
