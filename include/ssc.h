@@ -90,6 +90,36 @@ ssc_status ssc_build_index(const int32_t* coords, int64_t n, int32_t batch, cons
                            int32_t* nbr, void* workspace, size_t workspace_bytes, int32_t check,
                            void* stream);
 
+/* ssc_build_index with the choice of index structure (the map is the same, bit for bit):
+ *   SSC_INDEX_HASH   the open-addressing hash of the packed 64-bit keys (trellis-mac article,
+ *                    flowchart: a hash map of the active coordinates);
+ *   SSC_INDEX_DENSE  the sorted-key index (LATO.2 MLX port page, module table: a sorted-key
+ *                    indice map) kept as an occupancy bitmap over the dense voxel id
+ *                    v = ((b*Gx + x)*Gy + y)*Gz + z with running counts, so that the rank of
+ *                    a site's bit is its position in key order and a lookup is four loads
+ *                    without a search; its arrays take 3/16 byte per voxel + 4 bytes per site;
+ *   SSC_INDEX_AUTO   (what ssc_build_index uses) the dense index when its arrays fit in
+ *                    ssc_index_workspace_bytes(n), i.e. when batch*Gx*Gy*Gz is at most about
+ *                    85 voxels per hash slot; the hash otherwise.
+ * SSC_INDEX_DENSE with a larger grid than the workspace holds returns SSC_ERR_WORKSPACE (or
+ * SSC_ERR_UNSUPPORTED when batch*Gx*Gy*Gz >= 2^62); an unknown method SSC_ERR_ARG. */
+#define SSC_INDEX_AUTO 0
+#define SSC_INDEX_HASH 1
+#define SSC_INDEX_DENSE 2
+ssc_status ssc_build_index_ex(const int32_t* coords, int64_t n, int32_t batch,
+                              const int32_t* grid, int32_t* nbr, void* workspace,
+                              size_t workspace_bytes, int32_t check, int32_t method,
+                              void* stream);
+
+/* Workspace bytes of ssc_build_index_ex with that method (host only): the hash's size for
+ * SSC_INDEX_AUTO and SSC_INDEX_HASH (= ssc_index_workspace_bytes(n)), the dense index's own
+ * for SSC_INDEX_DENSE (0 when batch*Gx*Gy*Gz >= 2^62 or on bad arguments). */
+size_t ssc_index_workspace_bytes_ex(int64_t n, int32_t batch, const int32_t* grid,
+                                    int32_t method);
+
+/* The structure SSC_INDEX_AUTO picks for n sites in batch x grid (host only, no GPU). */
+int32_t ssc_index_method(int64_t n, int32_t batch, const int32_t* grid);
+
 /* ---------------------------------------------------------------------------------------
  * Warm plan (derived from the neighbour map once per coordinate set, reused by every layer)
  * ------------------------------------------------------------------------------------- */

@@ -90,6 +90,9 @@ def load_library():
         "ssc_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "ssc_index_workspace_bytes": ([i64], sz),
         "ssc_build_index": ([p, i64, i32, p, p, p, sz, i32, p], ctypes.c_int),
+        "ssc_build_index_ex": ([p, i64, i32, p, p, p, sz, i32, i32, p], ctypes.c_int),
+        "ssc_index_method": ([i64, i32, p], ctypes.c_int32),
+        "ssc_index_workspace_bytes_ex": ([i64, i32, p, i32], sz),
         "ssc_plan_bytes": ([i64], sz),
         "ssc_plan_workspace_bytes": ([i64], sz),
         "ssc_build_plan": ([p, p, i64, i32, p, p, sz, p, sz, p], ctypes.c_int),
@@ -173,9 +176,15 @@ def _dtype_code(dt: torch.dtype, name: str) -> int:
     raise ValueError(f"{name}: dtype {dt} not supported (float32, bfloat16 or float16)")
 
 
+INDEX_METHODS = {"auto": 0, "hash": 1, "dense": 2}
+
+
 def build_index(coords: torch.Tensor, batch: int, grid: Sequence[int],
-                check: bool = True) -> torch.Tensor:
-    """[N, 27] int32 neighbour map of the sites ``coords`` ([N, 4] int32 (b, x, y, z))."""
+                check: bool = True, method: str = "auto") -> torch.Tensor:
+    """[N, 27] int32 neighbour map of the sites ``coords`` ([N, 4] int32 (b, x, y, z)).
+    ``method``: "auto", "hash" or "dense" (the index structure; the map is the same)."""
+    if method not in INDEX_METHODS:
+        raise ValueError(f"method must be one of {sorted(INDEX_METHODS)}")
     _need_cuda(coords, "coords")
     if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 4:
         raise ValueError("coords must be int32 [N, 4]")
@@ -183,11 +192,13 @@ def build_index(coords: torch.Tensor, batch: int, grid: Sequence[int],
     dev = coords.device
     n = coords.shape[0]
     nbr = torch.empty((n, TAPS), dtype=torch.int32, device=dev)
-    ws = _workspace(lib.ssc_index_workspace_bytes(n), dev)
     g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
+    ws = _workspace(lib.ssc_index_workspace_bytes_ex(n, int(batch), g, INDEX_METHODS[method]),
+                    dev)
     with torch.cuda.device(dev):
-        st = lib.ssc_build_index(_ptr(coords), n, int(batch), g, _ptr(nbr), _ptr(ws), ws.numel(),
-                                 1 if check else 0, _stream(dev))
+        st = lib.ssc_build_index_ex(_ptr(coords), n, int(batch), g, _ptr(nbr), _ptr(ws),
+                                    ws.numel(), 1 if check else 0, INDEX_METHODS[method],
+                                    _stream(dev))
     _check(st, "ssc_build_index")
     return nbr
 

@@ -64,7 +64,8 @@ __global__ void k_parent_keys(const int4* __restrict__ coords, int64_t n, int ba
                               uint64_t* __restrict__ keys, uint32_t* __restrict__ vals,
                               uint32_t* __restrict__ totals, uint32_t* __restrict__ bad) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (blockIdx.x == 0 && threadIdx.x < kDigits) totals[threadIdx.x] = 0;
+  if (blockIdx.x == 0)
+    for (int d = threadIdx.x; d < kDigits; d += blockDim.x) totals[d] = 0;
   if (i >= n) return;
   const int4 c = coords[i];
   uint64_t key = 0;
@@ -443,7 +444,7 @@ ssc_status number_parents(const int32_t* coords, int64_t n, int32_t batch, const
       reinterpret_cast<const int4*>(coords), n, batch, grid[0], grid[1], grid[2], hx, hy, hz,
       keys, vals, totals, bad);
   const int bits = bits_for(static_cast<uint64_t>(batch) * hx * hy * hz);
-  if (radix_sort_pairs<uint64_t>(ws, L.sort, n, bits, s) == 1) {
+  if (radix_sort_pairs<uint64_t, 9>(ws, L.sort, n, bits, s) == 1) {
     keys = reinterpret_cast<uint64_t*>(ws + L.sort.off_keys_b);
     vals = reinterpret_cast<uint32_t*>(ws + L.sort.off_vals_b);
   }

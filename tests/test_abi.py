@@ -80,6 +80,28 @@ def test_build_index_argument_errors(lib):
     assert f(None, 0, 1, GRID, None, None, 0, 1, None) == ssc.SSC_OK  # empty: nothing to do
 
 
+def test_build_index_method_choice_and_errors(lib):
+    f = lib.ssc_build_index_ex
+    big = 1 << 30
+    assert f(FAKE, 10, 1, GRID, FAKE, FAKE, big, 0, 3, None) == ssc.SSC_ERR_ARG   # method
+    assert f(FAKE, 10, 1, GRID, FAKE, FAKE, big, 0, -1, None) == ssc.SSC_ERR_ARG
+    huge = (ctypes.c_int32 * 3)(65535, 65535, 65535)
+    # forced dense over 2^48 * batch voxels: beyond 62 bits -> unsupported; else short space
+    assert f(FAKE, 10, 65535, huge, FAKE, FAKE, big, 0, 2, None) == ssc.SSC_ERR_UNSUPPORTED
+    assert f(FAKE, 10, 1, huge, FAKE, FAKE, big, 0, 2, None) == ssc.SSC_ERR_WORKSPACE
+    # automatic choice: dense while its arrays fit the hash's workspace
+    m = lib.ssc_index_method
+    assert m(209473, 1, (ctypes.c_int32 * 3)(128, 128, 128)) == 2
+    assert m(1223408, 1, (ctypes.c_int32 * 3)(512, 512, 512)) == 2
+    assert m(10, 1, huge) == 1
+    assert m(1000, 1, (ctypes.c_int32 * 3)(512, 512, 512)) == 1      # too sparse for a bitmap
+    assert m(-1, 1, GRID) == 1
+    wb = lib.ssc_index_workspace_bytes_ex
+    assert wb(1000, 1, GRID, 0) == wb(1000, 1, GRID, 1) == lib.ssc_index_workspace_bytes(1000)
+    assert wb(1, 1, (ctypes.c_int32 * 3)(64, 64, 64), 2) >= 64 ** 3 // 8
+    assert wb(10, 65535, huge, 2) == 0 and wb(10, 1, GRID, 7) == 0 and wb(-1, 1, GRID, 0) == 0
+
+
 def test_build_plan_argument_errors(lib):
     f = lib.ssc_build_plan
     big = 1 << 30

@@ -552,3 +552,46 @@ def test_cached_index_reuse_and_invalidation():
         del t
     assert len(ssc._CACHE) <= ssc._CACHE_MAX
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["tiny", "iid128", "shell256", "batch4", "shell512"])
+def test_index_methods_bit_exact(name):
+    """Both index structures (the hash and the dense rank index) build the oracle's map bit for
+    bit on every workload, and the automatic choice is the dense one at these sizes."""
+    say(f"[index] {name} hash and dense")
+    w, m = workload_case(name)
+    c = torch.from_numpy(w.coords).to(DEV)
+    for method in ("hash", "dense"):
+        nbr = ssc.build_index(c, w.batch, w.grid, method=method)
+        torch.cuda.synchronize()
+        assert np.array_equal(nbr.cpu().numpy(), m), f"{name}: {method} map differs"
+    g = (__import__("ctypes").c_int32 * 3)(*w.grid)
+    assert ssc.load_library().ssc_index_method(w.n, w.batch, g) == 2
+
+
+def test_dense_index_errors_and_edges():
+    """Dense index: out-of-range rows and duplicates are reported like the hash's; grids at the
+    edge of their axes; sites only in the last batch entry; one site."""
+    say("[index] dense errors and edges")
+    grid = (9, 1, 70)
+    rng = np.random.default_rng(44)
+    coords = workloads.random_sites(rng, 3, grid, 40)
+    coords = coords[coords[:, 0] == 2]                               # last batch entry only
+    coords = np.concatenate([coords, np.array([[2, 8, 0, 69], [2, 0, 0, 0]], np.int32)])
+    coords = np.unique(coords, axis=0)[rng.permutation(len(np.unique(coords, axis=0)))]
+    c = torch.from_numpy(np.ascontiguousarray(coords)).to(DEV)
+    for method in ("hash", "dense"):
+        nbr = ssc.build_index(c, 3, grid, method=method)
+        assert np.array_equal(nbr.cpu().numpy(), oracle.build_map(coords, 3, grid))
+        one = torch.from_numpy(coords[:1].copy()).to(DEV)
+        assert np.array_equal(ssc.build_index(one, 3, grid, method=method).cpu().numpy(),
+                              oracle.build_map(coords[:1], 3, grid))
+        bad = coords.copy()
+        bad[0, 3] = grid[2]                                          # z outside the grid
+        with pytest.raises(ssc.SscError) as e:
+            ssc.build_index(torch.from_numpy(bad).to(DEV), 3, grid, method=method)
+        assert e.value.status == ssc.SSC_ERR_COORD_RANGE
+        dup = np.concatenate([coords, coords[3:4]])
+        with pytest.raises(ssc.SscError) as e:
+            ssc.build_index(torch.from_numpy(dup).to(DEV), 3, grid, method=method)
+        assert e.value.status == ssc.SSC_ERR_DUPLICATE
