@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "dense.h"
 #include "sort.h"
 
 namespace ssc {
@@ -148,181 +149,27 @@ __global__ void k_query(const int4* __restrict__ coords, int64_t n, int batch, i
 }
 
 // ------------------------------------------------------------------------------------------
-// Dense rank index: the sorted-key index map (LATO.2 MLX port page, module table: gather /
-// scatter over a sorted-key indice map) with the search replaced by a rank over an occupancy
-// bitmap.  Voxel (b, x, y, z) has the dense id v = ((b * Gx + x) * Gy + y) * Gz + z; bit v of
-// the bitmap is set for every site; the rank of a set bit (the number of set bits before it)
-// is the site's position in ascending key order, and sorted_rows[rank] is its row.  A lookup
-// is one bitmap word, the running counts of its superblock and of the word within it, and one
-// row: four loads, all from arrays of about 3/16 byte per voxel plus 4 bytes per site (1.2 MB
-// at 128^3, 10 %), which stay in L2.
-//   k_dense_clear   zero the bitmap and the error counters
-//   k_dense_mark    one thread per site: validate, set bit v; lanes of a wave that set bits of
-//                   the same word (runs of equal words, as sites in key order give) OR them
-//                   together first, so one 64-bit atomic OR serves the run; a bit set twice is
-//                   a duplicate (inside the run, or seen in the word the atomic returns)
-//   k_dense_count   one workgroup per superblock of 1024 words: each word's running count
-//                   inside the superblock (16-bit) and the superblock's total
-//   k_dense_scan    one workgroup: exclusive scan of the superblock totals (32-bit)
+// Dense rank index (dense.h): the sorted-key index map kept as an occupancy bitmap of the
+// sites with running counts; the rank of a site's bit is its position in key order and
+// sorted_rows[rank] its row.  The arrays take about 3/16 byte per voxel plus 4 bytes per site
+// (1.2 MB at 128^3, 10 %) and stay in L2.  After dense.h's clear, mark, count and scan:
 //   k_dense_rows    one thread per site: sorted_rows[rank(v)] = row
 //   k_dense_query   one thread per site: per (dx, dy) one word serves the three dz taps
 //                   unless they cross a word boundary; rows staged in LDS and written as
 //                   whole map rows
 // ------------------------------------------------------------------------------------------
-constexpr int kSuperWords = 1024;  // bitmap words per superblock (65536 voxels)
-
-struct DenseLayout {
-  uint64_t voxels, words, supers;
-  size_t off_bits, off_local, off_super, off_rows, total;
+struct DenseIndexLayout {
+  DenseBits b;
+  size_t off_rows, total;
 };
 
-// Voxels of the dense id space, or 0 when it does not fit 62 bits.
-inline uint64_t dense_voxels(int32_t batch, const int32_t* grid) {
-  const unsigned __int128 v = static_cast<unsigned __int128>(batch) * grid[0] * grid[1] * grid[2];
-  return v >> 62 ? 0 : static_cast<uint64_t>(v);
-}
-
-inline DenseLayout dense_layout(int64_t n, uint64_t voxels) {
-  DenseLayout L;
-  L.voxels = voxels;
-  L.words = (voxels + 63) / 64;
-  L.supers = (L.words + kSuperWords - 1) / kSuperWords;
-  L.off_bits = kAlign;  // [0, 256): two uint32 error counters
-  L.off_local = align_up(L.off_bits + sizeof(uint64_t) * L.supers * kSuperWords);
-  L.off_super = align_up(L.off_local + sizeof(uint16_t) * L.supers * kSuperWords);
-  L.off_rows = align_up(L.off_super + sizeof(uint32_t) * (L.supers + 1));
+// [0, 256): two uint32 error counters; the bitmap structure; the rows in key order.
+inline DenseIndexLayout dense_index_layout(int64_t n, uint64_t voxels) {
+  DenseIndexLayout L;
+  L.b = dense_bits_layout(voxels, kAlign);
+  L.off_rows = L.b.end;
   L.total = align_up(L.off_rows + sizeof(uint32_t) * (n > 0 ? n : 1));
   return L;
-}
-
-__device__ __forceinline__ uint64_t dense_id(int b, int x, int y, int z, int gx, int gy, int gz) {
-  return ((static_cast<uint64_t>(b) * gx + x) * gy + y) * static_cast<uint64_t>(gz) + z;
-}
-
-__device__ __forceinline__ bool in_range(int4 c, int batch, int gx, int gy, int gz) {
-  return c.x >= 0 && c.x < batch && c.y >= 0 && c.y < gx && c.z >= 0 && c.z < gy && c.w >= 0 &&
-         c.w < gz;
-}
-
-__global__ void k_dense_clear(uint64_t* __restrict__ bits, uint64_t words,
-                              uint32_t* __restrict__ counters) {
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
-  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words;
-       i += stride)
-    bits[i] = 0ull;
-  if (blockIdx.x == 0 && threadIdx.x < 2) counters[threadIdx.x] = 0;
-}
-
-// Grid-stride over whole waves (every lane of a wave runs the same iterations, so the lane
-// shuffles below see all 64 lanes).
-__global__ __launch_bounds__(256) void k_dense_mark(const int4* __restrict__ coords, int64_t n,
-                                                    int batch, int gx, int gy, int gz,
-                                                    unsigned long long* __restrict__ bits,
-                                                    uint32_t* __restrict__ counters) {
-  const int lane = threadIdx.x & 63;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * blockDim.x + (threadIdx.x & ~63);
-       base < n; base += stride) {
-    const int64_t i = base + lane;
-    bool bad = false;
-    uint64_t w = ~0ull;         // no word: lanes past n and sites outside the grid
-    unsigned long long m = 0ull;
-    if (i < n) {
-      const int4 c = coords[i];  // (b, x, y, z)
-      if (in_range(c, batch, gx, gy, gz)) {
-        const uint64_t v = dense_id(c.x, c.y, c.z, c.w, gx, gy, gz);
-        w = v >> 6;
-        m = 1ull << (v & 63);
-      } else {
-        bad = true;
-      }
-    }
-    // Runs of equal words among consecutive lanes: segment id = heads up to this lane.
-    const uint64_t wprev = __shfl_up(w, 1, 64);
-    const bool head = lane == 0 || wprev != w;
-    const unsigned long long heads = __ballot(head);
-    const int seg = __popcll(heads & ((2ull << lane) - 1ull));
-    bool dup = false;
-    unsigned long long acc = m;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const unsigned long long o = __shfl_up(acc, off, 64);
-      const int oseg = __shfl_up(seg, off, 64);
-      if (lane >= off && oseg == seg) {
-        dup |= (acc & o) != 0ull;   // the two ORs cover disjoint lanes of the run
-        acc |= o;
-      }
-    }
-    const int nseg = __shfl_down(seg, 1, 64);
-    const bool tail = lane == 63 || nseg != seg;
-    if (tail && w != ~0ull) {
-      if (atomicOr(&bits[w], acc) & acc) dup = true;
-    }
-    if (bad) atomicAdd(&counters[0], 1u);
-    if (dup) atomicAdd(&counters[1], 1u);
-  }
-}
-
-// One workgroup (1024 threads, one word each) per superblock: block-wide exclusive scan of
-// the words' popcounts (< 65536: 16 bits) and the superblock total.
-__global__ __launch_bounds__(1024) void k_dense_count(const uint64_t* __restrict__ bits,
-                                                      uint16_t* __restrict__ local,
-                                                      uint32_t* __restrict__ super_count) {
-  __shared__ uint32_t wsum[16];
-  const uint64_t wd = static_cast<uint64_t>(blockIdx.x) * kSuperWords + threadIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t c = static_cast<uint32_t>(__popcll(bits[wd]));
-  uint32_t incl = c;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int k = 0; k < wave; ++k) before += wsum[k];
-  local[wd] = static_cast<uint16_t>(before + incl - c);
-  if (threadIdx.x == kSuperWords - 1) super_count[blockIdx.x] = before + incl;
-}
-
-// One workgroup of 1024 threads: in-place exclusive scan of the superblock totals, in chunks
-// of 1024 with a running carry; super_count[supers] receives the grand total.
-__global__ __launch_bounds__(1024) void k_dense_scan(uint32_t* __restrict__ super_count,
-                                                     uint64_t supers) {
-  __shared__ uint32_t wsum[16];
-  __shared__ uint32_t carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (uint64_t base = 0; base < supers; base += 1024) {
-    const uint64_t i = base + threadIdx.x;
-    const uint32_t c = i < supers ? super_count[i] : 0u;
-    uint32_t incl = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    uint32_t before = carry;
-    for (int k = 0; k < wave; ++k) before += wsum[k];
-    if (i < supers) super_count[i] = before + incl - c;
-    __syncthreads();
-    if (threadIdx.x == 1023) carry = before + incl;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) super_count[supers] = carry;
-}
-
-// Rank of set bit v (its word given) among all set bits.
-__device__ __forceinline__ uint32_t dense_rank(const uint16_t* __restrict__ local,
-                                               const uint32_t* __restrict__ super_count,
-                                               uint64_t v, uint64_t word) {
-  const uint64_t w = v >> 6;
-  const uint64_t below = word & ((1ull << (v & 63)) - 1ull);
-  return super_count[w / kSuperWords] + local[w] + static_cast<uint32_t>(__popcll(below));
 }
 
 __global__ void k_dense_rows(const int4* __restrict__ coords, int64_t n, int batch, int gx,
@@ -605,7 +452,7 @@ namespace {
 // needs for the same n (so ssc_index_workspace_bytes covers both), which keeps it to grids of
 // at most about 85 voxels per hash slot; otherwise the hash does.
 bool dense_fits(int64_t n, uint64_t voxels) {
-  return voxels > 0 && dense_layout(n, voxels).total <= index_layout(n).total;
+  return voxels > 0 && dense_index_layout(n, voxels).total <= index_layout(n).total;
 }
 
 ssc_status build_index_hash(const int4* coords, int64_t n, int32_t batch, const int32_t* grid,
@@ -628,21 +475,15 @@ ssc_status build_index_hash(const int4* coords, int64_t n, int32_t batch, const 
 
 ssc_status build_index_dense(const int4* coords, int64_t n, int32_t batch, const int32_t* grid,
                              uint64_t voxels, int32_t* nbr, char* ws, hipStream_t s) {
-  const DenseLayout D = dense_layout(n, voxels);
+  const DenseIndexLayout D = dense_index_layout(n, voxels);
   uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
-  auto* bits = reinterpret_cast<uint64_t*>(ws + D.off_bits);
-  auto* local = reinterpret_cast<uint16_t*>(ws + D.off_local);
-  auto* sup = reinterpret_cast<uint32_t*>(ws + D.off_super);
+  auto* bits = reinterpret_cast<uint64_t*>(ws + D.b.off_bits);
+  auto* local = reinterpret_cast<uint16_t*>(ws + D.b.off_local);
+  auto* sup = reinterpret_cast<uint32_t*>(ws + D.b.off_super);
   auto* rows = reinterpret_cast<int32_t*>(ws + D.off_rows);
+  dense_build(coords, n, batch, grid, 0, D.b, ws, counters, 1, nullptr, s);
   const int bs = 256;
-  const uint64_t words = D.supers * kSuperWords;  // whole superblocks, tail words zero
-  k_dense_clear<<<static_cast<unsigned>(std::min<uint64_t>((words + bs - 1) / bs, 8192)), bs, 0,
-                  s>>>(bits, words, counters);
   const unsigned site_blocks = static_cast<unsigned>(std::min<int64_t>((n + bs - 1) / bs, 65536));
-  k_dense_mark<<<site_blocks, bs, 0, s>>>(coords, n, batch, grid[0], grid[1], grid[2],
-                                          reinterpret_cast<unsigned long long*>(bits), counters);
-  k_dense_count<<<static_cast<unsigned>(D.supers), kSuperWords, 0, s>>>(bits, local, sup);
-  k_dense_scan<<<1, 1024, 0, s>>>(sup, D.supers);
   k_dense_rows<<<site_blocks, bs, 0, s>>>(coords, n, batch, grid[0], grid[1], grid[2], bits,
                                           local, sup, rows);
   k_dense_query<<<static_cast<unsigned>((n + kQuerySites - 1) / kQuerySites), kQuerySites, 0,
@@ -668,7 +509,7 @@ extern "C" ssc_status ssc_build_index_ex(const int32_t* coords, int64_t n, int32
   bool dense = method == SSC_INDEX_DENSE || (method == SSC_INDEX_AUTO && dense_fits(n, voxels));
   if (dense) {
     if (voxels == 0) return SSC_ERR_UNSUPPORTED;
-    if (workspace_bytes < dense_layout(n, voxels).total) return SSC_ERR_WORKSPACE;
+    if (workspace_bytes < dense_index_layout(n, voxels).total) return SSC_ERR_WORKSPACE;
   } else if (workspace_bytes < index_layout(n).total) {
     return SSC_ERR_WORKSPACE;
   }
@@ -702,7 +543,7 @@ extern "C" size_t ssc_index_workspace_bytes_ex(int64_t n, int32_t batch, const i
   if (method != SSC_INDEX_DENSE) return index_layout(n).total;
   if (grid == nullptr || batch < 1) return 0;
   const uint64_t voxels = dense_voxels(batch, grid);
-  return voxels == 0 ? 0 : dense_layout(n, voxels).total;
+  return voxels == 0 ? 0 : dense_index_layout(n, voxels).total;
 }
 
 extern "C" int32_t ssc_index_method(int64_t n, int32_t batch, const int32_t* grid) {

@@ -7,12 +7,15 @@
 // SparseUpsample(2) with a downsample through the cached mapping.  Each produces a new
 // coordinate set, which the convolution then indexes cold.
 //
-//   downsample: parent(b,x,y,z) = (b, x>>1, y>>1, z>>1).  Parent keys are the dense row-major
-//               index of the parent in [batch, ceil(gx/2), ceil(gy/2), ceil(gz/2)]; a stable
-//               LSD radix sort of (key, site) orders the sites by parent, the first site of
-//               each run starts a parent (an exclusive scan numbers them), and each parent's
-//               feature is the channel-wise maximum over its run.  Output parents are in
-//               ascending (b, x, y, z) order; `parent[i]` maps every input site to its parent.
+//   downsample: parent(b,x,y,z) = (b, x>>1, y>>1, z>>1).  Parents are numbered in ascending
+//               order of their dense row-major index in [batch, ceil(gx/2), ceil(gy/2),
+//               ceil(gz/2)]: when that grid's bitmap fits the workspace, by the dense rank
+//               structure of dense.h (every site marks its parent cell; a parent's number is
+//               the rank of its bit: five launches); otherwise by a stable LSD radix sort of
+//               (key, site), the first site of each run starting a parent and an exclusive
+//               scan numbering them.  Either way each parent's 8 child slots (child k =
+//               4(x&1) + 2(y&1) + (z&1)) record its sites, and its feature is the channel-wise
+//               maximum over them.  `parent[i]` maps every input site to its parent.
 //   upsample:   out[i] = parent_feats[parent[i]] for the parent map of a downsample.
 //   spatial2channel: the same parents; parent p's features are its 8 children's, channel c of
 //               child k = 4(x&1) + 2(y&1) + (z&1) at column c*8 + k, zeros for absent
@@ -24,6 +27,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "dense.h"
 #include "sort.h"
 
 namespace ssc {
@@ -31,10 +35,13 @@ namespace {
 
 constexpr int kScanTile = 2048;  // items per workgroup in the parent numbering scan
 
+// Workspace of the downsample: the numbering's scratch (the sort path's buffers, or the dense
+// path's bitmap in the same bytes), the parents' child slots (8 int32 per site: m <= n
+// parents) and a counter.
 struct DownLayout {
   SortLayout<uint64_t> sort;
   int64_t scan_tiles;
-  size_t off_tile_sums, off_heads, off_counter, total;
+  size_t off_tile_sums, off_children, off_counter, total;
 };
 
 // Small device-side initialisations (no memset nodes in a stream a caller may capture).
@@ -51,10 +58,20 @@ inline DownLayout down_layout(int64_t n) {
   L.sort = sort_layout<uint64_t>(m, 0);
   L.scan_tiles = (m + kScanTile - 1) / kScanTile;
   L.off_tile_sums = align_up(L.sort.total);
-  L.off_heads = align_up(L.off_tile_sums + sizeof(uint32_t) * L.scan_tiles);
-  L.off_counter = align_up(L.off_heads + sizeof(int32_t) * m);
+  L.off_children = align_up(L.off_tile_sums + sizeof(uint32_t) * L.scan_tiles);
+  L.off_counter = align_up(L.off_children + sizeof(int32_t) * 8 * m);
   L.total = align_up(L.off_counter + sizeof(uint32_t) * 4);
   return L;
+}
+
+// The dense numbering's bitmap of the parent grid, in the numbering's scratch bytes.
+inline DenseBits down_dense(uint64_t parent_cells) { return dense_bits_layout(parent_cells, 0); }
+inline bool down_dense_fits(int64_t n, uint64_t parent_cells) {
+  return parent_cells > 0 && down_dense(parent_cells).end <= down_layout(n).off_children;
+}
+
+__device__ __forceinline__ int child_slot(int4 c) {
+  return ((c.y & 1) << 2) | ((c.z & 1) << 1) | (c.w & 1);
 }
 
 // Parent key of every site (invalid rows are counted and keyed 0); clears the sort totals and
@@ -62,11 +79,14 @@ inline DownLayout down_layout(int64_t n) {
 __global__ void k_parent_keys(const int4* __restrict__ coords, int64_t n, int batch, int gx, int gy,
                               int gz, uint64_t hx, uint64_t hy, uint64_t hz,
                               uint64_t* __restrict__ keys, uint32_t* __restrict__ vals,
-                              uint32_t* __restrict__ totals, uint32_t* __restrict__ bad) {
+                              uint32_t* __restrict__ totals, uint32_t* __restrict__ bad,
+                              int32_t* __restrict__ children) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (blockIdx.x == 0)
     for (int d = threadIdx.x; d < kDigits; d += blockDim.x) totals[d] = 0;
   if (i >= n) return;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) children[i * 8 + k] = -1;  // slots of parent i, if it exists
   const int4 c = coords[i];
   uint64_t key = 0;
   if (c.x < 0 || c.x >= batch || c.y < 0 || c.y >= gx || c.z < 0 || c.z >= gy || c.w < 0 ||
@@ -123,7 +143,8 @@ __global__ __launch_bounds__(256) void k_scan_tile_sums(uint32_t* __restrict__ t
 __global__ __launch_bounds__(256) void k_assign_parents(
     const uint64_t* __restrict__ keys, const uint32_t* __restrict__ vals, int64_t n,
     const uint32_t* __restrict__ tile_offsets, uint64_t hx, uint64_t hy, uint64_t hz,
-    int32_t* __restrict__ parent, int4* __restrict__ out_coords, int32_t* __restrict__ heads) {
+    const int4* __restrict__ coords, int32_t* __restrict__ parent, int4* __restrict__ out_coords,
+    int32_t* __restrict__ children) {
   __shared__ uint32_t sh[256];
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanTile;
   constexpr int kPer = kScanTile / 256;
@@ -143,7 +164,9 @@ __global__ __launch_bounds__(256) void k_assign_parents(
     if (r >= n) break;
     run += h[k];
     const int32_t p = static_cast<int32_t>(run) - 1;
-    parent[vals[r]] = p;
+    const uint32_t site = vals[r];
+    parent[site] = p;
+    children[static_cast<int64_t>(p) * 8 + child_slot(coords[site])] = static_cast<int32_t>(site);
     if (h[k]) {
       const uint64_t key = keys[r];
       const uint64_t z = key % hz, rest = key / hz;
@@ -151,17 +174,41 @@ __global__ __launch_bounds__(256) void k_assign_parents(
       const uint64_t x = rest2 % hx, b = rest2 / hx;
       out_coords[p] = make_int4(static_cast<int>(b), static_cast<int>(x), static_cast<int>(y),
                                 static_cast<int>(z));
-      heads[p] = static_cast<int32_t>(r);
     }
   }
 }
 
+// Dense numbering, after dense.h's build over the parent cells: site i's parent is the rank
+// of its cell's bit; it records the site in the parent's child slot and the parent's
+// coordinates (every child writes the same four values).
+__global__ void k_ds_assign(const int4* __restrict__ coords, int64_t n, int batch, int gx, int gy,
+                            int gz, int hx, int hy, int hz, const uint64_t* __restrict__ bits,
+                            const uint16_t* __restrict__ local,
+                            const uint32_t* __restrict__ super_count,
+                            int32_t* __restrict__ parent, int4* __restrict__ out_coords,
+                            int32_t* __restrict__ children) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += stride) {
+    const int4 c = coords[i];
+    if (!in_range(c, batch, gx, gy, gz)) {
+      parent[i] = -1;
+      continue;
+    }
+    const uint64_t v = dense_id(c.x, c.y >> 1, c.z >> 1, c.w >> 1, hx, hy, hz);
+    const uint32_t p = dense_rank(local, super_count, v, bits[v >> 6]);
+    parent[i] = static_cast<int32_t>(p);
+    children[static_cast<int64_t>(p) * 8 + child_slot(c)] = static_cast<int32_t>(i);
+    out_coords[p] = make_int4(c.x, c.y >> 1, c.z >> 1, c.w >> 1);
+  }
+}
+
 // Channel-wise maximum, 8 bf16 channels (one 16-byte word) per thread; channels % 8 == 0.
+// The parent's sites are its child slots, taken in slot order; a larger value replaces the
+// running maximum, so the result is one of the inputs, bit for bit.
 __global__ void k_maxpool_bf16x8(const uint4* __restrict__ feats, int32_t words,
-                                 const uint32_t* __restrict__ sorted_sites,
-                                 const int32_t* __restrict__ heads,
-                                 const int64_t* __restrict__ result, int64_t n,
-                                 uint4* __restrict__ out) {
+                                 const int32_t* __restrict__ children,
+                                 const int64_t* __restrict__ result, uint4* __restrict__ out) {
   const int64_t m = result[0];
   const int64_t total = m * words;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -169,21 +216,27 @@ __global__ void k_maxpool_bf16x8(const uint4* __restrict__ feats, int32_t words,
        g += stride) {
     const int64_t p = g / words;
     const int w = static_cast<int>(g - p * words);
-    const int64_t r0 = heads[p];
-    const int64_t r1 = p + 1 < m ? heads[p + 1] : n;
-    uint4 best = feats[static_cast<int64_t>(sorted_sites[r0]) * words + w];
-    for (int64_t r = r0 + 1; r < r1; ++r) {
-      const uint4 v = feats[static_cast<int64_t>(sorted_sites[r]) * words + w];
+    const int32_t* ch = children + p * 8;
+    int k0 = 0;
+    while (k0 < 7 && ch[k0] < 0) ++k0;  // every parent has at least one site
+    if (ch[k0] < 0) {
+      out[g] = make_uint4(0u, 0u, 0u, 0u);
+      continue;
+    }
+    uint4 best = feats[static_cast<int64_t>(ch[k0]) * words + w];
+    for (int k = k0 + 1; k < 8; ++k) {
+      if (ch[k] < 0) continue;
+      const uint4 v = feats[static_cast<int64_t>(ch[k]) * words + w];
       uint32_t* bb = reinterpret_cast<uint32_t*>(&best);
       const uint32_t* vv = reinterpret_cast<const uint32_t*>(&v);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int q = 0; q < 4; ++q) {
         // two bf16 per word: keep the larger of each half, bits and all
-        const uint32_t lo_b = bb[k] & 0xffffu, hi_b = bb[k] >> 16;
-        const uint32_t lo_v = vv[k] & 0xffffu, hi_v = vv[k] >> 16;
+        const uint32_t lo_b = bb[q] & 0xffffu, hi_b = bb[q] >> 16;
+        const uint32_t lo_v = vv[q] & 0xffffu, hi_v = vv[q] >> 16;
         const uint32_t lo = bf16_to_f32(static_cast<uint16_t>(lo_v)) > bf16_to_f32(static_cast<uint16_t>(lo_b)) ? lo_v : lo_b;
         const uint32_t hi = bf16_to_f32(static_cast<uint16_t>(hi_v)) > bf16_to_f32(static_cast<uint16_t>(hi_b)) ? hi_v : hi_b;
-        bb[k] = lo | (hi << 16);
+        bb[q] = lo | (hi << 16);
       }
     }
     out[g] = best;
@@ -194,13 +247,12 @@ __device__ __forceinline__ float ld_f(const float* p) { return *p; }
 __device__ __forceinline__ float ld_f(const uint16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float ld_f(const _Float16* p) { return static_cast<float>(*p); }
 
-// Channel-wise maximum over each parent's run of sites.  Thread per (parent, channel);
-// parents past the count (read on the device) do nothing.
+// Channel-wise maximum over each parent's sites (its child slots, in slot order).  Thread per
+// (parent, channel); parents past the count (read on the device) do nothing.
 template <typename T>
 __global__ void k_maxpool(const T* __restrict__ feats, int32_t channels,
-                          const uint32_t* __restrict__ sorted_sites,
-                          const int32_t* __restrict__ heads, const int64_t* __restrict__ result,
-                          int64_t n, T* __restrict__ out) {
+                          const int32_t* __restrict__ children,
+                          const int64_t* __restrict__ result, T* __restrict__ out) {
   const int64_t m = result[0];
   const int64_t total = m * channels;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -208,16 +260,21 @@ __global__ void k_maxpool(const T* __restrict__ feats, int32_t channels,
        g += stride) {
     const int64_t p = g / channels;
     const int c = static_cast<int>(g - p * channels);
-    const int64_t r0 = heads[p];
-    const int64_t r1 = p + 1 < m ? heads[p + 1] : n;
-    int64_t best_row = sorted_sites[r0];
+    const int32_t* ch = children + p * 8;
+    int k0 = 0;
+    while (k0 < 7 && ch[k0] < 0) ++k0;  // every parent has at least one site
+    if (ch[k0] < 0) {
+      out[g] = T{};
+      continue;
+    }
+    int64_t best_row = ch[k0];
     float best = ld_f(feats + best_row * channels + c);
-    for (int64_t r = r0 + 1; r < r1; ++r) {
-      const int64_t row = sorted_sites[r];
-      const float v = ld_f(feats + row * channels + c);
+    for (int k = k0 + 1; k < 8; ++k) {
+      if (ch[k] < 0) continue;
+      const float v = ld_f(feats + static_cast<int64_t>(ch[k]) * channels + c);
       if (v > best) {
         best = v;
-        best_row = row;
+        best_row = ch[k];
       }
     }
     out[g] = feats[best_row * channels + c];  // the maximum's own bits
@@ -229,11 +286,8 @@ __global__ void k_maxpool(const T* __restrict__ feats, int32_t channels,
 // Thread per (parent, channel); the element type only moves bits.
 template <typename T>
 __global__ void k_space2channel(const T* __restrict__ feats, int32_t channels,
-                                const int4* __restrict__ coords,
-                                const uint32_t* __restrict__ sorted_sites,
-                                const int32_t* __restrict__ heads,
-                                const int64_t* __restrict__ result, int64_t n,
-                                T* __restrict__ out) {
+                                const int32_t* __restrict__ children,
+                                const int64_t* __restrict__ result, T* __restrict__ out) {
   const int64_t m = result[0];
   const int64_t total = m * channels;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -241,22 +295,11 @@ __global__ void k_space2channel(const T* __restrict__ feats, int32_t channels,
        g += stride) {
     const int64_t p = g / channels;
     const int c = static_cast<int>(g - p * channels);
-    const int64_t r0 = heads[p];
-    const int64_t r1 = p + 1 < m ? heads[p + 1] : n;
-    T v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = T{};
-    for (int64_t r = r0; r < r1; ++r) {
-      const int64_t i = sorted_sites[r];
-      const int4 q = coords[i];
-      const int k = ((q.y & 1) << 2) | ((q.z & 1) << 1) | (q.w & 1);
-      const T x = feats[i * channels + c];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)  // a select per slot keeps v in registers
-        if (j == k) v[j] = x;
+    for (int k = 0; k < 8; ++k) {
+      const int32_t i = children[p * 8 + k];
+      out[g * 8 + k] = i >= 0 ? feats[static_cast<int64_t>(i) * channels + c] : T{};
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) out[g * 8 + k] = v[k];
   }
 }
 
@@ -274,11 +317,9 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
 template <int ESZ>
 __global__ __launch_bounds__(256) void k_space2channel_w(const uint4* __restrict__ feats,
                                                          int32_t words,
-                                                         const int4* __restrict__ coords,
-                                                         const uint32_t* __restrict__ sorted_sites,
-                                                         const int32_t* __restrict__ heads,
+                                                         const int32_t* __restrict__ children,
                                                          const int64_t* __restrict__ result,
-                                                         int64_t n, uint4* __restrict__ out) {
+                                                         uint4* __restrict__ out) {
   __shared__ uint4 stage[256 * 8];
   const int t = threadIdx.x;
   const int64_t m = result[0];
@@ -292,19 +333,11 @@ __global__ __launch_bounds__(256) void k_space2channel_w(const uint4* __restrict
     if (g < total) {
       const int64_t p = g / words;
       const int w = static_cast<int>(g - p * words);
-      const int64_t r0 = heads[p];
-      const int64_t r1 = p + 1 < m ? heads[p + 1] : n;
       uint4 v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = make_uint4(0u, 0u, 0u, 0u);
-      for (int64_t r = r0; r < r1; ++r) {
-        const int64_t i = sorted_sites[r];
-        const int4 q = coords[i];
-        const int k = ((q.y & 1) << 2) | ((q.z & 1) << 1) | (q.w & 1);
-        const uint4 x = feats[i * words + w];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j == k) v[j] = x;
+      for (int k = 0; k < 8; ++k) {
+        const int32_t i = children[p * 8 + k];
+        v[k] = i >= 0 ? feats[static_cast<int64_t>(i) * words + w] : make_uint4(0u, 0u, 0u, 0u);
       }
       if constexpr (ESZ == 2) {
 #pragma unroll
@@ -404,13 +437,15 @@ namespace ssc {
 namespace {
 
 // Shared front of the downsample and the spatial-to-channel: checks, then numbers the
-// parents.  On success *vals / *heads point at the sorted sites and at each parent's first
-// sorted position.  Returns SSC_OK with *done = true when there is nothing left to launch.
+// parents (dense rank structure when the parent grid's bitmap fits the numbering's scratch,
+// else the radix sort); both fill parent, out_coords, result and the child slots.  On success
+// *children points at the slots.  Returns SSC_OK with *done = true when there is nothing left
+// to launch.
 ssc_status number_parents(const int32_t* coords, int64_t n, int32_t batch, const int32_t* grid,
                           const void* feats, int32_t dtype, int32_t channels, int32_t* out_coords,
                           void* out_feats, int32_t* parent, int64_t* result, void* workspace,
-                          size_t workspace_bytes, hipStream_t s, const uint32_t** vals_out,
-                          const int32_t** heads_out, bool* done) {
+                          size_t workspace_bytes, hipStream_t s, const int32_t** children_out,
+                          bool* done) {
   *done = true;
   if (n < 0 || grid == nullptr || result == nullptr || channels < 0) return SSC_ERR_ARG;
   if (dtype != SSC_F32 && dtype != SSC_BF16 && dtype != SSC_F16) return SSC_ERR_ARG;
@@ -433,27 +468,38 @@ ssc_status number_parents(const int32_t* coords, int64_t n, int32_t batch, const
   }
   const uint64_t hx = (grid[0] + 1) / 2, hy = (grid[1] + 1) / 2, hz = (grid[2] + 1) / 2;
   char* ws = static_cast<char*>(workspace);
-  auto* keys = reinterpret_cast<uint64_t*>(ws + L.sort.off_keys_a);
-  auto* vals = reinterpret_cast<uint32_t*>(ws + L.sort.off_vals_a);
-  auto* totals = reinterpret_cast<uint32_t*>(ws + L.sort.off_totals);
-  auto* tile_sums = reinterpret_cast<uint32_t*>(ws + L.off_tile_sums);
-  auto* heads = reinterpret_cast<int32_t*>(ws + L.off_heads);
+  auto* children = reinterpret_cast<int32_t*>(ws + L.off_children);
   auto* bad = reinterpret_cast<uint32_t*>(ws + L.off_counter);
-  k_fill_u32<<<1, 64, 0, s>>>(bad, 1, 0u);
-  k_parent_keys<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
-      reinterpret_cast<const int4*>(coords), n, batch, grid[0], grid[1], grid[2], hx, hy, hz,
-      keys, vals, totals, bad);
-  const int bits = bits_for(static_cast<uint64_t>(batch) * hx * hy * hz);
-  if (radix_sort_pairs<uint64_t, 9>(ws, L.sort, n, bits, s) == 1) {
-    keys = reinterpret_cast<uint64_t*>(ws + L.sort.off_keys_b);
-    vals = reinterpret_cast<uint32_t*>(ws + L.sort.off_vals_b);
+  const int4* c4 = reinterpret_cast<const int4*>(coords);
+  int4* oc = reinterpret_cast<int4*>(out_coords);
+  const uint64_t cells = dense_voxels(batch, grid, 1);
+  if (down_dense_fits(n, cells)) {
+    const DenseBits D = down_dense(cells);
+    dense_build(c4, n, batch, grid, 1, D, ws, bad, 0, result, s, children, 8 * n);
+    k_ds_assign<<<grid_for(n), 256, 0, s>>>(
+        c4, n, batch, grid[0], grid[1], grid[2], static_cast<int>(hx), static_cast<int>(hy),
+        static_cast<int>(hz), reinterpret_cast<const uint64_t*>(ws + D.off_bits),
+        reinterpret_cast<const uint16_t*>(ws + D.off_local),
+        reinterpret_cast<const uint32_t*>(ws + D.off_super), parent, oc, children);
+  } else {
+    auto* keys = reinterpret_cast<uint64_t*>(ws + L.sort.off_keys_a);
+    auto* vals = reinterpret_cast<uint32_t*>(ws + L.sort.off_vals_a);
+    auto* totals = reinterpret_cast<uint32_t*>(ws + L.sort.off_totals);
+    auto* tile_sums = reinterpret_cast<uint32_t*>(ws + L.off_tile_sums);
+    k_fill_u32<<<1, 64, 0, s>>>(bad, 1, 0u);
+    k_parent_keys<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+        c4, n, batch, grid[0], grid[1], grid[2], hx, hy, hz, keys, vals, totals, bad, children);
+    const int bits = bits_for(static_cast<uint64_t>(batch) * hx * hy * hz);
+    if (radix_sort_pairs<uint64_t, 9>(ws, L.sort, n, bits, s) == 1) {
+      keys = reinterpret_cast<uint64_t*>(ws + L.sort.off_keys_b);
+      vals = reinterpret_cast<uint32_t*>(ws + L.sort.off_vals_b);
+    }
+    k_head_counts<<<static_cast<unsigned>(L.scan_tiles), 256, 0, s>>>(keys, n, tile_sums);
+    k_scan_tile_sums<<<1, 256, 0, s>>>(tile_sums, L.scan_tiles, result, bad);
+    k_assign_parents<<<static_cast<unsigned>(L.scan_tiles), 256, 0, s>>>(
+        keys, vals, n, tile_sums, hx, hy, hz, c4, parent, oc, children);
   }
-  k_head_counts<<<static_cast<unsigned>(L.scan_tiles), 256, 0, s>>>(keys, n, tile_sums);
-  k_scan_tile_sums<<<1, 256, 0, s>>>(tile_sums, L.scan_tiles, result, bad);
-  k_assign_parents<<<static_cast<unsigned>(L.scan_tiles), 256, 0, s>>>(
-      keys, vals, n, tile_sums, hx, hy, hz, parent, reinterpret_cast<int4*>(out_coords), heads);
-  *vals_out = vals;
-  *heads_out = heads;
+  *children_out = children;
   *done = channels == 0;
   return launch_status();
 }
@@ -467,27 +513,26 @@ extern "C" ssc_status ssc_downsample2(const int32_t* coords, int64_t n, int32_t 
                                       int32_t* parent, int64_t* result, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   hipStream_t s = as_stream(stream);
-  const uint32_t* vals = nullptr;
-  const int32_t* heads = nullptr;
+  const int32_t* ch = nullptr;
   bool done = true;
   const ssc_status st = number_parents(coords, n, batch, grid, feats, dtype, channels, out_coords,
                                        out_feats, parent, result, workspace, workspace_bytes, s,
-                                       &vals, &heads, &done);
+                                       &ch, &done);
   if (st != SSC_OK || done) return st;
   const unsigned g = grid_for(n * channels);
   if (dtype == SSC_BF16 && channels % 8 == 0 && aligned(feats, 16) && aligned(out_feats, 16))
     k_maxpool_bf16x8<<<grid_for(n * (channels / 8)), 256, 0, s>>>(
-        static_cast<const uint4*>(feats), channels / 8, vals, heads, result, n,
+        static_cast<const uint4*>(feats), channels / 8, ch, result,
         static_cast<uint4*>(out_feats));
   else if (dtype == SSC_BF16)
-    k_maxpool<uint16_t><<<g, 256, 0, s>>>(static_cast<const uint16_t*>(feats), channels, vals,
-                                          heads, result, n, static_cast<uint16_t*>(out_feats));
+    k_maxpool<uint16_t><<<g, 256, 0, s>>>(static_cast<const uint16_t*>(feats), channels, ch,
+                                          result, static_cast<uint16_t*>(out_feats));
   else if (dtype == SSC_F16)
-    k_maxpool<_Float16><<<g, 256, 0, s>>>(static_cast<const _Float16*>(feats), channels, vals,
-                                          heads, result, n, static_cast<_Float16*>(out_feats));
+    k_maxpool<_Float16><<<g, 256, 0, s>>>(static_cast<const _Float16*>(feats), channels, ch,
+                                          result, static_cast<_Float16*>(out_feats));
   else
-    k_maxpool<float><<<g, 256, 0, s>>>(static_cast<const float*>(feats), channels, vals, heads,
-                                       result, n, static_cast<float*>(out_feats));
+    k_maxpool<float><<<g, 256, 0, s>>>(static_cast<const float*>(feats), channels, ch, result,
+                                       static_cast<float*>(out_feats));
   return launch_status();
 }
 
@@ -499,14 +544,12 @@ extern "C" ssc_status ssc_spatial2channel2(const int32_t* coords, int64_t n, int
                                            void* stream) {
   if (channels < 1) return SSC_ERR_ARG;
   hipStream_t s = as_stream(stream);
-  const uint32_t* vals = nullptr;
-  const int32_t* heads = nullptr;
+  const int32_t* ch = nullptr;
   bool done = true;
   const ssc_status st = number_parents(coords, n, batch, grid, feats, dtype, channels, out_coords,
                                        out_feats, parent, result, workspace, workspace_bytes, s,
-                                       &vals, &heads, &done);
+                                       &ch, &done);
   if (st != SSC_OK || done) return st;
-  const int4* c4 = reinterpret_cast<const int4*>(coords);
   const int64_t row_bytes = static_cast<int64_t>(channels) * (dtype == SSC_F32 ? 4 : 2);
   if (row_bytes % 16 == 0 && aligned(feats, 16) && aligned(out_feats, 16)) {
     const int32_t words = static_cast<int32_t>(row_bytes / 16);
@@ -514,19 +557,18 @@ extern "C" ssc_status ssc_spatial2channel2(const int32_t* coords, int64_t n, int
     const auto* f4 = static_cast<const uint4*>(feats);
     auto* o4 = static_cast<uint4*>(out_feats);
     if (dtype == SSC_F32)
-      k_space2channel_w<4><<<gw, 256, 0, s>>>(f4, words, c4, vals, heads, result, n, o4);
+      k_space2channel_w<4><<<gw, 256, 0, s>>>(f4, words, ch, result, o4);
     else
-      k_space2channel_w<2><<<gw, 256, 0, s>>>(f4, words, c4, vals, heads, result, n, o4);
+      k_space2channel_w<2><<<gw, 256, 0, s>>>(f4, words, ch, result, o4);
     return launch_status();
   }
   const unsigned g = grid_for(n * channels);
   if (dtype == SSC_F32)
-    k_space2channel<float><<<g, 256, 0, s>>>(static_cast<const float*>(feats), channels, c4, vals,
-                                             heads, result, n, static_cast<float*>(out_feats));
+    k_space2channel<float><<<g, 256, 0, s>>>(static_cast<const float*>(feats), channels, ch,
+                                             result, static_cast<float*>(out_feats));
   else
     k_space2channel<uint16_t><<<g, 256, 0, s>>>(static_cast<const uint16_t*>(feats), channels,
-                                                c4, vals, heads, result, n,
-                                                static_cast<uint16_t*>(out_feats));
+                                                ch, result, static_cast<uint16_t*>(out_feats));
   return launch_status();
 }
 
