@@ -380,9 +380,8 @@ def time_convnext(ssc, torch, x, plan, dev, reps: int = 50) -> dict:
     h = torch.empty_like(x)
     m = torch.empty((n, 4 * c), dtype=bf, device=dev)
     y = torch.empty_like(x)
-    ws = torch.empty(max(lib.ssc_conv_workspace_bytes(c, 4 * c, ssc.SSC_BF16),
-                         lib.ssc_conv_workspace_bytes(4 * c, c, ssc.SSC_BF16)),
-                     dtype=torch.uint8, device=dev)
+    # k=1 weights re-laid out once, like the k=3 ones
+    pw1, pw2 = ssc.pack_weights(w1), ssc.pack_weights(w2)
     p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     BF = ssc.SSC_BF16
@@ -396,12 +395,12 @@ def time_convnext(ssc, torch, x, plan, dev, reps: int = 50) -> dict:
         lib.ssc_layer_norm(p(h), BF, n, c, p(g), p(be), 1e-6, 0, p(h), st)
 
     def lin1():
-        lib.ssc_linear_ex(p(h), BF, p(w1), p(b1), n, c, 4 * c, p(m), BF, ctypes.byref(e1), p(ws),
-                          ws.numel(), st)
+        lib.ssc_linear_packed_ex(p(h), p(pw1.buf), p(b1), n, c, 4 * c, p(m), BF,
+                                 ctypes.byref(e1), st)
 
     def lin2():
-        lib.ssc_linear_ex(p(m), BF, p(w2), p(b2), n, 4 * c, c, p(y), BF, ctypes.byref(e2), p(ws),
-                          ws.numel(), st)
+        lib.ssc_linear_packed_ex(p(m), p(pw2.buf), p(b2), n, 4 * c, c, p(y), BF,
+                                 ctypes.byref(e2), st)
 
     def block():
         conv()
@@ -680,6 +679,8 @@ def main():
     if two:
         l2 = w.layers[1]
         w2, b2 = l2.weight.to(dev), l2.bias.to(dev)
+        if w2.dtype == torch.bfloat16:
+            w2 = ssc.pack_weights(w2)  # the k=1 layer's weights, re-laid out once as well
         y2 = torch.empty((w.n, l2.cout), dtype=odt, device=dev)
 
     def conv():

@@ -236,13 +236,17 @@ ssc_status ssc_subm_conv3d_plan_static(const void* feats, int32_t in_dtype, cons
                                        void* stream);
 
 /* Weights re-laid out once for the matrix cores, for callers that keep a layer's weights
- * (the same re-layout ssc_subm_conv3d_plan performs into its workspace on every call).
- *   weight  [27, cin, cout] bf16.
- *   packed  >= ssc_packed_weight_bytes(27, cin, cout) bytes, 256-byte aligned; receives the
- *           weights in the k=3 kernel's fragment order (an opaque layout of the same bytes
- *           count, valid only for ssc_subm_conv3d_packed with the same cin and cout).
- * Only taps = 27 and bf16 with cin in {32, 64, 128}, cout in {16, 32, 64, 128} (the shapes
- * the matrix-core kernels are built for); otherwise SSC_ERR_UNSUPPORTED. */
+ * (the same re-layout ssc_subm_conv3d_plan and ssc_linear perform into their workspace on
+ * every call).
+ *   weight  [taps, cin, cout] bf16: taps = 27 (k=3) or 1 (k=1).
+ *   packed  >= ssc_packed_weight_bytes(taps, cin, cout) bytes, 256-byte aligned; receives
+ *           the weights in the kernel's fragment order (an opaque layout of the same byte
+ *           count, valid only for ssc_subm_conv3d_packed (taps = 27) or ssc_linear_packed
+ *           (taps = 1) with the same cin and cout).
+ * taps = 27: cin in {32, 64, 128}, cout in {16, 32, 64, 128} (the shapes the k=3
+ * matrix-core kernels are built for).  taps = 1: the shapes ssc_linear runs on the matrix
+ * cores (cin, cout in {32, 64, 128}, or multiples of 64 up to 1024).  Otherwise
+ * SSC_ERR_UNSUPPORTED. */
 size_t ssc_packed_weight_bytes(int32_t taps, int32_t cin, int32_t cout);
 ssc_status ssc_pack_weights(const void* weight, int32_t taps, int32_t cin, int32_t cout,
                             void* packed, size_t packed_bytes, void* stream);
@@ -271,6 +275,14 @@ ssc_status ssc_subm_conv3d_packed(const void* feats, const void* packed_weight,
 ssc_status ssc_linear(const void* feats, int32_t in_dtype, const void* weight, const float* bias,
                       int64_t n, int32_t cin, int32_t cout, void* out, int32_t out_dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ssc_linear with weights from ssc_pack_weights (taps = 1): one kernel launch, no
+ * workspace.  Same results, bit for bit, as ssc_linear on the unpacked weights.  bf16 feats,
+ * out_dtype SSC_F32 or SSC_BF16; shapes as ssc_pack_weights accepts for taps = 1 (else
+ * SSC_ERR_UNSUPPORTED). */
+ssc_status ssc_linear_packed(const void* feats, const void* packed_weight, const float* bias,
+                             int64_t n, int32_t cin, int32_t cout, void* out, int32_t out_dtype,
+                             void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Epilogues and the sparse group norm of the blocks around the convolution.
@@ -319,8 +331,8 @@ typedef struct ssc_epilogue {
   size_t gn_partials_bytes;
 } ssc_epilogue;
 
-/* ssc_subm_conv3d_plan, ssc_subm_conv3d_packed and ssc_linear with an epilogue (NULL = none);
- * other arguments, shapes and errors as there.  Bad epilogue fields return SSC_ERR_ARG, a
+/* ssc_subm_conv3d_plan, ssc_subm_conv3d_packed, ssc_linear and ssc_linear_packed with an
+ * epilogue (NULL = none); other arguments, shapes and errors as there.  Bad epilogue fields return SSC_ERR_ARG, a
  * short gn_partials buffer SSC_ERR_WORKSPACE. */
 ssc_status ssc_subm_conv3d_plan_ex(const void* feats, int32_t in_dtype, const void* weight,
                                    const float* bias, const void* plan, int64_t n,
@@ -335,6 +347,9 @@ ssc_status ssc_linear_ex(const void* feats, int32_t in_dtype, const void* weight
                          const float* bias, int64_t n, int32_t cin, int32_t cout, void* out,
                          int32_t out_dtype, const ssc_epilogue* epilogue, void* workspace,
                          size_t workspace_bytes, void* stream);
+ssc_status ssc_linear_packed_ex(const void* feats, const void* packed_weight, const float* bias,
+                                int64_t n, int32_t cin, int32_t cout, void* out,
+                                int32_t out_dtype, const ssc_epilogue* epilogue, void* stream);
 
 /* Bytes of the group-norm partial sums for n sites: one slot per 128 rows of n rounded up
  * to a multiple of 256, each slot holding float4 (count, sum, sum of squares, 0) per

@@ -119,6 +119,8 @@ def load_library():
                                     ctypes.c_int),
         "ssc_subm_conv3d_packed_ex": ([p, p, p, p, i64, i32, i32, p, i32, p, p], ctypes.c_int),
         "ssc_linear_ex": ([p, i32, p, p, i64, i32, i32, p, i32, p, p, sz, p], ctypes.c_int),
+        "ssc_linear_packed": ([p, p, p, i64, i32, i32, p, i32, p], ctypes.c_int),
+        "ssc_linear_packed_ex": ([p, p, p, i64, i32, i32, p, i32, p, p], ctypes.c_int),
         "ssc_gn_partials_bytes": ([i64, i32, i32], sz),
         "ssc_gn_partials": ([p, i32, i64, i32, p, i32, i32, p, sz, p], ctypes.c_int),
         "ssc_gn_finalize": ([p, i64, i32, i32, ctypes.c_float, p, p], ctypes.c_int),
@@ -383,13 +385,16 @@ def subm_conv3d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tens
     return out
 
 
-def linear(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+def linear(x: torch.Tensor, weight, bias: Optional[torch.Tensor],
            out_dtype: Optional[torch.dtype] = None,
            out: Optional[torch.Tensor] = None, act: str = "none",
            residual: Optional[torch.Tensor] = None,
            gn: Optional[GroupNormPartials] = None) -> torch.Tensor:
     """k=1 SubMConv3d = per-voxel linear map x @ weight + bias (weight [Cin, Cout] or
-    [1, Cin, Cout]); the same epilogue as subm_conv3d."""
+    [1, Cin, Cout], or a single-tap PackedWeight from pack_weights); the same epilogue as
+    subm_conv3d."""
+    if isinstance(weight, PackedWeight):
+        return _linear_packed(x, weight, bias, out_dtype, out, act, residual, gn)
     n, cin, cout, din, dout, odt = _conv_args(x, weight, bias, 1, out_dtype)
     lib = load_library()
     dev = x.device
@@ -621,8 +626,9 @@ class PackedWeight:
 
 
 def pack_weights(weight: torch.Tensor, flip: bool = False) -> PackedWeight:
-    """Re-lay out [27, Cin, Cout] bf16 weights once for subm_conv3d_packed.  flip=True packs
-    the other kernel orientation (tap at offset d reads site c - d)."""
+    """Re-lay out bf16 weights once: [27, Cin, Cout] for subm_conv3d_packed, [Cin, Cout] or
+    [1, Cin, Cout] for linear.  flip=True packs the other kernel orientation (tap at offset d
+    reads site c - d; nothing changes for a single tap)."""
     _need_cuda(weight, "weight")
     if weight.dtype != torch.bfloat16:
         raise ValueError("pack_weights takes bfloat16 weights")
@@ -672,6 +678,34 @@ def subm_conv3d_packed(x: torch.Tensor, packed: PackedWeight, bias: Optional[tor
                                                _ptr(plan.buf), n, packed.cin, packed.cout,
                                                _ptr(out), dout, ctypes.byref(epi), _stream(dev))
     _check(st, "ssc_subm_conv3d_packed")
+    return out
+
+
+def _linear_packed(x, packed, bias, out_dtype, out, act, residual, gn):
+    _need_cuda(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != packed.cin or packed.taps != 1:
+        raise ValueError("x must be bfloat16 [N, Cin] matching a single-tap packed weight")
+    n = x.shape[0]
+    if bias is not None:
+        _need_cuda(bias, "bias")
+        if bias.dtype != torch.float32 or bias.numel() != packed.cout:
+            raise ValueError("bias must be float32 [Cout]")
+    odt = torch.float32 if out_dtype is None else out_dtype
+    dout = _dtype_code(odt, "out_dtype")
+    lib = load_library()
+    dev = x.device
+    if out is None:
+        out = torch.empty((n, packed.cout), dtype=odt, device=dev)
+    epi = _epilogue(n, packed.cout, odt, act, residual, gn)
+    with torch.cuda.device(dev):
+        if epi is None:
+            st = lib.ssc_linear_packed(_ptr(x), _ptr(packed.buf), _ptr(bias), n, packed.cin,
+                                       packed.cout, _ptr(out), dout, _stream(dev))
+        else:
+            st = lib.ssc_linear_packed_ex(_ptr(x), _ptr(packed.buf), _ptr(bias), n, packed.cin,
+                                          packed.cout, _ptr(out), dout, ctypes.byref(epi),
+                                          _stream(dev))
+    _check(st, "ssc_linear_packed")
     return out
 
 

@@ -33,6 +33,7 @@ inline ssc_status launch_status() {
 constexpr int64_t kPlanMagic = 0x5353435031LL;  // "SSCP1"
 constexpr int kPlanRowAlign = 256;              // npad is a multiple of this
 constexpr int kBlockRows = 16;                  // rows per MFMA block
+constexpr int kTileRows = 128;                  // rows per tile of the k=3 matrix-core kernel
 constexpr int kPlanSchedWord = 4;               // header word holding the tile schedule
 // Tile schedules of the k=3 matrix-core kernel (which workgroup takes which tile):
 //   interleaved  workgroup b takes tile T-1-b: the hardware deals consecutive workgroups to

@@ -351,10 +351,10 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int wr = wave / WC, wc = wave % WC;
   const uint32_t lds0 = lds_addr(smem);
-  // Which tile this workgroup takes follows the plan's schedule.  Interleaved: the mask order
-  // makes per-tile work grow along the sites (a tile of near-empty masks has a tap or two, the
-  // last tiles a dozen or more), so the heavy end goes first and the workgroups dispatched
-  // last are the short ones.  Per XCD: consecutive workgroups go to the 8 XCDs in turn, and
+  // Which tile this workgroup takes follows the plan's schedule.  Interleaved: the plan puts
+  // the mask order's tiles in ascending cost (a tile of near-empty masks walks a tap or two,
+  // the costliest all 27), so taking them from the last, the heavy tiles go first and the
+  // workgroups dispatched last are the short ones.  Per XCD: consecutive workgroups go to the 8 XCDs in turn, and
   // XCD x takes the x-th contiguous eighth of a spatially ordered plan, in order.  Both
   // candidates' block masks are fetched while the schedule word is read, so choosing costs no
   // extra round trip.
@@ -1024,6 +1024,8 @@ struct LdsPick {
   static constexpr int WC = CO >= 64 ? 4 : CO / 16;
   static constexpr int WR = 4 / WC;
   static constexpr int NB = 8;
+  // The plan orders whole tiles of this many rows by cost.
+  static_assert(NB * 16 == kTileRows, "tile rows of the plan's tile order");
 };
 
 template <int CI, int CO, bool O16, int EK>
@@ -1385,15 +1387,60 @@ extern "C" ssc_status ssc_pack_weights_ex(const void* weight, int32_t taps, int3
                                           size_t packed_bytes, void* stream) {
   if (weight == nullptr || packed == nullptr) return SSC_ERR_ARG;
   if (flags & ~SSC_PACK_FLIP) return SSC_ERR_ARG;
-  if (taps != kTaps) return SSC_ERR_UNSUPPORTED;
   int threads = 0, rows = 0, wcg = 0;
-  if (pick_lds(cin, cout, false, 0, &threads, &rows, &wcg, false) == nullptr)
+  if (taps == kTaps) {
+    if (pick_lds(cin, cout, false, 0, &threads, &rows, &wcg, false) == nullptr)
+      return SSC_ERR_UNSUPPORTED;
+  } else if (taps == 1) {
+    // The k=1 kernels' layouts: the streaming kernel's column groups, else 16-column tiles.
+    if (pick_linear(cin, cout, false, 0, &wcg, &rows, false) == nullptr) {
+      if (!gemm_rows_supported(cin, cout)) return SSC_ERR_UNSUPPORTED;
+      wcg = cout / 16;
+    }
+  } else {
     return SSC_ERR_UNSUPPORTED;
+  }
   if (!aligned(weight, 16) || !aligned(packed, kAlign)) return SSC_ERR_ARG;
   if (packed_bytes < ssc_packed_weight_bytes(taps, cin, cout)) return SSC_ERR_WORKSPACE;
-  launch_pack_frag(weight, kTaps, cin, cout, wcg, (flags & SSC_PACK_FLIP) ? 1 : 0,
+  // A single tap is its own mirror image: the flag changes nothing there.
+  launch_pack_frag(weight, taps, cin, cout, wcg, (taps == kTaps && (flags & SSC_PACK_FLIP)) ? 1 : 0,
                    static_cast<uint16_t*>(packed), as_stream(stream));
   return launch_status();
+}
+
+extern "C" ssc_status ssc_linear_packed(const void* feats, const void* packed_weight,
+                                        const float* bias, int64_t n, int32_t cin, int32_t cout,
+                                        void* out, int32_t out_dtype, void* stream) {
+  return ssc_linear_packed_ex(feats, packed_weight, bias, n, cin, cout, out, out_dtype, nullptr,
+                              stream);
+}
+
+extern "C" ssc_status ssc_linear_packed_ex(const void* feats, const void* packed_weight,
+                                           const float* bias, int64_t n, int32_t cin,
+                                           int32_t cout, void* out, int32_t out_dtype,
+                                           const ssc_epilogue* epilogue, void* stream) {
+  if (n < 0 || !valid_dtype(out_dtype) || packed_weight == nullptr) return SSC_ERR_ARG;
+  if (n >= (int64_t(1) << 31) || out_dtype == SSC_F16) return SSC_ERR_UNSUPPORTED;
+  const bool out16 = out_dtype == SSC_BF16;
+  Epi ep;
+  if (const ssc_status st = check_epilogue(epilogue, n, cout, &ep); st != SSC_OK) return st;
+  const bool use_epi = ep.act != SSC_ACT_NONE || ep.res != nullptr;
+  int wcg = 0, rows = 0;
+  LinFn fn = pick_linear(cin, cout, out16, 0, &wcg, &rows, use_epi);
+  if (fn == nullptr && !gemm_rows_supported(cin, cout)) return SSC_ERR_UNSUPPORTED;
+  if (n > 0 && (feats == nullptr || out == nullptr)) return SSC_ERR_ARG;
+  if (!aligned(packed_weight, 16) || (n > 0 && (!aligned(feats, 16) || !aligned(out, 16))) ||
+      (bias && !aligned(bias, 4)))
+    return SSC_ERR_ARG;
+  hipStream_t s = as_stream(stream);
+  if (n == 0) return gn_after(epilogue, false, out, out_dtype, n, cout, s);
+  const auto* wp = static_cast<const uint16_t*>(packed_weight);
+  if (const ssc_status st =
+          fn ? launch_linear(fn, rows, feats, wp, bias, n, out, ep, s)
+             : gemm_rows_launch(feats, wp, bias, n, cin, cout, out, out16, 0, ep.act, ep.res, s);
+      st != SSC_OK)
+    return st;
+  return gn_after(epilogue, false, out, out_dtype, n, cout, s);
 }
 
 extern "C" ssc_status ssc_subm_conv3d_packed(const void* feats, const void* packed_weight,

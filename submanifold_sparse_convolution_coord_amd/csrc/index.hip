@@ -245,22 +245,51 @@ constexpr int kBrickShift = 7;                   // spatial order: bricks of 128
 constexpr int64_t kMinBricks = 8;                // ... tried when the grid holds this many
 constexpr int kCountSlots = 64;                  // (block, tap) counts: slots of partial sums
 
+// Tile order of the mask order: whole tiles of kTileRows sites are re-sorted by their cost,
+// estimated as kStageCost per tap the tile walks plus one per (16-row block, tap) pair it
+// computes (the k=3 kernel pays a fixed wait, barrier and issue per tap and matrix work per
+// active block; 11 is about their ratio at C = 128).  One workgroup sorts up to kOrderTiles
+// tiles; above that the mask order stays as it is.
+constexpr int kStageCost = 11;
+constexpr int kCostBins = 1024;                  // costs < 27 * (kStageCost + 8) < 1024
+constexpr int64_t kOrderTiles = 32768;
+static_assert(kTaps * (kStageCost + kTileRows / kBlockRows) < kCostBins, "tile cost range");
+
 // The plan's scratch: the mask-order sort (32-bit keys), the brick sort (64-bit keys), each
-// site's tap mask, and the two orders' (block, tap) counts in kCountSlots slots each (one
-// counter took every wave's atomic add and serialised them: 0.46 ms at 1.2M sites).
+// site's tap mask, the two orders' (block, tap) counts in kCountSlots slots each (one
+// counter took every wave's atomic add and serialised them: 0.46 ms at 1.2M sites), and the
+// full tiles' costs and cost order.
 struct PlanWork {
   SortLayout<uint32_t> g;
   SortLayout<uint64_t> b;
-  size_t off_mask, off_count, total;
+  int64_t full_tiles;
+  size_t off_mask, off_count, off_cost, off_tiles, total;
 };
 inline PlanWork plan_work_layout(int64_t n) {
   PlanWork W;
   W.g = sort_layout<uint32_t>(n, 0);
   W.b = sort_layout<uint64_t>(n, W.g.total);
+  W.full_tiles = n > 0 ? n / kTileRows : 0;
   W.off_mask = align_up(W.b.total);
   W.off_count = align_up(W.off_mask + sizeof(uint32_t) * (n > 0 ? n : 1));
-  W.total = align_up(W.off_count + 2 * kCountSlots * sizeof(unsigned long long));
+  W.off_cost = align_up(W.off_count + 2 * kCountSlots * sizeof(unsigned long long));
+  W.off_tiles = align_up(W.off_cost + sizeof(uint32_t) * (W.full_tiles > 0 ? W.full_tiles : 1));
+  W.total = align_up(W.off_tiles + sizeof(int32_t) * (W.full_tiles > 0 ? W.full_tiles : 1));
   return W;
+}
+
+// Whether the brick order replaces the mask order: its (block, tap) count is at most 21/20
+// of the mask order's.  Wave-uniform; every lane of the calling wave must take part.
+__device__ __forceinline__ bool brick_order_wins(const unsigned long long* __restrict__ counts) {
+  static_assert(kCountSlots == 64, "one slot per lane");
+  const int lane = threadIdx.x & 63;
+  unsigned long long g = counts[2 * lane], b = counts[2 * lane + 1];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    g += __shfl_xor(g, off, 64);
+    b += __shfl_xor(b, off, 64);
+  }
+  return b * 20 <= g * 21;
 }
 
 // Sort key of a site: bit (t < 13 ? t : t - 1) set when non-centre tap t has a neighbour.
@@ -384,18 +413,133 @@ __global__ __launch_bounds__(256) void k_block_taps(const uint32_t* __restrict__
   }
 }
 
+// Cost of every full tile of the mask order (nothing when the brick order wins).  A site's
+// mask comes back from its sorted key (the key is the prefix XOR of the mask from the top
+// bit, so mask = key ^ (key >> 1)); the centre tap, present at every site, is bit 26.  Two
+// tiles per workgroup, one per pair of waves.
+__global__ __launch_bounds__(256) void k_tile_cost(const uint32_t* __restrict__ keys,
+                                                   int64_t full_tiles,
+                                                   const unsigned long long* __restrict__ counts,
+                                                   uint32_t* __restrict__ cost) {
+  static_assert(kTileRows == 128, "two tiles per 256-thread workgroup");
+  if (counts != nullptr && brick_order_wins(counts)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint32_t m = 0u;
+  if (p < full_tiles * kTileRows) {
+    const uint32_t k = keys[p];
+    m = (k ^ (k >> 1)) | (1u << (kTaps - 1));
+  }
+#pragma unroll
+  for (int off = 1; off < kBlockRows; off <<= 1) m |= __shfl_xor(m, off, 64);
+  uint32_t active = (lane & (kBlockRows - 1)) == 0 ? __popc(m) : 0u;
+#pragma unroll
+  for (int off = kBlockRows; off < 64; off <<= 1) {
+    active += __shfl_xor(active, off, 64);
+    m |= __shfl_xor(m, off, 64);
+  }
+  __shared__ uint32_t part[4][2];
+  if (lane == 0) {
+    part[wave][0] = active;
+    part[wave][1] = m;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 2 + threadIdx.x;
+    if (t < full_tiles) {
+      const uint32_t a = part[2 * threadIdx.x][0] + part[2 * threadIdx.x + 1][0];
+      const uint32_t u = part[2 * threadIdx.x][1] | part[2 * threadIdx.x + 1][1];
+      cost[t] = kStageCost * __popc(u) + a;
+    }
+  }
+}
+
+// One workgroup: the full tiles in ascending cost, ties in tile order (a stable counting
+// sort) -> order[0, full_tiles).  The k=3 kernel's interleaved schedule walks the tiles from
+// the last, so the costliest start first and the cheapest fill the end.  Ranks among equal
+// costs inside a wave come from intersecting the ballots of the cost bits.
+__global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict__ cost,
+                                                     int64_t full_tiles,
+                                                     const unsigned long long* __restrict__ counts,
+                                                     int32_t* __restrict__ order) {
+  constexpr int kThreads = 1024, kWaves = kThreads / 64, kBits = 10;
+  static_assert((1 << kBits) == kCostBins && kCostBins == kThreads, "one bin per thread");
+  if (counts != nullptr && brick_order_wins(counts)) return;
+  __shared__ uint16_t c[kOrderTiles];
+  __shared__ uint32_t running[kCostBins];
+  __shared__ uint16_t wcnt[kWaves][kCostBins];
+  __shared__ uint32_t wsum[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int f = static_cast<int>(full_tiles);  // <= kOrderTiles
+  running[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < f; i += kThreads) {
+    const uint32_t v = cost[i];
+    c[i] = static_cast<uint16_t>(v);
+    atomicAdd(&running[v], 1u);
+  }
+  __syncthreads();
+  // Exclusive scan of the bin counts: bin b starts after every cheaper tile.
+  const uint32_t cnt = running[tid];
+  uint32_t incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int k = 0; k < wave; ++k) before += wsum[k];
+  running[tid] = before + incl - cnt;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int base = 0; base < f; base += kThreads) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) wcnt[w][tid] = 0;
+    __syncthreads();
+    const int i = base + tid;
+    const bool valid = i < f;
+    const uint32_t d = valid ? c[i] : 0u;
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kBits; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const unsigned long long bb = __ballot(bit);
+      peers &= bit ? bb : ~bb;
+    }
+    const uint32_t rank = __popcll(peers & lt);
+    if (valid && rank == 0) wcnt[wave][d] = static_cast<uint16_t>(__popcll(peers));
+    __syncthreads();
+    if (valid) {
+      uint32_t pos = running[d] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][d];
+      order[pos] = i;
+    }
+    __syncthreads();
+    uint32_t add = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) add += wcnt[w][tid];
+    running[tid] += add;
+    __syncthreads();
+  }
+}
+
 // perm, per-block tap masks and tap-major neighbour rows in sorted order.  A workgroup owns
 // 256 sorted positions: it reads their 256 map rows cooperatively (consecutive lanes read
 // consecutive entries of a row, so a wave touches a few 108-byte rows instead of 64 scattered
 // words), stages them in LDS, then writes each tap's 256 entries as one coalesced run.  Each
 // 16-lane group of a wave is one block for the tap masks.  With counts non-null the brick
 // order (brick_rows) replaces the mask order when its (block, tap) count is at most 21/20 of
-// the mask order's, and the header records the matching tile schedule.
+// the mask order's, and the header records the matching tile schedule.  With tile_order
+// non-null the mask order's full tiles are taken in that order (the tiles holding padding
+// stay last).
 __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ nbr, int64_t n,
                                                    const uint32_t* __restrict__ mask_rows,
                                                    const uint32_t* __restrict__ brick_rows,
                                                    const unsigned long long* __restrict__ counts,
-                                                   int64_t npad, int64_t* __restrict__ header,
+                                                   const int32_t* __restrict__ tile_order,
+                                                   int64_t full_tiles, int64_t npad,
+                                                   int64_t* __restrict__ header,
                                                    int32_t* __restrict__ perm,
                                                    uint32_t* __restrict__ bmask,
                                                    int32_t* __restrict__ gidx) {
@@ -403,20 +547,16 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ n
                                          // wave's column reads hit distinct banks
   __shared__ int32_t src[256];
   const int tid = threadIdx.x;
-  __shared__ unsigned long long total[2];
-  if (counts != nullptr && tid < 2) {
-    unsigned long long t = 0;
-    for (int k = 0; k < kCountSlots; ++k) t += counts[2 * k + tid];
-    total[tid] = t;
-  }
-  __syncthreads();
-  const bool spatial = counts != nullptr && total[1] * 20 <= total[0] * 21;
+  const bool spatial = counts != nullptr && brick_order_wins(counts);
   const uint32_t* sorted_rows = spatial ? brick_rows : mask_rows;
   if (blockIdx.x == 0 && tid == 0)
     header[kPlanSchedWord] = spatial ? kSchedPerXcd : kSchedInterleaved;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 256;
   const int64_t r = r0 + tid;  // < npad
-  const int32_t i = r < n ? static_cast<int32_t>(sorted_rows[r]) : -1;
+  int64_t from = r;
+  if (!spatial && tile_order != nullptr && r < full_tiles * kTileRows)
+    from = static_cast<int64_t>(tile_order[r / kTileRows]) * kTileRows + r % kTileRows;
+  const int32_t i = from < n ? static_cast<int32_t>(sorted_rows[from]) : -1;
   perm[r] = i;
   src[tid] = i;
   __syncthreads();
@@ -611,6 +751,8 @@ extern "C" ssc_status ssc_build_plan(const int32_t* nbr, const int32_t* coords, 
                                    reinterpret_cast<uint4*>(pb + P.off_zero));
   uint32_t* mask_rows = reinterpret_cast<uint32_t*>(ws + W.g.off_vals_a);
   uint32_t* brick_rows = nullptr;
+  const uint32_t* sorted_keys = nullptr;
+  int32_t* tile_order = nullptr;
   if (n > 0) {
     const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
     k_mask_keys<<<blocks, 256, 0, s>>>(nbr, n, reinterpret_cast<uint32_t*>(ws + W.g.off_keys_a),
@@ -618,8 +760,9 @@ extern "C" ssc_status ssc_build_plan(const int32_t* nbr, const int32_t* coords, 
                                        try_bricks ? masks : nullptr, counts,
                                        reinterpret_cast<int64_t*>(pb), P.npad, P.nblocks,
                                        reinterpret_cast<uint4*>(pb + P.off_zero));
-    if (radix_sort_pairs<uint32_t, 9>(ws, W.g, n, kKeyBits, s) == 1)
-      mask_rows = reinterpret_cast<uint32_t*>(ws + W.g.off_vals_b);
+    const bool keys_b = radix_sort_pairs<uint32_t, 9>(ws, W.g, n, kKeyBits, s) == 1;
+    if (keys_b) mask_rows = reinterpret_cast<uint32_t*>(ws + W.g.off_vals_b);
+    sorted_keys = reinterpret_cast<const uint32_t*>(ws + (keys_b ? W.g.off_keys_b : W.g.off_keys_a));
     if (try_bricks) {
       // Stable sort of the mask order by brick: within a brick the mask order remains.
       brick_rows = reinterpret_cast<uint32_t*>(ws + W.b.off_vals_a);
@@ -631,9 +774,20 @@ extern "C" ssc_status ssc_build_plan(const int32_t* nbr, const int32_t* coords, 
         brick_rows = reinterpret_cast<uint32_t*>(ws + W.b.off_vals_b);
       k_block_taps<<<blocks, 256, 0, s>>>(mask_rows, brick_rows, masks, n, counts);
     }
+    // Full tiles of the mask order by cost (both kernels return at once if the brick order
+    // wins).
+    if (W.full_tiles > 1 && W.full_tiles <= kOrderTiles) {
+      auto* cost = reinterpret_cast<uint32_t*>(ws + W.off_cost);
+      tile_order = reinterpret_cast<int32_t*>(ws + W.off_tiles);
+      k_tile_cost<<<static_cast<unsigned>((W.full_tiles + 1) / 2), 256, 0, s>>>(
+          sorted_keys, W.full_tiles, try_bricks ? counts : nullptr, cost);
+      k_tile_order<<<1, 1024, 0, s>>>(cost, W.full_tiles, try_bricks ? counts : nullptr,
+                                      tile_order);
+    }
   }
   k_plan_fill<<<static_cast<unsigned>(P.npad / 256), 256, 0, s>>>(
-      nbr, n, mask_rows, brick_rows, try_bricks ? counts : nullptr, P.npad,
+      nbr, n, mask_rows, brick_rows, try_bricks ? counts : nullptr, tile_order, W.full_tiles,
+      P.npad,
       reinterpret_cast<int64_t*>(pb), reinterpret_cast<int32_t*>(pb + P.off_perm),
       reinterpret_cast<uint32_t*>(pb + P.off_bmask), reinterpret_cast<int32_t*>(pb + P.off_gidx));
   return launch_status();

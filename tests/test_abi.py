@@ -210,10 +210,23 @@ def test_pack_weights_argument_errors(lib):
     assert f(FAKE, 27, 128, 128, 0, None, big, None) == ssc.SSC_ERR_ARG
     assert f(None, 27, 128, 128, 0, FAKE, big, None) == ssc.SSC_ERR_ARG
     assert f(FAKE, 27, 128, 128, 4, FAKE, big, None) == ssc.SSC_ERR_ARG        # unknown flag
-    assert f(FAKE, 1, 128, 128, 0, FAKE, big, None) == ssc.SSC_ERR_UNSUPPORTED  # k=3 only
+    assert f(FAKE, 2, 128, 128, 0, FAKE, big, None) == ssc.SSC_ERR_UNSUPPORTED  # 27 or 1 taps
+    assert f(FAKE, 1, 48, 48, 0, FAKE, big, None) == ssc.SSC_ERR_UNSUPPORTED    # no k=1 kernel
+    assert f(FAKE, 1, 128, 128, 0, FAKE, 100, None) == ssc.SSC_ERR_WORKSPACE
+    assert f(FAKE, 1, 128, 512, 0, ctypes.c_void_p((1 << 20) + 16), big,
+             None) == ssc.SSC_ERR_ARG                                               # misaligned
     assert f(FAKE, 27, 48, 128, 0, FAKE, big, None) == ssc.SSC_ERR_UNSUPPORTED  # no MFMA shape
     assert f(FAKE, 27, 128, 128, 1, FAKE, 100, None) == ssc.SSC_ERR_WORKSPACE
     assert lib.ssc_packed_weight_bytes(27, 128, 128) >= 27 * 128 * 128 * 2
+    h = lib.ssc_linear_packed
+    assert h(FAKE, FAKE, None, 0, 128, 128, FAKE, ssc.SSC_F32, None) == ssc.SSC_OK
+    assert h(FAKE, FAKE, None, 10, 48, 48, FAKE, ssc.SSC_F32, None) == ssc.SSC_ERR_UNSUPPORTED
+    assert h(FAKE, FAKE, None, 10, 128, 128, FAKE, ssc.SSC_F16, None) == ssc.SSC_ERR_UNSUPPORTED
+    assert h(FAKE, None, None, 10, 128, 128, FAKE, ssc.SSC_F32, None) == ssc.SSC_ERR_ARG
+    assert h(None, FAKE, None, 10, 128, 128, FAKE, ssc.SSC_F32, None) == ssc.SSC_ERR_ARG
+    assert h(FAKE, FAKE, None, -1, 128, 128, FAKE, ssc.SSC_F32, None) == ssc.SSC_ERR_ARG
+    assert h(FAKE, FAKE, None, 10, 128, 128, ctypes.c_void_p((1 << 20) + 4), ssc.SSC_F32,
+             None) == ssc.SSC_ERR_ARG
     g = lib.ssc_subm_conv3d_packed
     assert g(FAKE, FAKE, None, FAKE, 0, 128, 128, FAKE, ssc.SSC_F32, None) == ssc.SSC_OK
     assert g(FAKE, FAKE, None, FAKE, 10, 48, 128, FAKE, ssc.SSC_F32, None) == ssc.SSC_ERR_UNSUPPORTED
@@ -309,6 +322,9 @@ def test_epilogue_and_group_norm_argument_errors(lib):
     pk = lib.ssc_subm_conv3d_packed_ex(FAKE, FAKE, None, FAKE, 10, 128, 128, FAKE, ssc.SSC_F32,
                                        ctypes.byref(E(act=9)), None)
     assert pk == ssc.SSC_ERR_ARG
+    lp = lib.ssc_linear_packed_ex(FAKE, FAKE, None, 10, 128, 128, FAKE, ssc.SSC_F32,
+                                  ctypes.byref(E(act=9)), None)
+    assert lp == ssc.SSC_ERR_ARG
     # partial-sum buffer sizes: one float4 per (128-row slot, batch entry, group)
     assert lib.ssc_gn_partials_bytes(1000, 1, 32) == 8 * 32 * 16
     assert lib.ssc_gn_partials_bytes(0, 2, 4) >= 2 * 2 * 4 * 16

@@ -129,6 +129,39 @@ def test_packed_epilogue_equals_per_call(cin, cout):
     assert torch.equal(gn1.sums(), gn2.sums())
 
 
+@pytest.mark.parametrize("n,cin,cout,odt,act,with_res", [
+    (4097, 128, 128, torch.float32, "none", False),    # streaming kernel
+    (1000, 64, 128, torch.bfloat16, "silu", True),
+    (70001, 32, 32, torch.float32, "relu", True),
+    (1000, 128, 512, torch.bfloat16, "silu", False),   # tiled GEMM
+    (777, 512, 128, torch.float32, "none", True),
+    (1, 64, 1024, torch.bfloat16, "none", False),
+])
+def test_packed_linear_equals_per_call(n, cin, cout, odt, act, with_res):
+    say(f"[epi] packed linear n={n} {cin}->{cout} {odt} act={act} res={with_res}")
+    rng = np.random.default_rng(n + 3 * cin)
+    x = torch.from_numpy(rng.standard_normal((n, cin), dtype=np.float32)).to(torch.bfloat16)
+    w = (torch.from_numpy(rng.standard_normal((cin, cout), dtype=np.float32))
+         / np.sqrt(cin)).to(torch.bfloat16)
+    b = torch.from_numpy(rng.standard_normal(cout, dtype=np.float32))
+    res = (torch.from_numpy(rng.standard_normal((n, cout), dtype=np.float32)).to(odt).to(DEV)
+           if with_res else None)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    gn1 = ssc.GroupNormPartials(n, 1, 8, DEV)
+    gn2 = ssc.GroupNormPartials(n, 1, 8, DEV)
+    y1 = ssc.linear(xd, wd, bd, odt, act=act, residual=res, gn=gn1)
+    pw = ssc.pack_weights(wd)
+    y2 = ssc.linear(xd, pw, bd, odt, act=act, residual=res, gn=gn2)
+    assert torch.equal(y1.view(torch.uint8), y2.view(torch.uint8))
+    assert torch.equal(gn1.sums(), gn2.sums())
+    # the single-tap [1, Cin, Cout] form and the flip flag pack the same bytes
+    assert torch.equal(pw.buf, ssc.pack_weights(wd[None]).buf)
+    assert torch.equal(pw.buf, ssc.pack_weights(wd, flip=True).buf)
+    y3 = ssc.linear(xd, pw, None, odt)
+    ref = ssc.linear(xd, wd, None, odt)
+    assert torch.equal(y3.view(torch.uint8), ref.view(torch.uint8))
+
+
 @pytest.mark.parametrize("n,cin,cout,dtype,odt,act", [
     (1000, 64, 128, torch.bfloat16, torch.float32, "silu"),
     (4097, 128, 128, torch.bfloat16, torch.bfloat16, "relu"),

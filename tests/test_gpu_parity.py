@@ -350,21 +350,44 @@ def block_tap_pairs(nbr_sorted: np.ndarray) -> int:
     return int(valid.any(axis=1).sum())
 
 
+TILE_ROWS, STAGE_COST, ORDER_TILES = 128, 11, 32768
+
+
+def tile_costs(m_sorted: np.ndarray) -> np.ndarray:
+    """Cost of each full 128-row tile of a site order: STAGE_COST per tap present anywhere in
+    the tile plus one per (16-row block, tap present) pair, the centre tap included."""
+    f = len(m_sorted) // TILE_ROWS
+    blk = (m_sorted[:f * TILE_ROWS] >= 0).reshape(f, TILE_ROWS // 16, 16, 27).any(axis=2)
+    return STAGE_COST * blk.any(axis=1).sum(axis=1) + blk.sum(axis=(1, 2))
+
+
+def tile_cost_order(order: np.ndarray, m: np.ndarray) -> np.ndarray:
+    """The mask order with its full tiles stably re-sorted by ascending cost (the tiles that
+    hold padding stay last); unchanged for one tile or more than ORDER_TILES."""
+    f = len(order) // TILE_ROWS
+    if f < 2 or f > ORDER_TILES:
+        return order
+    t = np.argsort(tile_costs(m[order]), kind="stable")
+    full = order[:f * TILE_ROWS].reshape(f, TILE_ROWS)[t].reshape(-1)
+    return np.concatenate([full, order[f * TILE_ROWS:]])
+
+
 def expected_site_order(coords, batch, grid, m):
-    """The plan's site order from its definition: the mask order (stable sort by Gray rank);
+    """The plan's site order from its definition: the mask order (stable sort by Gray rank,
+    then its full 128-row tiles stably sorted by ascending cost);
     when the grid holds >= 8 bricks of 128^3 (batch entries apart), also the brick order (the
     mask order stably re-sorted by (entry, Morton code of the brick)), kept when its
     (block, tap) pairs are at most 21/20 of the mask order's.  Returns (order, spatial)."""
     mask_order = np.argsort(gray_rank_keys(m), kind="stable")
     per_axis = [(g - 1) // 128 + 1 for g in grid]
     if batch * np.prod(per_axis) < 8:
-        return mask_order, False
+        return tile_cost_order(mask_order, m), False
     bits = max(int(np.ceil(np.log2(p))) if p > 1 else 0 for p in per_axis)
     c = coords.astype(np.int64)[mask_order]
     key = (c[:, 0] << (3 * bits)) | morton3(c[:, 1] >> 7, c[:, 2] >> 7, c[:, 3] >> 7, bits)
     brick_order = mask_order[np.argsort(key, kind="stable")]
     spatial = block_tap_pairs(m[brick_order]) * 20 <= block_tap_pairs(m[mask_order]) * 21
-    return (brick_order if spatial else mask_order), spatial
+    return (brick_order if spatial else tile_cost_order(mask_order, m)), spatial
 
 
 def check_plan(idx, coords, batch, grid, m):
@@ -395,8 +418,13 @@ def test_plan_structure(name, shuffle, spatial):
     np.testing.assert_array_equal(idx.nbr.cpu().numpy(), m)
     assert check_plan(idx, w.coords, w.batch, w.grid, m) == spatial
     if not spatial:
-        keys = gray_rank_keys(m)[idx.plan.parts()[0][:w.n].cpu().numpy()]
-        assert (np.diff(keys) >= 0).all()
+        # whole tiles of the mask order, in ascending cost
+        perm = idx.plan.parts()[0][:w.n].cpu().numpy()
+        f = w.n // TILE_ROWS
+        keys = gray_rank_keys(m)[perm]
+        assert (np.diff(keys[:f * TILE_ROWS].reshape(f, TILE_ROWS), axis=1) >= 0).all()
+        assert (np.diff(keys[f * TILE_ROWS:]) >= 0).all()
+        assert (np.diff(tile_costs(m[perm])) >= 0).all()
 
 
 def test_plan_spatial_candidate_rejected_and_batched():
