@@ -7,10 +7,10 @@ SubMConv3d layer call on resident inputs with the layer's weights re-laid out on
 (the per-call entries are reported beside it); the two-layer workload adds its k=1 layer.
 
 Timing: after the warm-up steps, windows of --steps back-to-back steps are timed with HIP
-events on the kernels' stream until there are at least 25 windows and about 0.25 s of GPU
-work; ms_per_step is the median window / steps, and the k=3 kernel's time comes from the same
-windows (the step itself for one layer; events after each k=3 launch for two), so the kernel
-never exceeds the step.
+events on the kernels' stream (one before the window, one after it, nothing between the
+steps) until there are at least 25 windows and about 0.25 s of GPU work; ms_per_step is the
+median window / steps.  The k=3 kernel's time is the step itself for one layer (the same
+windows); for two layers it comes from further windows of the k=3 layer alone.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -554,31 +554,27 @@ def cpu_baseline(w) -> dict:
 
 
 class Windows:
-    """Device time of ``k`` back-to-back steps per window, over many windows: events on the
-    stream the kernels run on (torch's current stream) before the first step, after every
-    step and, with ``mid``, after the first kernel of every step.  Windows repeat until there
-    are at least ``min_windows`` and about ``min_s`` seconds of timed GPU work (at most
-    ``max_windows``); each window is synchronised before the next starts."""
+    """Device time of ``k`` back-to-back steps per window, over many windows: one event on the
+    stream the kernels run on (torch's current stream) before the first step and one after the
+    last, so nothing is enqueued between the steps.  Windows repeat until there are at least
+    ``min_windows`` and about ``min_s`` seconds of timed GPU work (at most ``max_windows``);
+    each window is synchronised before the next starts."""
 
-    def __init__(self, torch, step, k, mid=False, min_windows=25, min_s=0.25, max_windows=400):
-        self.step_ms, self.first_ms, self.windows = [], [], 0
-        ev = lambda: torch.cuda.Event(enable_timing=True)
-        starts = [ev() for _ in range(k + 1)]
-        mids = [ev() for _ in range(k)] if mid else None
+    def __init__(self, torch, step, k, min_windows=25, min_s=0.25, max_windows=400):
+        self.step_ms, self.windows = [], 0
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         total = 0.0
         while self.windows < min_windows or (total < min_s * 1e3 and
                                              self.windows < max_windows):
-            starts[0].record()
-            for j in range(k):
-                step(mids[j] if mid else None)
-                starts[j + 1].record()
+            e0.record()
+            for _ in range(k):
+                step()
+            e1.record()
             torch.cuda.synchronize()
-            win = starts[0].elapsed_time(starts[k])
+            win = e0.elapsed_time(e1)
             total += win
             self.step_ms.append(win / k)
-            self.first_ms.append(
-                float(np.mean([starts[j].elapsed_time(mids[j]) for j in range(k)])) if mid
-                else win / k)
             self.windows += 1
         self.k = k
 
@@ -691,10 +687,8 @@ def main():
         else:
             ssc.subm_conv3d(x, wt, bias, plan, mid_dt, out=y1)
 
-    def step(mid=None):
+    def step():
         conv()
-        if mid is not None:
-            mid.record()
         if two:
             ssc.linear(y1, w2, b2, odt, out=y2)
 
@@ -705,11 +699,10 @@ def main():
     win = Windows(torch, step, args.steps)
     t_wall = time.perf_counter() - t_wall
     st = win.summary(win.step_ms)
-    # Two layers: the k=3 kernel's share comes from windows that also record an event after
-    # each k=3 launch (the event between the layers lengthens those steps a little, so the
-    # step itself is taken from the plain windows above).
-    kwin = Windows(torch, step, args.steps, mid=True) if two else win
-    kt = kwin.summary(kwin.first_ms)
+    # Two layers: the k=3 kernel's time comes from windows of the k=3 layer alone, run back to
+    # back on the same inputs (events between the layers would lengthen what they bracket).
+    kwin = Windows(torch, conv, args.steps) if two else win
+    kt = kwin.summary(kwin.step_ms)
     ms_step, ms_kernel = st["median"], kt["median"]
     log(f"[bench] {win.windows} windows of {args.steps} steps ({t_wall:.2f} s wall): step "
         f"median {ms_step * 1e3:.2f} us (p10 {st['p10'] * 1e3:.2f}, p90 {st['p90'] * 1e3:.2f}, "
@@ -722,20 +715,18 @@ def main():
     t_host = (time.perf_counter() - t_host) / args.steps
     torch.cuda.synchronize()
 
-    def timed(fn, k):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(k):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / k
-
     # The same layer through the per-call entries: the weights re-laid out on every call
     # (ssc_subm_conv3d_plan: two launches), and on the neighbour map alone (ssc_subm_conv3d:
-    # the plan of the map is built on every call too).
-    ms_percall = timed(lambda: ssc.subm_conv3d(x, wt, bias, plan, mid_dt, out=y1), args.steps)
-    ms_map = timed(lambda: ssc.subm_conv3d(x, wt, bias, nbr, mid_dt, out=y1), args.steps)
+    # the plan of the map is built on every call too).  A few warm-up calls, then the median
+    # of windows as for the step.
+    def windowed(fn):
+        for _ in range(3):
+            fn()
+        wn = Windows(torch, fn, args.steps, min_windows=10, min_s=0.05)
+        return float(np.median(wn.step_ms))
+
+    ms_percall = windowed(lambda: ssc.subm_conv3d(x, wt, bias, plan, mid_dt, out=y1))
+    ms_map = windowed(lambda: ssc.subm_conv3d(x, wt, bias, nbr, mid_dt, out=y1))
     log(f"[bench] layer with per-call weight re-layout {ms_percall * 1e3:.1f} us; "
         f"on the map alone {ms_map * 1e3:.1f} us")
 
@@ -818,9 +809,9 @@ def main():
                    "parallelism": "single GPU"},
         "timing": {"windows": win.windows, "steps_per_window": args.steps,
                    "step_us": rnd(st), "kernel_us": rnd(kt),
-                   "note": "median over windows of back-to-back steps; kernel_us: the step "
-                           "itself for one layer (same windows), for two layers the k=3 share "
-                           "of windows with an event after each k=3 launch"},
+                   "note": "median over windows of back-to-back steps with events only at "
+                           "the window ends; kernel_us: the step itself for one layer (same "
+                           "windows), for two layers windows of the k=3 layer alone"},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel": kname,
