@@ -779,12 +779,25 @@ def main():
     flops = 2.0 * pairs * cin * cout
     achieved_gbs = bytes_alg / (ms_kernel * 1e-3) / 1e9
     tflops_kernel = flops / (ms_kernel * 1e-3) / 1e12
+    # The ceiling that binds at the algorithmic level: the matrix cores when the layer's FLOP
+    # take longer at the bf16 dense peak than its bytes at the HBM peak (arithmetic intensity
+    # above the ridge, 314.6 FLOP/B), else HBM.
+    mfma_bound = use_packed and flops / PEAK_BF16_TFLOPS > bytes_alg / PEAK_HBM_GBS * 1e3
+    if mfma_bound:
+        roofline = {"bound": "mfma", "achieved": round(tflops_kernel, 1),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops_kernel / PEAK_BF16_TFLOPS, 4)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4)}
     flops_step = flops + (2.0 * w.n * w.layers[1].cin * w.layers[1].cout if two else 0.0)
     tflops_step = flops_step / (ms_step * 1e-3) / 1e12
     value = mvox_per_s(w.n, ms_step * 1e-3)
     kname = f"k_subm_lds<{cin},{cout}>" if use_packed else "k_conv_valu"
     digest = source_digest()
     traffic = counted_traffic(kname, digest, args.workload, "f32" if out_bytes == 4 else "bf16")
+    roofline.update({"traffic": traffic, "kernel": kname, "bytes_alg_per_launch": bytes_alg,
+                     "flops_alg_per_launch": flops, "kernel_us": round(ms_kernel * 1e3, 2)})
     rnd = lambda d, k=1e3, nd=2: {a: round(v * k, nd) for a, v in d.items()}
 
     res = {
@@ -812,10 +825,7 @@ def main():
                    "note": "median over windows of back-to-back steps with events only at "
                            "the window ends; kernel_us: the step itself for one layer (same "
                            "windows), for two layers windows of the k=3 layer alone"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel": kname,
-                     "bytes_alg_per_launch": bytes_alg, "kernel_us": round(ms_kernel * 1e3, 2)},
+        "roofline": roofline,
         "mfma": {"effective_tflops_kernel": round(tflops_kernel, 2),
                  "frac_bf16_peak_kernel": round(tflops_kernel / PEAK_BF16_TFLOPS, 5),
                  "effective_tflops_step": round(tflops_step, 2),
