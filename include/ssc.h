@@ -208,9 +208,11 @@ size_t ssc_conv_workspace_bytes(int32_t cin, int32_t cout, int32_t in_dtype);
  *   workspace >= ssc_conv_workspace_bytes(cin, cout, in_dtype) bytes, 256-byte aligned.
  * fp16 is the checkpoints' source precision (trellis2-mlx-8bit page); the matrix-core kernels
  * store fp32 or the input's own 16-bit type.
- * Shapes: 1 <= cin, cout <= 1024.  bf16 or fp16 with cin in {32, 64, 128} and cout in
- * {16, 32, 64, 128} (and out_dtype fp32 or the input's type) runs on the matrix cores; the
- * rest runs a vector-ALU kernel with the same numerics contract.
+ * Shapes: 1 <= cin, cout <= 1024.  bf16 or fp16 with cin in {32, 64, 128} or a multiple of
+ * 128, and cout in {16, 32, 64, 128} or a multiple of 128 (and out_dtype fp32 or the input's
+ * type) runs on the matrix cores: wider layers as 128-channel input chunks summed in one
+ * kernel and 128-column output tiles.  The rest runs a vector-ALU kernel with the same
+ * numerics contract.
  * Errors: SSC_ERR_ARG (null or misaligned buffers, bad dtype, n < 0), SSC_ERR_UNSUPPORTED
  * (channels outside [1, 1024], n >= 2^31), SSC_ERR_WORKSPACE (short workspace). */
 ssc_status ssc_subm_conv3d_plan(const void* feats, int32_t in_dtype, const void* weight,
@@ -224,7 +226,8 @@ ssc_status ssc_subm_conv3d_plan(const void* feats, int32_t in_dtype, const void*
  * library holds on every GPU it runs on until the process ends.  The call allocates nothing
  * (no hipMalloc, no library allocation); its first call on a device looks the array's address
  * up once.  Limit: ssc_conv_workspace_bytes(cin, cout, in_dtype) <= SSC_STATIC_SCRATCH_BYTES
- * (every matrix-core shape, cin and cout <= 128, fits; larger 16-bit layers return
+ * (27 * cin * cout * 2 bytes: every matrix-core shape with cin and cout <= 128 fits, and
+ * wider ones as far as that bound, e.g. 256 -> 64; larger 16-bit layers return
  * SSC_ERR_WORKSPACE before anything is launched).  All calls on one GPU share that GPU's
  * array: calls that overlap on one GPU (concurrent streams, threads) race; calls in order on
  * one stream do not.  Other arguments, results (bit for bit) and errors as for
@@ -243,8 +246,8 @@ ssc_status ssc_subm_conv3d_plan_static(const void* feats, int32_t in_dtype, cons
  *           the weights in the kernel's fragment order (an opaque layout of the same byte
  *           count, valid only for ssc_subm_conv3d_packed (taps = 27) or ssc_linear_packed
  *           (taps = 1) with the same cin and cout).
- * taps = 27: cin in {32, 64, 128}, cout in {16, 32, 64, 128} (the shapes the k=3
- * matrix-core kernels are built for).  taps = 1: the shapes ssc_linear runs on the matrix
+ * taps = 27: the shapes ssc_subm_conv3d_plan runs on the matrix cores (cin in {32, 64, 128}
+ * or a multiple of 128, cout in {16, 32, 64, 128} or a multiple of 128).  taps = 1: the shapes ssc_linear runs on the matrix
  * cores (cin, cout in {32, 64, 128}, or multiples of 64 up to 1024).  Otherwise
  * SSC_ERR_UNSUPPORTED. */
 size_t ssc_packed_weight_bytes(int32_t taps, int32_t cin, int32_t cout);

@@ -128,15 +128,22 @@ struct LdsCfg {
 };
 
 // Fragment-major packed weights for WC column groups: element
-//   Wp[(((t*WC + wc)*NCT + c)*KS + s)*512 + lane*8 + e] = W[t][32s + 8(lane>>4) + e][wc*CS + 16c + (lane&15)]
-// i.e. the B fragment of (tap t, wave column group wc, column tile c, k-step s) for `lane`.
+//   Wp[(((v*WC + wc)*NCT + c)*KS + s)*512 + lane*8 + e]
+//     = W[t][kc*CK + 32s + 8(lane>>4) + e][ct*COT + wc*CS + 16c + (lane&15)]
+// i.e. the B fragment of (virtual tap v, wave column group wc, column tile c, k-step s) for
+// `lane`.  A layer wider than one kernel tile is cut into input chunks of CK channels (kc of
+// cin / CK) and output tiles of COT columns (ct of cout / COT); virtual tap v = (ct * taps +
+// t) * (cin / CK) + kc, so every (t, kc) block of one output tile has the layout of a CK x COT
+// layer's tap.  CK = cin and COT = cout give v = t.
 // flip = 1 packs W[taps-1-t] into tap t: the tap at offset d then reads site c - d, the other
 // orientation the LATO.2 page leaves open (its "--flip-kernel").
 __global__ __launch_bounds__(256) void k_pack_frag(const uint16_t* __restrict__ W, int taps,
-                                                   int cin, int cout, int wc_groups, int flip,
+                                                   int cin, int cout, int ck, int cot,
+                                                   int wc_groups, int flip,
                                                    uint16_t* __restrict__ Wp) {
-  const int cs = cout / wc_groups, nct = cs / 16, ks = cin / 32;
-  const int64_t total = static_cast<int64_t>(taps) * wc_groups * nct * ks * 64;
+  const int cs = cot / wc_groups, nct = cs / 16, ks = ck / 32;
+  const int kch = cin / ck, ctn = cout / cot;
+  const int64_t total = static_cast<int64_t>(taps) * kch * ctn * wc_groups * nct * ks * 64;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
        idx += stride) {
@@ -147,9 +154,12 @@ __global__ __launch_bounds__(256) void k_pack_frag(const uint16_t* __restrict__ 
     const int c = static_cast<int>(rest % nct);
     rest /= nct;
     const int wc = static_cast<int>(rest % wc_groups);
-    const int64_t t = rest / wc_groups;
-    const int o = wc * cs + c * 16 + (lane & 15);
-    const int k0 = s * 32 + (lane >> 4) * 8;
+    const int64_t v = rest / wc_groups;
+    const int kc = static_cast<int>(v % kch);
+    const int64_t t = (v / kch) % taps;
+    const int ct = static_cast<int>(v / (static_cast<int64_t>(kch) * taps));
+    const int o = ct * cot + wc * cs + c * 16 + (lane & 15);
+    const int k0 = kc * ck + s * 32 + (lane >> 4) * 8;
     const int64_t ts = flip ? taps - 1 - t : t;
     const uint16_t* src = W + (ts * cin + k0) * cout + o;
     uint16_t* dst = Wp + idx * 8;
@@ -203,9 +213,11 @@ __device__ __forceinline__ uint32_t block_taps(uint32_t bmv, int t) {
   return static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(((bmv >> t) & 1u) != 0u));
 }
 
+// X points at the stage's input chunk (channel kc * CIN of row 0); xs is the row stride in
+// elements (CIN times the number of chunks).
 template <int CIN, int COUT, int NB, int WR, int WC>
 __device__ __forceinline__ void issue_gather(int q, uint32_t act, const uint16_t* __restrict__ X,
-                                             const uint16_t* __restrict__ zrow,
+                                             int64_t xs, const uint16_t* __restrict__ zrow,
                                              const int32_t* sG, uint32_t sA, int wave, int lane) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
   const int32_t* g = sG + q * (NB * 16);
@@ -229,7 +241,7 @@ __device__ __forceinline__ void issue_gather(int q, uint32_t act, const uint16_t
       if (!((act >> b) & 1u)) continue;
       const int chunk = (lane % C::CPR) ^ swz<C::CPR>(part * RPI + rsub);
       const uint16_t* src =
-          j[i] >= 0 ? X + static_cast<int64_t>(j[i]) * CIN + chunk * 8 : zrow + chunk * 8;
+          j[i] >= 0 ? X + static_cast<int64_t>(j[i]) * xs + chunk * 8 : zrow + chunk * 8;
       dma16(src, sA + b * C::A_BLOCK * 2 + part * 1024);
     }
   } else {
@@ -244,7 +256,7 @@ __device__ __forceinline__ void issue_gather(int q, uint32_t act, const uint16_t
     for (int b = 0; b < NB; ++b) {
       if (!((act >> b) & 1u)) continue;
       const uint16_t* src =
-          j[b] >= 0 ? X + static_cast<int64_t>(j[b]) * CIN + chunk * 8 : zrow + chunk * 8;
+          j[b] >= 0 ? X + static_cast<int64_t>(j[b]) * xs + chunk * 8 : zrow + chunk * 8;
       dma16(src, sA + b * C::A_BLOCK * 2 + wave * C::RPW * CIN * 2);
     }
   }
@@ -330,14 +342,16 @@ __device__ __forceinline__ float load_out(const void* p, int64_t i) {
 }
 
 // EPI = false is the plain convolution (bias only); EPI = true adds the activation, the
-// residual and the group-norm statistics as the Epi arguments ask.
-template <int CIN, int COUT, int NB, int WR, int WC, bool OUT16, int EK, bool EPI>
+// residual and the group-norm statistics as the Epi arguments ask.  WIDE = true runs a layer
+// wider than the tile (kch input chunks, gridDim.y output tiles); WIDE = false compiles the
+// single chunk and tile in.
+template <int CIN, int COUT, int NB, int WR, int WC, bool OUT16, int EK, bool EPI, bool WIDE>
 __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
     const float* __restrict__ bias, const int32_t* __restrict__ perm,
     const uint32_t* __restrict__ bmask, const int32_t* __restrict__ gidx,
     const uint16_t* __restrict__ zrow, const int64_t* __restrict__ sched, int64_t npad,
-    void* __restrict__ Y, Epi ep) {
+    int kch, void* __restrict__ Y, Epi ep) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_BYTES];
   const char* sA0 = smem;
@@ -351,6 +365,13 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int wr = wave / WC, wc = wave % WC;
   const uint32_t lds0 = lds_addr(smem);
+  // A layer wider than the tile: this workgroup computes output columns [ct * COUT, (ct + 1)
+  // * COUT) (ct = blockIdx.y of gridDim.y tiles), and each tap is summed over kch input
+  // chunks of CIN channels, whose packed weights follow the tile's (k_pack_frag).
+  if constexpr (!WIDE) kch = 1;
+  const int ct = WIDE ? static_cast<int>(blockIdx.y) : 0;
+  const int64_t xs = WIDE ? static_cast<int64_t>(CIN) * kch : CIN;
+  if constexpr (WIDE) Wp += static_cast<int64_t>(ct) * kTaps * kch * (CIN * COUT);
   // Which tile this workgroup takes follows the plan's schedule.  Interleaved: the plan puts
   // the mask order's tiles in ascending cost (a tile of near-empty masks walks a tap or two,
   // the costliest all 27), so taking them from the last, the heavy tiles go first and the
@@ -412,14 +433,19 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   for (int c = 0; c < C::NCT; ++c)
 #pragma unroll
     for (int i = 0; i < 4; ++i)  // bias needs only 4-byte alignment: scalar loads
-      bv[c][i] = bias ? bias[wc * C::CS + c * 16 + 4 * (lane >> 4) + i] : 0.f;
+      bv[c][i] = bias ? bias[ct * COUT + wc * C::CS + c * 16 + 4 * (lane >> 4) + i] : 0.f;
   wait_vm_lgkm0();
   __builtin_amdgcn_s_barrier();
 
   // Output staging geometry (used by the epilogue below).
   constexpr int ESZ = OUT16 ? 2 : 4;
-  constexpr int ROWB = COUT * ESZ;
+  constexpr int ROWB = COUT * ESZ;  // a row of the tile (staged)
   constexpr int CHUNKS = ROWB / 16;
+  // Output and residual rows in memory: all gridDim.y tiles wide; this tile's part.
+  const int64_t yrowb = WIDE ? static_cast<int64_t>(ROWB) * gridDim.y : ROWB;
+  char* const ycol = static_cast<char*>(Y) + static_cast<int64_t>(ct) * ROWB;
+  const char* const rcol =
+      ep.res ? static_cast<const char*>(ep.res) + static_cast<int64_t>(ct) * ROWB : nullptr;
   constexpr int SWM = (CHUNKS < 16 ? CHUNKS : 16) - 1;
   constexpr int BPP_RAW = C::STAGE_BYTES / (16 * ROWB);
   // Blocks per pass: the largest power of two that fits (NB is a power of two, so every pass
@@ -443,8 +469,7 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
         const int idx = threadIdx.x + k * C::THREADS;
         const int row = idx / CHUNKS, ch = idx % CHUNKS;
         const int32_t o = sP[row];
-        rpre[k] = o >= 0 ? *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(ep.res) +
-                                                              static_cast<int64_t>(o) * ROWB +
+        rpre[k] = o >= 0 ? *reinterpret_cast<const u32x4_t*>(rcol + static_cast<int64_t>(o) * yrowb +
                                                               ch * 16)
                          : u32x4_t{0u, 0u, 0u, 0u};
       }
@@ -458,49 +483,61 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     for (int c = 0; c < C::NCT; ++c) acc[bl][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   if (U) {
-    // Stage q lives in (sA0, bw0) for even q and (sA1, bw1) for odd q.  Per stage: wait until
+    // Even stages live in (sA0, bw0), odd ones in (sA1, bw1).  Per stage: wait until
     // this wave's copies and loads of the stage have landed (nothing newer is outstanding at
     // that point), barrier, issue the next stage, then run the matrix cores on this one.
     bf16x8_t bw0[C::NCT][C::KS], bw1[C::NCT][C::KS];
     uint32_t aoff[C::KS];
     a_frag_offsets<CIN>(lane, aoff);
+    // Stages walk (tap, input chunk) pairs: taps in ascending order, each tap's chunks in
+    // order.  q counts the taps (their slot of neighbour rows), kc the chunk.
     uint32_t rem = U;
     int t_cur = __builtin_ctz(rem);
     rem &= rem - 1;
-    int q = 0;
+    int q = 0, kc = 0;
     uint32_t act = block_taps(bmv, t_cur);
-    load_weights<CIN, COUT, NB, WR, WC>(t_cur, Wp, wc, lane, bw0);
-    issue_gather<CIN, COUT, NB, WR, WC>(0, act, X, zrow, sG, lds0, wave, lane);
+    load_weights<CIN, COUT, NB, WR, WC>(t_cur * kch, Wp, wc, lane, bw0);
+    issue_gather<CIN, COUT, NB, WR, WC>(0, act, X, xs, zrow, sG, lds0, wave, lane);
+    // The stage after the current one: the tap's next chunk, else the next tap's first
+    // (t_next = -1 when none is left).  Uniform across the workgroup.
+    auto next = [&](int& t_next, int& kc_next, int& q_next, uint32_t& act_next)
+        __attribute__((always_inline)) {
+      if (WIDE && kc + 1 < kch) {
+        t_next = t_cur, kc_next = kc + 1, q_next = q, act_next = act;
+      } else if (rem) {
+        t_next = __builtin_ctz(rem), kc_next = 0, q_next = q + 1;
+        act_next = block_taps(bmv, t_next);
+      } else {
+        t_next = -1, kc_next = 0, q_next = q, act_next = 0;
+      }
+    };
     while (true) {
       wait_vm_lgkm0();
       __builtin_amdgcn_s_barrier();
-      int t_next = rem ? __builtin_ctz(rem) : -1;
-      uint32_t act_next = 0;
+      int t_next, kc_next, q_next;
+      uint32_t act_next;
+      next(t_next, kc_next, q_next, act_next);
       if (t_next >= 0) {
-        act_next = block_taps(bmv, t_next);
-        load_weights<CIN, COUT, NB, WR, WC>(t_next, Wp, wc, lane, bw1);
-        issue_gather<CIN, COUT, NB, WR, WC>(q + 1, act_next, X, zrow, sG, lds0 + C::OFF_A1, wave,
-                                            lane);
+        load_weights<CIN, COUT, NB, WR, WC>(t_next * kch + kc_next, Wp, wc, lane, bw1);
+        issue_gather<CIN, COUT, NB, WR, WC>(q_next, act_next, X + (WIDE ? kc_next * CIN : 0), xs, zrow, sG,
+                                            lds0 + C::OFF_A1, wave, lane);
       }
       compute_stage<CIN, COUT, NB, WR, WC, EK>(act, sA0, bw0, aoff, wr, acc);
       if (t_next < 0) break;
-      rem &= rem - 1;
-      act = act_next;
-      ++q;
+      if (kc_next == 0) rem &= rem - 1;
+      t_cur = t_next, kc = kc_next, q = q_next, act = act_next;
       wait_vm_lgkm0();
       __builtin_amdgcn_s_barrier();
-      t_next = rem ? __builtin_ctz(rem) : -1;
-      act_next = 0;
+      next(t_next, kc_next, q_next, act_next);
       if (t_next >= 0) {
-        act_next = block_taps(bmv, t_next);
-        load_weights<CIN, COUT, NB, WR, WC>(t_next, Wp, wc, lane, bw0);
-        issue_gather<CIN, COUT, NB, WR, WC>(q + 1, act_next, X, zrow, sG, lds0, wave, lane);
+        load_weights<CIN, COUT, NB, WR, WC>(t_next * kch + kc_next, Wp, wc, lane, bw0);
+        issue_gather<CIN, COUT, NB, WR, WC>(q_next, act_next, X + (WIDE ? kc_next * CIN : 0), xs, zrow, sG,
+                                            lds0, wave, lane);
       }
       compute_stage<CIN, COUT, NB, WR, WC, EK>(act, sA1, bw1, aoff, wr, acc);
       if (t_next < 0) break;
-      rem &= rem - 1;
-      act = act_next;
-      ++q;
+      if (kc_next == 0) rem &= rem - 1;
+      t_cur = t_next, kc = kc_next, q = q_next, act = act_next;
     }
   }
 
@@ -546,8 +583,7 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
             const int32_t o = sP[p0 * 16 + row];
             if (o < 0) continue;
             *reinterpret_cast<u32x4_t*>(sOut + row * ROWB + ((ch ^ (row & SWM)) << 4)) =
-                *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(ep.res) +
-                                                  static_cast<int64_t>(o) * ROWB + ch * 16);
+                *reinterpret_cast<const u32x4_t*>(rcol + static_cast<int64_t>(o) * yrowb + ch * 16);
           }
         }
         wait_vm_lgkm0();
@@ -619,8 +655,7 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
         // Non-temporal: the output is not read again here, and streaming it past the caches
         // keeps them for the feature rows other tiles gather (about 2% at 128^3, 10%).
         __builtin_nontemporal_store(
-            v, reinterpret_cast<u32x4_t*>(static_cast<char*>(Y) + static_cast<int64_t>(o) * ROWB +
-                                          ch * 16));
+            v, reinterpret_cast<u32x4_t*>(ycol + static_cast<int64_t>(o) * yrowb + ch * 16));
       }
       if (p0 + BPP < NB) {
         wait_vm_lgkm0();
@@ -991,7 +1026,7 @@ using LinFn = void (*)(const uint16_t*, const uint16_t*, const float*, int64_t, 
                       const void*);
 using LdsFn = void (*)(const uint16_t*, const uint16_t*, const float*, const int32_t*,
                        const uint32_t*, const int32_t*, const uint16_t*, const int64_t*,
-                       int64_t, void*, Epi);
+                       int64_t, int, void*, Epi);
 
 // k=1 streaming kernel for the channel counts the matrix-core path is built for.
 template <int CI, int CO, bool O16, int EK>
@@ -1029,22 +1064,37 @@ struct LdsPick {
 };
 
 template <int CI, int CO, bool O16, int EK>
-LdsFn lds_fn(bool epi) {
+LdsFn lds_fn(bool epi, bool wide) {
   using P = LdsPick<CI, CO>;
-  return epi ? k_subm_lds<CI, CO, P::NB, P::WR, P::WC, O16, EK, true>
-             : k_subm_lds<CI, CO, P::NB, P::WR, P::WC, O16, EK, false>;
+  // Wide variants exist only for the chunk / tile widths a wider layer is cut into.
+  if constexpr (CI == 128 || CO == 128) {
+    if (wide)
+      return epi ? k_subm_lds<CI, CO, P::NB, P::WR, P::WC, O16, EK, true, true>
+                 : k_subm_lds<CI, CO, P::NB, P::WR, P::WC, O16, EK, false, true>;
+  }
+  return epi ? k_subm_lds<CI, CO, P::NB, P::WR, P::WC, O16, EK, true, false>
+             : k_subm_lds<CI, CO, P::NB, P::WR, P::WC, O16, EK, false, false>;
 }
 
+// Layers wider than 128 channels run the 128-wide kernels: cin in chunks of 128 (kch of
+// them, summed over in the stage loop), cout in tiles of 128 (ctn workgroups per row tile).
+// *ck / *cot receive the kernel's chunk and tile widths.
 LdsFn pick_lds(int cin, int cout, bool out16, int ek, int* threads, int* rows_per_tile,
-               int* wc_groups, bool epi) {
+               int* wc_groups, bool epi, int* ck_out = nullptr, int* cot_out = nullptr) {
+  if ((cin > 128 && cin % 128 != 0) || (cout > 128 && cout % 128 != 0)) return nullptr;
+  const int ck = cin > 128 ? 128 : cin, cot = cout > 128 ? 128 : cout;
+  const bool wide = cin > 128 || cout > 128;
+  if (ck_out) *ck_out = ck;
+  if (cot_out) *cot_out = cot;
 #define SSC_CASE(CI, CO)                                                             \
-  if (cin == CI && cout == CO) {                                                     \
+  if (ck == CI && cot == CO) {                                                       \
     using P = LdsPick<CI, CO>;                                                       \
     *threads = P::WR * P::WC * 64;                                                   \
     *rows_per_tile = P::NB * 16;                                                     \
     *wc_groups = P::WC;                                                              \
-    if (ek == 1) return out16 ? lds_fn<CI, CO, true, 1>(epi) : lds_fn<CI, CO, false, 1>(epi); \
-    return out16 ? lds_fn<CI, CO, true, 0>(epi) : lds_fn<CI, CO, false, 0>(epi);     \
+    if (ek == 1)                                                                     \
+      return out16 ? lds_fn<CI, CO, true, 1>(epi, wide) : lds_fn<CI, CO, false, 1>(epi, wide); \
+    return out16 ? lds_fn<CI, CO, true, 0>(epi, wide) : lds_fn<CI, CO, false, 0>(epi, wide); \
   }
   SSC_CASE(32, 16) SSC_CASE(32, 32) SSC_CASE(32, 64) SSC_CASE(32, 128)
   SSC_CASE(64, 16) SSC_CASE(64, 32) SSC_CASE(64, 64) SSC_CASE(64, 128)
@@ -1088,19 +1138,22 @@ ssc_status launch_linear(LinFn fn, int rows_per_tile, const void* feats, const u
   return launch_status();
 }
 
+// kch input chunks and ctn output tiles of the kernel's widths (1 and 1 for a layer of them).
 ssc_status launch_lds(LdsFn fn, int threads, int rows_per_tile, const void* feats,
                       const uint16_t* wt, const float* bias, const void* plan, int64_t n,
-                      void* out, const Epi& ep, hipStream_t s) {
+                      void* out, const Epi& ep, hipStream_t s, int kch = 1, int ctn = 1) {
   const PlanLayout P = plan_layout(n);
   const char* pb = static_cast<const char*>(plan);
   const int64_t tiles = P.npad / rows_per_tile;
-  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(tiles)), dim3(threads), 0, s,
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(ctn)),
+                     dim3(threads), 0, s,
                      static_cast<const uint16_t*>(feats), wt, bias,
                      reinterpret_cast<const int32_t*>(pb + P.off_perm),
                      reinterpret_cast<const uint32_t*>(pb + P.off_bmask),
                      reinterpret_cast<const int32_t*>(pb + P.off_gidx),
                      reinterpret_cast<const uint16_t*>(pb + P.off_zero),
-                     reinterpret_cast<const int64_t*>(pb) + kPlanSchedWord, P.npad, out, ep);
+                     reinterpret_cast<const int64_t*>(pb) + kPlanSchedWord, P.npad, kch, out,
+                     ep);
   return launch_status();
 }
 
@@ -1129,7 +1182,8 @@ ssc_status check_epilogue(const ssc_epilogue* e, int64_t n, int cout, Epi* ep) {
 // Whether the k=3 kernel sums the group-norm statistics in its epilogue: one batch entry and
 // groups of a power-of-two number of channels up to 16 (a group inside one 16-column tile).
 bool gn_fusable(const ssc_epilogue* e, int cout) {
-  if (e == nullptr || e->gn_partials == nullptr || e->batch != 1) return false;
+  // One output tile only (the kernel's statistics cover the columns of its own tile).
+  if (e == nullptr || e->gn_partials == nullptr || e->batch != 1 || cout > 128) return false;
   const int gs = cout / e->gn_groups;
   return gs <= 16 && (gs & (gs - 1)) == 0;
 }
@@ -1142,12 +1196,14 @@ ssc_status gn_after(const ssc_epilogue* e, bool fused, const void* out, int out_
                             e->gn_partials, s);
 }
 
+// ck / cot: the input chunk and output tile of the kernel the weights are for (0: the layer's
+// own cin / cout).
 void launch_pack_frag(const void* weight, int taps, int cin, int cout, int wc_groups, int flip,
-                      uint16_t* wp, hipStream_t s) {
+                      uint16_t* wp, hipStream_t s, int ck = 0, int cot = 0) {
   const int64_t total = static_cast<int64_t>(taps) * (cout / 16) * (cin / 32) * 64;
   const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((total + 255) / 256, 65536));
   k_pack_frag<<<blocks, 256, 0, s>>>(static_cast<const uint16_t*>(weight), taps, cin, cout,
-                                     wc_groups, flip, wp);
+                                     ck ? ck : cin, cot ? cot : cout, wc_groups, flip, wp);
 }
 
 
@@ -1204,9 +1260,11 @@ ssc_status run_conv(bool dense, const void* feats, int in_dtype, const void* wei
       const bool fused = gn_fusable(epi, cout);
       if (fused) ep.gn = epi->gn_partials;
       const bool use_epi = fused || ep.act != SSC_ACT_NONE || ep.res != nullptr;
-      if (LdsFn fn = pick_lds(cin, cout, out16, ek, &threads, &rows, &wcg, use_epi)) {
-        launch_pack_frag(weight, kTaps, cin, cout, wcg, 0, wt, s);
-        if (const ssc_status st = launch_lds(fn, threads, rows, feats, wt, bias, plan, n, out, ep, s);
+      int ck = 0, cot = 0;
+      if (LdsFn fn = pick_lds(cin, cout, out16, ek, &threads, &rows, &wcg, use_epi, &ck, &cot)) {
+        launch_pack_frag(weight, kTaps, cin, cout, wcg, 0, wt, s, ck, cot);
+        if (const ssc_status st = launch_lds(fn, threads, rows, feats, wt, bias, plan, n, out, ep,
+                                             s, cin / ck, cout / cot);
             st != SSC_OK)
           return st;
         return gn_after(epi, fused, out, out_dtype, n, cout, s);
@@ -1388,8 +1446,9 @@ extern "C" ssc_status ssc_pack_weights_ex(const void* weight, int32_t taps, int3
   if (weight == nullptr || packed == nullptr) return SSC_ERR_ARG;
   if (flags & ~SSC_PACK_FLIP) return SSC_ERR_ARG;
   int threads = 0, rows = 0, wcg = 0;
+  int ck = 0, cot = 0;
   if (taps == kTaps) {
-    if (pick_lds(cin, cout, false, 0, &threads, &rows, &wcg, false) == nullptr)
+    if (pick_lds(cin, cout, false, 0, &threads, &rows, &wcg, false, &ck, &cot) == nullptr)
       return SSC_ERR_UNSUPPORTED;
   } else if (taps == 1) {
     // The k=1 kernels' layouts: the streaming kernel's column groups, else 16-column tiles.
@@ -1404,7 +1463,7 @@ extern "C" ssc_status ssc_pack_weights_ex(const void* weight, int32_t taps, int3
   if (packed_bytes < ssc_packed_weight_bytes(taps, cin, cout)) return SSC_ERR_WORKSPACE;
   // A single tap is its own mirror image: the flag changes nothing there.
   launch_pack_frag(weight, taps, cin, cout, wcg, (taps == kTaps && (flags & SSC_PACK_FLIP)) ? 1 : 0,
-                   static_cast<uint16_t*>(packed), as_stream(stream));
+                   static_cast<uint16_t*>(packed), as_stream(stream), ck, cot);
   return launch_status();
 }
 
@@ -1473,10 +1532,12 @@ extern "C" ssc_status ssc_subm_conv3d_packed_ex(const void* feats, const void* p
   const bool fused = gn_fusable(epilogue, cout);
   if (fused) ep.gn = epilogue->gn_partials;
   const bool use_epi = fused || ep.act != SSC_ACT_NONE || ep.res != nullptr;
-  LdsFn fn = pick_lds(cin, cout, out_dtype == SSC_BF16, 0, &threads, &rows, &wcg, use_epi);
+  int ck = 0, cot = 0;
+  LdsFn fn = pick_lds(cin, cout, out_dtype == SSC_BF16, 0, &threads, &rows, &wcg, use_epi, &ck,
+                      &cot);
   if (const ssc_status st = launch_lds(fn, threads, rows, feats,
                                        static_cast<const uint16_t*>(packed_weight), bias, plan, n,
-                                       out, ep, s);
+                                       out, ep, s, cin / ck, cout / cot);
       st != SSC_OK)
     return st;
   return gn_after(epilogue, fused, out, out_dtype, n, cout, s);

@@ -86,6 +86,9 @@ def index(coords, batch, grid):
     (64, 64, torch.float16, torch.float16, "silu", True),
     (16, 24, torch.float32, torch.float32, "silu", True),       # vector-ALU path
     (48, 24, torch.bfloat16, torch.float32, "relu", True),      # vector-ALU path
+    (256, 256, torch.bfloat16, torch.bfloat16, "silu", True),   # 2 input chunks, 2 output tiles
+    (384, 128, torch.bfloat16, torch.float32, "relu", True),    # 3 input chunks
+    (64, 256, torch.float16, torch.float16, "silu", True),      # 2 output tiles
 ])
 def test_conv_epilogue(cin, cout, dtype, odt, act, with_res):
     say(f"[epi] conv {cin}->{cout} {dtype} -> {odt} act={act} res={with_res}")
@@ -239,7 +242,8 @@ def test_group_norm_empty_entry_and_empty_input():
 
 
 @pytest.mark.parametrize("cin,cout,odt", [(128, 128, torch.bfloat16), (32, 32, torch.float32),
-                                          (64, 128, torch.float32), (32, 128, torch.bfloat16)])
+                                          (64, 128, torch.float32), (32, 128, torch.bfloat16),
+                                          (256, 256, torch.bfloat16)])
 def test_conv_group_norm_statistics(cin, cout, odt):
     say(f"[gn] conv-fused statistics {cin}->{cout} {odt}")
     coords, x, w, b, _ = case(100 + cin + cout, 1, (16, 15, 14), 0.45, cin, cout, torch.bfloat16)

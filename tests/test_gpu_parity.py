@@ -126,6 +126,33 @@ def check_conv(coords, batch, grid, x, w, b, tau):
     return idx, y
 
 
+@pytest.mark.parametrize("cin,cout,dtype", [
+    (256, 128, torch.bfloat16), (256, 256, torch.bfloat16), (512, 64, torch.bfloat16),
+    (128, 256, torch.bfloat16), (64, 384, torch.float16), (384, 32, torch.float16),
+    (1024, 16, torch.bfloat16), (32, 1024, torch.bfloat16)])
+def test_wide_layers(cin, cout, dtype):
+    """Layers wider than the 128-channel matrix-core kernel: cin in chunks of 128 summed in the
+    stage loop, cout in tiles of 128 as separate workgroups.  fp32 store against the oracle
+    (both bars); the 16-bit store is its RNE bit for bit; packed weights (bf16) give the same
+    bits as the per-call path, and the flipped packing matches the oracle's other
+    orientation."""
+    say(f"[parity] wide {cin}->{cout} {dtype}")
+    tau = TAU["bf16" if dtype == torch.bfloat16 else "f16"]
+    coords, x, w, b = small_case(cin + 7 * cout, 1, (13, 12, 11), 0.35, cin, cout, dtype)
+    idx, y = check_conv(coords, 1, (13, 12, 11), x, w, b, tau)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    y16 = idx.conv(xd, wd, bd, out_dtype=dtype)
+    assert torch.equal(y16.cpu().view(torch.int16), y.cpu().to(dtype).view(torch.int16))
+    if dtype == torch.bfloat16:
+        yp = ssc.subm_conv3d_packed(xd, ssc.pack_weights(wd), bd, idx.plan, torch.float32)
+        assert torch.equal(yp.view(torch.int32), y.view(torch.int32))
+        yf = ssc.subm_conv3d_packed(xd, ssc.pack_weights(wd, flip=True), bd, idx.plan,
+                                    torch.float32)
+        m = oracle.build_map(coords, 1, (13, 12, 11))
+        ref = oracle.conv(x.float().numpy(), w.float().numpy(), b.numpy(), m, flip=True)
+        assert rel_err(yf.cpu().numpy(), ref) <= TAU_ACC
+
+
 @pytest.mark.parametrize("cin,cout", [(c, o) for c in (32, 64, 128) for o in (16, 32, 64, 128)])
 def test_mfma_shapes_ragged(cin, cout):
     # ~1500 sites: several 128-row tiles and a ragged last tile
