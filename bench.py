@@ -87,11 +87,28 @@ def _counter_rows(d: str, kernel_substr: str, counter: str):
     return vals
 
 
-def conv_kernel_name(cin: int, cout: int, out16: bool) -> str:
-    """The plain k=3 kernel instantiation a workload's timed layer runs (bf16 inputs)."""
+def conv_kernel_name(cin: int, cout: int, out16: bool, c2: int = 0) -> str:
+    """The k=3 kernel instantiation a workload's timed step runs (bf16 inputs): the plain one,
+    or with c2 > 0 the pair kernel that applies the k=1 layer of c2 outputs after it."""
     wc = 4 if cout >= 64 else cout // 16
     return (f"k_subm_lds<{cin}, {cout}, 8, {4 // wc}, {wc}, {'true' if out16 else 'false'}, 0, "
-            f"false>")
+            f"false, false, {c2}>")
+
+
+PAIR_SHAPES = {(32, 64, 64), (64, 64, 64), (128, 64, 64), (64, 128, 64), (64, 128, 128),
+               (128, 128, 64), (128, 128, 128)}  # (cin, cmid, cout) of the fused k=3 -> k=1 kernel
+
+
+def step_kernel(layers) -> tuple:
+    """(kernel instance, label, output dtype name) of the dominant kernel of a workload's step:
+    the pair kernel when its two layers fit one, else the k=3 kernel."""
+    l1 = layers[0]
+    if len(layers) > 1 and (l1.cin, l1.cout, layers[1].cout) in PAIR_SHAPES:
+        c2 = layers[1].cout
+        return (conv_kernel_name(l1.cin, l1.cout, True, c2),
+                f"k_subm_lds<{l1.cin},{l1.cout}> + k=1 {l1.cout}->{c2} (pair)", "f32")
+    out16 = len(layers) > 1
+    return conv_kernel_name(l1.cin, l1.cout, out16), f"k_subm_lds<{l1.cin},{l1.cout}>", None
 
 
 def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mb, out_path,
@@ -101,11 +118,11 @@ def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_m
     copy of cal_mb MiB.  The kernel filter names the plain variant the workload's timed layer
     runs (its output type as stored between layers: bf16 for the two-layer workload)."""
     import workloads
-    layer = workloads.make(workload).layers
-    two = len(layer) > 1
-    out16 = two or out_dtype == "bf16"
-    kernel = conv_kernel_name(layer[0].cin, layer[0].cout, out16)
-    label = f"k_subm_lds<{layer[0].cin},{layer[0].cout}>"
+    layers = workloads.make(workload).layers
+    kernel, label, pair_out = step_kernel(layers)
+    if pair_out is None and out_dtype == "bf16":
+        kernel = conv_kernel_name(layers[0].cin, layers[0].cout, True)
+    out16 = (pair_out is None and len(layers) > 1) or out_dtype == "bf16"
     copy = "copy"  # torch's elementwise copy kernel
     f = _counter_rows(fetch_dir, kernel, "FETCH_SIZE")
     w = _counter_rows(write_dir, kernel, "WRITE_SIZE")
@@ -672,11 +689,17 @@ def main():
     two = len(w.layers) > 1
     mid_dt = torch.bfloat16 if two else odt
     y1 = torch.empty((w.n, cout), dtype=mid_dt, device=dev)
+    pair = None
     if two:
         l2 = w.layers[1]
         w2, b2 = l2.weight.to(dev), l2.bias.to(dev)
         if w2.dtype == torch.bfloat16:
-            w2 = ssc.pack_weights(w2)  # the k=1 layer's weights, re-laid out once as well
+            # the k=1 layer's weights, re-laid out once as well: for the pair kernel when the
+            # two layers fit one (the bf16 intermediate then never leaves the chip), and for
+            # the k=1 kernel of the two-launch step reported beside it
+            if use_packed and (cin, cout, l2.cout) in PAIR_SHAPES:
+                pair = ssc.pack_weights(w2, pair=True)
+            w2 = ssc.pack_weights(w2)
         y2 = torch.empty((w.n, l2.cout), dtype=odt, device=dev)
 
     def conv():
@@ -687,10 +710,17 @@ def main():
         else:
             ssc.subm_conv3d(x, wt, bias, plan, mid_dt, out=y1)
 
-    def step():
+    def two_launches():
         conv()
-        if two:
-            ssc.linear(y1, w2, b2, odt, out=y2)
+        ssc.linear(y1, w2, b2, odt, out=y2)
+
+    def step():
+        if pair is not None:
+            ssc.subm_conv3d_pair(x, packed, bias, plan, pair, b2, odt, out=y2)
+        elif two:
+            two_launches()
+        else:
+            conv()
 
     for _ in range(args.warmup):
         step()
@@ -699,11 +729,22 @@ def main():
     win = Windows(torch, step, args.steps)
     t_wall = time.perf_counter() - t_wall
     st = win.summary(win.step_ms)
-    # Two layers: the k=3 kernel's time comes from windows of the k=3 layer alone, run back to
-    # back on the same inputs (events between the layers would lengthen what they bracket).
-    kwin = Windows(torch, conv, args.steps) if two else win
+    # The dominant kernel's time: the step itself for one layer or the pair kernel (same
+    # windows); for two launches, windows of the k=3 layer alone on the same inputs (events
+    # between the layers would lengthen what they bracket).
+    kwin = Windows(torch, conv, args.steps) if two and pair is None else win
     kt = kwin.summary(kwin.step_ms)
     ms_step, ms_kernel = st["median"], kt["median"]
+    two_launch = None
+    if pair is not None:
+        # The same two layers as two launches (k=3 with a bf16 store, then k=1), and the k=3
+        # layer alone, for comparison.
+        w2l = Windows(torch, two_launches, args.steps, min_windows=10, min_s=0.05)
+        w3 = Windows(torch, conv, args.steps, min_windows=10, min_s=0.05)
+        two_launch = {"step_us": round(float(np.median(w2l.step_ms)) * 1e3, 2),
+                      "k3_us": round(float(np.median(w3.step_ms)) * 1e3, 2)}
+        log(f"[bench] pair kernel {ms_step * 1e3:.2f} us; as two launches "
+            f"{two_launch['step_us']} us (k=3 alone {two_launch['k3_us']} us)")
     log(f"[bench] {win.windows} windows of {args.steps} steps ({t_wall:.2f} s wall): step "
         f"median {ms_step * 1e3:.2f} us (p10 {st['p10'] * 1e3:.2f}, p90 {st['p90'] * 1e3:.2f}, "
         f"first window {st['first'] * 1e3:.2f}); k=3 kernel {ms_kernel * 1e3:.2f} us")
@@ -774,9 +815,19 @@ def main():
 
     out_bytes = 4 if mid_dt == torch.float32 else 2
     in_bytes = x.element_size()
-    bytes_alg = (w.n * cin * in_bytes + w.n * cout * out_bytes + 27 * cin * cout * in_bytes
-                 + 4 * pairs)
-    flops = 2.0 * pairs * cin * cout
+    # Algorithmic bytes and FLOP of the dominant kernel: X, W and 4 B per valid pair in, Y out
+    # (for the pair kernel: W2 in as well, its output out, the intermediate on chip; FLOP of
+    # both layers).
+    if pair is not None:
+        c2 = w.layers[1].cout
+        out_bytes = 4 if odt == torch.float32 else 2
+        bytes_alg = (w.n * cin * in_bytes + 27 * cin * cout * in_bytes + cout * c2 * in_bytes
+                     + w.n * c2 * out_bytes + 4 * pairs)
+        flops = 2.0 * pairs * cin * cout + 2.0 * w.n * cout * c2
+    else:
+        bytes_alg = (w.n * cin * in_bytes + w.n * cout * out_bytes + 27 * cin * cout * in_bytes
+                     + 4 * pairs)
+        flops = 2.0 * pairs * cin * cout
     achieved_gbs = bytes_alg / (ms_kernel * 1e-3) / 1e9
     tflops_kernel = flops / (ms_kernel * 1e-3) / 1e12
     # The ceiling that binds at the algorithmic level: the matrix cores when the layer's FLOP
@@ -790,10 +841,12 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4)}
-    flops_step = flops + (2.0 * w.n * w.layers[1].cin * w.layers[1].cout if two else 0.0)
+    flops_step = flops + (2.0 * w.n * w.layers[1].cin * w.layers[1].cout
+                          if two and pair is None else 0.0)
     tflops_step = flops_step / (ms_step * 1e-3) / 1e12
     value = mvox_per_s(w.n, ms_step * 1e-3)
-    kname = f"k_subm_lds<{cin},{cout}>" if use_packed else "k_conv_valu"
+    kname = (step_kernel(w.layers)[1] if pair is not None
+             else f"k_subm_lds<{cin},{cout}>" if use_packed else "k_conv_valu")
     digest = source_digest()
     traffic = counted_traffic(kname, digest, args.workload, "f32" if out_bytes == 4 else "bf16")
     roofline.update({"traffic": traffic, "kernel": kname, "bytes_alg_per_launch": bytes_alg,
@@ -823,8 +876,10 @@ def main():
         "timing": {"windows": win.windows, "steps_per_window": args.steps,
                    "step_us": rnd(st), "kernel_us": rnd(kt),
                    "note": "median over windows of back-to-back steps with events only at "
-                           "the window ends; kernel_us: the step itself for one layer (same "
-                           "windows), for two layers windows of the k=3 layer alone"},
+                           "the window ends; kernel_us: the step's dominant kernel, i.e. the "
+                           "step itself for one layer or the fused two-layer kernel (same "
+                           "windows), else windows of the k=3 layer alone"},
+        "two_launch": two_launch,
         "roofline": roofline,
         "mfma": {"effective_tflops_kernel": round(tflops_kernel, 2),
                  "frac_bf16_peak_kernel": round(tflops_kernel / PEAK_BF16_TFLOPS, 5),

@@ -259,8 +259,28 @@ ssc_status ssc_pack_weights(const void* weight, int32_t taps, int32_t cin, int32
  *                  with "--flip-kernel" ("Correctness"): the tap at offset d reads the site
  *                  c - d, i.e. out[i] = bias + sum_t feats[nbr[i][26-t]] @ weight[t]. */
 #define SSC_PACK_FLIP 1
+/*   SSC_PACK_PAIR  taps = 1 only: the k=1 layer of ssc_subm_conv3d_pair_packed (cin = the k=3
+ *                  layer's cout); not combined with SSC_PACK_FLIP. */
+#define SSC_PACK_PAIR 2
 ssc_status ssc_pack_weights_ex(const void* weight, int32_t taps, int32_t cin, int32_t cout,
                                int32_t flags, void* packed, size_t packed_bytes, void* stream);
+
+/* A k=3 layer followed by a k=1 layer in one kernel (the two-layer stack of the benchmark's
+ * batched workload; LATO.2 page, "Status": SubMConv3d k=3 and k=1):
+ *   out = (bf16(conv(feats) + bias1)) @ W2 + bias2
+ * where bf16() is the round to nearest even that ssc_subm_conv3d_packed applies when it
+ * stores bf16, so the result is that of the two calls (conv with out_dtype SSC_BF16, then
+ * ssc_linear on its output) without the intermediate ever reaching memory.
+ *   feats [n, cin] bf16; packed1 from ssc_pack_weights (taps = 27, cin -> cmid); packed2 from
+ *   ssc_pack_weights_ex (taps = 1, cmid -> cout, SSC_PACK_PAIR); bias1 [cmid], bias2 [cout]
+ *   fp32 or NULL; plan from ssc_build_plan; out [n, cout] in out_dtype (SSC_F32 or SSC_BF16).
+ * Shapes (cin, cmid, cout): (32 | 64 | 128, 64, 64), (64 | 128, 128, 64 | 128); otherwise
+ * SSC_ERR_UNSUPPORTED.  Other errors as for ssc_subm_conv3d_packed. */
+ssc_status ssc_subm_conv3d_pair_packed(const void* feats, const void* packed1,
+                                       const float* bias1, const void* plan, int64_t n,
+                                       int32_t cin, int32_t cmid, const void* packed2,
+                                       const float* bias2, int32_t cout, void* out,
+                                       int32_t out_dtype, void* stream);
 
 /* ssc_subm_conv3d_plan with weights from ssc_pack_weights (taps = 27): one kernel launch, no
  * workspace.  Same results, bit for bit, as ssc_subm_conv3d_plan on the unpacked weights.

@@ -39,6 +39,7 @@ _LIB_PATH = os.path.join(_PKG, "libssc.so")
 SSC_OK, SSC_ERR_ARG, SSC_ERR_COORD_RANGE, SSC_ERR_DUPLICATE = 0, -1, -2, -3
 SSC_ERR_UNSUPPORTED, SSC_ERR_WORKSPACE, SSC_ERR_HIP = -4, -5, -6
 SSC_F32, SSC_BF16, SSC_F16 = 0, 1, 2
+SSC_PACK_FLIP, SSC_PACK_PAIR = 1, 2
 ACTS = {"none": 0, "relu": 1, "silu": 2}
 GN_MAX_BATCH = 64
 
@@ -120,6 +121,8 @@ def load_library():
         "ssc_subm_conv3d_packed_ex": ([p, p, p, p, i64, i32, i32, p, i32, p, p], ctypes.c_int),
         "ssc_linear_ex": ([p, i32, p, p, i64, i32, i32, p, i32, p, p, sz, p], ctypes.c_int),
         "ssc_linear_packed": ([p, p, p, i64, i32, i32, p, i32, p], ctypes.c_int),
+        "ssc_subm_conv3d_pair_packed": ([p, p, p, p, i64, i32, i32, p, p, i32, p, i32, p],
+                                        ctypes.c_int),
         "ssc_linear_packed_ex": ([p, p, p, i64, i32, i32, p, i32, p, p], ctypes.c_int),
         "ssc_gn_partials_bytes": ([i64, i32, i32], sz),
         "ssc_gn_partials": ([p, i32, i64, i32, p, i32, i32, p, sz, p], ctypes.c_int),
@@ -619,16 +622,18 @@ def subdivide2(coords: torch.Tensor, grid: Sequence[int], feats: Optional[torch.
 
 
 class PackedWeight:
-    """A layer's [taps, Cin, Cout] bf16 weights re-laid out once for the matrix cores."""
+    """A layer's [taps, Cin, Cout] bf16 weights re-laid out once for the matrix cores (pair:
+    packed as the k=1 layer of subm_conv3d_pair)."""
 
-    def __init__(self, buf: torch.Tensor, taps: int, cin: int, cout: int):
-        self.buf, self.taps, self.cin, self.cout = buf, taps, cin, cout
+    def __init__(self, buf: torch.Tensor, taps: int, cin: int, cout: int, pair: bool = False):
+        self.buf, self.taps, self.cin, self.cout, self.pair = buf, taps, cin, cout, pair
 
 
-def pack_weights(weight: torch.Tensor, flip: bool = False) -> PackedWeight:
+def pack_weights(weight: torch.Tensor, flip: bool = False, pair: bool = False) -> PackedWeight:
     """Re-lay out bf16 weights once: [27, Cin, Cout] for subm_conv3d_packed, [Cin, Cout] or
     [1, Cin, Cout] for linear.  flip=True packs the other kernel orientation (tap at offset d
-    reads site c - d; nothing changes for a single tap)."""
+    reads site c - d; nothing changes for a single tap).  pair=True packs a single-tap weight
+    as the k=1 layer of subm_conv3d_pair."""
     _need_cuda(weight, "weight")
     if weight.dtype != torch.bfloat16:
         raise ValueError("pack_weights takes bfloat16 weights")
@@ -638,10 +643,48 @@ def pack_weights(weight: torch.Tensor, flip: bool = False) -> PackedWeight:
     dev = weight.device
     buf = _workspace(lib.ssc_packed_weight_bytes(taps, cin, cout), dev)
     with torch.cuda.device(dev):
-        st = lib.ssc_pack_weights_ex(_ptr(weight), taps, cin, cout, 1 if flip else 0, _ptr(buf),
-                                     buf.numel(), _stream(dev))
+        st = lib.ssc_pack_weights_ex(_ptr(weight), taps, cin, cout,
+                                     (SSC_PACK_FLIP if flip else 0) | (SSC_PACK_PAIR if pair else 0),
+                                     _ptr(buf), buf.numel(), _stream(dev))
     _check(st, "ssc_pack_weights")
-    return PackedWeight(buf, taps, cin, cout)
+    return PackedWeight(buf, taps, cin, cout, pair)
+
+
+def subm_conv3d_pair(x: torch.Tensor, packed1: PackedWeight, bias1: Optional[torch.Tensor],
+                     plan: Plan, packed2: PackedWeight, bias2: Optional[torch.Tensor],
+                     out_dtype: Optional[torch.dtype] = None,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A k=3 layer and the k=1 layer after it in one kernel: the result of subm_conv3d_packed
+    with a bf16 output followed by linear, the intermediate never written (packed2 from
+    pack_weights(w2, pair=True))."""
+    _need_cuda(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != packed1.cin:
+        raise ValueError("x must be bfloat16 [N, Cin] matching packed1")
+    if packed1.taps != TAPS or packed2.taps != 1 or not packed2.pair:
+        raise ValueError("packed1 must be a 27-tap weight, packed2 a pair=True single-tap one")
+    if packed2.cin != packed1.cout:
+        raise ValueError("packed2's inputs must be packed1's outputs")
+    n = x.shape[0]
+    if plan.n != n:
+        raise ValueError(f"plan is for {plan.n} sites, x has {n}")
+    for b, c, name in ((bias1, packed1.cout, "bias1"), (bias2, packed2.cout, "bias2")):
+        if b is not None:
+            _need_cuda(b, name)
+            if b.dtype != torch.float32 or b.numel() != c:
+                raise ValueError(f"{name} must be float32 [{c}]")
+    odt = torch.float32 if out_dtype is None else out_dtype
+    dout = _dtype_code(odt, "out_dtype")
+    lib = load_library()
+    dev = x.device
+    if out is None:
+        out = torch.empty((n, packed2.cout), dtype=odt, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.ssc_subm_conv3d_pair_packed(_ptr(x), _ptr(packed1.buf), _ptr(bias1),
+                                             _ptr(plan.buf), n, packed1.cin, packed1.cout,
+                                             _ptr(packed2.buf), _ptr(bias2), packed2.cout,
+                                             _ptr(out), dout, _stream(dev))
+    _check(st, "ssc_subm_conv3d_pair_packed")
+    return out
 
 
 def subm_conv3d_packed(x: torch.Tensor, packed: PackedWeight, bias: Optional[torch.Tensor],

@@ -330,6 +330,13 @@ struct Epi {
   int64_t rows;      // n: plan rows at or past it are padding (they sort last)
   int act;           // SSC_ACT_*
   int gn_groups;     // with gn: groups of cout / gn_groups channels, a power of two <= 16
+  // The k=1 layer a pair kernel (C2 > 0) applies to its 16-bit k=3 output: packed weights
+  // (the conv's column groups, one tap), fp32 bias or null, output [n, C2], and whether that
+  // output is fp32 (else the input's 16-bit type).
+  const uint16_t* w2;
+  const float* b2;
+  void* y2;
+  int y2_f32;
 };
 
 // One value of the output's own type (a residual element, here read where it is staged).
@@ -344,8 +351,11 @@ __device__ __forceinline__ float load_out(const void* p, int64_t i) {
 // EPI = false is the plain convolution (bias only); EPI = true adds the activation, the
 // residual and the group-norm statistics as the Epi arguments ask.  WIDE = true runs a layer
 // wider than the tile (kch input chunks, gridDim.y output tiles); WIDE = false compiles the
-// single chunk and tile in.
-template <int CIN, int COUT, int NB, int WR, int WC, bool OUT16, int EK, bool EPI, bool WIDE>
+// single chunk and tile in.  C2 > 0 makes a pair kernel: the plain convolution's output,
+// rounded to the 16-bit type as a store would round it, stays in LDS and a k=1 layer of C2
+// outputs (Epi w2, b2, y2) is applied to it; only that layer's output is written.
+template <int CIN, int COUT, int NB, int WR, int WC, bool OUT16, int EK, bool EPI, bool WIDE,
+          int C2 = 0>
 __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
     const float* __restrict__ bias, const int32_t* __restrict__ perm,
@@ -434,6 +444,27 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
 #pragma unroll
     for (int i = 0; i < 4; ++i)  // bias needs only 4-byte alignment: scalar loads
       bv[c][i] = bias ? bias[ct * COUT + wc * C::CS + c * 16 + 4 * (lane >> 4) + i] : 0.f;
+  // Pair kernels: the k=1 layer's weight fragments (its COUT inputs in KS2 k-steps, this
+  // wave's NCT2 16-column tiles of its C2 outputs) and bias, loaded with the prologue.
+  constexpr int NCT2 = C2 > 0 ? C2 / WC / 16 : 1;
+  constexpr int KS2 = COUT / 32;
+  bf16x8_t bw2[NCT2][KS2];
+  f32x4_t bv2[NCT2];
+  if constexpr (C2 > 0) {
+    static_assert(OUT16 && !EPI && !WIDE && C2 % (16 * WC) == 0, "pair kernel shape");
+    const uint16_t* w2 = ep.w2 + wc * (NCT2 * KS2 * 512) + lane * 8;
+#pragma unroll
+    for (int c = 0; c < NCT2; ++c)
+#pragma unroll
+      for (int s2 = 0; s2 < KS2; ++s2)
+        bw2[c][s2] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(w2 + (c * KS2 + s2) * 512));
+#pragma unroll
+    for (int c = 0; c < NCT2; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bv2[c][i] = ep.b2 ? ep.b2[wc * (C2 / WC) + c * 16 + 4 * (lane >> 4) + i] : 0.f;
+  }
   wait_vm_lgkm0();
   __builtin_amdgcn_s_barrier();
 
@@ -668,7 +699,110 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
   using A2 = std::integral_constant<int, SSC_ACT_SILU>;
   using T_ = std::true_type;
   using F_ = std::false_type;
-  if constexpr (!EPI) {
+  if constexpr (C2 > 0) {
+    static_assert(BPP == NB, "the pair's intermediate tile stays in LDS whole");
+    // 1. The convolution's tile plus bias, rounded to the 16-bit type (the value its 16-bit
+    //    store would hold), into the staging tile: rows of COUT channels, 16-byte chunks
+    //    swizzled by row.
+#pragma unroll
+    for (int bl = 0; bl < C::BPW; ++bl) {
+      const int b = bl * WR + wr;
+#pragma unroll
+      for (int c = 0; c < C::NCT; ++c) {
+        const int col = wc * C::CS + c * 16 + 4 * (lane >> 4);
+        const int row = b * 16 + (lane & 15);
+        const int byte = col * 2;
+        uint16_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = to16<EK>(acc[bl][c][i] + bv[c][i]);
+        *reinterpret_cast<uint2*>(sOut + row * ROWB + (((byte >> 4) ^ (row & SWM)) << 4) +
+                                  (byte & 15)) =
+            make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16),
+                       h[2] | (static_cast<uint32_t>(h[3]) << 16));
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_s_barrier();
+    // 2. The k=1 layer on the staged rows, the same transposed product as the convolution's
+    //    (lane l: row l & 15, its k-values at chunk (l >> 4) + 4 s).
+    f32x4_t acc2[C::BPW][NCT2];
+#pragma unroll
+    for (int bl = 0; bl < C::BPW; ++bl) {
+      const int row = (bl * WR + wr) * 16 + (lane & 15);
+      bf16x8_t a2[KS2];
+#pragma unroll
+      for (int s2 = 0; s2 < KS2; ++s2)
+        a2[s2] = lds_read16(sOut + row * ROWB + ((((lane >> 4) + 4 * s2) ^ (row & SWM)) << 4));
+#pragma unroll
+      for (int c = 0; c < NCT2; ++c) {
+        acc2[bl][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < KS2; ++s2)
+          acc2[bl][c] = mfma16x16x32<EK>(bw2[c][s2], a2[s2], acc2[bl][c]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();  // every wave is done reading the intermediate tile
+    // 3. The k=1 output (plus its bias), staged and written as whole rows like the
+    //    convolution's, BPP2 blocks per pass.
+    auto store2 = [&](auto f32_c) __attribute__((always_inline)) {
+      constexpr bool F32 = decltype(f32_c)::value;
+      constexpr int ROWB2 = C2 * (F32 ? 4 : 2);
+      constexpr int CHUNKS2 = ROWB2 / 16;
+      constexpr int SWM2 = (CHUNKS2 < 16 ? CHUNKS2 : 16) - 1;
+      constexpr int RAW2 = C::STAGE_BYTES / (16 * ROWB2);
+      constexpr int BPP2 = RAW2 >= NB ? NB : RAW2 >= 8 ? 8 : RAW2 >= 4 ? 4 : RAW2 >= 2 ? 2 : 1;
+      static_assert(RAW2 >= 1 && NB % BPP2 == 0 && BPP2 * 16 * ROWB2 <= C::STAGE_BYTES,
+                    "pair output staging");
+      char* y2 = static_cast<char*>(ep.y2);
+#pragma unroll
+      for (int p0 = 0; p0 < NB; p0 += BPP2) {
+#pragma unroll
+        for (int bl = 0; bl < C::BPW; ++bl) {
+          const int b = bl * WR + wr;
+          if (b < p0 || b >= p0 + BPP2) continue;
+#pragma unroll
+          for (int c = 0; c < NCT2; ++c) {
+            const int col = wc * (C2 / WC) + c * 16 + 4 * (lane >> 4);
+            const int row = (b - p0) * 16 + (lane & 15);
+            const int byte = col * (F32 ? 4 : 2);
+            char* dst = sOut + row * ROWB2 + (((byte >> 4) ^ (row & SWM2)) << 4) + (byte & 15);
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc2[bl][c][i] + bv2[c][i];
+            if constexpr (F32) {
+              *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v[0], v[1], v[2], v[3]};
+            } else {
+              *reinterpret_cast<uint2*>(dst) =
+                  make_uint2(to16<EK>(v[0]) | (static_cast<uint32_t>(to16<EK>(v[1])) << 16),
+                             to16<EK>(v[2]) | (static_cast<uint32_t>(to16<EK>(v[3])) << 16));
+            }
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        constexpr int PIECES2 = BPP2 * 16 * CHUNKS2;
+#pragma unroll 4
+        for (int idx = threadIdx.x; idx < PIECES2; idx += C::THREADS) {
+          const int row = idx / CHUNKS2, ch = idx % CHUNKS2;
+          const int32_t o = sP[p0 * 16 + row];
+          if (o < 0) continue;
+          const u32x4_t v =
+              *reinterpret_cast<const u32x4_t*>(sOut + row * ROWB2 + ((ch ^ (row & SWM2)) << 4));
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<u32x4_t*>(y2 + static_cast<int64_t>(o) * ROWB2 + ch * 16));
+        }
+        if (p0 + BPP2 < NB) {
+          wait_vm_lgkm0();
+          __builtin_amdgcn_s_barrier();
+        }
+      }
+    };
+    if (ep.y2_f32)
+      store2(T_{});
+    else
+      store2(F_{});
+  } else if constexpr (!EPI) {
     epilogue(A0{}, F_{}, F_{});
   } else {
     switch (ep.act * 4 + (ep.res ? 2 : 0) + (ep.gn ? 1 : 0)) {
@@ -1103,6 +1237,30 @@ LdsFn pick_lds(int cin, int cout, bool out16, int ek, int* threads, int* rows_pe
   return nullptr;
 }
 
+// Pair kernels (k=3 cin -> cmid, then k=1 cmid -> c2, bf16): the shapes whose 16-bit
+// intermediate tile fits the conv kernel's staging space and whose k=1 outputs divide into
+// the conv's column groups.
+template <int CI, int CM, int CO>
+LdsFn pair_fn() {
+  using P = LdsPick<CI, CM>;
+  return k_subm_lds<CI, CM, P::NB, P::WR, P::WC, true, 0, false, false, CO>;
+}
+
+LdsFn pick_pair(int cin, int cmid, int c2, int* threads, int* rows_per_tile, int* wc_groups) {
+#define SSC_PAIR(CI, CM, CO)                                                         \
+  if (cin == CI && cmid == CM && c2 == CO) {                                         \
+    using P = LdsPick<CI, CM>;                                                       \
+    *threads = P::WR * P::WC * 64;                                                   \
+    *rows_per_tile = P::NB * 16;                                                     \
+    *wc_groups = P::WC;                                                              \
+    return pair_fn<CI, CM, CO>();                                                    \
+  }
+  SSC_PAIR(32, 64, 64) SSC_PAIR(64, 64, 64) SSC_PAIR(128, 64, 64)
+  SSC_PAIR(64, 128, 64) SSC_PAIR(64, 128, 128) SSC_PAIR(128, 128, 64) SSC_PAIR(128, 128, 128)
+#undef SSC_PAIR
+  return nullptr;
+}
+
 bool valid_dtype(int d) { return d == SSC_F32 || d == SSC_BF16 || d == SSC_F16; }
 
 // Element kind of a 16-bit feature type for the matrix-core kernels (-1: none).
@@ -1160,7 +1318,7 @@ ssc_status launch_lds(LdsFn fn, int threads, int rows_per_tile, const void* feat
 // Host checks of an epilogue; fills the kernel-side arguments (gn left null: the caller
 // decides whether the kernel sums the statistics itself).
 ssc_status check_epilogue(const ssc_epilogue* e, int64_t n, int cout, Epi* ep) {
-  *ep = Epi{nullptr, nullptr, n, SSC_ACT_NONE, 0};
+  *ep = Epi{nullptr, nullptr, n, SSC_ACT_NONE, 0, nullptr, nullptr, nullptr, 0};
   if (e == nullptr) return SSC_OK;
   if (e->act < SSC_ACT_NONE || e->act > SSC_ACT_SILU || e->reserved != 0) return SSC_ERR_ARG;
   if (e->residual && !aligned(e->residual, 16)) return SSC_ERR_ARG;
@@ -1444,10 +1602,19 @@ extern "C" ssc_status ssc_pack_weights_ex(const void* weight, int32_t taps, int3
                                           int32_t cout, int32_t flags, void* packed,
                                           size_t packed_bytes, void* stream) {
   if (weight == nullptr || packed == nullptr) return SSC_ERR_ARG;
-  if (flags & ~SSC_PACK_FLIP) return SSC_ERR_ARG;
+  if ((flags & ~(SSC_PACK_FLIP | SSC_PACK_PAIR)) ||
+      ((flags & SSC_PACK_PAIR) && (taps != 1 || (flags & SSC_PACK_FLIP))))
+    return SSC_ERR_ARG;
   int threads = 0, rows = 0, wcg = 0;
   int ck = 0, cot = 0;
-  if (taps == kTaps) {
+  if (flags & SSC_PACK_PAIR) {
+    // The k=1 layer (cin -> cout) of a pair kernel, in the column groups of the k=3 layer
+    // before it (whose output width is this layer's cin).
+    bool any = false;
+    for (const int ci : {32, 64, 128})
+      any = any || pick_pair(ci, cin, cout, &threads, &rows, &wcg) != nullptr;
+    if (!any) return SSC_ERR_UNSUPPORTED;
+  } else if (taps == kTaps) {
     if (pick_lds(cin, cout, false, 0, &threads, &rows, &wcg, false, &ck, &cot) == nullptr)
       return SSC_ERR_UNSUPPORTED;
   } else if (taps == 1) {
@@ -1500,6 +1667,31 @@ extern "C" ssc_status ssc_linear_packed_ex(const void* feats, const void* packed
       st != SSC_OK)
     return st;
   return gn_after(epilogue, false, out, out_dtype, n, cout, s);
+}
+
+extern "C" ssc_status ssc_subm_conv3d_pair_packed(const void* feats, const void* packed1,
+                                                  const float* bias1, const void* plan,
+                                                  int64_t n, int32_t cin, int32_t cmid,
+                                                  const void* packed2, const float* bias2,
+                                                  int32_t cout, void* out, int32_t out_dtype,
+                                                  void* stream) {
+  if (n < 0 || !valid_dtype(out_dtype) || packed1 == nullptr || packed2 == nullptr ||
+      plan == nullptr)
+    return SSC_ERR_ARG;
+  if (n >= (int64_t(1) << 31) || out_dtype == SSC_F16) return SSC_ERR_UNSUPPORTED;
+  int threads = 0, rows = 0, wcg = 0;
+  LdsFn fn = pick_pair(cin, cmid, cout, &threads, &rows, &wcg);
+  if (fn == nullptr) return SSC_ERR_UNSUPPORTED;
+  if (n > 0 && (feats == nullptr || out == nullptr)) return SSC_ERR_ARG;
+  if (!aligned(packed1, 16) || !aligned(packed2, 16) || !aligned(plan, kAlign) ||
+      (n > 0 && (!aligned(feats, 16) || !aligned(out, 16))) || (bias1 && !aligned(bias1, 4)) ||
+      (bias2 && !aligned(bias2, 4)))
+    return SSC_ERR_ARG;
+  if (n == 0) return SSC_OK;
+  const Epi ep{nullptr, nullptr, n, SSC_ACT_NONE, 0, static_cast<const uint16_t*>(packed2),
+               bias2, out, out_dtype == SSC_F32 ? 1 : 0};
+  return launch_lds(fn, threads, rows, feats, static_cast<const uint16_t*>(packed1), bias1, plan,
+                    n, nullptr, ep, as_stream(stream));
 }
 
 extern "C" ssc_status ssc_subm_conv3d_packed(const void* feats, const void* packed_weight,

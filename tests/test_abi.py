@@ -218,6 +218,29 @@ def test_pack_weights_argument_errors(lib):
     assert f(FAKE, 27, 48, 128, 0, FAKE, big, None) == ssc.SSC_ERR_UNSUPPORTED  # no MFMA shape
     assert f(FAKE, 27, 128, 128, 1, FAKE, 100, None) == ssc.SSC_ERR_WORKSPACE
     assert lib.ssc_packed_weight_bytes(27, 128, 128) >= 27 * 128 * 128 * 2
+    # SSC_PACK_PAIR: single-tap only, not with FLIP, pair shapes only
+    assert f(FAKE, 27, 128, 128, ssc.SSC_PACK_PAIR, FAKE, big, None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 1, 128, 128, ssc.SSC_PACK_PAIR | ssc.SSC_PACK_FLIP, FAKE, big,
+             None) == ssc.SSC_ERR_ARG
+    assert f(FAKE, 1, 128, 32, ssc.SSC_PACK_PAIR, FAKE, big, None) == ssc.SSC_ERR_UNSUPPORTED
+    assert f(FAKE, 1, 32, 32, ssc.SSC_PACK_PAIR, FAKE, big, None) == ssc.SSC_ERR_UNSUPPORTED
+    assert f(FAKE, 1, 128, 128, ssc.SSC_PACK_PAIR, FAKE, 100, None) == ssc.SSC_ERR_WORKSPACE
+    pp = lib.ssc_subm_conv3d_pair_packed
+    # (feats, packed1, bias1, plan, n, cin, cmid, packed2, bias2, cout, out, out_dtype, stream)
+    assert pp(FAKE, FAKE, None, FAKE, 0, 64, 128, FAKE, None, 128, FAKE, ssc.SSC_F32,
+              None) == ssc.SSC_OK
+    assert pp(FAKE, FAKE, None, FAKE, 10, 32, 128, FAKE, None, 128, FAKE, ssc.SSC_F32,
+              None) == ssc.SSC_ERR_UNSUPPORTED                          # intermediate too wide
+    assert pp(FAKE, FAKE, None, FAKE, 10, 64, 128, FAKE, None, 32, FAKE, ssc.SSC_F32,
+              None) == ssc.SSC_ERR_UNSUPPORTED
+    assert pp(FAKE, FAKE, None, FAKE, 10, 64, 128, FAKE, None, 128, FAKE, ssc.SSC_F16,
+              None) == ssc.SSC_ERR_UNSUPPORTED
+    assert pp(FAKE, None, None, FAKE, 10, 64, 128, FAKE, None, 128, FAKE, ssc.SSC_F32,
+              None) == ssc.SSC_ERR_ARG
+    assert pp(None, FAKE, None, FAKE, 10, 64, 128, FAKE, None, 128, FAKE, ssc.SSC_F32,
+              None) == ssc.SSC_ERR_ARG
+    assert pp(FAKE, FAKE, None, FAKE, 10, 64, 128, FAKE, ctypes.c_void_p((1 << 20) + 2), 128,
+              FAKE, ssc.SSC_F32, None) == ssc.SSC_ERR_ARG                # misaligned bias2
     h = lib.ssc_linear_packed
     assert h(FAKE, FAKE, None, 0, 128, 128, FAKE, ssc.SSC_F32, None) == ssc.SSC_OK
     assert h(FAKE, FAKE, None, 10, 48, 48, FAKE, ssc.SSC_F32, None) == ssc.SSC_ERR_UNSUPPORTED

@@ -153,6 +153,45 @@ def test_wide_layers(cin, cout, dtype):
         assert rel_err(yf.cpu().numpy(), ref) <= TAU_ACC
 
 
+@pytest.mark.parametrize("cin,cmid,cout,odt,frac", [
+    (64, 128, 128, torch.float32, 0.3), (64, 128, 128, torch.bfloat16, 0.3),
+    (128, 128, 64, torch.float32, 0.5), (128, 128, 128, torch.bfloat16, 0.05),
+    (32, 64, 64, torch.float32, 0.3), (64, 64, 64, torch.bfloat16, 0.3),
+    (128, 64, 64, torch.float32, 0.001)])
+def test_pair_equals_two_layers(cin, cmid, cout, odt, frac):
+    """The fused k=3 -> k=1 kernel against the two calls it replaces (the conv stored as bf16,
+    then the k=1 layer) and against the oracle's k=1 layer applied to that bf16 intermediate
+    (16-bit products are exact in fp32, so the fp32 result is within TAU_ACC); a bf16 output
+    is the RNE of the fp32 one, bit for bit."""
+    say(f"[parity] pair {cin}->{cmid}->{cout} {odt} occupancy {frac}")
+    grid = (15, 14, 13)
+    coords, x, w, b = small_case(cin + 3 * cmid + cout, 1, grid, frac, cin, cmid)
+    rng = np.random.default_rng(cout + 11)
+    w2 = (torch.from_numpy(rng.standard_normal((cmid, cout), dtype=np.float32))
+          / np.sqrt(cmid)).to(torch.bfloat16)
+    b2 = torch.from_numpy(rng.standard_normal(cout, dtype=np.float32))
+    idx = run_gpu(coords, 1, grid)
+    xd, wd, bd, w2d, b2d = x.to(DEV), w.to(DEV), b.to(DEV), w2.to(DEV), b2.to(DEV)
+    pk1, pk2 = ssc.pack_weights(wd), ssc.pack_weights(w2d, pair=True)
+    mid = ssc.subm_conv3d_packed(xd, pk1, bd, idx.plan, torch.bfloat16)
+    two = ssc.linear(mid, w2d, b2d, torch.float32)
+    f32 = ssc.subm_conv3d_pair(xd, pk1, bd, idx.plan, pk2, b2d, torch.float32)
+    ref = oracle.linear(mid.float().cpu().numpy(), w2.float().numpy(), b2.numpy())
+    err = rel_err(f32.cpu().numpy(), ref)
+    diff = rel_err(f32.cpu().numpy(), two.cpu().numpy().astype(np.float64))
+    say(f"[parity]   vs oracle k=1 {err:.3e}, vs the two calls {diff:.3e}, bit-identical "
+        f"{bool(torch.equal(f32.view(torch.int32), two.view(torch.int32)))}")
+    assert err <= TAU_ACC and diff <= TAU_ACC
+    if odt != torch.float32:
+        y = ssc.subm_conv3d_pair(xd, pk1, bd, idx.plan, pk2, b2d, odt)
+        assert torch.equal(y.cpu().view(torch.int16), f32.cpu().to(odt).view(torch.int16))
+    # no biases
+    f0 = ssc.subm_conv3d_pair(xd, pk1, None, idx.plan, pk2, None, torch.float32)
+    mid0 = ssc.subm_conv3d_packed(xd, pk1, None, idx.plan, torch.bfloat16)
+    ref0 = oracle.linear(mid0.float().cpu().numpy(), w2.float().numpy(), None)
+    assert rel_err(f0.cpu().numpy(), ref0) <= TAU_ACC
+
+
 @pytest.mark.parametrize("cin,cout", [(c, o) for c in (32, 64, 128) for o in (16, 32, 64, 128)])
 def test_mfma_shapes_ragged(cin, cout):
     # ~1500 sites: several 128-row tiles and a ragged last tile
