@@ -67,6 +67,8 @@ __device__ __forceinline__ bool in_range(int4 c, int batch, int gx, int gy, int 
 }
 
 // Also sets fill[0, fill_count) to -1 when fill is given (a table the caller fills next).
+// counters[0, 3) are cleared: out-of-range sites, duplicates, and a flag the index's row pass
+// sets when the sites are not in key order.
 __global__ void k_dense_clear(uint64_t* __restrict__ bits, uint64_t words,
                               uint32_t* __restrict__ counters, int32_t* __restrict__ fill,
                               int64_t fill_count) {
@@ -78,7 +80,7 @@ __global__ void k_dense_clear(uint64_t* __restrict__ bits, uint64_t words,
     for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
          i < static_cast<uint64_t>(fill_count); i += stride)
       fill[i] = -1;
-  if (blockIdx.x == 0 && threadIdx.x < 2) counters[threadIdx.x] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < 3) counters[threadIdx.x] = 0;
 }
 
 // Sites outside [0, batch) x (gx, gy, gz) count in counters[0] and mark nothing; the bit of a

@@ -163,7 +163,8 @@ struct DenseIndexLayout {
   size_t off_rows, total;
 };
 
-// [0, 256): two uint32 error counters; the bitmap structure; the rows in key order.
+// [0, 256): two uint32 error counters and the "sites not in key order" flag; the bitmap
+// structure; the rows in key order.
 inline DenseIndexLayout dense_index_layout(int64_t n, uint64_t voxels) {
   DenseIndexLayout L;
   L.b = dense_bits_layout(voxels, kAlign);
@@ -172,20 +173,30 @@ inline DenseIndexLayout dense_index_layout(int64_t n, uint64_t voxels) {
   return L;
 }
 
+// rows[rank of site i] = i.  *unsorted becomes 1 if any site's rank differs from its row (the
+// sites are not in ascending key order, or some are out of range); the query then maps ranks
+// through rows, else a rank is the row itself.  One store per wave at most.
 __global__ void k_dense_rows(const int4* __restrict__ coords, int64_t n, int batch, int gx,
                              int gy, int gz, const uint64_t* __restrict__ bits,
                              const uint16_t* __restrict__ local,
                              const uint32_t* __restrict__ super_count,
-                             int32_t* __restrict__ rows) {
+                             int32_t* __restrict__ rows, uint32_t* __restrict__ unsorted) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  bool moved = false;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += stride) {
     const int4 c = coords[i];
-    if (!in_range(c, batch, gx, gy, gz)) continue;
+    if (!in_range(c, batch, gx, gy, gz)) {
+      moved = true;
+      continue;
+    }
     const uint64_t v = dense_id(c.x, c.y, c.z, c.w, gx, gy, gz);
     // rank < number of set bits <= n, so the write stays inside rows[0, n)
-    rows[dense_rank(local, super_count, v, bits[v >> 6])] = static_cast<int32_t>(i);
+    const uint32_t r = dense_rank(local, super_count, v, bits[v >> 6]);
+    rows[r] = static_cast<int32_t>(i);
+    moved = moved || static_cast<int64_t>(r) != i;
   }
+  if (__ballot(moved) != 0ull && (threadIdx.x & 63) == 0) *unsorted = 1u;
 }
 
 // One thread per site (256 sites per workgroup): for each (dx, dy) one bitmap word serves the
@@ -198,8 +209,9 @@ __global__ __launch_bounds__(kQuerySites) void k_dense_query(
     const int4* __restrict__ coords, int64_t n, int batch, int gx, int gy, int gz,
     const uint64_t* __restrict__ bits, const uint16_t* __restrict__ local,
     const uint32_t* __restrict__ super_count, const int32_t* __restrict__ rows,
-    int32_t* __restrict__ nbr) {
+    const uint32_t* __restrict__ unsorted, int32_t* __restrict__ nbr) {
   __shared__ int32_t out[kQuerySites * kTaps];
+  const bool in_order = *unsorted == 0u;  // every site's row is its rank
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kQuerySites;
   const int64_t i = i0 + threadIdx.x;
   int32_t* mine = out + threadIdx.x * kTaps;
@@ -224,7 +236,10 @@ __global__ __launch_bounds__(kQuerySites) void k_dense_query(
           if (row_ok && z >= 0 && z < gz) {
             const uint64_t v = vc + static_cast<uint64_t>(z - zc);
             const uint64_t word = (v >> 6) == (vc >> 6) ? word_c : bits[v >> 6];
-            if ((word >> (v & 63)) & 1ull) r = rows[dense_rank(local, super_count, v, word)];
+            if ((word >> (v & 63)) & 1ull) {
+              const uint32_t k = dense_rank(local, super_count, v, word);
+              r = in_order ? static_cast<int32_t>(k) : rows[k];
+            }
           }
           mine[t0 + dz + 1] = r;
         }
@@ -625,9 +640,10 @@ ssc_status build_index_dense(const int4* coords, int64_t n, int32_t batch, const
   const int bs = 256;
   const unsigned site_blocks = static_cast<unsigned>(std::min<int64_t>((n + bs - 1) / bs, 65536));
   k_dense_rows<<<site_blocks, bs, 0, s>>>(coords, n, batch, grid[0], grid[1], grid[2], bits,
-                                          local, sup, rows);
+                                          local, sup, rows, counters + 2);
   k_dense_query<<<static_cast<unsigned>((n + kQuerySites - 1) / kQuerySites), kQuerySites, 0,
-                  s>>>(coords, n, batch, grid[0], grid[1], grid[2], bits, local, sup, rows, nbr);
+                  s>>>(coords, n, batch, grid[0], grid[1], grid[2], bits, local, sup, rows,
+                       counters + 2, nbr);
   return launch_status();
 }
 }  // namespace
