@@ -937,12 +937,21 @@ __global__ __launch_bounds__(256) void k_conv_valu(const T* __restrict__ X, cons
     const int64_t orow = DENSE ? r : perm[r];
     if (orow < 0) continue;
     float acc = 0.f;
-    const int taps = DENSE ? 1 : kTaps;
+    constexpr int taps = DENSE ? 1 : kTaps;
+    // All taps' neighbour rows first (independent loads in flight together), then the taps in
+    // ascending order; the channel loop is unrolled so its loads overlap too (the sum keeps
+    // its order: taps, then channels, ascending).
+    int32_t js[taps];
+#pragma unroll
+    for (int t = 0; t < taps; ++t)
+      js[t] = DENSE ? static_cast<int32_t>(r) : gidx[static_cast<int64_t>(t) * npad + r];
+#pragma unroll
     for (int t = 0; t < taps; ++t) {
-      const int64_t j = DENSE ? r : gidx[static_cast<int64_t>(t) * npad + r];
+      const int64_t j = js[t];
       if (j < 0) continue;
       const T* xr = X + j * cin;
       const T* wt = W + static_cast<int64_t>(t) * cin * cout + o;
+#pragma unroll 8
       for (int c = 0; c < cin; ++c)
         acc = fmaf(load_feat<T>(xr + c), load_feat<T>(wt + static_cast<int64_t>(c) * cout), acc);
     }
