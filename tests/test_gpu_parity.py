@@ -99,6 +99,17 @@ def test_workload_parity(name, shuffle):
         ref_chain = oracle.linear(rne_bf16(torch.from_numpy(ref).float()).float().numpy(),
                                   l2.weight.float().numpy(), l2.bias.numpy())
         assert rel_err(y2.cpu().numpy(), ref_chain) <= TAU[w.dtype]
+        # the launch configuration the benchmark times for the two layers: one fused kernel,
+        # whose bf16 intermediate is the k=3 layer's bf16 store (so ref2 is its exact input)
+        w2 = l2.weight.to(DEV)
+        yp2 = ssc.subm_conv3d_pair(x, ssc.pack_weights(wt), b, idx.plan,
+                                   ssc.pack_weights(w2, pair=True), l2.bias.to(DEV),
+                                   torch.float32)
+        torch.cuda.synchronize()
+        errp = rel_err(yp2.cpu().numpy(), ref2)
+        say(f"[parity] {name} fused pair max|err|/rms = {errp:.3e}")
+        assert errp <= TAU_ACC
+        assert rel_err(yp2.cpu().numpy(), ref_chain) <= TAU[w.dtype]
 
 
 def small_case(seed, batch, grid, frac, cin, cout, dtype=torch.bfloat16, bias=True):
