@@ -289,22 +289,36 @@ __device__ __forceinline__ void a_frag_offsets(int lane, uint32_t (&off)[CIN / 3
   }
 }
 
+// This wave's first block's A fragments of a stage (block wr of the gather buffer at sA).
+// The stage loop reads them right after the barrier that publishes the stage, before it issues
+// the next stage's loads, so they are in registers when the matrix work starts.  (Read inside
+// the stage's first block, the compiler waited for each of them in turn.)
+template <int CIN, int COUT, int NB, int WR, int WC>
+__device__ __forceinline__ void read_first(const char* sA, const uint32_t (&aoff)[CIN / 32],
+                                           int wr, bf16x8_t (&a0)[CIN / 32]) {
+  using C = LdsCfg<CIN, COUT, NB, WR, WC>;
+#pragma unroll
+  for (int s = 0; s < C::KS; ++s) a0[s] = lds_read16(sA + wr * (C::A_BLOCK * 2) + aoff[s]);
+}
+
 // Matrix work of one stage.  The product is computed transposed, D = W^T X^T (the weight
 // fragment as the A operand, the gathered rows as the B operand: the same registers, the
 // roles swapped), so that each lane's four accumulators are four consecutive output channels
 // of one site (lane l: site row l & 15, channels 4 (l >> 4) .. +3 of the 16-column tile), which
 // the epilogue stores as one 16-byte (fp32) or 8-byte (16-bit) piece.  The A fragments of this
 // wave's blocks are read from LDS one block ahead of the MFMAs that use them (register set
-// bl & 1), so the LDS latency of a block hides behind the previous block's matrix work.
+// bl & 1), so the LDS latency of a block hides behind the previous block's matrix work; the
+// first block's (a0) were read by read_first.
 template <int CIN, int COUT, int NB, int WR, int WC, int EK>
 __device__ __forceinline__ void compute_stage(uint32_t act, const char* sA,
                                               const bf16x8_t (&bw)[COUT / WC / 16][CIN / 32],
                                               const uint32_t (&aoff)[CIN / 32], int wr,
+                                              const bf16x8_t (&a0)[CIN / 32],
                                               f32x4_t (&acc)[NB / WR][COUT / WC / 16]) {
   using C = LdsCfg<CIN, COUT, NB, WR, WC>;
   bf16x8_t a[2][C::KS];
 #pragma unroll
-  for (int s = 0; s < C::KS; ++s) a[0][s] = lds_read16(sA + wr * (C::A_BLOCK * 2) + aoff[s]);
+  for (int s = 0; s < C::KS; ++s) a[0][s] = a0[s];
 #pragma unroll
   for (int bl = 0; bl < C::BPW; ++bl) {
     if (bl + 1 < C::BPW) {
@@ -545,27 +559,34 @@ __global__ __launch_bounds__(WR * WC * 64, 2) void k_subm_lds(
     while (true) {
       wait_vm_lgkm0();
       __builtin_amdgcn_s_barrier();
+      // The barrier builtin does not order memory for the compiler: keep the LDS reads below
+      // after it.
+      asm volatile("" ::: "memory");
       int t_next, kc_next, q_next;
       uint32_t act_next;
       next(t_next, kc_next, q_next, act_next);
+      bf16x8_t a0[C::KS];
+      read_first<CIN, COUT, NB, WR, WC>(sA0, aoff, wr, a0);
       if (t_next >= 0) {
         load_weights<CIN, COUT, NB, WR, WC>(t_next * kch + kc_next, Wp, wc, lane, bw1);
         issue_gather<CIN, COUT, NB, WR, WC>(q_next, act_next, X + (WIDE ? kc_next * CIN : 0), xs, zrow, sG,
                                             lds0 + C::OFF_A1, wave, lane);
       }
-      compute_stage<CIN, COUT, NB, WR, WC, EK>(act, sA0, bw0, aoff, wr, acc);
+      compute_stage<CIN, COUT, NB, WR, WC, EK>(act, sA0, bw0, aoff, wr, a0, acc);
       if (t_next < 0) break;
       if (kc_next == 0) rem &= rem - 1;
       t_cur = t_next, kc = kc_next, q = q_next, act = act_next;
       wait_vm_lgkm0();
       __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
       next(t_next, kc_next, q_next, act_next);
+      read_first<CIN, COUT, NB, WR, WC>(sA1, aoff, wr, a0);
       if (t_next >= 0) {
         load_weights<CIN, COUT, NB, WR, WC>(t_next * kch + kc_next, Wp, wc, lane, bw0);
         issue_gather<CIN, COUT, NB, WR, WC>(q_next, act_next, X + (WIDE ? kc_next * CIN : 0), xs, zrow, sG,
                                             lds0, wave, lane);
       }
-      compute_stage<CIN, COUT, NB, WR, WC, EK>(act, sA1, bw1, aoff, wr, acc);
+      compute_stage<CIN, COUT, NB, WR, WC, EK>(act, sA1, bw1, aoff, wr, a0, acc);
       if (t_next < 0) break;
       if (kc_next == 0) rem &= rem - 1;
       t_cur = t_next, kc = kc_next, q = q_next, act = act_next;
