@@ -2,14 +2,19 @@
 // ConvNeXt-style block; LATO.2 MLX port page, "Status": SparseLinear): out = act(X @ W +
 // bias) + residual for 16-bit X [n, cin] and W, fp32 accumulation on the matrix cores.
 //
-// A workgroup owns 128 rows x 64 columns; its 4 waves own 32 rows each and all 64 columns
-// (128-column tiles need 238 VGPRs, 2 waves per SIMD, and ran 10-20% slower).  For Cin of 192
-// and more the K loop runs in stages of 64: the rows' next stage is loaded into registers
-// while the matrix cores consume this one from LDS (16-byte chunks XOR-swizzled by row), then
-// written to the other LDS buffer; the weight fragments (packed per 16-column tile, 1 KB per
-// fragment) go straight from global memory (L2-resident) into VGPRs, one stage ahead.  Cin of
-// 64 and 128 takes a one-pass kernel (k_gemm_rows_narrow).  Rows past n are read as row n-1
-// and never stored.
+// A workgroup owns 128 rows x 64 columns (128-column tiles need 238 VGPRs, 2 waves per SIMD,
+// and ran 10-20% slower).  For Cin of 192 and more the K loop runs in stages of 64: the rows'
+// next stage is loaded into registers while the matrix cores consume this one from LDS
+// (16-byte chunks XOR-swizzled by row), then written to the other LDS buffer; the weight
+// fragments (packed per 16-column tile, 1 KB per fragment) go straight from global memory
+// (L2-resident) into VGPRs, one stage ahead.  Each of the 4 waves owns one 16-column tile for
+// all 128 rows, so every weight fragment is loaded once per workgroup; with 32 rows x 64
+// columns per wave the 4 waves loaded the same fragments, twice the rows' bytes per stage
+// (512 -> 128 + skip at 209K rows: 84.7 -> 73.7 us, bit-identical).  Cin of 64 and 128 takes a
+// one-pass kernel (k_gemm_rows_narrow), whose waves keep 32 rows x 64 columns: with all of K
+// at once, reading every row fragment four times from LDS cost more than the shared weight
+// loads saved (128 -> 512 + silu: 86.4 against 81.9 us).  Rows past n are read as row n-1 and
+// never stored.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -55,12 +60,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict
                                                       const float* __restrict__ bias, int64_t n,
                                                       int cin, int cout, void* Y, int act,
                                                       const void* res, int64_t row_tiles) {
-  constexpr int NCT = CT / 16;  // 16-column tiles (every wave has all of them)
+  constexpr int NCT = CT / 16;  // 16-column tiles, one per wave
+  static_assert(NCT == 4, "one 16-column tile per wave");
   constexpr int ESZ = OUT16 ? 2 : 4;
-  constexpr int ROWB = CT * ESZ;          // bytes of a wave's output row
+  constexpr int ROWB = CT * ESZ;          // bytes of an output row of the tile
   constexpr int CHUNKS = ROWB / 16;
   constexpr int SWM = (CHUNKS < 16 ? CHUNKS : 16) - 1;
-  constexpr int OUT_BYTES = 4 * 32 * ROWB;  // the 4 waves' 32 output rows each
+  constexpr int OUT_BYTES = kGRows * ROWB;  // the staged output tile
   constexpr int A_BYTES = 2 * kGRows * kGK * 2;
   __shared__ __attribute__((aligned(16))) char smem[OUT_BYTES > A_BYTES ? OUT_BYTES : A_BYTES];
   // two 16 KB stages of 128 rows x 8 chunks of 16 bytes
@@ -98,13 +104,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict
       sA[buf][row * 8 + (ch ^ (row & 7))] = r[k];
     }
   };
-  // Bias of this lane's columns, and the wave's residual rows (whole 16-byte pieces, in the
-  // order the epilogue stages them), loaded before the K loop so that their latency is hidden
-  // behind it.
+  // The wave's 32 residual rows of the tile (whole 16-byte pieces, in the order the epilogue
+  // stages them), loaded before the K loop so that their latency is hidden behind it.
   constexpr int RPT = 32 * CHUNKS / 64;  // residual pieces per lane
-  float bcol[NCT];
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) bcol[c] = bias ? bias[(ct0 + c) * 16 + (lane & 15)] : 0.f;
   const int64_t wrow0 = row0 + wave * 32;
   const int64_t col0b = static_cast<int64_t>(ct0) * 16 * ESZ;  // byte offset of the tile
   g_u32x4_t rres[RPT];
@@ -118,21 +120,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict
                                                     g * cout * ESZ + col0b + ch * 16);
     }
   }
-  auto load_b = [&](int st, g_u32x4_t (&b)[2][NCT]) __attribute__((always_inline)) {
+  // Wave w owns the 16-column tile ct0 + w for all 128 rows: each weight fragment is loaded
+  // by one wave only, and the rows' fragments are read from LDS by all four.
+  const int ctw = ct0 + wave;
+  auto load_b = [&](int st, g_u32x4_t (&b)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int c = 0; c < NCT; ++c)
-        b[ks][c] = *reinterpret_cast<const g_u32x4_t*>(
-            Wp + (static_cast<int64_t>(ct0 + c) * ksteps + st * 2 + ks) * 512 + lane * 8);
+      b[ks] = *reinterpret_cast<const g_u32x4_t*>(
+          Wp + (static_cast<int64_t>(ctw) * ksteps + st * 2 + ks) * 512 + lane * 8);
   };
-
-  g_f32x4_t acc[2][NCT];
+  g_f32x4_t acc[8];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) acc[rt][c] = g_f32x4_t{0.f, 0.f, 0.f, 0.f};
-  g_u32x4_t ra[4], bw[2][NCT], bn[2][NCT];
+  for (int rb = 0; rb < 8; ++rb) acc[rb] = g_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  g_u32x4_t ra[4], bw[2], bn[2];
   load_a(0, ra);
   store_a(0, ra);
   load_b(0, bw);
@@ -147,49 +147,43 @@ __global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int row = wave * 32 + rt * 16 + (lane & 15);
+      for (int rb = 0; rb < 8; ++rb) {
+        const int row = rb * 16 + (lane & 15);
         const int ch = ks * 4 + (lane >> 4);
         const g_u32x4_t a = sA[cur][row * 8 + (ch ^ (row & 7))];
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) acc[rt][c] = gemm_mfma<EK>(a, bw[ks][c], acc[rt][c]);
+        acc[rb] = gemm_mfma<EK>(a, bw[ks], acc[rb]);
       }
     if (more) {
       store_a(cur ^ 1, ra);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) bw[ks][c] = bn[ks][c];
+      for (int ks = 0; ks < 2; ++ks) bw[ks] = bn[ks];
     }
     __syncthreads();
   }
-  // Epilogue.  Each wave stages its 32 output rows in LDS (16-byte chunks XOR-swizzled by
-  // row), with the residual rows fetched first as whole pieces into the same places, then
-  // writes whole 16-byte pieces of rows.  v = act(acc + bias) + residual, rounded once.
-  // After the loop's last barrier no wave reads the A stages any more.
-  char* sO = smem + wave * 32 * ROWB;
+  // Epilogue: one staging tile of 128 rows for the workgroup (16-byte chunks XOR-swizzled by
+  // row); residual pieces first (each wave its 32 rows), then every wave its 16 columns.
+  char* sO = smem;
   if (res) {
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int idx = lane + k * 64;
-      const int r = idx / CHUNKS, ch = idx % CHUNKS;
+      const int r = wave * 32 + idx / CHUNKS, ch = idx % CHUNKS;
       *reinterpret_cast<g_u32x4_t*>(sO + r * ROWB + ((ch ^ (r & SWM)) << 4)) = rres[k];
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the pieces are in LDS (only this wave
-                                         // reads them)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __syncthreads();
   }
+  {
+    const int col = wave * 16 + (lane & 15);
+    const float bc = bias ? bias[ctw * 16 + (lane & 15)] : 0.f;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      const int col = c * 16 + (lane & 15);  // within the tile
-      const float bc = bcol[c];
+    for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = rt * 16 + (lane >> 4) * 4 + i;
+        const int r = rb * 16 + (lane >> 4) * 4 + i;
         const int byte = col * ESZ;
         char* dst = sO + r * ROWB + (((byte >> 4) ^ (r & SWM)) << 4) + (byte & 15);
-        float v = apply_act(acc[rt][c][i] + bc, act);
+        float v = apply_act(acc[rb][i] + bc, act);
         if (res) {
           if constexpr (OUT16)
             v += from16<EK>(*reinterpret_cast<const uint16_t*>(dst));
@@ -201,16 +195,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict
         else
           *reinterpret_cast<float*>(dst) = v;
       }
-    }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's staging writes are done
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __syncthreads();
 #pragma unroll
   for (int k = 0; k < 32 * CHUNKS / 64; ++k) {
     const int idx = lane + k * 64;
     const int r = idx / CHUNKS, ch = idx % CHUNKS;
+    const int tr = wave * 32 + r;
     if (wrow0 + r < n)
       *reinterpret_cast<g_u32x4_t*>(static_cast<char*>(Y) + (wrow0 + r) * cout * ESZ + col0b +
                                     ch * 16) =
-          *reinterpret_cast<const g_u32x4_t*>(sO + r * ROWB + ((ch ^ (r & SWM)) << 4));
+          *reinterpret_cast<const g_u32x4_t*>(sO + tr * ROWB + ((ch ^ (tr & SWM)) << 4));
   }
 }
 
