@@ -25,7 +25,11 @@ namespace {
 
 constexpr int kSlotRows = 128;       // rows per partial-sum slot
 constexpr int kPassBatch = 4;        // batch entries one partials pass accumulates
-constexpr int kApplyRows = 8;        // rows each apply thread handles per step
+// Rows each apply thread handles per step of its stride.  Two: with 8 the 128-channel apply of
+// 209K bf16 rows took 26.4 us, with 2 24.2 us (64 channels, 268K rows: 20.0 -> 15.9 us; 32
+// channels, 1.2M rows: 32.7 -> 27.7 us); 16 rows, or a grid without the 1024-workgroup cap,
+// were slower still.
+constexpr int kApplyRows = 2;
 
 __device__ __forceinline__ float ld_val(const float* p) { return *p; }
 __device__ __forceinline__ float ld_val(const uint16_t* p) { return bf16_to_f32(*p); }
@@ -118,8 +122,11 @@ __device__ __forceinline__ void word_to_f32(const uint4& w, float* f) {
 // words, t / words) owns word w (channels E*w ...) and rows rl, rl + lanes, ... of the slot,
 // all loaded before any is summed; per-channel sums for 4 batch entries per pass, then, one
 // entry at a time, a fixed-order sum over the row lanes and over each group's channels.
-// A block covers spb slots (spb = max(1, 16 / words), so that every thread has about 8 rows)
-// and writes their sum into the first of them and zeros into the rest: finalize adds all.
+// A block covers spb slots, spb = max(4, 16 / words), so that every thread has at least 8 rows
+// and a block's reduction is paid once per 512 rows or more (max(1, 16 / words) took 21.3
+// against 20.1 us at 128 bf16 channels and 209K rows, 16.3 against 13.6 us at 64 channels and
+// 268K rows).  It writes their sum into the first of them and zeros into the rest: finalize
+// adds all.
 template <typename T>
 __global__ __launch_bounds__(256) void k_gn_partials_w(const uint4* __restrict__ x, int64_t n,
                                                        int channels, int groups,
@@ -133,7 +140,7 @@ __global__ __launch_bounds__(256) void k_gn_partials_w(const uint4* __restrict__
   const int base = blockIdx.y * kPassBatch;
   const int words = channels / E;
   const int lanes = 256 / words;
-  const int spb = words >= 16 ? 1 : 16 / words;
+  const int spb = 16 / words > 4 ? 16 / words : 4;
   const int64_t slot = static_cast<int64_t>(blockIdx.x) * spb;
   const int MAXR = spb * kSlotRows;            // rows of this block
   const int w = t % words, rl = t / words;
@@ -494,7 +501,7 @@ ssc_status gn_partials_launch(const void* x, int32_t dtype, int64_t n, int32_t c
   if (row_bytes % 16 == 0 && row_bytes / 16 <= 256 && channels <= 1024 && aligned(x, 16)) {
     const auto* x4 = static_cast<const uint4*>(x);
     const int64_t words = row_bytes / 16, slots = gn_slots(n);
-    const int64_t spb = words >= 16 ? 1 : 16 / words;
+    const int64_t spb = 16 / words > 4 ? 16 / words : 4;
     const dim3 gw(static_cast<unsigned>((slots + spb - 1) / spb), grid.y);
     if (dtype == SSC_F32)
       k_gn_partials_w<float><<<gw, 256, 0, s>>>(x4, n, channels, groups, c4, batch, slots, p4);
