@@ -1181,7 +1181,7 @@ __global__ __launch_bounds__(256, 2) void k_linear_stream(const uint16_t* __rest
       const u32x4_t v =
           *reinterpret_cast<const u32x4_t*>(sOut + row * L::ROWB + ((ch ^ (row & L::SWM)) << 4));
       if (row0 + row < n)
-        *reinterpret_cast<u32x4_t*>(static_cast<char*>(Y) + (row0 + row) * L::ROWB + ch * 16) = v;
+        st16(reinterpret_cast<u32x4_t*>(static_cast<char*>(Y) + (row0 + row) * L::ROWB + ch * 16), v);
     }
   }
 }

@@ -204,9 +204,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_rows(const uint16_t* __restrict
     const int r = idx / CHUNKS, ch = idx % CHUNKS;
     const int tr = wave * 32 + r;
     if (wrow0 + r < n)
-      *reinterpret_cast<g_u32x4_t*>(static_cast<char*>(Y) + (wrow0 + r) * cout * ESZ + col0b +
-                                    ch * 16) =
-          *reinterpret_cast<const g_u32x4_t*>(sO + tr * ROWB + ((ch ^ (tr & SWM)) << 4));
+      st16(reinterpret_cast<g_u32x4_t*>(static_cast<char*>(Y) + (wrow0 + r) * cout * ESZ + col0b +
+                                        ch * 16),
+           *reinterpret_cast<const g_u32x4_t*>(sO + tr * ROWB + ((ch ^ (tr & SWM)) << 4)));
   }
 }
 
@@ -333,9 +333,9 @@ __global__ __launch_bounds__(256, (OUT16 || KS < 4) ? 4 : 3) void k_gemm_rows_na
     const int idx = lane + k * 64;
     const int r = idx / CHUNKS, ch = idx % CHUNKS;
     if (wrow0 + r < n)
-      *reinterpret_cast<g_u32x4_t*>(static_cast<char*>(Y) + (wrow0 + r) * cout * ESZ + col0b +
-                                    ch * 16) =
-          *reinterpret_cast<const g_u32x4_t*>(sO + r * ROWB + ((ch ^ (r & SWM)) << 4));
+      st16(reinterpret_cast<g_u32x4_t*>(static_cast<char*>(Y) + (wrow0 + r) * cout * ESZ + col0b +
+                                        ch * 16),
+           *reinterpret_cast<const g_u32x4_t*>(sO + r * ROWB + ((ch ^ (r & SWM)) << 4)));
   }
 }
 

@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void k_layer_norm_w(const uint4* x, int64_t n,
 #pragma unroll
       for (int e = 0; e < E; ++e)
         st_val(&o[e], apply_act(fmaf(f[k][e] * rstd, gm[e], bt[e]), act));
-      out[row * WORDS + w] = *reinterpret_cast<const uint4*>(o);
+      st16(&out[row * WORDS + w], *reinterpret_cast<const uint4*>(o));
     }
   }
 }
