@@ -216,19 +216,31 @@ __global__ void k_maxpool_bf16x8(const uint4* __restrict__ feats, int32_t words,
        g += stride) {
     const int64_t p = g / words;
     const int w = static_cast<int>(g - p * words);
-    const int32_t* ch = children + p * 8;
-    int k0 = 0;
-    while (k0 < 7 && ch[k0] < 0) ++k0;  // every parent has at least one site
-    if (ch[k0] < 0) {
-      out[g] = make_uint4(0u, 0u, 0u, 0u);
-      continue;
-    }
-    uint4 best = feats[static_cast<int64_t>(ch[k0]) * words + w];
-    for (int k = k0 + 1; k < 8; ++k) {
-      if (ch[k] < 0) continue;
-      const uint4 v = feats[static_cast<int64_t>(ch[k]) * words + w];
+    // The parent's 8 child slots (32-byte aligned: the slot array starts on a 256-byte boundary
+    // of the workspace) in two 16-byte loads, then every present child's word loaded before any
+    // is compared, so that a thread has all its loads in flight at once (a loop of index load,
+    // branch and feature load kept one in flight).  The maximum is taken in child order, keeping
+    // the first of equal values, as before.
+    const int4 c0 = *reinterpret_cast<const int4*>(children + p * 8);
+    const int4 c1 = *reinterpret_cast<const int4*>(children + p * 8 + 4);
+    const int32_t idx[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      v[k] = idx[k] >= 0 ? feats[static_cast<int64_t>(idx[k]) * words + w]
+                         : make_uint4(0u, 0u, 0u, 0u);
+    uint4 best = make_uint4(0u, 0u, 0u, 0u);  // every parent has a site; zeros if none
+    bool have = false;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (idx[k] < 0) continue;
+      if (!have) {
+        best = v[k];
+        have = true;
+        continue;
+      }
       uint32_t* bb = reinterpret_cast<uint32_t*>(&best);
-      const uint32_t* vv = reinterpret_cast<const uint32_t*>(&v);
+      const uint32_t* vv = reinterpret_cast<const uint32_t*>(&v[k]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // two bf16 per word: keep the larger of each half, bits and all
