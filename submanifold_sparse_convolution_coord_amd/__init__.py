@@ -16,6 +16,7 @@ reuses it while the coordinate tensor is unchanged (the pages' spatial cache).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import weakref
@@ -152,8 +153,23 @@ def _check(status: int, what: str):
         raise SscError(status, what)
 
 
+# torch's raw current-stream lookup (one C call) when this torch has it; the Stream object
+# route costs about 2 us per call, which small layers pay on every launch.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(dev: torch.device) -> ctypes.c_void_p:
+    if _raw_stream is not None:
+        idx = dev.index if dev.index is not None else torch.cuda.current_device()
+        return ctypes.c_void_p(_raw_stream(idx))
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _on(dev: torch.device):
+    """torch.cuda.device(dev), or nothing when dev is already the current device."""
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(dev)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -200,7 +216,7 @@ def build_index(coords: torch.Tensor, batch: int, grid: Sequence[int],
     g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
     ws = _workspace(lib.ssc_index_workspace_bytes_ex(n, int(batch), g, INDEX_METHODS[method]),
                     dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.ssc_build_index_ex(_ptr(coords), n, int(batch), g, _ptr(nbr), _ptr(ws),
                                     ws.numel(), 1 if check else 0, INDEX_METHODS[method],
                                     _stream(dev))
@@ -259,7 +275,7 @@ def build_plan(nbr: torch.Tensor, coords: Optional[torch.Tensor] = None, batch: 
         g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
     buf = _workspace(lib.ssc_plan_bytes(n), dev)
     ws = _workspace(lib.ssc_plan_workspace_bytes(n), dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.ssc_build_plan(_ptr(nbr), None if coords is None else _ptr(coords), n,
                                 int(batch), g, _ptr(buf), buf.numel(), _ptr(ws), ws.numel(),
                                 _stream(dev))
@@ -360,7 +376,7 @@ def subm_conv3d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tens
         if out is None:
             out = torch.empty((n, cout), dtype=odt, device=dev)
         ws = _workspace(lib.ssc_subm_conv3d_workspace_bytes(n, cin, cout, din), dev)
-        with torch.cuda.device(dev):
+        with _on(dev):
             st = lib.ssc_subm_conv3d(_ptr(x), din, _ptr(weight), _ptr(bias), _ptr(nbr), n, cin,
                                      cout, _ptr(out), dout, _ptr(ws), ws.numel(), _stream(dev))
         _check(st, "ssc_subm_conv3d")
@@ -373,16 +389,18 @@ def subm_conv3d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tens
     if out is None:
         out = torch.empty((n, cout), dtype=odt, device=dev)
     epi = _epilogue(n, cout, odt, act, residual, gn)
-    ws = _workspace(lib.ssc_conv_workspace_bytes(cin, cout, din), dev)
-    with torch.cuda.device(dev):
+    need = lib.ssc_conv_workspace_bytes(cin, cout, din)
+    ws = _workspace(need, dev) if need > 0 else None  # none when nothing is re-laid out
+    wsn = ws.numel() if ws is not None else 0
+    with _on(dev):
         if epi is None:
             st = lib.ssc_subm_conv3d_plan(_ptr(x), din, _ptr(weight), _ptr(bias), _ptr(plan.buf),
-                                          n, cin, cout, _ptr(out), dout, _ptr(ws), ws.numel(),
+                                          n, cin, cout, _ptr(out), dout, _ptr(ws), wsn,
                                           _stream(dev))
         else:
             st = lib.ssc_subm_conv3d_plan_ex(_ptr(x), din, _ptr(weight), _ptr(bias),
                                              _ptr(plan.buf), n, cin, cout, _ptr(out), dout,
-                                             ctypes.byref(epi), _ptr(ws), ws.numel(),
+                                             ctypes.byref(epi), _ptr(ws), wsn,
                                              _stream(dev))
     _check(st, "ssc_subm_conv3d_plan")
     return out
@@ -405,7 +423,7 @@ def linear(x: torch.Tensor, weight, bias: Optional[torch.Tensor],
         out = torch.empty((n, cout), dtype=odt, device=dev)
     epi = _epilogue(n, cout, odt, act, residual, gn)
     ws = _workspace(lib.ssc_conv_workspace_bytes(cin, cout, din), dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         if epi is None:
             st = lib.ssc_linear(_ptr(x), din, _ptr(weight), _ptr(bias), n, cin, cout, _ptr(out),
                                 dout, _ptr(ws), ws.numel(), _stream(dev))
@@ -446,7 +464,7 @@ def gn_finalize(parts: GroupNormPartials, eps: float = 1e-5) -> torch.Tensor:
     dev = parts.buf.device
     stats = torch.empty((parts.batch, parts.groups, 2), dtype=torch.float32, device=dev)
     lib = load_library()
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.ssc_gn_finalize(_ptr(parts.buf), parts.n, parts.batch, parts.groups,
                                  float(eps), _ptr(stats), _stream(dev))
     _check(st, "ssc_gn_finalize")
@@ -540,7 +558,7 @@ def downsample2(coords: torch.Tensor, batch: int, grid: Sequence[int],
     parent = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
     result = torch.zeros(2, dtype=torch.int64, device=dev)
     ws = _workspace(lib.ssc_downsample_workspace_bytes(n), dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.ssc_downsample2(_ptr(coords), n, int(batch), g, _ptr(feats), dt, ch, _ptr(out_c),
                                  _ptr(out_f), _ptr(parent), _ptr(result), _ptr(ws), ws.numel(),
                                  _stream(dev))
@@ -572,7 +590,7 @@ def spatial2channel2(coords: torch.Tensor, batch: int, grid: Sequence[int],
     parent = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
     result = torch.zeros(2, dtype=torch.int64, device=dev)
     ws = _workspace(lib.ssc_downsample_workspace_bytes(n), dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.ssc_spatial2channel2(_ptr(coords), n, int(batch), g, _ptr(feats), dt, ch,
                                       _ptr(out_c), _ptr(out_f), _ptr(parent), _ptr(result),
                                       _ptr(ws), ws.numel(), _stream(dev))
@@ -614,7 +632,7 @@ def subdivide2(coords: torch.Tensor, grid: Sequence[int], feats: Optional[torch.
     out_c = torch.empty((8 * n, 4), dtype=torch.int32, device=dev)
     out_f = torch.empty((8 * n, ch), dtype=feats.dtype, device=dev) if ch else None
     lib = load_library()
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.ssc_subdivide2(_ptr(coords), n, g, _ptr(feats), dt, ch, _ptr(out_c), _ptr(out_f),
                                 _stream(dev))
     _check(st, "ssc_subdivide2")
@@ -642,7 +660,7 @@ def pack_weights(weight: torch.Tensor, flip: bool = False, pair: bool = False) -
     lib = load_library()
     dev = weight.device
     buf = _workspace(lib.ssc_packed_weight_bytes(taps, cin, cout), dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.ssc_pack_weights_ex(_ptr(weight), taps, cin, cout,
                                      (SSC_PACK_FLIP if flip else 0) | (SSC_PACK_PAIR if pair else 0),
                                      _ptr(buf), buf.numel(), _stream(dev))
@@ -678,7 +696,7 @@ def subm_conv3d_pair(x: torch.Tensor, packed1: PackedWeight, bias1: Optional[tor
     dev = x.device
     if out is None:
         out = torch.empty((n, packed2.cout), dtype=odt, device=dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.ssc_subm_conv3d_pair_packed(_ptr(x), _ptr(packed1.buf), _ptr(bias1),
                                              _ptr(plan.buf), n, packed1.cin, packed1.cout,
                                              _ptr(packed2.buf), _ptr(bias2), packed2.cout,
@@ -711,7 +729,7 @@ def subm_conv3d_packed(x: torch.Tensor, packed: PackedWeight, bias: Optional[tor
     if out is None:
         out = torch.empty((n, packed.cout), dtype=odt, device=dev)
     epi = _epilogue(n, packed.cout, odt, act, residual, gn)
-    with torch.cuda.device(dev):
+    with _on(dev):
         if epi is None:
             st = lib.ssc_subm_conv3d_packed(_ptr(x), _ptr(packed.buf), _ptr(bias), _ptr(plan.buf),
                                             n, packed.cin, packed.cout, _ptr(out), dout,
@@ -740,7 +758,7 @@ def _linear_packed(x, packed, bias, out_dtype, out, act, residual, gn):
     if out is None:
         out = torch.empty((n, packed.cout), dtype=odt, device=dev)
     epi = _epilogue(n, packed.cout, odt, act, residual, gn)
-    with torch.cuda.device(dev):
+    with _on(dev):
         if epi is None:
             st = lib.ssc_linear_packed(_ptr(x), _ptr(packed.buf), _ptr(bias), n, packed.cin,
                                        packed.cout, _ptr(out), dout, _stream(dev))
